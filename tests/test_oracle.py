@@ -1,0 +1,142 @@
+"""Pins for the CPU oracle, against facts the pages and the mathematics fix.
+
+* the worked example: matrix of Eq. (2.1), x and root values of Figure 4.2,
+  row roots of Eq. (2.4) (page "Right Multiplication on Grammar-Compressed
+  Matrices", section 2 and Figure 4.2);
+* exact rational dense products on small random matrices (non-square, so a
+  transposed operand fails), with every entry and x exact;
+* compensated summation on sums where plain fp64 summation loses the answer;
+* closed forms: x = ones gives row sums, x = e_j gives column j;
+* Boolean and int64 products against brute force; the BFS fixpoint against a
+  Warshall closure (a different algorithm) and a path graph whose pass count
+  is known in closed form.
+"""
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+U = 2.0 ** -53
+
+
+def _we_dense(we):
+    return we["M"]["rows"], we["x"]["values"]
+
+
+def test_worked_example(oracle_mod, worked_example):
+    rows, x = _we_dense(worked_example)
+    rp, col, val = oracle_mod.dense_to_csr(rows)
+    y, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    roots = worked_example["C"]["row_roots"]
+    rv = worked_example["root_values"]
+    expect = np.array([rv["N%d" % r] for r in roots])
+    assert np.all(np.abs(y - expect) <= 1e-12 * absum)
+    # the same rows agree with the exact rational product of Eq. (2.1) and x
+    exact = oracle_mod.dense_product_exact(rows, x)
+    for yi, ei in zip(y, exact):
+        assert abs(Fraction(yi) - ei) <= Fraction(4 * U) * abs(ei)
+
+
+def _random_dense(rng, n, m, density, kind):
+    M = []
+    for _ in range(n):
+        row = []
+        for _ in range(m):
+            if rng.random() < density:
+                if kind == "int":
+                    row.append(rng.choice([1, 2, -3, 7]))
+                else:
+                    row.append(rng.uniform(-4, 4))
+            else:
+                row.append(0)
+        M.append(row)
+    return M
+
+
+@pytest.mark.parametrize("n,m,density", [(1, 1, 1.0), (5, 17, 0.4), (17, 5, 0.6), (40, 64, 0.3), (64, 3, 0.9),
+                                         (9, 30, 0.0)])
+def test_dense_exact(oracle_mod, n, m, density):
+    rng = random.Random(n * 1000 + m)
+    M = _random_dense(rng, n, m, density, "float")
+    x = [rng.uniform(-2, 2) for _ in range(m)]
+    rp, col, val = oracle_mod.dense_to_csr(M)
+    y, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    exact = oracle_mod.dense_product_exact(M, x)
+    for r in range(n):
+        a = sum(abs(Fraction(M[r][j]) * Fraction(x[j])) for j in range(m))
+        assert abs(Fraction(y[r]) - exact[r]) <= Fraction(3 * U) * a + Fraction(2 * U) * abs(exact[r])
+        assert abs(absum[r] - float(a)) <= 1e-12 * float(a)
+    # the row-sampled entry point returns the same rows one by one
+    rows = np.arange(n)[::-1].copy()
+    ys, _ = oracle_mod.spmv_f64_rows(rows, rp, col, val, x)
+    assert np.array_equal(ys, y[rows])
+
+
+def test_compensated_sum(oracle_mod):
+    # plain left-to-right fp64 summation returns 0.0 for both rows
+    rows = [[1e16, 1.0, -1e16], [1.0, 1e100, 1.0, -1e100]]
+    rp = np.array([0, 3, 7], np.int64)
+    col = np.array([0, 1, 2, 0, 1, 2, 3], np.int32)
+    val = np.array(rows[0] + rows[1], np.float64)
+    y, _ = oracle_mod.spmv_f64(rp, col, val, np.ones(4))
+    assert y[0] == 1.0 and y[1] == 2.0
+
+
+def test_closed_forms_genotype(oracle_mod, synth_mod):
+    rp, col, val = synth_mod.genotype(synth_mod.GENOTYPE_512x4096)
+    n, m = 512, 4096
+    # x = ones: y = row sums of the stored genotype values (exact integers)
+    y, _ = oracle_mod.spmv_f64(rp, col, val, np.ones(m))
+    sums = np.add.reduceat(val.astype(np.int64), rp[:-1]) * (np.diff(rp) > 0)
+    assert np.array_equal(y, sums.astype(np.float64))
+    # x = e_j: y = column j
+    import scipy.sparse as sp
+    A = sp.csr_matrix((val.astype(np.float64), col, rp), shape=(n, m)).toarray()
+    for j in (0, 1, 777, m - 1):
+        e = np.zeros(m)
+        e[j] = 1.0
+        y, _ = oracle_mod.spmv_f64(rp, col, val, e)
+        assert np.array_equal(y, A[:, j])
+    yi = oracle_mod.spmv_i64(rp, col, val, np.arange(m, dtype=np.int64) - 2000)
+    assert np.array_equal(yi, A.astype(np.int64) @ (np.arange(m, dtype=np.int64) - 2000))
+
+
+def test_bool_and_int_brute_force(oracle_mod):
+    rng = random.Random(7)
+    for n, m in [(1, 1), (13, 29), (50, 50), (7, 1)]:
+        M = _random_dense(rng, n, m, 0.2, "int")
+        rp, col, _ = oracle_mod.dense_to_csr(M)
+        x = [rng.random() < 0.3 for _ in range(m)]
+        yb = oracle_mod.spmv_bool(rp, col, np.array(x, np.uint8))
+        for r in range(n):
+            assert yb[r] == any(M[r][j] != 0 and x[j] for j in range(m))
+        vi = np.array([M[r][j] for r in range(n) for j in range(m) if M[r][j] != 0], np.int8)
+        xi = [rng.randrange(-1000, 1000) for _ in range(m)]
+        yi = oracle_mod.spmv_i64(rp, col, vi, np.array(xi, np.int64))
+        for r in range(n):
+            assert yi[r] == sum(M[r][j] * xi[j] for j in range(m))
+
+
+def test_bfs_path_closed_form(oracle_mod):
+    # out-list of node i is {i+1}: every node reaches n-1, one new node per pass
+    n = 40
+    rp = np.arange(n + 1, dtype=np.int64).clip(max=n - 1)
+    col = np.arange(1, n, dtype=np.int32)
+    vis, counts = oracle_mod.bfs(rp, col, [n - 1])
+    assert vis.all()
+    assert list(counts) == [1] * (n - 1) + [0]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_bfs_vs_warshall(oracle_mod, seed):
+    rng = random.Random(seed)
+    n = 45
+    adj = [sorted(rng.sample(range(n), rng.choice([0, 1, 1, 2, 3]))) for _ in range(n)]
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum([len(a) for a in adj])
+    col = np.array([j for a in adj for j in a], np.int32)
+    srcs = rng.sample(range(n), 3)
+    vis, counts = oracle_mod.bfs(rp, col, srcs)
+    assert sorted(np.nonzero(vis)[0].tolist()) == oracle_mod.reverse_reachable(adj, srcs)
+    assert counts[-1] == 0 and counts.sum() + len(srcs) == vis.sum()
