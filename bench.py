@@ -1,0 +1,227 @@
+"""Benchmark: the right product y = M x swept over a layered RePair grammar.
+
+One step = one sweep (terminal array, every level with its emission, final
+emission) over the uploaded grammar with x already in HBM.  The grammar is
+built and uploaded before the timed region (a one-time cost, reported
+separately as on the pages' Table B.1).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Prints one JSON line (metric, value = nnz/s, roofline of the level kernel,
+CPU baseline = the oracle on the host cores, footprint vs CSR).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def level_bytes(lay, elem, yelem):
+    """Algorithmic bytes of each level launch k = 1..L: child indices (8 B per
+    binary node), one write per completed node, one read of every value of
+    level k-1 (the terminal array for k = 1), and the emission of level k-1
+    (erow + eoff per group, 4 B epos per root, y read and written per group)."""
+    meta = lay["level_meta"]
+    L = meta.shape[0] - 1
+    eoff = lay["eoff"]
+    out = []
+    for k in range(1, L + 1):
+        nb, npt = int(meta[k][0]), int(meta[k][1])
+        if k == 1:
+            prev_w = int(lay["alpha"])
+        else:
+            prev_w = int(meta[k - 1][0] + meta[k - 1][1])
+        g0, ng = int(meta[k - 1][6]), int(meta[k - 1][7])
+        roots = int(eoff[g0 + ng] - eoff[g0]) if ng else 0
+        b = 8 * nb + elem * (nb + npt) + elem * prev_w + 8 * ng + 4 * roots + 2 * yelem * ng
+        out.append(b)
+    return np.array(out, np.float64)
+
+
+def cpu_baseline(rp, col, val, x64, nnz, budget_s=10.0):
+    import oracle
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.spmv_f64(rp, col, val, x64)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 50:
+            break
+    return {"value": nnz * passes / el, "unit": "nnz/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full matrix, {passes} fp64 compensated CSR passes ({el:.1f} s)"}
+
+
+def csr_comparator(torch, rp, col, val, x, steps):
+    """rocSPARSE CSR SpMV through torch.sparse (context: time and footprint)."""
+    try:
+        n = rp.shape[0] - 1
+        m = x.numel()
+        crow = torch.from_numpy(rp.astype(np.int32)).cuda()
+        ci = torch.from_numpy(col).cuda()
+        vv = torch.from_numpy(val.astype(np.float32)).cuda()
+        A = torch.sparse_csr_tensor(crow, ci, vv, size=(n, m))
+        y = torch.mv(A, x)
+        for _ in range(3):
+            y = torch.mv(A, x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            y = torch.mv(A, x)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        nbytes = crow.numel() * 4 + ci.numel() * 4 + vv.numel() * 4 + x.numel() * 4 + y.numel() * 4
+        del A, crow, ci, vv
+        torch.cuda.empty_cache()
+        return {"ms_per_spmv": ms, "device_bytes": nbytes, "via": "torch.mv on a sparse CSR tensor (int32, fp32)"}
+    except Exception as e:  # context only
+        return {"error": str(e)[:200]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="genotype_20000x100000_f32")
+    ap.add_argument("--col-chunk", type=int, default=2000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-csr", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the sweep is a single-GPU engine here (multi-GPU sharding is a "
+              "design note, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    from grammar_compressed_sparse_amd import gcs, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    spec = wl["matrix"]
+    if not isinstance(spec, synth.GenotypeSpec):
+        raise SystemExit("bench.py times the genotype workloads; the graph BFS has its own test")
+    t = time.perf_counter()
+    rp, col, val = synth.genotype(spec)
+    nnz = int(rp[-1])
+    log(f"generated {spec.n_rows}x{spec.n_cols} nnz={nnz} in {time.perf_counter() - t:.1f}s")
+    t = time.perf_counter()
+    g = gcs.build_grammar(rp, col, val, n_cols=spec.n_cols, col_chunk=args.col_chunk)
+    build_s = time.perf_counter() - t
+    st = g.stats()
+    log(f"grammar built in {build_s:.1f}s: {st}")
+    lay = g.layout()
+    lay["alpha"] = st["n_terminals"]
+    policy = gcs.PLUS_F32 if wl["dtype"] == "f32" else gcs.PLUS_F64
+    xdt = np.float32 if wl["dtype"] == "f32" else np.float64
+    elem = 4 if wl["dtype"] == "f32" else 8
+
+    torch.cuda.init()
+    t = time.perf_counter()
+    dev = gcs.upload(g, policy)
+    torch.cuda.synchronize()
+    upload_s = time.perf_counter() - t
+    xs = [torch.from_numpy(synth.normal(spec.n_cols, s).astype(xdt)).cuda() for s in wl["x_seeds"]]
+    y = dev.new_y()
+    log(f"uploaded {dev.device_bytes / 1e6:.1f} MB in {upload_s:.2f}s; {dev.sweep_launches()} launches per sweep")
+
+    # correctness on sampled rows (outside the timed region)
+    dev.sweep_right(xs[0], y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, spec.n_rows, max(1, spec.n_rows // 512)), [spec.n_rows - 1]]))
+    yo, absum = oracle.spmv_f64_rows(rows, rp, col, val, xs[0].cpu().numpy().astype(np.float64))
+    err = np.abs(y.cpu().numpy().astype(np.float64)[rows] - yo) / np.maximum(absum, 1e-300)
+    tol = 1e-5 if elem == 4 else 1e-12
+    log(f"sampled-row check: {rows.size} rows, max rel err {err.max():.2e} (tol {tol})")
+    if not np.all(err <= tol):
+        raise SystemExit("sweep disagrees with the oracle")
+
+    for i in range(args.warmup):
+        dev.sweep_right(xs[i % len(xs)], y)
+    torch.cuda.synchronize()
+    dev.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dev.sweep_right_profiled(xs[i % len(xs)], y)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = dev.profile_end()  # (steps, launches)
+    ms_per_step = elapsed * 1e3 / args.steps
+    L = st["depth"]
+    # launch 0 = terminal array, 1..L = levels (with emission of the previous level), L+1 = last emission
+    lvl_ms = launch_ms[:, 1:L + 1].mean(axis=0)
+    lb = level_bytes(lay, elem, elem)
+    achieved = lb.sum() / (lvl_ms.sum() * 1e-3) / 1e9
+    per_level = [{"k": k + 1, "width": int(lay["level_meta"][k + 1][0] + lay["level_meta"][k + 1][1]),
+                  "bytes": int(lb[k]), "us": float(lvl_ms[k] * 1e3),
+                  "GBs": float(lb[k] / (lvl_ms[k] * 1e-3) / 1e9)} for k in range(L)]
+    widest = int(np.argmax([p["width"] for p in per_level])) if per_level else 0
+
+    csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
+    eng_bytes = dev.device_bytes + xs[0].numel() * elem + y.numel() * elem
+    csr = None if args.no_csr else csr_comparator(torch, rp, col, val, xs[0], min(args.steps, 20))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(rp, col, val, xs[0].cpu().numpy().astype(np.float64), nnz)
+
+    value = nnz * args.steps / elapsed
+    out = {
+        "metric": "nnz/s for y=Mx sweep; achieved HBM GB/s (% peak); device bytes vs CSR",
+        "value": value,
+        "unit": "nnz/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if elem == 4 else "f64",
+        "data": "synthetic (seeded genotype mosaic)",
+        "config": {
+            "workload": args.workload,
+            "n_rows": spec.n_rows, "n_cols": spec.n_cols, "nnz": nnz,
+            "founders": spec.founders, "seg_mean": spec.seg_mean, "mu": spec.mu, "seed": spec.seed,
+            "vectors": len(xs),
+            "grammar": {k: st[k] for k in ("n_rules", "n_passthrough", "depth", "max_width", "c_len",
+                                           "n_terminals", "n_tiles", "n_emit_groups")},
+            "build_s": build_s, "upload_s": upload_s,
+            "launches_per_sweep": int(launch_ms.shape[1]),
+            "grammar_bytes_per_s": (8 * st["n_rules"] + 8 * st["n_emit_groups"] + 4 * st["c_len"] +
+                                    8 * st["n_terminals"]) / (ms_per_step * 1e-3),
+            "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
+            "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
+            "csr_rocsparse": csr,
+            "per_level_widest": per_level[widest] if per_level else None,
+            "level_us_total": float(lvl_ms.sum() * 1e3),
+            "leaf_us": float(launch_ms[:, 0].mean() * 1e3),
+            "final_emit_us": float(launch_ms[:, -1].mean() * 1e3) if launch_ms.shape[1] > L + 1 else 0.0,
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "level_kernel (all L launches of a sweep)",
+                     "bytes_per_sweep": float(lb.sum())},
+        "cpu_baseline": cpu,
+    }
+    if os.environ.get("GCS_BENCH_LEVELS"):
+        out["config"]["per_level"] = per_level
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

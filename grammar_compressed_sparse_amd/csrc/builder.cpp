@@ -1,0 +1,754 @@
+// Host builder: CSRV encoding -> RePair per tile -> merge -> levels ->
+// pass-through completion -> level-bucketed layout.
+//
+// Page: "Right Multiplication on Grammar-Compressed Matrices: A Streaming,
+// Memory-Bounded GPU Engine" (arXiv 2607.24971v1).
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <sched.h>
+#include <thread>
+
+#include "grammar.hpp"
+
+namespace gcs {
+
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+const char* last_error() { return g_err.c_str(); }
+
+int resolve_threads(int requested)
+{
+    if (requested > 0) return requested;
+    if (const char* e = std::getenv("OMP_NUM_THREADS")) {
+        int v = std::atoi(e);
+        if (v > 0) return v;
+    }
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+        int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    unsigned h = std::thread::hardware_concurrency();
+    return h ? (int)h : 1;
+}
+
+template <class F>
+static void parallel_for(int64_t n, int threads, F&& f)
+{
+    threads = (int)std::min<int64_t>(threads, std::max<int64_t>(n, 1));
+    if (threads <= 1) {
+        for (int64_t i = 0; i < n; ++i) f(i);
+        return;
+    }
+    std::atomic<int64_t> next{0};
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t)
+        pool.emplace_back([&] {
+            for (int64_t i; (i = next.fetch_add(1)) < n;) f(i);
+        });
+    for (auto& th : pool) th.join();
+}
+
+static double ms_since(std::chrono::steady_clock::time_point t0)
+{
+    return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// ---------------------------------------------------------------------------
+// levels, completion, layout
+// ---------------------------------------------------------------------------
+
+// Levels by Eq. (3.1): lvl(terminal) = 0, lvl(N -> AB) = 1 + max(lvl A, lvl B).
+// P(v) (plast) = the highest level among v's rule parents; C references do not
+// count (a root is emitted at its own level and never carried upward,
+// section 4.3).  Completion (section 4.2, Figure 3.1) gives v one shared chain
+// of pass-through copies at levels lvl(v)+1 .. P(v)-1, so each completed
+// level holds exactly the values alive across it.
+//
+// Layout of level k (section 4.3: levels contiguous, buffers alternate):
+//   [ binary nodes not needed above level k+1, in rule order
+//   | binary nodes carried upward ("block k"), by P descending
+//   | pass-through segment ]
+// The pass-through segment of level k is the concatenation, for origin levels
+// j = k-1, k-2, ..., 1, of the prefix of block j whose chains still reach
+// level k (P(v) >= k+1).  Because every block is sorted by P descending, the
+// prefix for level k is a prefix of the one for level k-1, so each origin's
+// copies read one contiguous source range of level k-1 and write one
+// contiguous range of level k: the pass-through segment is a handful of range
+// copies (at most k-1, merged when adjacent) with no per-node index.
+gcs_status finish_layout(Grammar& g)
+{
+    auto t0 = std::chrono::steady_clock::now();
+    const int64_t alpha = g.alpha(), R = g.nrules();
+    if (alpha + R >= (int64_t)INT32_MAX) {
+        set_error("grammar exceeds the 32-bit symbol space");
+        return GCS_ERANGE;
+    }
+    g.lvl.assign((size_t)R, 0);
+    g.plast.assign((size_t)R, 0);
+    int32_t L = 0;
+    for (int64_t i = 0; i < R; ++i) {
+        int32_t a = g.ra[i], b = g.rb[i];
+        int32_t la = a < alpha ? 0 : g.lvl[a - alpha], lb = b < alpha ? 0 : g.lvl[b - alpha];
+        int32_t l = 1 + std::max(la, lb);
+        g.lvl[i] = l;
+        L = std::max(L, l);
+        if (a >= alpha) g.plast[a - alpha] = std::max(g.plast[a - alpha], l);
+        if (b >= alpha) g.plast[b - alpha] = std::max(g.plast[b - alpha], l);
+    }
+    g.L = L;
+
+    // bucket rules by level; split into non-carried / carried (block)
+    std::vector<int64_t> cnt_lvl((size_t)L + 2, 0);
+    for (int64_t i = 0; i < R; ++i) cnt_lvl[g.lvl[i]]++;
+    std::vector<int64_t> lvl_start((size_t)L + 2, 0);
+    for (int k = 1; k <= L + 1; ++k) lvl_start[k] = lvl_start[k - 1] + cnt_lvl[k - 1];
+    std::vector<int32_t> order((size_t)R);
+    {
+        std::vector<int64_t> fill(lvl_start.begin(), lvl_start.end());
+        for (int64_t i = 0; i < R; ++i) order[fill[g.lvl[i]]++] = (int32_t)i;
+    }
+    std::vector<int64_t> nonc((size_t)L + 1, 0);   // non-carried count per level
+    std::vector<int32_t> pos((size_t)R, 0);         // position within own level
+    std::vector<int32_t> rank((size_t)R, -1);       // rank within own block
+    std::vector<std::vector<int32_t>> block_plast((size_t)L + 1);  // P values of block j, descending
+    for (int k = 1; k <= L; ++k) {
+        auto b = order.begin() + lvl_start[k], e = order.begin() + lvl_start[k + 1];
+        auto mid = std::stable_partition(b, e, [&](int32_t v) { return g.plast[v] < k + 2; });
+        std::stable_sort(mid, e, [&](int32_t u, int32_t v) { return g.plast[u] > g.plast[v]; });
+        nonc[k] = mid - b;
+        int32_t p = 0;
+        for (auto it = b; it != e; ++it) pos[*it] = p++;
+        int32_t rk = 0;
+        for (auto it = mid; it != e; ++it) {
+            rank[*it] = rk++;
+            block_plast[k].push_back(g.plast[*it]);
+        }
+    }
+    // cnt(j, k) = |{v in block j : P(v) >= k+1}| for j < k
+    auto cnt_reach = [&](int j, int k) -> int64_t {
+        const auto& bp = block_plast[j];
+        // bp descending: count of entries >= k+1
+        return std::upper_bound(bp.begin(), bp.end(), k + 1, [](int32_t key, int32_t x) { return key > x; }) -
+               bp.begin();
+    };
+    // offsets of origin blocks inside each level's pass-through segment
+    std::vector<std::vector<int64_t>> ptoff((size_t)L + 1);  // ptoff[k][j], j < k
+    g.lv.assign((size_t)L + 1, Level{});
+    g.wmax = 0;
+    g.pt_total = 0;
+    for (int k = 1; k <= L; ++k) {
+        ptoff[k].assign((size_t)k, 0);
+        int64_t o = 0;
+        for (int j = k - 1; j >= 1; --j) {
+            ptoff[k][j] = o;
+            o += cnt_reach(j, k);
+        }
+        g.lv[k].nb = cnt_lvl[k];
+        g.lv[k].npt = o;
+        g.pt_total += o;
+        g.wmax = std::max<int64_t>(g.wmax, cnt_lvl[k] + o);
+    }
+    auto align64 = [](int64_t v) { return (v + 63) & ~int64_t(63); };
+    g.buf_a = align64(alpha);
+    g.buf_b = g.buf_a + align64(g.wmax);
+    g.arena = L > 0 ? g.buf_b + align64(g.wmax) : alpha;
+    if (g.arena >= (int64_t)INT32_MAX) {
+        set_error("value arena exceeds 2^31-1 elements");
+        return GCS_ERANGE;
+    }
+    g.lv[0].base = 0;
+    g.lv[0].nb = 0;
+    g.lv[0].npt = 0;
+    for (int k = 1; k <= L; ++k) g.lv[k].base = (k & 1) ? g.buf_a : g.buf_b;
+
+    // arena offset of nonterminal v as read by a parent at level k
+    auto read_off = [&](int32_t v, int k) -> int32_t {
+        int lv = g.lvl[v];
+        const Level& P = g.lv[k - 1];
+        if (lv == k - 1) return (int32_t)(P.base + pos[v]);
+        return (int32_t)(P.base + P.nb + ptoff[k - 1][lv] + rank[v]);
+    };
+
+    // children
+    g.child.resize((size_t)2 * R);
+    int64_t co = 0;
+    for (int k = 1; k <= L; ++k) {
+        g.lv[k].child_off = co;
+        for (int64_t t = lvl_start[k]; t < lvl_start[k + 1]; ++t) {
+            int32_t v = order[t];
+            int32_t a = g.ra[v], b = g.rb[v];
+            g.child[2 * (co + pos[v])] = a < alpha ? a : read_off(a - (int32_t)alpha, k);
+            g.child[2 * (co + pos[v]) + 1] = b < alpha ? b : read_off(b - (int32_t)alpha, k);
+        }
+        co += cnt_lvl[k];
+    }
+    // pass-through ranges
+    g.range.clear();
+    int64_t ro = 0;
+    for (int k = 1; k <= L; ++k) {
+        g.lv[k].range_off = ro;
+        int64_t nr = 0, last_dst_end = -1, last_src_end = -1;
+        for (int j = k - 1; j >= 1; --j) {
+            int64_t c = cnt_reach(j, k);
+            if (c == 0) continue;
+            int64_t dst = ptoff[k][j];
+            const Level& P = g.lv[k - 1];
+            int64_t src = (j == k - 1) ? P.base + nonc[k - 1] : P.base + P.nb + ptoff[k - 1][j];
+            if (nr > 0 && dst == last_dst_end && src == last_src_end) {
+                // extends the previous range
+            } else {
+                g.range.push_back((int32_t)dst);
+                g.range.push_back((int32_t)src);
+                ++nr;
+            }
+            last_dst_end = dst + c;
+            last_src_end = src + c;
+        }
+        g.lv[k].nranges = nr;
+        ro += nr;
+    }
+
+    // emission groups: C-occurrences at their symbol's level, grouped by
+    // (level, row), rows ascending, C order within a row (section 4.3:
+    // a root is emitted the moment its level is computed)
+    const int64_t n = g.n_rows;
+    std::vector<int64_t> per_level((size_t)L + 2, 0), grp_level((size_t)L + 2, 0);
+    std::vector<int32_t> last_row((size_t)L + 1, -1);
+    auto sym_level = [&](int32_t s) -> int { return s < alpha ? 0 : g.lvl[s - alpha]; };
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
+            int l = sym_level(g.c_sym[e]);
+            per_level[l]++;
+            if (last_row[l] != (int32_t)r) {
+                last_row[l] = (int32_t)r;
+                grp_level[l]++;
+            }
+        }
+    const int64_t C = (int64_t)g.c_sym.size();
+    int64_t G = 0;
+    for (int l = 0; l <= L; ++l) G += grp_level[l];
+    if (C >= (int64_t)INT32_MAX || G >= (int64_t)INT32_MAX) {
+        set_error("C exceeds the 32-bit index space");
+        return GCS_ERANGE;
+    }
+    g.erow.assign((size_t)G, 0);
+    g.eoff.assign((size_t)G + 1, 0);
+    g.epos.assign((size_t)C, 0);
+    std::vector<int64_t> gfill((size_t)L + 1), efill((size_t)L + 1);
+    {
+        int64_t go = 0, eo = 0;
+        for (int l = 0; l <= L; ++l) {
+            g.lv[l].grp_off = go;
+            g.lv[l].ngrp = grp_level[l];
+            gfill[l] = go;
+            efill[l] = eo;
+            go += grp_level[l];
+            eo += per_level[l];
+        }
+    }
+    std::fill(last_row.begin(), last_row.end(), -1);
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
+            int32_t s = g.c_sym[e];
+            int l = sym_level(s);
+            if (last_row[l] != (int32_t)r) {
+                last_row[l] = (int32_t)r;
+                g.erow[gfill[l]] = (int32_t)r;
+                g.eoff[gfill[l]] = (int32_t)efill[l];
+                gfill[l]++;
+            }
+            g.epos[efill[l]++] = s < alpha ? s : (int32_t)(g.lv[l].base + pos[s - alpha]);
+        }
+    g.eoff[G] = (int32_t)C;
+    g.t_layer = ms_since(t0);
+    return GCS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// CSRV + RePair
+// ---------------------------------------------------------------------------
+
+static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* opts, Grammar& g)
+{
+    auto t0 = std::chrono::steady_clock::now();
+    if (!m || m->n_rows < 0 || m->n_cols < 0 || (m->n_rows > 0 && !m->row_ptr)) {
+        set_error("invalid matrix view");
+        return GCS_EINVAL;
+    }
+    if (m->val_kind < GCS_VAL_ONES || m->val_kind > GCS_VAL_F64 || (m->val_kind != GCS_VAL_ONES && !m->val &&
+                                                                     m->n_rows > 0 && m->row_ptr[m->n_rows] > 0)) {
+        set_error("invalid value kind or missing values");
+        return GCS_EINVAL;
+    }
+    if (m->n_rows >= (int64_t)INT32_MAX || m->n_cols >= (int64_t)INT32_MAX) {
+        set_error("matrix dimensions exceed 2^31-1");
+        return GCS_ERANGE;
+    }
+    const int64_t n = m->n_rows, mc = m->n_cols;
+    const int64_t nnz_stored = n > 0 ? m->row_ptr[n] : 0;
+    if (n > 0 && m->row_ptr[0] != 0) {
+        set_error("row_ptr[0] must be 0");
+        return GCS_EINVAL;
+    }
+    if (nnz_stored > 0 && !m->col) {
+        set_error("missing column array");
+        return GCS_EINVAL;
+    }
+    const int threads = resolve_threads(opts ? opts->n_threads : 0);
+    g.n_rows = n;
+    g.n_cols = mc;
+
+    // validate rows in parallel
+    std::atomic<int> bad{0};
+    const int64_t vblk = 4096;
+    parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
+        for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
+            int64_t s = m->row_ptr[r], e = m->row_ptr[r + 1];
+            if (e < s || e > nnz_stored) {
+                bad = 1;
+                return;
+            }
+            for (int64_t k = s; k < e; ++k) {
+                int32_t c = m->col[k];
+                if (c < 0 || c >= mc || (k > s && c <= m->col[k - 1])) {
+                    bad = 2;
+                    return;
+                }
+                if (m->val_kind == GCS_VAL_F64 && !std::isfinite(((const double*)m->val)[k])) {
+                    bad = 3;
+                    return;
+                }
+            }
+        }
+    });
+    if (bad) {
+        set_error(bad == 1 ? "row_ptr not monotone" : bad == 2 ? "columns must be strictly increasing and < n_cols"
+                                                                : "non-finite matrix value");
+        return GCS_EINVAL;
+    }
+
+    // V: distinct nonzero values, ascending (CSRV, section 2)
+    const int kind = m->val_kind;
+    std::vector<int32_t> i8_index(256, -1);
+    if (kind == GCS_VAL_ONES) {
+        if (nnz_stored > 0) g.V = {1.0};
+    } else if (kind == GCS_VAL_I8) {
+        std::vector<char> seen(256, 0);
+        const int8_t* v = (const int8_t*)m->val;
+        for (int64_t k = 0; k < nnz_stored; ++k) seen[(int)v[k] + 128] = 1;
+        for (int c = 0; c < 256; ++c)
+            if (seen[c] && c != 128) {
+                i8_index[c] = (int32_t)g.V.size();
+                g.V.push_back((double)(c - 128));
+            }
+    } else {
+        const double* v = (const double*)m->val;
+        std::vector<double> vals;
+        vals.reserve((size_t)nnz_stored);
+        for (int64_t k = 0; k < nnz_stored; ++k)
+            if (v[k] != 0.0) vals.push_back(v[k]);
+        std::sort(vals.begin(), vals.end());
+        vals.erase(std::unique(vals.begin(), vals.end()), vals.end());
+        g.V = vals;
+    }
+    const int64_t nV = (int64_t)g.V.size();
+    auto vindex = [&](int64_t k) -> int32_t {  // -1 = stored zero (dropped)
+        if (kind == GCS_VAL_ONES) return 0;
+        if (kind == GCS_VAL_I8) return i8_index[(int)((const int8_t*)m->val)[k] + 128];
+        double x = ((const double*)m->val)[k];
+        if (x == 0.0) return -1;
+        return (int32_t)(std::lower_bound(g.V.begin(), g.V.end(), x) - g.V.begin());
+    };
+
+    // terminal compaction: distinct <l, j> in use, sorted by (j, l)
+    std::vector<int64_t> cbase;      // per column: first terminal id
+    std::vector<uint64_t> cmask;     // per column: value indices present (|V| <= 64)
+    std::vector<int64_t> tkeys;      // general path: sorted keys j*|V|+l
+    const bool small_v = nV <= 64;
+    if (small_v) {
+        cmask.assign((size_t)mc, 0);
+        const int64_t nblk = std::min<int64_t>(threads, std::max<int64_t>(1, n / 1024));
+        std::vector<std::vector<uint64_t>> part((size_t)nblk);
+        parallel_for(nblk, threads, [&](int64_t b) {
+            std::vector<uint64_t>& pm = part[b];
+            pm.assign((size_t)mc, 0);
+            int64_t r0 = n * b / nblk, r1 = n * (b + 1) / nblk;
+            for (int64_t k = (n ? m->row_ptr[r0] : 0); k < (n ? m->row_ptr[r1] : 0); ++k) {
+                int32_t vi = vindex(k);
+                if (vi >= 0) pm[m->col[k]] |= 1ULL << vi;
+            }
+        });
+        for (auto& pm : part)
+            for (int64_t j = 0; j < mc; ++j) cmask[j] |= pm[j];
+        cbase.assign((size_t)mc + 1, 0);
+        for (int64_t j = 0; j < mc; ++j) cbase[j + 1] = cbase[j] + __builtin_popcountll(cmask[j]);
+        const int64_t alpha = cbase[mc];
+        g.tcol.resize((size_t)alpha);
+        g.tval.resize((size_t)alpha);
+        for (int64_t j = 0; j < mc; ++j) {
+            int64_t t = cbase[j];
+            for (uint64_t mk = cmask[j]; mk; mk &= mk - 1) {
+                g.tcol[t] = (int32_t)j;
+                g.tval[t] = __builtin_ctzll(mk);
+                ++t;
+            }
+        }
+    } else {
+        tkeys.reserve((size_t)nnz_stored);
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t k = m->row_ptr[r]; k < m->row_ptr[r + 1]; ++k) {
+                int32_t vi = vindex(k);
+                if (vi >= 0) tkeys.push_back((int64_t)m->col[k] * nV + vi);
+            }
+        std::sort(tkeys.begin(), tkeys.end());
+        tkeys.erase(std::unique(tkeys.begin(), tkeys.end()), tkeys.end());
+        g.tcol.resize(tkeys.size());
+        g.tval.resize(tkeys.size());
+        for (size_t t = 0; t < tkeys.size(); ++t) {
+            g.tcol[t] = (int32_t)(tkeys[t] / nV);
+            g.tval[t] = (int32_t)(tkeys[t] % nV);
+        }
+    }
+    const int64_t alpha = g.alpha();
+    if (alpha >= (int64_t)INT32_MAX) {
+        set_error("too many distinct terminals");
+        return GCS_ERANGE;
+    }
+    auto term_id = [&](int64_t k) -> int32_t {
+        int32_t vi = vindex(k);
+        if (vi < 0) return -1;
+        int32_t j = m->col[k];
+        if (small_v) return (int32_t)(cbase[j] + __builtin_popcountll(cmask[j] & ((1ULL << vi) - 1)));
+        return (int32_t)(std::lower_bound(tkeys.begin(), tkeys.end(), (int64_t)j * nV + vi) - tkeys.begin());
+    };
+    g.t_csrv = ms_since(t0);
+
+    // tiles
+    auto t1 = std::chrono::steady_clock::now();
+    const int64_t cc = (opts && opts->col_chunk > 0) ? opts->col_chunk : std::max<int64_t>(mc, 1);
+    const int64_t rc = (opts && opts->row_chunk > 0) ? opts->row_chunk : std::max<int64_t>(n, 1);
+    const int64_t ncc = std::max<int64_t>(1, (mc + cc - 1) / cc), nrc = std::max<int64_t>(1, (n + rc - 1) / rc);
+    const int64_t ntiles = ncc * nrc;
+    g.n_tiles = ntiles;
+    std::vector<RePairResult> res((size_t)ntiles);
+    std::atomic<int> fail{0};
+    std::atomic<int64_t> nnz_total{0};
+    // tiles are independent; run the larger ones first
+    parallel_for(ntiles, threads, [&](int64_t t) {
+        if (fail) return;
+        const int64_t rb = t / ncc, cb = t % ncc;
+        const int64_t r0 = rb * rc, r1 = std::min(n, r0 + rc);
+        const int32_t c0 = (int32_t)(cb * cc), c1 = (int32_t)std::min<int64_t>(mc, (cb + 1) * cc);
+        std::vector<int64_t> off;
+        std::vector<int32_t> seq;
+        try {
+            off.reserve((size_t)(r1 - r0 + 1));
+            off.push_back(0);
+            for (int64_t r = r0; r < r1; ++r) {
+                const int32_t* cb_ = m->col + m->row_ptr[r];
+                const int32_t* ce_ = m->col + m->row_ptr[r + 1];
+                const int32_t* s = (ncc == 1) ? cb_ : std::lower_bound(cb_, ce_, c0);
+                const int32_t* e = (ncc == 1) ? ce_ : std::lower_bound(s, ce_, c1);
+                for (const int32_t* p = s; p < e; ++p) {
+                    int32_t tid = term_id(p - m->col);
+                    if (tid >= 0) seq.push_back(tid);
+                }
+                off.push_back((int64_t)seq.size());
+            }
+        } catch (const std::bad_alloc&) {
+            fail = 1;
+            return;
+        }
+        if ((int64_t)seq.size() >= (int64_t)INT32_MAX) {
+            fail = 2;
+            return;
+        }
+        nnz_total += (int64_t)seq.size();
+        if (!repair_tile(seq, off, (int32_t)alpha, res[t])) fail = 1;
+    });
+    if (fail) {
+        set_error(fail == 2 ? "a RePair tile exceeds 2^31-1 symbols (use col_chunk/row_chunk)"
+                            : "out of host memory in RePair");
+        return fail == 2 ? GCS_ERANGE : GCS_ENOMEM;
+    }
+    g.nnz = nnz_total;
+
+    // merge: global rule ids = tile rule base + local index
+    std::vector<int64_t> rbase((size_t)ntiles + 1, 0);
+    for (int64_t t = 0; t < ntiles; ++t) rbase[t + 1] = rbase[t] + (int64_t)res[t].rule_a.size();
+    const int64_t R = rbase[ntiles];
+    if (alpha + R >= (int64_t)INT32_MAX) {
+        set_error("grammar exceeds the 32-bit symbol space");
+        return GCS_ERANGE;
+    }
+    try {
+        g.ra.resize((size_t)R);
+        g.rb.resize((size_t)R);
+        parallel_for(ntiles, threads, [&](int64_t t) {
+            const int32_t shift = (int32_t)rbase[t];
+            auto remap = [&](int32_t s) { return s < alpha ? s : s + shift; };
+            for (size_t i = 0; i < res[t].rule_a.size(); ++i) {
+                g.ra[rbase[t] + i] = remap(res[t].rule_a[i]);
+                g.rb[rbase[t] + i] = remap(res[t].rule_b[i]);
+            }
+        });
+        // C: row r = concatenation over column chunks of its tile sequences
+        g.c_off.assign((size_t)n + 1, 0);
+        std::vector<std::vector<int64_t>> tile_row_start((size_t)ntiles);
+        for (int64_t t = 0; t < ntiles; ++t) {
+            auto& s = tile_row_start[t];
+            s.resize(res[t].row_len.size() + 1, 0);
+            for (size_t i = 0; i < res[t].row_len.size(); ++i) s[i + 1] = s[i] + res[t].row_len[i];
+        }
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t rb = r / rc, ri = r - rb * rc, len = 0;
+            for (int64_t cb = 0; cb < ncc; ++cb) len += res[rb * ncc + cb].row_len[ri];
+            g.c_off[r + 1] = g.c_off[r] + len;
+        }
+        g.c_sym.resize((size_t)g.c_off[n]);
+        parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
+            for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
+                int64_t rb = r / rc, ri = r - rb * rc, o = g.c_off[r];
+                for (int64_t cb = 0; cb < ncc; ++cb) {
+                    const int64_t t = rb * ncc + cb;
+                    const int32_t shift = (int32_t)rbase[t];
+                    for (int64_t e = tile_row_start[t][ri]; e < tile_row_start[t][ri + 1]; ++e) {
+                        int32_t s = res[t].seq[e];
+                        g.c_sym[o++] = s < alpha ? s : s + shift;
+                    }
+                }
+            }
+        });
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory merging tiles");
+        return GCS_ENOMEM;
+    }
+    g.t_repair = ms_since(t1);
+    return finish_layout(g);
+}
+
+}  // namespace gcs
+
+// ---------------------------------------------------------------------------
+// C ABI: host builder and inspection
+// ---------------------------------------------------------------------------
+
+using gcs::Grammar;
+
+extern "C" const char* gcs_last_error(void) { return gcs::last_error(); }
+
+extern "C" gcs_status gcs_build_grammar(const gcs_csr_view* m, const gcs_build_opts* opts, gcs_grammar** out)
+{
+    if (!out) {
+        gcs::set_error("null output pointer");
+        return GCS_EINVAL;
+    }
+    *out = nullptr;
+    try {
+        auto* h = new gcs_grammar();
+        gcs_status st = gcs::build_from_csr(m, opts, h->g);
+        if (st != GCS_OK) {
+            delete h;
+            return st;
+        }
+        *out = h;
+        return GCS_OK;
+    } catch (const std::bad_alloc&) {
+        gcs::set_error("out of host memory");
+        return GCS_ENOMEM;
+    }
+}
+
+extern "C" gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, const double* values, int64_t n_values,
+                                             const int32_t* term_col, const int32_t* term_val, int64_t n_terms,
+                                             const int32_t* rule_a, const int32_t* rule_b, int64_t n_rules,
+                                             const int64_t* c_off, const int32_t* c_sym, gcs_grammar** out)
+{
+    if (!out || n_rows < 0 || n_cols < 0 || n_values < 0 || n_terms < 0 || n_rules < 0 ||
+        (n_values && !values) || (n_terms && (!term_col || !term_val)) || (n_rules && (!rule_a || !rule_b)) ||
+        !c_off) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    *out = nullptr;
+    if (n_terms + n_rules >= (int64_t)INT32_MAX || n_rows >= (int64_t)INT32_MAX) {
+        gcs::set_error("grammar exceeds the 32-bit symbol space");
+        return GCS_ERANGE;
+    }
+    for (int64_t t = 0; t < n_terms; ++t)
+        if (term_col[t] < 0 || term_col[t] >= n_cols || term_val[t] < 0 || term_val[t] >= n_values) {
+            gcs::set_error("terminal out of range");
+            return GCS_EINVAL;
+        }
+    for (int64_t i = 0; i < n_rules; ++i)
+        if (rule_a[i] < 0 || rule_b[i] < 0 || rule_a[i] >= n_terms + i || rule_b[i] >= n_terms + i) {
+            gcs::set_error("rule symbol out of range or not in topological order");
+            return GCS_EINVAL;
+        }
+    if (c_off[0] != 0) {
+        gcs::set_error("c_off[0] must be 0");
+        return GCS_EINVAL;
+    }
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (c_off[r + 1] < c_off[r]) {
+            gcs::set_error("c_off not monotone");
+            return GCS_EINVAL;
+        }
+    const int64_t C = c_off[n_rows];
+    if (C && !c_sym) {
+        gcs::set_error("missing c_sym");
+        return GCS_EINVAL;
+    }
+    for (int64_t e = 0; e < C; ++e)
+        if (c_sym[e] < 0 || c_sym[e] >= n_terms + n_rules) {
+            gcs::set_error("C symbol out of range");
+            return GCS_EINVAL;
+        }
+    try {
+        auto* h = new gcs_grammar();
+        Grammar& g = h->g;
+        g.n_rows = n_rows;
+        g.n_cols = n_cols;
+        g.V.assign(values, values + n_values);
+        g.tcol.assign(term_col, term_col + n_terms);
+        g.tval.assign(term_val, term_val + n_terms);
+        g.ra.assign(rule_a, rule_a + n_rules);
+        g.rb.assign(rule_b, rule_b + n_rules);
+        g.c_off.assign(c_off, c_off + n_rows + 1);
+        g.c_sym.assign(c_sym, c_sym + C);
+        // nnz = total expansion length
+        std::vector<int64_t> len((size_t)n_rules);
+        for (int64_t i = 0; i < n_rules; ++i)
+            len[i] = (rule_a[i] < n_terms ? 1 : len[rule_a[i] - n_terms]) +
+                     (rule_b[i] < n_terms ? 1 : len[rule_b[i] - n_terms]);
+        for (int64_t e = 0; e < C; ++e) g.nnz += c_sym[e] < n_terms ? 1 : len[c_sym[e] - n_terms];
+        gcs_status st = gcs::finish_layout(g);
+        if (st != GCS_OK) {
+            delete h;
+            return st;
+        }
+        *out = h;
+        return GCS_OK;
+    } catch (const std::bad_alloc&) {
+        gcs::set_error("out of host memory");
+        return GCS_ENOMEM;
+    }
+}
+
+extern "C" gcs_status gcs_grammar_stats(const gcs_grammar* h, gcs_stats* out)
+{
+    if (!h || !out) {
+        gcs::set_error("null argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    out->n_rows = g.n_rows;
+    out->n_cols = g.n_cols;
+    out->nnz = g.nnz;
+    out->n_values = (int64_t)g.V.size();
+    out->n_terminals = g.alpha();
+    out->n_rules = g.nrules();
+    out->n_passthrough = g.pt_total;
+    out->depth = g.L;
+    out->max_width = g.wmax;
+    out->c_len = (int64_t)g.c_sym.size();
+    out->n_tiles = g.n_tiles;
+    out->n_emit_groups = (int64_t)g.erow.size();
+    out->t_csrv_ms = g.t_csrv;
+    out->t_repair_ms = g.t_repair;
+    out->t_layer_ms = g.t_layer;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_level_widths(const gcs_grammar* h, int64_t* w, int64_t cap)
+{
+    if (!h || (cap > 0 && !w)) {
+        gcs::set_error("null argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    for (int64_t k = 0; k <= g.L && k < cap; ++k) w[k] = k == 0 ? g.alpha() : g.lv[k].nb + g.lv[k].npt;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_export_grammar(const gcs_grammar* h, double* values, int32_t* term_col, int32_t* term_val,
+                                         int32_t* rule_a, int32_t* rule_b, int32_t* rule_level, int32_t* rule_plast,
+                                         int64_t* c_off, int32_t* c_sym)
+{
+    if (!h) {
+        gcs::set_error("null grammar");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    auto cp = [](auto* dst, const auto& v) {
+        if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(v[0]));
+    };
+    cp(values, g.V);
+    cp(term_col, g.tcol);
+    cp(term_val, g.tval);
+    cp(rule_a, g.ra);
+    cp(rule_b, g.rb);
+    cp(rule_level, g.lvl);
+    cp(rule_plast, g.plast);
+    cp(c_off, g.c_off);
+    cp(c_sym, g.c_sym);
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_layout_counts(const gcs_grammar* h, int64_t* c)
+{
+    if (!h || !c) {
+        gcs::set_error("null argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    c[0] = g.L + 1;
+    c[1] = (int64_t)g.child.size() / 2;
+    c[2] = (int64_t)g.range.size() / 2;
+    c[3] = (int64_t)g.erow.size();
+    c[4] = (int64_t)g.epos.size();
+    c[5] = g.arena;
+    c[6] = g.buf_a;
+    c[7] = g.buf_b;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_meta, int32_t* child, int32_t* range,
+                                        int32_t* erow, int32_t* eoff, int32_t* epos)
+{
+    if (!h) {
+        gcs::set_error("null grammar");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    if (level_meta)
+        for (int k = 0; k <= g.L; ++k) {
+            const gcs::Level& l = g.lv[k];
+            int64_t* o = level_meta + 8 * k;
+            o[0] = l.nb;
+            o[1] = l.npt;
+            o[2] = l.child_off;
+            o[3] = l.range_off;
+            o[4] = l.nranges;
+            o[5] = l.base;
+            o[6] = l.grp_off;
+            o[7] = l.ngrp;
+        }
+    auto cp = [](auto* dst, const auto& v) {
+        if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(v[0]));
+    };
+    cp(child, g.child);
+    cp(range, g.range);
+    cp(erow, g.erow);
+    cp(eoff, g.eoff);
+    cp(epos, g.epos);
+    return GCS_OK;
+}
+
+extern "C" void gcs_free_grammar(gcs_grammar* h) { delete h; }

@@ -1,0 +1,342 @@
+"""Python binding of the C ABI in ``include/gcs.h`` (argument marshalling only).
+
+Every step of the product runs in ``libgcs.so``: the host builder (CSRV,
+RePair, levels, pass-through completion, layout) and the HIP sweep.  PyTorch
+provides device memory (``torch.empty(..., device='cuda')``) and streams.
+There is no fallback: if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_PKG, "libgcs.so")
+
+if not os.path.exists(_SO):
+    raise ImportError(f"{_SO} is not built; run __graft_entry__.build() (hipcc for gfx950)")
+_lib = ctypes.CDLL(_SO)
+
+# policies (gcs_policy)
+PLUS_F64, PLUS_F32, PLUS_F32_ACC_F64, BOOL_OR, PLUS_I64 = range(5)
+POLICY_NAMES = {"f64": PLUS_F64, "f32": PLUS_F32, "f32_acc_f64": PLUS_F32_ACC_F64, "bool": BOOL_OR, "i64": PLUS_I64}
+VAL_ONES, VAL_I8, VAL_F64 = 0, 1, 2
+_STATUS = {0: "GCS_OK", -1: "GCS_EINVAL", -2: "GCS_ENOMEM", -3: "GCS_EHIP", -4: "GCS_ERANGE", -5: "GCS_ESTATE"}
+
+
+class GcsError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CsrView(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64), ("row_ptr", ctypes.c_void_p),
+                ("col", ctypes.c_void_p), ("val_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("val", ctypes.c_void_p)]
+
+
+class BuildOpts(ctypes.Structure):
+    _fields_ = [("n_threads", ctypes.c_int32), ("col_chunk", ctypes.c_int32), ("row_chunk", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("n_rows", "n_cols", "nnz", "n_values", "n_terminals", "n_rules",
+                                             "n_passthrough", "depth", "max_width", "c_len", "n_tiles",
+                                             "n_emit_groups")] + \
+               [(n, ctypes.c_double) for n in ("t_csrv_ms", "t_repair_ms", "t_layer_ms")]
+
+
+class DevSizes(ctypes.Structure):
+    _fields_ = [("grammar_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t), ("x_len", ctypes.c_int64),
+                ("y_len", ctypes.c_int64), ("x_elem_bytes", ctypes.c_int32), ("y_elem_bytes", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_st = ctypes.c_int
+_lib.gcs_last_error.restype = ctypes.c_char_p
+_lib.gcs_build_grammar.argtypes = [ctypes.POINTER(CsrView), ctypes.POINTER(BuildOpts), ctypes.POINTER(_P)]
+_lib.gcs_grammar_from_rules.argtypes = [_I64, _I64, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P, ctypes.POINTER(_P)]
+_lib.gcs_grammar_stats.argtypes = [_P, ctypes.POINTER(Stats)]
+_lib.gcs_level_widths.argtypes = [_P, _P, _I64]
+_lib.gcs_export_grammar.argtypes = [_P] + [_P] * 9
+_lib.gcs_layout_counts.argtypes = [_P, _P]
+_lib.gcs_export_layout.argtypes = [_P] + [_P] * 6
+_lib.gcs_free_grammar.argtypes = [_P]
+_lib.gcs_free_grammar.restype = None
+_lib.gcs_device_layout.argtypes = [_P, ctypes.c_int, ctypes.POINTER(DevSizes)]
+_lib.gcs_upload.argtypes = [_P, ctypes.c_int, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
+_lib.gcs_sweep_right.argtypes = [_P, _P, _P, _P]
+_lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
+_lib.gcs_sweep_launches.argtypes = [_P]
+_lib.gcs_sweep_launches.restype = _I64
+_lib.gcs_profile_begin.argtypes = [_P, _I64]
+_lib.gcs_sweep_right_profiled.argtypes = [_P, _P, _P, _P]
+_lib.gcs_profile_end.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+_lib.gcs_free_device.argtypes = [_P]
+_lib.gcs_free_device.restype = None
+for _f in ("gcs_build_grammar", "gcs_grammar_from_rules", "gcs_grammar_stats", "gcs_level_widths",
+           "gcs_export_grammar", "gcs_layout_counts", "gcs_export_layout", "gcs_device_layout", "gcs_upload",
+           "gcs_sweep_right", "gcs_bfs", "gcs_profile_begin", "gcs_sweep_right_profiled", "gcs_profile_end"):
+    getattr(_lib, _f).restype = _st
+
+
+def _check(status):
+    if status != 0:
+        raise GcsError(status, (_lib.gcs_last_error() or b"").decode())
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+def last_error() -> str:
+    return (_lib.gcs_last_error() or b"").decode()
+
+
+def library_path() -> str:
+    return _SO
+
+
+class Grammar:
+    """A host grammar owned by the library (``gcs_grammar``)."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    @property
+    def handle(self):
+        return self._h
+
+    def stats(self) -> dict:
+        s = Stats()
+        _check(_lib.gcs_grammar_stats(self._h, ctypes.byref(s)))
+        return {n: getattr(s, n) for n, _ in Stats._fields_}
+
+    def level_widths(self) -> np.ndarray:
+        L = self.stats()["depth"]
+        w = np.zeros(L + 1, np.int64)
+        _check(_lib.gcs_level_widths(self._h, _ptr(w), L + 1))
+        return w
+
+    def export(self) -> dict:
+        s = self.stats()
+        a, R, n, C = s["n_terminals"], s["n_rules"], s["n_rows"], s["c_len"]
+        out = dict(values=np.zeros(s["n_values"], np.float64), term_col=np.zeros(a, np.int32),
+                   term_val=np.zeros(a, np.int32), rule_a=np.zeros(R, np.int32), rule_b=np.zeros(R, np.int32),
+                   rule_level=np.zeros(R, np.int32), rule_plast=np.zeros(R, np.int32),
+                   c_off=np.zeros(n + 1, np.int64), c_sym=np.zeros(C, np.int32))
+        _check(_lib.gcs_export_grammar(self._h, *[_ptr(out[k]) for k in (
+            "values", "term_col", "term_val", "rule_a", "rule_b", "rule_level", "rule_plast", "c_off", "c_sym")]))
+        return out
+
+    def layout(self) -> dict:
+        c = np.zeros(8, np.int64)
+        _check(_lib.gcs_layout_counts(self._h, _ptr(c)))
+        nl, ncp, nr, ng, ne, arena, ba, bb = (int(v) for v in c)
+        out = dict(level_meta=np.zeros((nl, 8), np.int64), child=np.zeros((ncp, 2), np.int32),
+                   range=np.zeros((nr, 2), np.int32), erow=np.zeros(ng, np.int32), eoff=np.zeros(ng + 1, np.int32),
+                   epos=np.zeros(ne, np.int32), arena=arena, buf_a=ba, buf_b=bb)
+        _check(_lib.gcs_export_layout(self._h, *[_ptr(out[k]) for k in (
+            "level_meta", "child", "range", "erow", "eoff", "epos")]))
+        return out
+
+    def device_layout(self, policy: int) -> dict:
+        d = DevSizes()
+        _check(_lib.gcs_device_layout(self._h, policy, ctypes.byref(d)))
+        return {n: getattr(d, n) for n, _ in DevSizes._fields_}
+
+    def free(self):
+        if self._h:
+            _lib.gcs_free_grammar(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0) -> Grammar:
+    """gcs_build_grammar on a host CSR matrix (val: None = all ones, int8, or fp64)."""
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    cl = np.ascontiguousarray(col, dtype=np.int32)
+    n = rp.shape[0] - 1
+    if n_cols is None:
+        n_cols = int(cl.max()) + 1 if cl.size else 0
+    if val is None:
+        kind, vv = VAL_ONES, None
+    elif np.asarray(val).dtype == np.int8:
+        kind, vv = VAL_I8, np.ascontiguousarray(val)
+    else:
+        kind, vv = VAL_F64, np.ascontiguousarray(val, dtype=np.float64)
+    view = CsrView(n, n_cols, rp.ctypes.data, cl.ctypes.data if cl.size else None, kind, 0,
+                   vv.ctypes.data if vv is not None and vv.size else None)
+    opts = BuildOpts(n_threads, col_chunk, row_chunk, 0)
+    h = _P()
+    _check(_lib.gcs_build_grammar(ctypes.byref(view), ctypes.byref(opts), ctypes.byref(h)))
+    return Grammar(h)
+
+
+def grammar_from_rules(n_rows, n_cols, values, term_col, term_val, rule_a, rule_b, c_off, c_sym) -> Grammar:
+    """gcs_grammar_from_rules: an explicit (C, R, V) grammar."""
+    v = np.ascontiguousarray(values, np.float64)
+    tc = np.ascontiguousarray(term_col, np.int32)
+    tv = np.ascontiguousarray(term_val, np.int32)
+    a = np.ascontiguousarray(rule_a, np.int32)
+    b = np.ascontiguousarray(rule_b, np.int32)
+    co = np.ascontiguousarray(c_off, np.int64)
+    cs = np.ascontiguousarray(c_sym, np.int32)
+    h = _P()
+    _check(_lib.gcs_grammar_from_rules(n_rows, n_cols, _ptr(v), v.size, _ptr(tc), _ptr(tv), tc.size, _ptr(a),
+                                       _ptr(b), a.size, _ptr(co), _ptr(cs), ctypes.byref(h)))
+    return Grammar(h)
+
+
+# ---------------------------------------------------------------------------
+# device side (torch supplies memory and streams)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+_X_DTYPES = {PLUS_F64: "float64", PLUS_F32: "float32", PLUS_F32_ACC_F64: "float32", BOOL_OR: "uint8",
+             PLUS_I64: "int64"}
+_Y_DTYPES = {PLUS_F64: "float64", PLUS_F32: "float32", PLUS_F32_ACC_F64: "float64", BOOL_OR: "uint8",
+             PLUS_I64: "int64"}
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Device:
+    """An uploaded grammar (``gcs_device``) plus the torch buffers it lives in."""
+
+    def __init__(self, handle, policy, grammar_buf, workspace, sizes, device):
+        self._h = handle
+        self.policy = policy
+        self.grammar_buf = grammar_buf
+        self.workspace = workspace
+        self.sizes = sizes
+        self.device = device
+        torch = _torch()
+        self.x_dtype = getattr(torch, _X_DTYPES[policy])
+        self.y_dtype = getattr(torch, _Y_DTYPES[policy])
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def device_bytes(self) -> int:
+        return self.grammar_buf.numel() + self.workspace.numel()
+
+    def new_y(self):
+        torch = _torch()
+        return torch.empty(self.sizes["y_len"], dtype=self.y_dtype, device=self.device)
+
+    def sweep_right(self, x, y=None, stream=None):
+        return sweep_right(self, x, y, stream)
+
+    def bfs(self, sources, max_passes=1 << 16, stream=None):
+        return bfs(self, sources, max_passes, stream)
+
+    def sweep_launches(self) -> int:
+        return int(_lib.gcs_sweep_launches(self._h))
+
+    def profile_begin(self, max_sweeps: int):
+        _check(_lib.gcs_profile_begin(self._h, max_sweeps))
+
+    def sweep_right_profiled(self, x, y, stream=None):
+        _check_xy(self, x, y)
+        _check(_lib.gcs_sweep_right_profiled(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                             _stream_ptr(stream)))
+        return y
+
+    def profile_end(self) -> np.ndarray:
+        """Per-launch durations (ms), shape (sweeps, launches)."""
+        cap = 1 << 22
+        buf = np.zeros(cap, np.float32)
+        ns, nl = _I64(0), _I64(0)
+        _check(_lib.gcs_profile_end(self._h, _ptr(buf), cap, ctypes.byref(ns), ctypes.byref(nl)))
+        return buf[:ns.value * nl.value].reshape(ns.value, nl.value).copy()
+
+    def free(self):
+        if self._h:
+            _lib.gcs_free_device(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def upload(grammar: Grammar, policy, device="cuda", stream=None) -> Device:
+    """gcs_device_layout + caller-owned torch allocations + gcs_upload."""
+    torch = _torch()
+    policy = POLICY_NAMES.get(policy, policy)
+    sz = grammar.device_layout(policy)
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        gbuf = torch.empty(max(sz["grammar_bytes"], 256), dtype=torch.uint8, device=dev)
+        wbuf = torch.empty(max(sz["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+        h = _P()
+        _check(_lib.gcs_upload(grammar.handle, policy, ctypes.c_void_p(gbuf.data_ptr()), gbuf.numel(),
+                               ctypes.c_void_p(wbuf.data_ptr()), wbuf.numel(), _stream_ptr(stream),
+                               ctypes.byref(h)))
+    return Device(h, policy, gbuf, wbuf, sz, dev)
+
+
+def _check_xy(dev, x, y):
+    if not dev.handle:
+        raise GcsError(-5, "device handle already freed")
+    if x.dtype != dev.x_dtype or x.numel() != dev.sizes["x_len"] or not x.is_contiguous() or x.device != dev.device:
+        raise GcsError(-1, f"x must be a contiguous {dev.x_dtype} tensor of {dev.sizes['x_len']} elements on "
+                           f"{dev.device}")
+    if y.dtype != dev.y_dtype or y.numel() != dev.sizes["y_len"] or not y.is_contiguous() or y.device != dev.device:
+        raise GcsError(-1, f"y must be a contiguous {dev.y_dtype} tensor of {dev.sizes['y_len']} elements")
+
+
+def sweep_right(dev: Device, x, y=None, stream=None):
+    """gcs_sweep_right: y = M x on the device (async on the stream)."""
+    if y is None:
+        y = dev.new_y()
+    _check_xy(dev, x, y)
+    torch = _torch()
+    with torch.cuda.device(dev.device):
+        _check(_lib.gcs_sweep_right(dev.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    _stream_ptr(stream)))
+    return y
+
+
+def bfs(dev: Device, sources, max_passes=1 << 16, stream=None):
+    """gcs_bfs: BFS fixpoint from ``sources``; returns (visited uint8 tensor, counts)."""
+    torch = _torch()
+    n = dev.sizes["y_len"]
+    srcs = np.asarray(sources, np.int64)
+    if srcs.size and (srcs.min() < 0 or srcs.max() >= n):
+        raise GcsError(-1, "BFS source outside [0, n)")
+    with torch.cuda.device(dev.device):
+        src = torch.as_tensor(srcs).to(dev.device)
+        f = torch.empty(n, dtype=torch.uint8, device=dev.device)
+        vis = torch.empty(n, dtype=torch.uint8, device=dev.device)
+        y = torch.empty(n, dtype=torch.uint8, device=dev.device)
+        counts = np.zeros(max_passes, np.int64)
+        passes = ctypes.c_int64(0)
+        _check(_lib.gcs_bfs(dev.handle, ctypes.c_void_p(src.data_ptr()) if src.numel() else None, src.numel(),
+                            ctypes.c_void_p(f.data_ptr()), ctypes.c_void_p(vis.data_ptr()),
+                            ctypes.c_void_p(y.data_ptr()), _ptr(counts), max_passes, ctypes.byref(passes),
+                            _stream_ptr(stream)))
+    return vis, counts[:passes.value].copy()

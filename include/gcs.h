@@ -1,0 +1,242 @@
+/*
+ * gcs.h -- C ABI of the grammar-compressed right product y = M x on MI355X.
+ *
+ * Method: "Right Multiplication on Grammar-Compressed Matrices: A Streaming,
+ * Memory-Bounded GPU Engine" (arXiv 2607.24971v1).  The matrix is encoded
+ * as a CSRV string (section 2, Eq. 2.2), compressed by RePair into
+ * (C, R, V) (section 2, Eq. 2.3-2.4; section 4.1), completed with
+ * pass-through nodes into a properly layered grammar (Definition 3.2,
+ * section 4.2) and evaluated by a bottom-up, level-synchronous sweep over two
+ * alternating value buffers (Lemma 3.3, section 4.3, Listing 1), with the
+ * leaf / combine / emit operations chosen by a policy (section 5).
+ *
+ * Conventions
+ *   - Every call returns a gcs_status (0 = GCS_OK, < 0 = error) unless it is
+ *     declared void; nothing throws across the ABI.  gcs_last_error() returns
+ *     a thread-local message describing the most recent failure.
+ *   - Host arrays passed in are borrowed for the duration of the call only.
+ *   - Host grammars (gcs_grammar) are owned by the library until
+ *     gcs_free_grammar.
+ *   - ALL DEVICE MEMORY IS OWNED BY THE CALLER.  gcs_device_layout reports
+ *     the byte sizes; the caller allocates (e.g. torch.empty(..., 'cuda')),
+ *     passes the pointers to gcs_upload and keeps them alive until
+ *     gcs_free_device.  The library never allocates device memory.  It does
+ *     allocate one small pinned host word per device handle (BFS counter).
+ *   - Streams are hipStream_t passed as void*; NULL is the null stream.  All
+ *     device work is enqueued asynchronously on the given stream; kernel
+ *     faults surface at the caller's next synchronisation.
+ */
+#ifndef GCS_H
+#define GCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GCS_OK = 0,
+    GCS_EINVAL = -1, /* malformed argument or input matrix                      */
+    GCS_ENOMEM = -2, /* host allocation failed                                   */
+    GCS_EHIP = -3,   /* a HIP runtime call failed (message holds the HIP error)  */
+    GCS_ERANGE = -4, /* a size exceeds the 32-bit index space of the layout      */
+    GCS_ESTATE = -5  /* call not valid in the object's state (e.g. wrong policy) */
+} gcs_status;
+
+/* Leaf / combine / emit policy (section 5: any monoid homomorphism by swapping
+ * a small leaf/combine/emit policy).  Element types of x and y:
+ *   GCS_PLUS_F64          x double,  y double;  T and buffers double
+ *   GCS_PLUS_F32          x float,   y float;   T and buffers float
+ *   GCS_PLUS_F32_ACC_F64  x float,   y double;  T and buffers double
+ *   GCS_BOOL_OR           x uint8 0/1, y uint8 0/1; leaf = x[j], combine = OR
+ *   GCS_PLUS_I64          x int64,   y int64; matrix values must be integers  */
+typedef enum {
+    GCS_PLUS_F64 = 0,
+    GCS_PLUS_F32 = 1,
+    GCS_PLUS_F32_ACC_F64 = 2,
+    GCS_BOOL_OR = 3,
+    GCS_PLUS_I64 = 4
+} gcs_policy;
+
+/* Value array of a CSR input. */
+typedef enum {
+    GCS_VAL_ONES = 0, /* every stored entry is 1 (val ignored, may be NULL) */
+    GCS_VAL_I8 = 1,   /* int8_t val[nnz]                                    */
+    GCS_VAL_F64 = 2   /* double val[nnz]                                    */
+} gcs_val_kind;
+
+/* A sparse matrix in CSR form (host memory, borrowed).  Columns of each row
+ * must be strictly increasing and < n_cols; row_ptr[0] == 0 and row_ptr is
+ * non-decreasing.  Stored zeros are dropped; non-finite values are rejected. */
+typedef struct {
+    int64_t n_rows;
+    int64_t n_cols;
+    const int64_t* row_ptr; /* n_rows + 1 */
+    const int32_t* col;     /* row_ptr[n_rows] */
+    int32_t val_kind;       /* gcs_val_kind */
+    int32_t reserved;
+    const void* val;
+} gcs_csr_view;
+
+/* Builder options.  RePair runs independently on each tile of a
+ * (row chunk x column chunk) partition; tiles run in parallel.  Column chunks
+ * lose no rule sharing (terminals carry their column, so rules never span
+ * two column ranges); they only cut pairs that straddle a chunk border.  The
+ * pages' prior work partitions by row blocks (section 1). */
+typedef struct {
+    int32_t n_threads; /* 0 = OMP_NUM_THREADS if set, else the CPUs of the affinity mask */
+    int32_t col_chunk; /* columns per tile; 0 = all columns                               */
+    int32_t row_chunk; /* rows per tile; 0 = all rows                                     */
+    int32_t reserved;
+} gcs_build_opts;
+
+/* Structural figures of a built grammar (section 4.4, Table 4.1 columns). */
+typedef struct {
+    int64_t n_rows, n_cols, nnz;
+    int64_t n_values;      /* |V|: distinct nonzero values                      */
+    int64_t n_terminals;   /* alpha: distinct <l, j> terminals in use           */
+    int64_t n_rules;       /* |R|                                                */
+    int64_t n_passthrough; /* +pt: pass-through nodes added by completion       */
+    int64_t depth;         /* L                                                  */
+    int64_t max_width;     /* w*: widest completed level (= streaming buffer)   */
+    int64_t c_len;         /* |C|: symbols of the final sequence                */
+    int64_t n_tiles;       /* RePair tiles                                       */
+    int64_t n_emit_groups; /* (row, level) emission groups                      */
+    double t_csrv_ms;      /* CSRV encoding                                      */
+    double t_repair_ms;    /* RePair (all tiles, wall time)                      */
+    double t_layer_ms;     /* levels + completion + bucketing + layout ("+pt")  */
+} gcs_stats;
+
+typedef struct gcs_grammar gcs_grammar;
+typedef struct gcs_device gcs_device;
+
+/* ---- host builder ---------------------------------------------------- */
+
+/* CSRV encoding (section 2, 'CSRV', Eq. 2.2), RePair never pairing across
+ * rows (section 2 'Grammar', section 4.1), levels (Eq. 3.1), pass-through
+ * completion (section 4.2) and the level-bucketed layout (section 4.3).
+ * opts may be NULL (defaults).  *out receives a new grammar on GCS_OK. */
+gcs_status gcs_build_grammar(const gcs_csr_view* m, const gcs_build_opts* opts, gcs_grammar** out);
+
+/* A grammar given explicitly (e.g. Eq. 2.3-2.4 of the pages' worked
+ * example), then levelled, completed and laid out as above.
+ *   values[n_values]        V, distinct nonzero values
+ *   term_col/term_val[n_terms]  terminal t = <term_val[t]+1, term_col[t]+1>
+ *                           (0-based value index and column), distinct pairs
+ *   rule_a/rule_b[n_rules]  rule i: N_i -> rule_a[i] rule_b[i]; a symbol s <
+ *                           n_terms is terminal s, s >= n_terms is rule
+ *                           s - n_terms, which must be < i (topological order)
+ *   c_off[n_rows+1], c_sym[c_off[n_rows]]  row r's sequence in C.
+ * Rejected (GCS_EINVAL) if any index is out of range or the order is not
+ * topological. */
+gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, const double* values, int64_t n_values,
+                                  const int32_t* term_col, const int32_t* term_val, int64_t n_terms,
+                                  const int32_t* rule_a, const int32_t* rule_b, int64_t n_rules,
+                                  const int64_t* c_off, const int32_t* c_sym, gcs_grammar** out);
+
+gcs_status gcs_grammar_stats(const gcs_grammar* g, gcs_stats* out);
+
+/* Completed widths w_k, k = 0..L (w_0 = alpha, the terminal array).  Writes
+ * min(cap, L+1) entries. */
+gcs_status gcs_level_widths(const gcs_grammar* g, int64_t* w, int64_t cap);
+
+/* Copies of the grammar (test and inspection hooks).  Each pointer may be
+ * NULL to skip that array; sizes follow gcs_grammar_stats.
+ *   values[|V|]; term_col/term_val[alpha]; rule_a/rule_b/rule_level/
+ *   rule_plast[|R|] (plast = highest level of a rule parent, 0 if none);
+ *   c_off[n_rows+1], c_sym[|C|].  Symbols as in gcs_grammar_from_rules. */
+gcs_status gcs_export_grammar(const gcs_grammar* g, double* values, int32_t* term_col, int32_t* term_val,
+                              int32_t* rule_a, int32_t* rule_b, int32_t* rule_level, int32_t* rule_plast,
+                              int64_t* c_off, int32_t* c_sym);
+
+/* The layered layout exactly as uploaded (for host-side emulation).
+ * Arena = [T (alpha) | buffer A | buffer B]; odd levels live in A, even in
+ * B.  Per level k (0..L): level_meta[8*k + ...] =
+ *   {nb, npt, child_off, range_off, n_ranges, base, grp_off, n_grp};
+ * child[2*i], child[2*i+1]: arena offsets of binary node i's children;
+ * range[2*i] = first pass-through index of the range (relative to the level's
+ * pass-through segment), range[2*i+1] = arena offset of its first source;
+ * emit groups g: erow[g], epos[eoff[g] .. eoff[g+1]) (arena offsets).
+ * Counts come from gcs_layout_counts. */
+gcs_status gcs_layout_counts(const gcs_grammar* g, int64_t* counts8);
+/* counts8 = {n_levels (L+1), n_child_pairs, n_ranges, n_groups, n_epos, arena_elems, buf_a, buf_b} */
+gcs_status gcs_export_layout(const gcs_grammar* g, int64_t* level_meta, int32_t* child, int32_t* range,
+                             int32_t* erow, int32_t* eoff, int32_t* epos);
+
+void gcs_free_grammar(gcs_grammar* g);
+
+/* ---- device ----------------------------------------------------------- */
+
+typedef struct {
+    size_t grammar_bytes;   /* read-only grammar image (child indices, ranges, emit lists, terminals, V) */
+    size_t workspace_bytes; /* value arena [T | A | B] plus a 256-byte counter block                    */
+    int64_t x_len;          /* elements of x (= n_cols)                                                 */
+    int64_t y_len;          /* elements of y (= n_rows)                                                 */
+    int32_t x_elem_bytes;
+    int32_t y_elem_bytes;
+} gcs_dev_sizes;
+
+/* Sizes for a policy.  GCS_EINVAL for GCS_PLUS_I64 when V has non-integral
+ * values; GCS_ERANGE if the arena exceeds 2^31 - 1 elements. */
+gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* out);
+
+/* One-time host-to-device copy (the host/device boundary) of the grammar
+ * image into grammar_dev (>= grammar_bytes, 256-byte aligned) on `stream`;
+ * workspace_dev (>= workspace_bytes, 256-byte aligned) is the value arena.
+ * Both stay owned by the caller.  The grammar object may be freed after this
+ * call returns.  The copy is complete when the stream reaches it. */
+gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
+                      void* workspace_dev, size_t workspace_bytes, void* stream, gcs_device** out);
+
+/* y = M x under the uploaded policy: zero y, evaluate the terminal array,
+ * then for k = 1..L evaluate level k and emit the roots of level k-1, and
+ * finally emit level L (section 4.3, Listing 1).  x_dev holds x_len
+ * elements, y_dev y_len elements, both device memory of the policy's types;
+ * x is not modified.  Asynchronous on `stream`.  Calls on one device handle
+ * share its workspace, so they must be ordered (same stream or synchronised). */
+gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
+
+/* BFS fixpoint with the Boolean policy on a square matrix (section 5: one
+ * Boolean pass is one frontier expansion; the fixpoint repeats it):
+ *   f = visited = sources; repeat { y = M f; f = y AND NOT visited;
+ *   visited |= f } until f is empty.
+ * sources_dev: int64 device array of n_sources node ids (< n); frontier_dev,
+ * visited_dev, y_dev: n-byte device arrays.  new_counts (host, cap entries)
+ * receives |f| after each pass (the last pass gives 0); *passes the number
+ * of passes.  Synchronises `stream` once per pass to read the count.
+ * GCS_ESTATE if not uploaded with GCS_BOOL_OR or not square; GCS_ERANGE if the
+ * fixpoint needs more than cap passes. */
+gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t n_sources, uint8_t* frontier_dev,
+                   uint8_t* visited_dev, uint8_t* y_dev, int64_t* new_counts, int64_t cap, int64_t* passes,
+                   void* stream);
+
+/* ---- profiling --------------------------------------------------------- */
+
+/* Kernel launches of one sweep: 1 (terminal array, zero y) + L (level k with
+ * emission of level k-1) + 1 (emission of level L), minus launches with no
+ * work (none when the matrix has nonzeros). */
+int64_t gcs_sweep_launches(const gcs_device* d);
+
+/* Timing of sweeps with HIP events on the sweep's own stream, for
+ * benchmarking.  gcs_profile_begin reserves events for up to max_sweeps
+ * sweeps; each gcs_sweep_right_profiled is gcs_sweep_right plus one event
+ * before every launch and one after the last; gcs_profile_end synchronises
+ * the events and writes launch_ms[s * launches + i] = time from the event
+ * before launch i of sweep s to the next event (the launch's duration
+ * including any gap before the next launch), then releases the events.
+ * GCS_ERANGE if more than max_sweeps sweeps were profiled or cap is too
+ * small; GCS_ESTATE without gcs_profile_begin. */
+gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps);
+gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
+gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t* sweeps, int64_t* launches);
+
+void gcs_free_device(gcs_device* d);
+
+const char* gcs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GCS_H */

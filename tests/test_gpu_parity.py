@@ -1,0 +1,220 @@
+"""Parity of the HIP sweep (through the C ABI) with the CPU oracle.
+
+Tolerances (per row r, s_r = sum_j |M[r][j] x[j]| from the oracle):
+  fp64 and fp32->fp64 policies: |y_r - y_ref_r| <= 1e-12 s_r
+  fp32 policy:                  |y_r - y_ref_r| <= 1e-5  s_r
+  Boolean, int64, x = ones, x = e_j: bit-exact.
+The fp32 bound holds with margin: the sweep sums each row as a tree of depth
+at most L (levels) plus the C length of the row within one (row, level) group
+plus L emissions, and the first-order rounding bound of such a sum is
+depth * 2^-24 * s_r (Higham, Accuracy and Stability of Numerical Algorithms,
+section 4.2); depths here stay below 170.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from grammar_compressed_sparse_amd import gcs
+    return torch, gcs
+
+
+def _sweep(env, g, policy, x_np):
+    torch, gcs = env
+    dev = gcs.upload(g, policy)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to("cuda")
+    y = dev.sweep_right(x)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), dev
+
+
+def _rel_ok(y, yo, absum, tol):
+    err = np.abs(y.astype(np.float64) - yo)
+    zero_rows = absum == 0
+    assert np.all(y[zero_rows] == 0)
+    assert np.all(err <= tol * absum), f"max rel err {np.max(err / np.maximum(absum, 1e-300))}"
+
+
+def test_worked_example_eq23(env, worked_example):
+    torch, gcs = env
+    _say("worked example Eq. 2.3 grammar, fp64")
+    g = gcs.grammar_from_rules(**H.we_grammar_arrays(worked_example))
+    y, _ = _sweep(env, g, gcs.PLUS_F64, np.array(worked_example["x"]["values"], np.float64))
+    rv = worked_example["root_values"]
+    expect = np.array([rv["N%d" % r] for r in worked_example["C"]["row_roots"]])
+    assert np.all(np.abs(y - expect) <= 1e-12 * np.abs(expect))
+
+
+def test_worked_example_own_repair(env, oracle_mod, worked_example):
+    torch, gcs = env
+    rp, col, val = H.csr_from_dense(worked_example["M"]["rows"])
+    g = gcs.build_grammar(rp, col, val, n_cols=7)
+    x = np.array(worked_example["x"]["values"], np.float64)
+    y, _ = _sweep(env, g, gcs.PLUS_F64, x)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    _rel_ok(y, yo, absum, 1e-12)
+
+
+@pytest.fixture(scope="module")
+def c1(env, synth_mod):
+    torch, gcs = env
+    spec = synth_mod.GENOTYPE_512x4096
+    rp, col, val = synth_mod.genotype(spec)
+    g = gcs.build_grammar(rp, col, val, n_cols=spec.n_cols)
+    _say(f"genotype 512x4096 grammar: {g.stats()}")
+    return spec, rp, col, val, g
+
+
+def test_c1_f64(env, oracle_mod, synth_mod, c1):
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    x = synth_mod.normal(spec.n_cols, 101)
+    y, dev = _sweep(env, g, gcs.PLUS_F64, x)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    _rel_ok(y, yo, absum, 1e-12)
+    # repeated sweeps are bit-identical (no atomics in the emission)
+    xt = torch.from_numpy(x).cuda()
+    for _ in range(10):
+        assert np.array_equal(dev.sweep_right(xt).cpu().numpy(), y)
+
+
+def test_c1_exact_cases(env, oracle_mod, synth_mod, c1):
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    m = spec.n_cols
+    for pol, dt in ((gcs.PLUS_F64, np.float64), (gcs.PLUS_F32, np.float32)):
+        y, _ = _sweep(env, g, pol, np.ones(m, dt))
+        yo, _ = oracle_mod.spmv_f64(rp, col, val, np.ones(m))
+        assert np.array_equal(y.astype(np.float64), yo)  # integer row sums < 2^24
+        for j in (0, 1234, m - 1):
+            e = np.zeros(m, dt)
+            e[j] = 1
+            y, _ = _sweep(env, g, pol, e)
+            yo, _ = oracle_mod.spmv_f64(rp, col, val, e)
+            assert np.array_equal(y.astype(np.float64), yo)
+    xi = (np.arange(m, dtype=np.int64) * 7919) % 100_003 - 50_000
+    y, _ = _sweep(env, g, gcs.PLUS_I64, xi)
+    assert np.array_equal(y, oracle_mod.spmv_i64(rp, col, val, xi))
+    xb = (synth_mod.normal(m, 5) > 1.5).astype(np.uint8)
+    y, _ = _sweep(env, g, gcs.BOOL_OR, xb)
+    assert np.array_equal(y, oracle_mod.spmv_bool(rp, col, xb))
+
+
+def test_c1_f32_policies(env, oracle_mod, synth_mod, c1):
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    x32 = synth_mod.normal(spec.n_cols, 102).astype(np.float32)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x32.astype(np.float64))
+    y, _ = _sweep(env, g, gcs.PLUS_F32, x32)
+    _rel_ok(y, yo, absum, 1e-5)
+    y, _ = _sweep(env, g, gcs.PLUS_F32_ACC_F64, x32)
+    assert y.dtype == np.float64
+    _rel_ok(y, yo, absum, 1e-12)
+
+
+@pytest.mark.parametrize("col_chunk,row_chunk", [(0, 0), (997, 0), (1500, 333)])
+def test_genotype_mid_tiles(env, oracle_mod, synth_mod, col_chunk, row_chunk):
+    """Several tiles, ragged tails, many levels and thousands of blocks per launch."""
+    torch, gcs = env
+    spec = synth_mod.GenotypeSpec(2000, 12_000, 32, 300.0, 0.002, seed=12)
+    rp, col, val = synth_mod.genotype(spec)
+    g = gcs.build_grammar(rp, col, val, n_cols=spec.n_cols, col_chunk=col_chunk, row_chunk=row_chunk)
+    st = g.stats()
+    _say(f"genotype 2000x12000 tiles ({col_chunk},{row_chunk}): L={st['depth']} w*={st['max_width']}")
+    x32 = synth_mod.normal(spec.n_cols, 7).astype(np.float32)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x32.astype(np.float64))
+    y, _ = _sweep(env, g, gcs.PLUS_F32, x32)
+    _rel_ok(y, yo, absum, 1e-5)
+    y, _ = _sweep(env, g, gcs.PLUS_F64, x32.astype(np.float64))
+    _rel_ok(y, yo, absum, 1e-12)
+
+
+def test_random_values_many_distinct(env, oracle_mod):
+    torch, gcs = env
+    rng = np.random.default_rng(3)
+    n, m = 300, 500
+    dense = (rng.random((n, m)) < 0.2) * rng.choice(np.linspace(-3, 3, 200), size=(n, m))
+    dense[::7] = dense[0]  # repeated rows so that RePair finds pairs
+    rp, col, val = H.csr_from_dense(dense.tolist())
+    g = gcs.build_grammar(rp, col, val, n_cols=m)
+    x = rng.standard_normal(m)
+    y, _ = _sweep(env, g, gcs.PLUS_F64, x)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    _rel_ok(y, yo, absum, 1e-12)
+
+
+@pytest.mark.parametrize("case", ["identity", "spine", "dense_row", "empty_rows", "no_rows", "no_cols"])
+def test_edge_cases(env, oracle_mod, case):
+    torch, gcs = env
+    if case == "identity":
+        n = m = 1000
+        rp, col = np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32)
+    elif case == "spine":
+        n, m = 5, 300
+        rp, col = np.arange(n + 1, dtype=np.int64) * m, np.tile(np.arange(m, dtype=np.int32), n)
+    elif case == "dense_row":
+        n, m = 1, 70_000
+        rp, col = np.array([0, m], np.int64), np.arange(m, dtype=np.int32)
+    elif case == "empty_rows":
+        n, m = 100, 10
+        rp = np.zeros(n + 1, np.int64)
+        rp[51:] = 3
+        col = np.array([1, 4, 9], np.int32)
+    elif case == "no_rows":
+        n, m = 0, 10
+        rp, col = np.zeros(1, np.int64), np.zeros(0, np.int32)
+    else:
+        n, m = 10, 0
+        rp, col = np.zeros(n + 1, np.int64), np.zeros(0, np.int32)
+    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    x = (np.arange(m) % 13 - 6).astype(np.float64)
+    y, _ = _sweep(env, g, gcs.PLUS_F64, x)
+    yo, _ = oracle_mod.spmv_f64(rp, col, None, x)
+    assert y.shape == (n,) and np.array_equal(y, yo)  # small integers: exact
+
+
+def test_bfs_copy_graph(env, oracle_mod, synth_mod):
+    torch, gcs = env
+    spec = synth_mod.GraphSpec(300_000, seed=55)
+    rp, col = synth_mod.copy_graph(spec)
+    g = gcs.build_grammar(rp, col, None, n_cols=spec.n)
+    st = g.stats()
+    _say(f"copy graph 300K: nnz={st['nnz']} R={st['n_rules']} L={st['depth']}")
+    src = synth_mod.sources(spec.n, 16, 501)
+    dev = gcs.upload(g, gcs.BOOL_OR)
+    vis, counts = dev.bfs(src)
+    vis_o, counts_o = oracle_mod.bfs(rp, col, src)
+    assert np.array_equal(vis.cpu().numpy(), vis_o)
+    assert np.array_equal(counts, counts_o)
+    # one Boolean pass alone
+    xb = np.zeros(spec.n, np.uint8)
+    xb[src] = 1
+    y, _ = _sweep(env, g, gcs.BOOL_OR, xb)
+    assert np.array_equal(y, oracle_mod.spmv_bool(rp, col, xb))
+
+
+def test_abi_errors_on_device(env):
+    torch, gcs = env
+    g = gcs.build_grammar(np.array([0, 2], np.int64), np.array([0, 1], np.int32), None, n_cols=2)
+    dev = gcs.upload(g, gcs.PLUS_F32)
+    with pytest.raises(gcs.GcsError):
+        dev.sweep_right(torch.zeros(3, dtype=torch.float32, device="cuda"))  # wrong length
+    with pytest.raises(gcs.GcsError):
+        dev.sweep_right(torch.zeros(2, dtype=torch.float64, device="cuda"))  # wrong dtype
+    with pytest.raises(gcs.GcsError, match="ESTATE"):
+        dev.bfs([0])  # not Boolean (matrix is 1x2 and policy fp32)
