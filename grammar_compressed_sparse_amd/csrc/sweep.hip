@@ -47,6 +47,7 @@ struct PolPlusF64 {
     __device__ static A comb(A a, A b) { return a + b; }
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0; }
+    __device__ static A ident() { return 0.0; }
 };
 struct PolPlusF32 {
     using X = float;
@@ -57,6 +58,7 @@ struct PolPlusF32 {
     __device__ static A comb(A a, A b) { return a + b; }
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0f; }
+    __device__ static A ident() { return 0.0f; }
 };
 struct PolPlusF32AccF64 {
     using X = float;
@@ -67,6 +69,7 @@ struct PolPlusF32AccF64 {
     __device__ static A comb(A a, A b) { return a + b; }
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0; }
+    __device__ static A ident() { return 0.0; }
 };
 struct PolBoolOr {
     using X = uint8_t;
@@ -77,6 +80,7 @@ struct PolBoolOr {
     __device__ static A comb(A a, A b) { return a | b; }
     __device__ static Y emit(Y y, A s) { return y | s; }
     __device__ static Y yzero() { return 0; }
+    __device__ static A ident() { return 0; }
 };
 struct PolPlusI64 {
     using X = int64_t;
@@ -87,7 +91,14 @@ struct PolPlusI64 {
     __device__ static A comb(A a, A b) { return a + b; }
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0; }
+    __device__ static A ident() { return 0; }
 };
+
+// lane exchange inside a wave for every arena type
+__device__ inline double xchg(double v, int m) { return __shfl_xor(v, m, 64); }
+__device__ inline float xchg(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ inline int64_t xchg(int64_t v, int m) { return __shfl_xor((long long)v, m, 64); }
+__device__ inline uint8_t xchg(uint8_t v, int m) { return (uint8_t)__shfl_xor((int)v, m, 64); }
 
 // ---------------------------------------------------------------- kernels
 
@@ -116,6 +127,7 @@ struct LevelArgs {
     int32_t nb, npt, nranges, ngrp;
     int32_t cur;           // arena offset of this level's buffer
     int32_t blk_bin, blk_pt;
+    int32_t team_log2;     // lanes per emission group = 1 << team_log2 (<= 64)
 };
 
 template <class P>
@@ -153,11 +165,19 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
             arena[a.cur + a.nb + t] = arena[r.y + (t - r.x)];
         }
     } else {
-        const int32_t g = (b - a.blk_bin - a.blk_pt) * kBlock + threadIdx.x;
+        // a team of 2^team_log2 adjacent lanes per (row, level) group: lanes
+        // stride over the group's roots, then a fixed xor butterfly combines
+        // the team (deterministic), and the team's first lane updates y[row]
+        const int32_t gl = (b - a.blk_bin - a.blk_pt) * kBlock + threadIdx.x;
+        const int32_t team = 1 << a.team_log2;
+        const int32_t g = gl >> a.team_log2, sub = gl & (team - 1);
+        A s = P::ident();
         if (g < a.ngrp) {
-            const int32_t e0 = a.eoff[g], e1 = a.eoff[g + 1];
-            A s = arena[a.epos[e0]];
-            for (int32_t e = e0 + 1; e < e1; ++e) s = P::comb(s, arena[a.epos[e]]);
+            const int32_t e1 = a.eoff[g + 1];
+            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
+        }
+        for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+        if (g < a.ngrp && sub == 0) {
             const int32_t row = a.erow[g];
             y[row] = P::emit(y[row], s);
         }
@@ -216,6 +236,7 @@ struct gcs_device {
     int device;
     int64_t n_rows, n_cols, alpha, L;
     std::vector<gcs::Level> lv;
+    std::vector<int32_t> team_log2;  // per level: lanes per emission group
     const int2* child;
     const int2* range;
     const int32_t *erow, *eoff, *epos, *tcol, *tval;
@@ -393,7 +414,8 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         a.ngrp = (int32_t)e.ngrp;
         a.blk_bin = (a.nb + kBlock * kBinItems - 1) / (kBlock * kBinItems);
         a.blk_pt = (a.npt + kBlock - 1) / kBlock;
-        const int32_t blk_emit = (a.ngrp + kBlock - 1) / kBlock;
+        a.team_log2 = d->team_log2[k - 1];
+        const int32_t blk_emit = (int32_t)(((int64_t)a.ngrp << a.team_log2) + kBlock - 1) / kBlock;
         const int32_t grid = a.blk_bin + a.blk_pt + blk_emit;
         if (grid > 0) {
             mark();
@@ -509,6 +531,17 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->alpha = g.alpha();
     d->L = g.L;
     d->lv = g.lv;
+    // emission team per level: about four roots per lane, at most one wave
+    d->team_log2.assign(g.lv.size(), 0);
+    for (size_t k = 0; k < g.lv.size(); ++k) {
+        const gcs::Level& l = g.lv[k];
+        if (l.ngrp == 0) continue;
+        const int64_t roots = g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off];
+        const double per_lane = 4.0, mean = (double)roots / (double)l.ngrp;
+        int t = 0;
+        while (t < 6 && (double)(1 << t) * per_lane < mean && (l.ngrp << (t + 1)) < (int64_t)INT32_MAX - gcs::kBlock) ++t;
+        d->team_log2[k] = t;
+    }
     d->child = (const int2*)(base + im.child);
     d->range = (const int2*)(base + im.range);
     d->erow = (const int32_t*)(base + im.erow);

@@ -289,6 +289,10 @@ def upload(grammar: Grammar, policy, device="cuda", stream=None) -> Device:
     policy = POLICY_NAMES.get(policy, policy)
     sz = grammar.device_layout(policy)
     dev = torch.device(device)
+    if dev.type != "cuda":
+        raise GcsError(-1, "upload needs a GPU device")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
     with torch.cuda.device(dev):
         gbuf = torch.empty(max(sz["grammar_bytes"], 256), dtype=torch.uint8, device=dev)
         wbuf = torch.empty(max(sz["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
