@@ -33,9 +33,10 @@ def log(msg):
 
 def level_bytes(lay, elem, yelem):
     """Algorithmic bytes of each level launch k = 1..L: child indices (8 B per
-    binary node), one write per completed node, one read of every value of
-    level k-1 (the terminal array for k = 1), and the emission of level k-1
-    (erow + eoff per group, 4 B epos per root, y read and written per group)."""
+    binary node, 4 B per pass-through node), one write per completed node, one
+    read of every value of level k-1 (the terminal array for k = 1), and the
+    emission of level k-1 (erow + eoff per group, 4 B epos per root, y read and
+    written per group)."""
     meta = lay["level_meta"]
     L = meta.shape[0] - 1
     eoff = lay["eoff"]
@@ -48,7 +49,7 @@ def level_bytes(lay, elem, yelem):
             prev_w = int(meta[k - 1][0] + meta[k - 1][1])
         g0, ng = int(meta[k - 1][6]), int(meta[k - 1][7])
         roots = int(eoff[g0 + ng] - eoff[g0]) if ng else 0
-        b = 8 * nb + elem * (nb + npt) + elem * prev_w + 8 * ng + 4 * roots + 2 * yelem * ng
+        b = 8 * nb + 4 * npt + elem * (nb + npt) + elem * prev_w + 8 * ng + 4 * roots + 2 * yelem * ng
         out.append(b)
     return np.array(out, np.float64)
 

@@ -71,16 +71,16 @@ static double ms_since(std::chrono::steady_clock::time_point t0)
 // level holds exactly the values alive across it.
 //
 // Layout of level k (section 4.3: levels contiguous, buffers alternate):
-//   [ binary nodes not needed above level k+1, in rule order
-//   | binary nodes carried upward ("block k"), by P descending
-//   | pass-through segment ]
-// The pass-through segment of level k is the concatenation, for origin levels
-// j = k-1, k-2, ..., 1, of the prefix of block j whose chains still reach
-// level k (P(v) >= k+1).  Because every block is sorted by P descending, the
-// prefix for level k is a prefix of the one for level k-1, so each origin's
-// copies read one contiguous source range of level k-1 and write one
-// contiguous range of level k: the pass-through segment is a handful of range
-// copies (at most k-1, merged when adjacent) with no per-node index.
+//   [ binary nodes (rules of level k) | pass-through nodes ]
+// each segment ordered by the first column of the node's expansion, then by
+// rule id.  A rule's expansion is a run of consecutive columns and its left
+// child starts at the same column, so consecutive parents read children that
+// sit close together in the level below: the gathers of a wavefront touch few
+// cache lines.  (The pages keep nodes in RePair index order for the same
+// purpose.)  Each pass-through node stores the arena offset of its source;
+// the pass-through nodes of level k are the carried binary nodes of level k-1
+// merged with the continuing pass-through nodes of level k-1, two lists that
+// are already sorted by first column.
 gcs_status finish_layout(Grammar& g)
 {
     auto t0 = std::chrono::steady_clock::now();
@@ -91,19 +91,21 @@ gcs_status finish_layout(Grammar& g)
     }
     g.lvl.assign((size_t)R, 0);
     g.plast.assign((size_t)R, 0);
+    std::vector<int32_t> fc((size_t)R, 0);  // first column of the expansion
     int32_t L = 0;
     for (int64_t i = 0; i < R; ++i) {
         int32_t a = g.ra[i], b = g.rb[i];
         int32_t la = a < alpha ? 0 : g.lvl[a - alpha], lb = b < alpha ? 0 : g.lvl[b - alpha];
         int32_t l = 1 + std::max(la, lb);
         g.lvl[i] = l;
+        fc[i] = a < alpha ? g.tcol[a] : fc[a - alpha];
         L = std::max(L, l);
         if (a >= alpha) g.plast[a - alpha] = std::max(g.plast[a - alpha], l);
         if (b >= alpha) g.plast[b - alpha] = std::max(g.plast[b - alpha], l);
     }
     g.L = L;
 
-    // bucket rules by level; split into non-carried / carried (block)
+    // rules of each level, ordered by (first column, id)
     std::vector<int64_t> cnt_lvl((size_t)L + 2, 0);
     for (int64_t i = 0; i < R; ++i) cnt_lvl[g.lvl[i]]++;
     std::vector<int64_t> lvl_start((size_t)L + 2, 0);
@@ -113,46 +115,46 @@ gcs_status finish_layout(Grammar& g)
         std::vector<int64_t> fill(lvl_start.begin(), lvl_start.end());
         for (int64_t i = 0; i < R; ++i) order[fill[g.lvl[i]]++] = (int32_t)i;
     }
-    std::vector<int64_t> nonc((size_t)L + 1, 0);   // non-carried count per level
-    std::vector<int32_t> pos((size_t)R, 0);         // position within own level
-    std::vector<int32_t> rank((size_t)R, -1);       // rank within own block
-    std::vector<std::vector<int32_t>> block_plast((size_t)L + 1);  // P values of block j, descending
+    auto by_fc = [&](int32_t u, int32_t v) { return fc[u] != fc[v] ? fc[u] < fc[v] : u < v; };
+    std::vector<int32_t> pos((size_t)R, 0);  // position within own level
     for (int k = 1; k <= L; ++k) {
         auto b = order.begin() + lvl_start[k], e = order.begin() + lvl_start[k + 1];
-        auto mid = std::stable_partition(b, e, [&](int32_t v) { return g.plast[v] < k + 2; });
-        std::stable_sort(mid, e, [&](int32_t u, int32_t v) { return g.plast[u] > g.plast[v]; });
-        nonc[k] = mid - b;
+        std::sort(b, e, by_fc);  // ids are unique: the order is total
         int32_t p = 0;
         for (auto it = b; it != e; ++it) pos[*it] = p++;
-        int32_t rk = 0;
-        for (auto it = mid; it != e; ++it) {
-            rank[*it] = rk++;
-            block_plast[k].push_back(g.plast[*it]);
-        }
     }
-    // cnt(j, k) = |{v in block j : P(v) >= k+1}| for j < k
-    auto cnt_reach = [&](int j, int k) -> int64_t {
-        const auto& bp = block_plast[j];
-        // bp descending: count of entries >= k+1
-        return std::upper_bound(bp.begin(), bp.end(), k + 1, [](int32_t key, int32_t x) { return key > x; }) -
-               bp.begin();
-    };
-    // offsets of origin blocks inside each level's pass-through segment
-    std::vector<std::vector<int64_t>> ptoff((size_t)L + 1);  // ptoff[k][j], j < k
+
     g.lv.assign((size_t)L + 1, Level{});
+    g.lv[0] = Level{};
     g.wmax = 0;
     g.pt_total = 0;
+    // pass-through lists, level by level: pt(k) = {v : lvl v < k <= P(v) - 1}
+    std::vector<int32_t> pt_prev, pt_cur;        // rule ids, sorted by (fc, id)
+    std::vector<int32_t> ptpos_a((size_t)R, -1), ptpos_b((size_t)R, -1);
+    std::vector<int32_t>* ptpos_prev = &ptpos_a;  // position in level k-1's pt segment
+    std::vector<int32_t>* ptpos_cur = &ptpos_b;
+    std::vector<int64_t> nb_of((size_t)L + 1, 0), npt_of((size_t)L + 1, 0);
+    std::vector<std::vector<int32_t>> pt_lists((size_t)L + 1);
     for (int k = 1; k <= L; ++k) {
-        ptoff[k].assign((size_t)k, 0);
-        int64_t o = 0;
-        for (int j = k - 1; j >= 1; --j) {
-            ptoff[k][j] = o;
-            o += cnt_reach(j, k);
+        // carried binaries of level k-1 (P >= k+1) and continuing pass-throughs (P >= k+1)
+        pt_cur.clear();
+        if (k >= 2) {
+            auto b = order.begin() + lvl_start[k - 1], e = order.begin() + lvl_start[k];
+            std::vector<int32_t> carried;
+            for (auto it = b; it != e; ++it)
+                if (g.plast[*it] >= k + 1) carried.push_back(*it);
+            std::vector<int32_t> cont;
+            for (int32_t v : pt_prev)
+                if (g.plast[v] >= k + 1) cont.push_back(v);
+            pt_cur.resize(carried.size() + cont.size());
+            std::merge(carried.begin(), carried.end(), cont.begin(), cont.end(), pt_cur.begin(), by_fc);
         }
-        g.lv[k].nb = cnt_lvl[k];
-        g.lv[k].npt = o;
-        g.pt_total += o;
-        g.wmax = std::max<int64_t>(g.wmax, cnt_lvl[k] + o);
+        pt_lists[k] = pt_cur;
+        nb_of[k] = cnt_lvl[k];
+        npt_of[k] = (int64_t)pt_cur.size();
+        g.pt_total += npt_of[k];
+        g.wmax = std::max<int64_t>(g.wmax, nb_of[k] + npt_of[k]);
+        pt_prev.swap(pt_cur);
     }
     auto align64 = [](int64_t v) { return (v + 63) & ~int64_t(63); };
     g.buf_a = align64(alpha);
@@ -162,56 +164,40 @@ gcs_status finish_layout(Grammar& g)
         set_error("value arena exceeds 2^31-1 elements");
         return GCS_ERANGE;
     }
-    g.lv[0].base = 0;
-    g.lv[0].nb = 0;
-    g.lv[0].npt = 0;
-    for (int k = 1; k <= L; ++k) g.lv[k].base = (k & 1) ? g.buf_a : g.buf_b;
-
-    // arena offset of nonterminal v as read by a parent at level k
-    auto read_off = [&](int32_t v, int k) -> int32_t {
-        int lv = g.lvl[v];
-        const Level& P = g.lv[k - 1];
-        if (lv == k - 1) return (int32_t)(P.base + pos[v]);
-        return (int32_t)(P.base + P.nb + ptoff[k - 1][lv] + rank[v]);
-    };
-
-    // children
-    g.child.resize((size_t)2 * R);
-    int64_t co = 0;
     for (int k = 1; k <= L; ++k) {
+        g.lv[k].nb = nb_of[k];
+        g.lv[k].npt = npt_of[k];
+        g.lv[k].base = (k & 1) ? g.buf_a : g.buf_b;
+    }
+
+    // children and pass-through sources
+    g.child.resize((size_t)2 * R);
+    g.ptsrc.resize((size_t)g.pt_total);
+    int64_t co = 0, po = 0;
+    for (int k = 1; k <= L; ++k) {
+        const Level& P = g.lv[k - 1];
+        // arena offset of nonterminal v as read at level k (v alive at level k-1)
+        auto read_off = [&](int32_t v) -> int32_t {
+            if (g.lvl[v] == k - 1) return (int32_t)(P.base + pos[v]);
+            return (int32_t)(P.base + P.nb + (*ptpos_prev)[v]);
+        };
         g.lv[k].child_off = co;
         for (int64_t t = lvl_start[k]; t < lvl_start[k + 1]; ++t) {
             int32_t v = order[t];
             int32_t a = g.ra[v], b = g.rb[v];
-            g.child[2 * (co + pos[v])] = a < alpha ? a : read_off(a - (int32_t)alpha, k);
-            g.child[2 * (co + pos[v]) + 1] = b < alpha ? b : read_off(b - (int32_t)alpha, k);
+            g.child[2 * (co + pos[v])] = a < alpha ? a : read_off(a - (int32_t)alpha);
+            g.child[2 * (co + pos[v]) + 1] = b < alpha ? b : read_off(b - (int32_t)alpha);
         }
-        co += cnt_lvl[k];
-    }
-    // pass-through ranges
-    g.range.clear();
-    int64_t ro = 0;
-    for (int k = 1; k <= L; ++k) {
-        g.lv[k].range_off = ro;
-        int64_t nr = 0, last_dst_end = -1, last_src_end = -1;
-        for (int j = k - 1; j >= 1; --j) {
-            int64_t c = cnt_reach(j, k);
-            if (c == 0) continue;
-            int64_t dst = ptoff[k][j];
-            const Level& P = g.lv[k - 1];
-            int64_t src = (j == k - 1) ? P.base + nonc[k - 1] : P.base + P.nb + ptoff[k - 1][j];
-            if (nr > 0 && dst == last_dst_end && src == last_src_end) {
-                // extends the previous range
-            } else {
-                g.range.push_back((int32_t)dst);
-                g.range.push_back((int32_t)src);
-                ++nr;
-            }
-            last_dst_end = dst + c;
-            last_src_end = src + c;
+        co += nb_of[k];
+        g.lv[k].pt_off = po;
+        const auto& pl = pt_lists[k];
+        for (size_t i = 0; i < pl.size(); ++i) {
+            g.ptsrc[po + i] = read_off(pl[i]);
+            (*ptpos_cur)[pl[i]] = (int32_t)i;
         }
-        g.lv[k].nranges = nr;
-        ro += nr;
+        po += (int64_t)pl.size();
+        std::swap(ptpos_prev, ptpos_cur);
+        std::vector<int32_t>().swap(pt_lists[k]);
     }
 
     // emission groups: C-occurrences at their symbol's level, grouped by
@@ -710,7 +696,7 @@ extern "C" gcs_status gcs_layout_counts(const gcs_grammar* h, int64_t* c)
     const Grammar& g = h->g;
     c[0] = g.L + 1;
     c[1] = (int64_t)g.child.size() / 2;
-    c[2] = (int64_t)g.range.size() / 2;
+    c[2] = (int64_t)g.ptsrc.size();
     c[3] = (int64_t)g.erow.size();
     c[4] = (int64_t)g.epos.size();
     c[5] = g.arena;
@@ -719,7 +705,7 @@ extern "C" gcs_status gcs_layout_counts(const gcs_grammar* h, int64_t* c)
     return GCS_OK;
 }
 
-extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_meta, int32_t* child, int32_t* range,
+extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_meta, int32_t* child, int32_t* ptsrc,
                                         int32_t* erow, int32_t* eoff, int32_t* epos)
 {
     if (!h) {
@@ -734,8 +720,8 @@ extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_met
             o[0] = l.nb;
             o[1] = l.npt;
             o[2] = l.child_off;
-            o[3] = l.range_off;
-            o[4] = l.nranges;
+            o[3] = l.pt_off;
+            o[4] = 0;
             o[5] = l.base;
             o[6] = l.grp_off;
             o[7] = l.ngrp;
@@ -744,7 +730,7 @@ extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_met
         if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(v[0]));
     };
     cp(child, g.child);
-    cp(range, g.range);
+    cp(ptsrc, g.ptsrc);
     cp(erow, g.erow);
     cp(eoff, g.eoff);
     cp(epos, g.epos);

@@ -30,8 +30,8 @@ struct Level {
     int64_t nb;        // binary nodes (rules whose level is k)
     int64_t npt;       // pass-through nodes
     int64_t child_off; // first child pair of this level
-    int64_t range_off; // first pass-through range of this level
-    int64_t nranges;
+    int64_t pt_off;    // first pass-through source of this level
+    int64_t reserved;
     int64_t base;      // arena offset of this level's values (level 0: terminal array)
     int64_t grp_off;   // first emission group of this level
     int64_t ngrp;
@@ -50,7 +50,7 @@ struct Grammar {
     // layout (section 4.3)
     std::vector<Level> lv;                 // 0..L
     std::vector<int32_t> child;            // 2 per binary node
-    std::vector<int32_t> range;            // 2 per pass-through range {first pt index, first source}
+    std::vector<int32_t> ptsrc;            // arena offset of each pass-through node's source
     std::vector<int32_t> erow, eoff, epos; // emission groups
     int64_t wmax = 0, pt_total = 0, buf_a = 0, buf_b = 0, arena = 0;
     double t_csrv = 0, t_repair = 0, t_layer = 0;

@@ -6,7 +6,7 @@
 // policies).
 //
 // Device memory (all owned by the caller):
-//   grammar image  child pairs | pass-through ranges | emission groups
+//   grammar image  child pairs | pass-through sources | emission groups
 //                  (erow, eoff, epos) | terminal descriptors | V
 //   workspace      value arena [T (alpha) | buffer A | buffer B] | counters
 // Level k's values live in A (k odd) or B (k even); every child index is an
@@ -17,7 +17,7 @@
 // One sweep = 1 + (L + 1) launches on the caller's stream:
 //   leaf:        T[p] = V[l_p] (x) x[j_p], and y = identity
 //   level k:     binary nodes  cur[t] = arena[left] (+) arena[right]
-//                pass-throughs cur[nb + t] = arena[src(t)] (range copies)
+//                pass-throughs cur[nb + t] = arena[src[t]]
 //                emission of level k-1: y[row] = y[row] (+) sum of its roots
 //   final:       emission of level L
 // Emission of a level runs in the launch after the level is computed, while
@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -120,11 +121,11 @@ __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict_
 
 struct LevelArgs {
     const int2* child;     // this level's binary nodes
-    const int2* range;     // this level's pass-through ranges {first index, first source}
+    const int32_t* ptsrc;  // this level's pass-through sources
     const int32_t* erow;   // emission groups of the previous level
     const int32_t* eoff;
     const int32_t* epos;
-    int32_t nb, npt, nranges, ngrp;
+    int32_t nb, npt, xcd_remap, ngrp;
     int32_t cur;           // arena offset of this level's buffer
     int32_t blk_bin, blk_pt;
     int32_t team_log2;     // lanes per emission group = 1 << team_log2 (<= 64)
@@ -135,7 +136,14 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
                                                        typename P::Y* __restrict__ y)
 {
     using A = typename P::A;
-    const int32_t b = blockIdx.x;
+    int32_t b = blockIdx.x;
+    if (a.xcd_remap) {
+        // workgroups are dealt to the 8 XCDs round-robin; renumber them so
+        // that each XCD (and its L2) works on one contiguous share of the
+        // level, whose children sit together in the level below
+        const int32_t G = gridDim.x, x = b & 7, i = b >> 3, q = G >> 3, r = G & 7;
+        b = x * q + (x < r ? x : r) + i;
+    }
     if (b < a.blk_bin) {
         const int32_t t0 = b * (kBlock * kBinItems) + threadIdx.x;
         int2 c[kBinItems];
@@ -153,16 +161,20 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
             if (t < a.nb) arena[a.cur + t] = v[u];
         }
     } else if (b < a.blk_bin + a.blk_pt) {
-        const int32_t t = (b - a.blk_bin) * kBlock + threadIdx.x;
-        if (t < a.npt) {
-            int32_t lo = 0, hi = a.nranges - 1;
-            while (lo < hi) {
-                const int32_t mid = (lo + hi + 1) >> 1;
-                if (a.range[mid].x <= t) lo = mid;
-                else hi = mid - 1;
-            }
-            const int2 r = a.range[lo];
-            arena[a.cur + a.nb + t] = arena[r.y + (t - r.x)];
+        const int32_t t0 = (b - a.blk_bin) * (kBlock * kBinItems) + threadIdx.x;
+        int32_t src[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kBlock;
+            src[u] = t < a.npt ? a.ptsrc[t] : 0;
+        }
+        A v[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u]];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kBlock;
+            if (t < a.npt) arena[a.cur + a.nb + t] = v[u];
         }
     } else {
         // a team of 2^team_log2 adjacent lanes per (row, level) group: lanes
@@ -237,8 +249,9 @@ struct gcs_device {
     int64_t n_rows, n_cols, alpha, L;
     std::vector<gcs::Level> lv;
     std::vector<int32_t> team_log2;  // per level: lanes per emission group
+    int32_t xcd_remap;
     const int2* child;
-    const int2* range;
+    const int32_t* ptsrc;
     const int32_t *erow, *eoff, *epos, *tcol, *tval;
     const void* V;
     void* arena;
@@ -271,7 +284,7 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, range, erow, eoff, epos, tcol, tval, V, total;
+    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, total;
 };
 
 Image image_layout(const Grammar& g, gcs_policy p)
@@ -280,8 +293,8 @@ Image image_layout(const Grammar& g, gcs_policy p)
     size_t o = 0;
     m.child = o;
     o = al256(o + g.child.size() * 4);
-    m.range = o;
-    o = al256(o + g.range.size() * 4);
+    m.ptsrc = o;
+    o = al256(o + g.ptsrc.size() * 4);
     m.erow = o;
     o = al256(o + g.erow.size() * 4);
     m.eoff = o;
@@ -310,17 +323,17 @@ bool layout_in_bounds(const Grammar& g)
     const int64_t arena = g.arena, alpha = g.alpha();
     for (int32_t c : g.child)
         if (c < 0 || c >= arena) return false;
+    for (int32_t c : g.ptsrc)
+        if (c < 0 || c >= arena) return false;
+    int64_t co = 0, po = 0;
     for (int k = 1; k <= g.L; ++k) {
         const Level& l = g.lv[k];
         if (l.base < 0 || l.base + l.nb + l.npt > arena) return false;
-        for (int64_t r = 0; r < l.nranges; ++r) {
-            const int64_t dst = g.range[2 * (l.range_off + r)], src = g.range[2 * (l.range_off + r) + 1];
-            const int64_t end = r + 1 < l.nranges ? g.range[2 * (l.range_off + r + 1)] : l.npt;
-            if (dst < 0 || end < dst || end > l.npt || src < 0 || src + (end - dst) > arena) return false;
-            if (r == 0 && dst != 0) return false;
-        }
-        if (l.npt > 0 && l.nranges == 0) return false;
+        if (l.child_off != co || l.pt_off != po) return false;
+        co += l.nb;
+        po += l.npt;
     }
+    if (2 * co != (int64_t)g.child.size() || po != (int64_t)g.ptsrc.size()) return false;
     for (size_t i = 0; i + 1 < g.eoff.size(); ++i)
         if (g.eoff[i] < 0 || g.eoff[i] > g.eoff[i + 1]) return false;
     if (!g.eoff.empty() && g.eoff.back() != (int32_t)g.epos.size()) return false;
@@ -401,10 +414,9 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         if (k <= d->L) {
             const Level& l = d->lv[k];
             a.child = d->child + l.child_off;
-            a.range = d->range + l.range_off;
+            a.ptsrc = d->ptsrc + l.pt_off;
             a.nb = (int32_t)l.nb;
             a.npt = (int32_t)l.npt;
-            a.nranges = (int32_t)l.nranges;
             a.cur = (int32_t)l.base;
         }
         const Level& e = d->lv[k - 1];
@@ -413,7 +425,8 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         a.epos = d->epos;
         a.ngrp = (int32_t)e.ngrp;
         a.blk_bin = (a.nb + kBlock * kBinItems - 1) / (kBlock * kBinItems);
-        a.blk_pt = (a.npt + kBlock - 1) / kBlock;
+        a.blk_pt = (a.npt + kBlock * kBinItems - 1) / (kBlock * kBinItems);
+        a.xcd_remap = d->xcd_remap;
         a.team_log2 = d->team_log2[k - 1];
         const int32_t blk_emit = (int32_t)(((int64_t)a.ngrp << a.team_log2) + kBlock - 1) / kBlock;
         const int32_t grid = a.blk_bin + a.blk_pt + blk_emit;
@@ -510,7 +523,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const void* src;
         size_t bytes;
     } secs[] = {
-        {im.child, g.child.data(), g.child.size() * 4}, {im.range, g.range.data(), g.range.size() * 4},
+        {im.child, g.child.data(), g.child.size() * 4}, {im.ptsrc, g.ptsrc.data(), g.ptsrc.size() * 4},
         {im.erow, g.erow.data(), g.erow.size() * 4},    {im.eoff, g.eoff.data(), g.eoff.size() * 4},
         {im.epos, g.epos.data(), g.epos.size() * 4},    {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
@@ -531,6 +544,10 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->alpha = g.alpha();
     d->L = g.L;
     d->lv = g.lv;
+    {
+        const char* e = std::getenv("GCS_XCD_REMAP");
+        d->xcd_remap = e ? std::atoi(e) != 0 : 1;
+    }
     // emission team per level: about four roots per lane, at most one wave
     d->team_log2.assign(g.lv.size(), 0);
     for (size_t k = 0; k < g.lv.size(); ++k) {
@@ -543,7 +560,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         d->team_log2[k] = t;
     }
     d->child = (const int2*)(base + im.child);
-    d->range = (const int2*)(base + im.range);
+    d->ptsrc = (const int32_t*)(base + im.ptsrc);
     d->erow = (const int32_t*)(base + im.erow);
     d->eoff = (const int32_t*)(base + im.eoff);
     d->epos = (const int32_t*)(base + im.epos);

@@ -139,10 +139,10 @@ class Grammar:
         _check(_lib.gcs_layout_counts(self._h, _ptr(c)))
         nl, ncp, nr, ng, ne, arena, ba, bb = (int(v) for v in c)
         out = dict(level_meta=np.zeros((nl, 8), np.int64), child=np.zeros((ncp, 2), np.int32),
-                   range=np.zeros((nr, 2), np.int32), erow=np.zeros(ng, np.int32), eoff=np.zeros(ng + 1, np.int32),
+                   ptsrc=np.zeros(nr, np.int32), erow=np.zeros(ng, np.int32), eoff=np.zeros(ng + 1, np.int32),
                    epos=np.zeros(ne, np.int32), arena=arena, buf_a=ba, buf_b=bb)
         _check(_lib.gcs_export_layout(self._h, *[_ptr(out[k]) for k in (
-            "level_meta", "child", "range", "erow", "eoff", "epos")]))
+            "level_meta", "child", "ptsrc", "erow", "eoff", "epos")]))
         return out
 
     def device_layout(self, policy: int) -> dict:

@@ -153,16 +153,16 @@ gcs_status gcs_export_grammar(const gcs_grammar* g, double* values, int32_t* ter
 
 /* The layered layout exactly as uploaded (for host-side emulation).
  * Arena = [T (alpha) | buffer A | buffer B]; odd levels live in A, even in
- * B.  Per level k (0..L): level_meta[8*k + ...] =
- *   {nb, npt, child_off, range_off, n_ranges, base, grp_off, n_grp};
+ * B.  Level k occupies [base, base + nb + npt): its nb binary nodes, then its
+ * npt pass-through nodes.  Per level k (0..L): level_meta[8*k + ...] =
+ *   {nb, npt, child_off, pt_off, 0, base, grp_off, n_grp};
  * child[2*i], child[2*i+1]: arena offsets of binary node i's children;
- * range[2*i] = first pass-through index of the range (relative to the level's
- * pass-through segment), range[2*i+1] = arena offset of its first source;
+ * ptsrc[i]: arena offset of pass-through node i's source;
  * emit groups g: erow[g], epos[eoff[g] .. eoff[g+1]) (arena offsets).
  * Counts come from gcs_layout_counts. */
 gcs_status gcs_layout_counts(const gcs_grammar* g, int64_t* counts8);
-/* counts8 = {n_levels (L+1), n_child_pairs, n_ranges, n_groups, n_epos, arena_elems, buf_a, buf_b} */
-gcs_status gcs_export_layout(const gcs_grammar* g, int64_t* level_meta, int32_t* child, int32_t* range,
+/* counts8 = {n_levels (L+1), n_child_pairs, n_passthrough, n_groups, n_epos, arena_elems, buf_a, buf_b} */
+gcs_status gcs_export_layout(const gcs_grammar* g, int64_t* level_meta, int32_t* child, int32_t* ptsrc,
                              int32_t* erow, int32_t* eoff, int32_t* epos);
 
 void gcs_free_grammar(gcs_grammar* g);
@@ -170,7 +170,7 @@ void gcs_free_grammar(gcs_grammar* g);
 /* ---- device ----------------------------------------------------------- */
 
 typedef struct {
-    size_t grammar_bytes;   /* read-only grammar image (child indices, ranges, emit lists, terminals, V) */
+    size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, terminals, V) */
     size_t workspace_bytes; /* value arena [T | A | B] plus a 256-byte counter block                    */
     int64_t x_len;          /* elements of x (= n_cols)                                                 */
     int64_t y_len;          /* elements of y (= n_rows)                                                 */

@@ -163,12 +163,7 @@ def emulate_layout(lay, ex, x, op="plus", dtype=np.float64, poison=True):
                 arena[base:base + width] = bad
             ch = lay["child"][co:co + nb]
             vals = comb(arena[ch[:, 0]], arena[ch[:, 1]])
-            rg = lay["range"][ro:ro + nr]
-            bounds = list(rg[:, 0]) + [npt]
-            ptv = np.empty(npt, dtype)
-            for i in range(nr):
-                d0, d1, s0 = bounds[i], bounds[i + 1], rg[i, 1]
-                ptv[d0:d1] = arena[s0:s0 + (d1 - d0)]
+            ptv = arena[lay["ptsrc"][ro:ro + npt]]
             emit(k - 1)  # reads level k-1 before level k overwrites nothing of it
             arena[base:base + nb] = vals
             arena[base + nb:base + nb + npt] = ptv
