@@ -142,7 +142,7 @@ def main():
 
     # correctness on sampled rows (outside the timed region)
     dev.sweep_right(xs[0], y)
-    torch.cuda.synchronize()
+    dev.check()
     rows = np.unique(np.concatenate([np.arange(0, spec.n_rows, max(1, spec.n_rows // 512)), [spec.n_rows - 1]]))
     yo, absum = oracle.spmv_f64_rows(rows, rp, col, val, xs[0].cpu().numpy().astype(np.float64))
     err = np.abs(y.cpu().numpy().astype(np.float64)[rows] - yo) / np.maximum(absum, 1e-300)
@@ -162,15 +162,21 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     launch_ms = dev.profile_end()  # (steps, launches)
+    dev.check()
     ms_per_step = elapsed * 1e3 / args.steps
     L = st["depth"]
-    # launch 0 = terminal array, 1..L = levels (with emission of the previous level), L+1 = last emission
-    lvl_ms = launch_ms[:, 1:L + 1].mean(axis=0)
-    lb = level_bytes(lay, elem, elem)
+    # launch 0 = terminal array, 1..k0-1 = wide levels (each with the emission
+    # of the level below), last = the persistent tail (levels k0..L, the last
+    # emission and the slice reduction)
+    nwide = launch_ms.shape[1] - 2
+    lvl_ms = launch_ms[:, 1:1 + nwide].mean(axis=0)
+    tail_ms = float(launch_ms[:, -1].mean())
+    lb_all = level_bytes(lay, elem, elem)
+    lb = lb_all[:nwide]
     achieved = lb.sum() / (lvl_ms.sum() * 1e-3) / 1e9
     per_level = [{"k": k + 1, "width": int(lay["level_meta"][k + 1][0] + lay["level_meta"][k + 1][1]),
                   "bytes": int(lb[k]), "us": float(lvl_ms[k] * 1e3),
-                  "GBs": float(lb[k] / (lvl_ms[k] * 1e-3) / 1e9)} for k in range(L)]
+                  "GBs": float(lb[k] / (lvl_ms[k] * 1e-3) / 1e9)} for k in range(nwide)]
     widest = int(np.argmax([p["width"] for p in per_level])) if per_level else 0
 
     csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
@@ -209,14 +215,17 @@ def main():
             "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
             "csr_rocsparse": csr,
             "per_level_widest": per_level[widest] if per_level else None,
+            "wide_levels": nwide,
             "level_us_total": float(lvl_ms.sum() * 1e3),
             "leaf_us": float(launch_ms[:, 0].mean() * 1e3),
-            "final_emit_us": float(launch_ms[:, -1].mean() * 1e3) if launch_ms.shape[1] > L + 1 else 0.0,
+            "tail_us": tail_ms * 1e3,
+            "tail_levels": L - nwide,
+            "tail_bytes": float(lb_all[nwide:].sum()),
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "level_kernel (all L launches of a sweep)",
-                     "bytes_per_sweep": float(lb.sum())},
+                     "kernel": "level_kernel (the wide levels of a sweep, one launch each)",
+                     "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,
     }
     if os.environ.get("GCS_BENCH_LEVELS"):

@@ -170,6 +170,50 @@ gcs_status finish_layout(Grammar& g)
         g.lv[k].base = (k & 1) ? g.buf_a : g.buf_b;
     }
 
+    // column slices: weighted quantiles of the first column, every rule
+    // weighted by the level slots it occupies (itself plus its chain)
+    {
+        const int64_t mcols = std::max<int64_t>(g.n_cols, 1);
+        std::vector<double> w((size_t)mcols + 1, 0.0);
+        double tot = 0;
+        for (int64_t i = 0; i < R; ++i) {
+            double wi = 1.0 + std::max(0, g.plast[i] - g.lvl[i] - 1);
+            w[fc[i]] += wi;
+            tot += wi;
+        }
+        for (int64_t t = 0; t < alpha; ++t) {  // bare terminals and the terminal array
+            w[g.tcol[t]] += 1.0;
+            tot += 1.0;
+        }
+        g.col_cut[0] = 0;
+        double run = 0;
+        int x = 1;
+        for (int64_t c = 0; c < mcols && x < kSlices; ++c) {
+            run += w[c];
+            while (x < kSlices && run >= tot * x / kSlices) g.col_cut[x++] = (int32_t)(c + 1);
+        }
+        for (; x < kSlices; ++x) g.col_cut[x] = (int32_t)mcols;
+        g.col_cut[kSlices] = INT32_MAX;
+    }
+    auto slice_of = [&](int32_t col) -> int {
+        return (int)(std::upper_bound(g.col_cut + 1, g.col_cut + kSlices, col) - (g.col_cut + 1));
+    };
+    for (int k = 1; k <= L; ++k) {
+        Level& l = g.lv[k];
+        auto b = order.begin() + lvl_start[k];
+        for (int x = 0; x <= kSlices; ++x) {
+            const int32_t cut = g.col_cut[x];
+            l.bsl[x] = x == kSlices ? l.nb : std::partition_point(b, b + l.nb, [&](int32_t v) { return fc[v] < cut; }) - b;
+            const auto& pl = pt_lists[k];
+            l.psl[x] = x == kSlices ? l.npt
+                                    : std::partition_point(pl.begin(), pl.end(), [&](int32_t v) { return fc[v] < cut; }) -
+                                          pl.begin();
+        }
+    }
+    for (int x = 0; x <= kSlices; ++x) {
+        g.lv[0].bsl[x] = g.lv[0].psl[x] = 0;
+    }
+
     // children and pass-through sources
     g.child.resize((size_t)2 * R);
     g.ptsrc.resize((size_t)g.pt_total);
@@ -200,25 +244,30 @@ gcs_status finish_layout(Grammar& g)
         std::vector<int32_t>().swap(pt_lists[k]);
     }
 
-    // emission groups: C-occurrences at their symbol's level, grouped by
-    // (level, row), rows ascending, C order within a row (section 4.3:
-    // a root is emitted the moment its level is computed)
+    // emission groups: C-occurrences at their symbol's level (section 4.3: a
+    // root is emitted the moment its level is computed), grouped by (level,
+    // slice of the symbol's first column, row), rows ascending, C order within
+    // a group
     const int64_t n = g.n_rows;
-    std::vector<int64_t> per_level((size_t)L + 2, 0), grp_level((size_t)L + 2, 0);
-    std::vector<int32_t> last_row((size_t)L + 1, -1);
-    auto sym_level = [&](int32_t s) -> int { return s < alpha ? 0 : g.lvl[s - alpha]; };
+    const int NB = (L + 1) * kSlices;
+    std::vector<int64_t> per_b((size_t)NB, 0), grp_b((size_t)NB, 0);
+    std::vector<int32_t> last_row((size_t)NB, -1);
+    auto bucket_of = [&](int32_t s) -> int {
+        if (s < alpha) return slice_of(g.tcol[s]);
+        return g.lvl[s - alpha] * kSlices + slice_of(fc[s - alpha]);
+    };
     for (int64_t r = 0; r < n; ++r)
         for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
-            int l = sym_level(g.c_sym[e]);
-            per_level[l]++;
-            if (last_row[l] != (int32_t)r) {
-                last_row[l] = (int32_t)r;
-                grp_level[l]++;
+            int bk = bucket_of(g.c_sym[e]);
+            per_b[bk]++;
+            if (last_row[bk] != (int32_t)r) {
+                last_row[bk] = (int32_t)r;
+                grp_b[bk]++;
             }
         }
     const int64_t C = (int64_t)g.c_sym.size();
     int64_t G = 0;
-    for (int l = 0; l <= L; ++l) G += grp_level[l];
+    for (int bk = 0; bk < NB; ++bk) G += grp_b[bk];
     if (C >= (int64_t)INT32_MAX || G >= (int64_t)INT32_MAX) {
         set_error("C exceeds the 32-bit index space");
         return GCS_ERANGE;
@@ -226,30 +275,36 @@ gcs_status finish_layout(Grammar& g)
     g.erow.assign((size_t)G, 0);
     g.eoff.assign((size_t)G + 1, 0);
     g.epos.assign((size_t)C, 0);
-    std::vector<int64_t> gfill((size_t)L + 1), efill((size_t)L + 1);
+    std::vector<int64_t> gfill((size_t)NB), efill((size_t)NB);
     {
         int64_t go = 0, eo = 0;
         for (int l = 0; l <= L; ++l) {
             g.lv[l].grp_off = go;
-            g.lv[l].ngrp = grp_level[l];
-            gfill[l] = go;
-            efill[l] = eo;
-            go += grp_level[l];
-            eo += per_level[l];
+            for (int x = 0; x < kSlices; ++x) {
+                const int bk = l * kSlices + x;
+                g.lv[l].gsl[x] = go - g.lv[l].grp_off;
+                gfill[bk] = go;
+                efill[bk] = eo;
+                go += grp_b[bk];
+                eo += per_b[bk];
+            }
+            g.lv[l].gsl[kSlices] = go - g.lv[l].grp_off;
+            g.lv[l].ngrp = go - g.lv[l].grp_off;
         }
     }
     std::fill(last_row.begin(), last_row.end(), -1);
     for (int64_t r = 0; r < n; ++r)
         for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
             int32_t s = g.c_sym[e];
-            int l = sym_level(s);
-            if (last_row[l] != (int32_t)r) {
-                last_row[l] = (int32_t)r;
-                g.erow[gfill[l]] = (int32_t)r;
-                g.eoff[gfill[l]] = (int32_t)efill[l];
-                gfill[l]++;
+            int bk = bucket_of(s);
+            int l = bk / kSlices;
+            if (last_row[bk] != (int32_t)r) {
+                last_row[bk] = (int32_t)r;
+                g.erow[gfill[bk]] = (int32_t)r;
+                g.eoff[gfill[bk]] = (int32_t)efill[bk];
+                gfill[bk]++;
             }
-            g.epos[efill[l]++] = s < alpha ? s : (int32_t)(g.lv[l].base + pos[s - alpha]);
+            g.epos[efill[bk]++] = s < alpha ? s : (int32_t)(g.lv[l].base + pos[s - alpha]);
         }
     g.eoff[G] = (int32_t)C;
     g.t_layer = ms_since(t0);
@@ -734,6 +789,25 @@ extern "C" gcs_status gcs_export_layout(const gcs_grammar* h, int64_t* level_met
     cp(erow, g.erow);
     cp(eoff, g.eoff);
     cp(epos, g.epos);
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_export_slices(const gcs_grammar* h, int64_t* out, int32_t* col_cut)
+{
+    if (!h) {
+        gcs::set_error("null grammar");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    constexpr int S = gcs::kSlices + 1;
+    if (out)
+        for (int k = 0; k <= g.L; ++k)
+            for (int x = 0; x < S; ++x) {
+                out[(int64_t)k * 3 * S + x] = g.lv[k].bsl[x];
+                out[(int64_t)k * 3 * S + S + x] = g.lv[k].psl[x];
+                out[(int64_t)k * 3 * S + 2 * S + x] = g.lv[k].gsl[x];
+            }
+    if (col_cut) std::memcpy(col_cut, g.col_cut, sizeof(g.col_cut));
     return GCS_OK;
 }
 

@@ -26,6 +26,10 @@ struct RePairResult {
 bool repair_tile(const std::vector<int32_t>& seq_in, const std::vector<int64_t>& row_off, int32_t nt_base,
                  RePairResult& out);
 
+// Column slices: every level is cut into kSlices contiguous pieces by global
+// first-column thresholds, one piece per XCD of the device.
+constexpr int kSlices = 8;
+
 struct Level {
     int64_t nb;        // binary nodes (rules whose level is k)
     int64_t npt;       // pass-through nodes
@@ -35,6 +39,9 @@ struct Level {
     int64_t base;      // arena offset of this level's values (level 0: terminal array)
     int64_t grp_off;   // first emission group of this level
     int64_t ngrp;
+    // slice x covers binary nodes [bsl[x], bsl[x+1]), pass-through nodes
+    // [psl[x], psl[x+1]) and emission groups grp_off + [gsl[x], gsl[x+1])
+    int64_t bsl[kSlices + 1], psl[kSlices + 1], gsl[kSlices + 1];
 };
 
 struct Grammar {
@@ -51,7 +58,8 @@ struct Grammar {
     std::vector<Level> lv;                 // 0..L
     std::vector<int32_t> child;            // 2 per binary node
     std::vector<int32_t> ptsrc;            // arena offset of each pass-through node's source
-    std::vector<int32_t> erow, eoff, epos; // emission groups
+    std::vector<int32_t> erow, eoff, epos; // emission groups, ordered by (level, slice, row)
+    int32_t col_cut[kSlices + 1] = {};     // slice x = first columns [col_cut[x], col_cut[x+1])
     int64_t wmax = 0, pt_total = 0, buf_a = 0, buf_b = 0, arena = 0;
     double t_csrv = 0, t_repair = 0, t_layer = 0;
 

@@ -105,6 +105,7 @@ __device__ inline uint8_t xchg(uint8_t v, int m) { return (uint8_t)__shfl_xor((i
 
 constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
+constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
 template <class P>
 __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict__ tcol,
@@ -112,45 +113,51 @@ __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict_
                                                       const typename P::W* __restrict__ V,
                                                       const typename P::X* __restrict__ x,
                                                       typename P::A* __restrict__ T, int32_t alpha,
-                                                      typename P::Y* __restrict__ y, int32_t n_rows)
+                                                      typename P::A* __restrict__ acc, int32_t n_acc,
+                                                      unsigned* __restrict__ barrier)
 {
     const int32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i < alpha) T[i] = P::leaf(V[tval[i]], x[tcol[i]]);
-    if (i < n_rows) y[i] = P::yzero();
+    if (i < n_acc) acc[i] = P::ident();
+    if (i == 0) {  // the tail kernel's grid barrier counts rounds from 0 in every sweep
+        barrier[0] = 0;
+        barrier[kFlagOffset] = 0;
+    }
 }
 
+// Per-launch arguments.  Every part of the grid (binary nodes, pass-through
+// nodes, emission groups) is cut into kSlices column slices; a part holds
+// kSlices * blocks-per-slice workgroups and workgroup b of a part serves slice
+// b % kSlices.  Workgroups are dealt to the XCDs round-robin, so all of a
+// slice's work lands on one XCD and its gathers stay inside that XCD's L2.
 struct LevelArgs {
     const int2* child;     // this level's binary nodes
     const int32_t* ptsrc;  // this level's pass-through sources
     const int32_t* erow;   // emission groups of the previous level
     const int32_t* eoff;
     const int32_t* epos;
-    int32_t nb, npt, xcd_remap, ngrp;
-    int32_t cur;           // arena offset of this level's buffer
-    int32_t blk_bin, blk_pt;
+    int32_t cur, nb;       // arena offset of this level's buffer; binary node count
+    int32_t n_rows;        // stride of the per-slice row accumulators
     int32_t team_log2;     // lanes per emission group = 1 << team_log2 (<= 64)
+    int32_t pb_bin, pb_pt, pb_emit;  // workgroups per slice in each part
+    int32_t bsl[kSlices + 1], psl[kSlices + 1], gsl[kSlices + 1];
 };
 
+// One workgroup's share of a level launch: virtual block b of the grid.
 template <class P>
-__global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::A* __restrict__ arena,
-                                                       typename P::Y* __restrict__ y)
+__device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, typename P::A* __restrict__ arena,
+                                            typename P::A* __restrict__ acc)
 {
     using A = typename P::A;
-    int32_t b = blockIdx.x;
-    if (a.xcd_remap) {
-        // workgroups are dealt to the 8 XCDs round-robin; renumber them so
-        // that each XCD (and its L2) works on one contiguous share of the
-        // level, whose children sit together in the level below
-        const int32_t G = gridDim.x, x = b & 7, i = b >> 3, q = G >> 3, r = G & 7;
-        b = x * q + (x < r ? x : r) + i;
-    }
-    if (b < a.blk_bin) {
-        const int32_t t0 = b * (kBlock * kBinItems) + threadIdx.x;
+    const int32_t part_bin = a.pb_bin * kSlices, part_pt = a.pb_pt * kSlices;
+    if (b < part_bin) {
+        const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
+        const int32_t t0 = a.bsl[x] + i * (kBlock * kBinItems) + threadIdx.x;
         int2 c[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
-            c[u] = t < a.nb ? a.child[t] : make_int2(0, 0);
+            c[u] = t < end ? a.child[t] : make_int2(0, 0);
         }
         A v[kBinItems];
 #pragma unroll
@@ -158,15 +165,19 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
-            if (t < a.nb) arena[a.cur + t] = v[u];
+            if (t < end) arena[a.cur + t] = v[u];
         }
-    } else if (b < a.blk_bin + a.blk_pt) {
-        const int32_t t0 = (b - a.blk_bin) * (kBlock * kBinItems) + threadIdx.x;
+        return;
+    }
+    b -= part_bin;
+    if (b < part_pt) {
+        const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
+        const int32_t t0 = a.psl[x] + i * (kBlock * kBinItems) + threadIdx.x;
         int32_t src[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
-            src[u] = t < a.npt ? a.ptsrc[t] : 0;
+            src[u] = t < end ? a.ptsrc[t] : 0;
         }
         A v[kBinItems];
 #pragma unroll
@@ -174,25 +185,101 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
-            if (t < a.npt) arena[a.cur + a.nb + t] = v[u];
+            if (t < end) arena[a.cur + a.nb + t] = v[u];
         }
-    } else {
-        // a team of 2^team_log2 adjacent lanes per (row, level) group: lanes
-        // stride over the group's roots, then a fixed xor butterfly combines
-        // the team (deterministic), and the team's first lane updates y[row]
-        const int32_t gl = (b - a.blk_bin - a.blk_pt) * kBlock + threadIdx.x;
-        const int32_t team = 1 << a.team_log2;
-        const int32_t g = gl >> a.team_log2, sub = gl & (team - 1);
-        A s = P::ident();
-        if (g < a.ngrp) {
-            const int32_t e1 = a.eoff[g + 1];
-            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
+        return;
+    }
+    b -= part_pt;
+    // emission: a team of 2^team_log2 adjacent lanes per (slice, row) group;
+    // lanes stride over the group's roots, a fixed xor butterfly combines the
+    // team (deterministic), and the team's first lane updates the slice's
+    // accumulator of the row (each (slice, row) has one group per level and
+    // levels are ordered launches, so a plain read-modify-write suffices)
+    const int32_t x = b % kSlices, i = b / kSlices;
+    const int32_t gl = i * kBlock + threadIdx.x;
+    const int32_t team = 1 << a.team_log2;
+    const int32_t g = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
+    const bool valid = g < a.gsl[x + 1];
+    A s = P::ident();
+    if (valid) {
+        const int32_t e1 = a.eoff[g + 1];
+        for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
+    }
+    for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+    if (valid && sub == 0) {
+        A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
+        *r = P::comb(*r, s);
+    }
+}
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::A* __restrict__ arena,
+                                                       typename P::A* __restrict__ acc)
+{
+    level_block<P>(a, blockIdx.x, arena, acc);
+}
+
+// Grid-wide barrier for the co-resident tail grid.  bar[0] counts arrivals
+// in this sweep; bar[kFlagOffset] (another cache line) holds the last round
+// released.  Every wave first waits for its own stores to complete; one lane
+// per workgroup then arrives with a device-scope release increment, the last
+// arriver of the round publishes the round number with a release store, and
+// the others poll that flag with relaxed device-scope loads (pollers never
+// touch the line the arrivals update) and acquire once it is released.  The
+// wait is bounded: after about a second of polling the workgroup gives up and
+// returns false (the caller flags the sweep as failed), so the grid always
+// drains.
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, const int* err)
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
+    __syncthreads();
+    __shared__ int ok;
+    if (threadIdx.x == 0) {
+        ok = 1;
+        unsigned* flag = bar + kFlagOffset;
+        const unsigned prev = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1 == round * gridDim.x) {
+            __hip_atomic_store(flag, round, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            unsigned spins = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < round) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins == (1u << 25)) {
+                    ok = 0;
+                    break;
+                }
+            }
         }
-        for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
-        if (g < a.ngrp && sub == 0) {
-            const int32_t row = a.erow[g];
-            y[row] = P::emit(y[row], s);
-        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return ok != 0;
+}
+
+// The narrow levels k0..L (each with the emission of the level below), the
+// emission of level L and the final slice reduction, in one launch.  The grid
+// is a multiple of kSlices workgroups, so virtual block vb = blockIdx.x +
+// j * gridDim.x serves slice vb % kSlices = blockIdx.x % kSlices: every
+// workgroup keeps working on one slice, on one XCD.
+template <class P>
+__global__ __launch_bounds__(kBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t nent,
+                                                      typename P::A* __restrict__ arena,
+                                                      typename P::A* __restrict__ acc,
+                                                      typename P::Y* __restrict__ y, int32_t n_rows,
+                                                      unsigned* __restrict__ bar, int* __restrict__ err)
+{
+    for (int32_t li = 0; li < nent; ++li) {
+        const LevelArgs& a = table[li];
+        const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
+        for (int32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) level_block<P>(a, vb, arena, acc);
+        if (!grid_barrier(bar, (unsigned)(li + 1), err) && threadIdx.x == 0)
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int32_t r = blockIdx.x * kBlock + threadIdx.x; r < n_rows; r += gridDim.x * kBlock) {
+        typename P::A s = acc[r];
+#pragma unroll
+        for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
+        y[r] = P::emit(P::yzero(), s);
     }
 }
 
@@ -249,13 +336,19 @@ struct gcs_device {
     int64_t n_rows, n_cols, alpha, L;
     std::vector<gcs::Level> lv;
     std::vector<int32_t> team_log2;  // per level: lanes per emission group
-    int32_t xcd_remap;
     const int2* child;
     const int32_t* ptsrc;
     const int32_t *erow, *eoff, *epos, *tcol, *tval;
     const void* V;
     void* arena;
-    unsigned long long* counters;
+    void* acc;  // kSlices x n_rows row accumulators
+    unsigned long long* counters;  // [0], [1]: BFS counts
+    unsigned* barrier;             // tail grid barrier counter
+    int* err;                      // set by the tail kernel if its barrier timed out
+    std::vector<gcs::LevelArgs> largs;  // launch k = 1..L+1 at index k-1
+    int64_t tail_k0 = 1, tail_nent = 0;  // levels tail_k0..L and the last emission run in the tail kernel
+    int32_t tail_wgs = 0;
+    const gcs::LevelArgs* tail_table = nullptr;
     int64_t* pinned;
     // profiling
     std::vector<hipEvent_t> events;
@@ -284,7 +377,7 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, total;
+    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, table, total;
 };
 
 Image image_layout(const Grammar& g, gcs_policy p)
@@ -307,11 +400,15 @@ Image image_layout(const Grammar& g, gcs_policy p)
     o = al256(o + g.tval.size() * 4);
     m.V = o;
     o = al256(o + g.V.size() * v_bytes(p));
-    m.total = o > 0 ? o : 256;
+    m.table = o;
+    o = al256(o + (size_t)(g.L + 1) * sizeof(LevelArgs));
+    m.total = o;
     return m;
 }
 
-size_t workspace_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)g.arena * elem_bytes(p)) + 256; }
+size_t arena_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)g.arena * elem_bytes(p)); }
+size_t acc_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)kSlices * g.n_rows * elem_bytes(p)); }
+size_t workspace_bytes(const Grammar& g, gcs_policy p) { return arena_bytes(g, p) + acc_bytes(g, p) + 256; }
 
 bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_PLUS_I64; }
 
@@ -326,6 +423,16 @@ bool layout_in_bounds(const Grammar& g)
     for (int32_t c : g.ptsrc)
         if (c < 0 || c >= arena) return false;
     int64_t co = 0, po = 0;
+    for (int k = 0; k <= g.L; ++k) {
+        const Level& l = g.lv[k];
+        for (int x = 0; x < kSlices; ++x)
+            if (l.gsl[x] > l.gsl[x + 1] || (k > 0 && (l.bsl[x] > l.bsl[x + 1] || l.psl[x] > l.psl[x + 1])))
+                return false;
+        if (l.gsl[0] != 0 || l.gsl[kSlices] != l.ngrp) return false;
+        if (k > 0 && (l.bsl[0] != 0 || l.bsl[kSlices] != l.nb || l.psl[0] != 0 || l.psl[kSlices] != l.npt))
+            return false;
+    }
+    if (g.n_rows * kSlices >= (int64_t)INT32_MAX) return false;
     for (int k = 1; k <= g.L; ++k) {
         const Level& l = g.lv[k];
         if (l.base < 0 || l.base + l.nb + l.npt > arena) return false;
@@ -382,15 +489,61 @@ struct DeviceGuard {
     }
 };
 
-// launches of one sweep with work in them
+inline int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+inline int64_t vblocks(const LevelArgs& a) { return (int64_t)kSlices * (a.pb_bin + a.pb_pt + a.pb_emit); }
+
+// Launch arguments of level launch k = 1..L+1 (level k, or none for k = L+1,
+// with the emission of level k-1), device pointers included.
+LevelArgs make_args(const gcs_device* d, int64_t k)
+{
+    LevelArgs a{};
+    int64_t mb = 0, mp = 0, mg = 0;
+    if (k <= d->L) {
+        const Level& l = d->lv[k];
+        a.child = d->child + l.child_off;
+        a.ptsrc = d->ptsrc + l.pt_off;
+        a.nb = (int32_t)l.nb;
+        a.cur = (int32_t)l.base;
+        for (int x = 0; x <= kSlices; ++x) {
+            a.bsl[x] = (int32_t)l.bsl[x];
+            a.psl[x] = (int32_t)l.psl[x];
+        }
+        for (int x = 0; x < kSlices; ++x) {
+            mb = std::max<int64_t>(mb, l.bsl[x + 1] - l.bsl[x]);
+            mp = std::max<int64_t>(mp, l.psl[x + 1] - l.psl[x]);
+        }
+    }
+    const Level& e = d->lv[k - 1];
+    a.erow = d->erow + e.grp_off;
+    a.eoff = d->eoff + e.grp_off;
+    a.epos = d->epos;
+    a.n_rows = (int32_t)d->n_rows;
+    a.team_log2 = d->team_log2[k - 1];
+    for (int x = 0; x <= kSlices; ++x) a.gsl[x] = (int32_t)e.gsl[x];
+    for (int x = 0; x < kSlices; ++x) mg = std::max<int64_t>(mg, e.gsl[x + 1] - e.gsl[x]);
+    a.pb_bin = ceil_div(mb, kBlock * kBinItems);
+    a.pb_pt = ceil_div(mp, kBlock * kBinItems);
+    a.pb_emit = ceil_div(mg << a.team_log2, kBlock);
+    return a;
+}
+
+bool has_tail(const gcs_device* d)
+{
+    if (d->n_rows > 0) return true;
+    for (int64_t k = d->tail_k0; k <= d->L + 1; ++k)
+        if (vblocks(d->largs[k - 1]) > 0) return true;
+    return false;
+}
+// the leaf launch also resets the tail's barrier counter
+bool has_leaf(const gcs_device* d) { return d->alpha > 0 || d->n_rows > 0 || has_tail(d); }
+
+// launches of one sweep
 int64_t count_launches(const gcs_device* d)
 {
-    int64_t c = std::max<int64_t>(d->alpha, d->n_rows) > 0 ? 1 : 0;
-    for (int64_t k = 1; k <= d->L + 1; ++k) {
-        const int64_t w = (k <= d->L ? d->lv[k].nb + d->lv[k].npt : 0) + d->lv[k - 1].ngrp;
-        c += w > 0;
-    }
-    return c;
+    int64_t c = has_leaf(d) ? 1 : 0;
+    for (int64_t k = 1; k < d->tail_k0; ++k) c += vblocks(d->largs[k - 1]) > 0;
+    return c + (has_tail(d) ? 1 : 0);
 }
 
 template <class P>
@@ -398,42 +551,37 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
 {
     using A = typename P::A;
     auto* arena = (A*)d->arena;
+    auto* acc = (A*)d->acc;
     auto* y = (typename P::Y*)yv;
     int64_t li = 0;
     auto mark = [&]() {
         if (ev) (void)hipEventRecord(ev[li++], s);
     };
-    const int32_t leaf_n = (int32_t)std::max<int64_t>(d->alpha, d->n_rows);
-    if (leaf_n > 0) mark();
-    if (leaf_n > 0)
-        leaf_kernel<P><<<(leaf_n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-            d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha, y,
-            (int32_t)d->n_rows);
-    for (int64_t k = 1; k <= d->L + 1; ++k) {
-        LevelArgs a{};
-        if (k <= d->L) {
-            const Level& l = d->lv[k];
-            a.child = d->child + l.child_off;
-            a.ptsrc = d->ptsrc + l.pt_off;
-            a.nb = (int32_t)l.nb;
-            a.npt = (int32_t)l.npt;
-            a.cur = (int32_t)l.base;
-        }
-        const Level& e = d->lv[k - 1];
-        a.erow = d->erow + e.grp_off;
-        a.eoff = d->eoff + e.grp_off;
-        a.epos = d->epos;
-        a.ngrp = (int32_t)e.ngrp;
-        a.blk_bin = (a.nb + kBlock * kBinItems - 1) / (kBlock * kBinItems);
-        a.blk_pt = (a.npt + kBlock * kBinItems - 1) / (kBlock * kBinItems);
-        a.xcd_remap = d->xcd_remap;
-        a.team_log2 = d->team_log2[k - 1];
-        const int32_t blk_emit = (int32_t)(((int64_t)a.ngrp << a.team_log2) + kBlock - 1) / kBlock;
-        const int32_t grid = a.blk_bin + a.blk_pt + blk_emit;
+    const int32_t n_acc = (int32_t)(kSlices * d->n_rows);
+    if (has_leaf(d)) {
+        mark();
+        leaf_kernel<P><<<std::max(1, ceil_div(std::max<int64_t>(d->alpha, n_acc), kBlock)), kBlock, 0, s>>>(
+            d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha, acc,
+            n_acc, d->barrier);
+    }
+    for (int64_t k = 1; k < d->tail_k0; ++k) {
+        const LevelArgs& a = d->largs[k - 1];
+        const int64_t grid = vblocks(a);
         if (grid > 0) {
             mark();
-            level_kernel<P><<<grid, kBlock, 0, s>>>(a, arena, y);
+            level_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(a, arena, acc);
         }
+    }
+    if (has_tail(d)) {
+        mark();
+        const LevelArgs* table = d->tail_table;
+        int32_t nent = (int32_t)d->tail_nent, n_rows = (int32_t)d->n_rows;
+        unsigned* bar = d->barrier;
+        int* errp = d->err;
+        void* args[] = {&table, &nent, &arena, &acc, &y, &n_rows, &bar, &errp};
+        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
+                                                  dim3(kBlock), args, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
     }
     mark();
     hipError_t err = hipGetLastError();
@@ -544,10 +692,6 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->alpha = g.alpha();
     d->L = g.L;
     d->lv = g.lv;
-    {
-        const char* e = std::getenv("GCS_XCD_REMAP");
-        d->xcd_remap = e ? std::atoi(e) != 0 : 1;
-    }
     // emission team per level: about four roots per lane, at most one wave
     d->team_log2.assign(g.lv.size(), 0);
     for (size_t k = 0; k < g.lv.size(); ++k) {
@@ -568,8 +712,50 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tval = (const int32_t*)(base + im.tval);
     d->V = base + im.V;
     d->arena = workspace_dev;
-    d->counters = (unsigned long long*)((unsigned char*)workspace_dev + gcs::al256((size_t)g.arena *
-                                                                                  gcs::elem_bytes(p)));
+    d->acc = (unsigned char*)workspace_dev + gcs::arena_bytes(g, p);
+    d->counters = (unsigned long long*)((unsigned char*)workspace_dev + gcs::arena_bytes(g, p) + gcs::acc_bytes(g, p));
+    d->barrier = (unsigned*)(d->counters + 2);
+    d->err = (int*)(d->counters + 3);
+    // launch arguments of every level; the narrow levels at the top go to the
+    // persistent tail kernel: from the first level k0 after which no launch
+    // needs more than tail_vb virtual blocks per tail workgroup
+    int dev_cu = 0;
+    (void)hipDeviceGetAttribute(&dev_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    int coop = 0;
+    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (!coop) {
+        delete d;
+        gcs::set_error("the device does not support cooperative launches");
+        return GCS_EHIP;
+    }
+    auto env_int = [](const char* name, int dflt) {
+        const char* v = std::getenv(name);
+        return v ? std::atoi(v) : dflt;
+    };
+    // 64 workgroups (8 per XCD) and at most 4 virtual blocks each per level
+    // measured best on MI355X for the tail (fewer arrivals per barrier round)
+    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu, gcs::kSlices)) /
+                                          gcs::kSlices) * gcs::kSlices);
+    const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 4));
+    d->largs.resize((size_t)g.L + 1);
+    for (int64_t k = 1; k <= g.L + 1; ++k) d->largs[k - 1] = gcs::make_args(d, k);
+    d->tail_k0 = g.L + 1;
+    while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * d->tail_wgs) --d->tail_k0;
+    d->tail_nent = g.L + 2 - d->tail_k0;
+    d->tail_table = (const gcs::LevelArgs*)(base + im.table) + (d->tail_k0 - 1);
+    e = hipMemcpyAsync(base + im.table, d->largs.data(), d->largs.size() * sizeof(gcs::LevelArgs),
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete d;
+        return gcs::hip_fail(e, "hipMemcpyAsync (launch table)");
+    }
+    e = hipMemsetAsync(d->counters, 0, 256, s);  // BFS counts, barrier, error flag
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete d;
+        return gcs::hip_fail(e, "hipMemsetAsync (counters)");
+    }
     d->pinned = nullptr;
     e = hipHostMalloc((void**)&d->pinned, 64, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -747,6 +933,28 @@ extern "C" gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t
         if (c == 0) break;
     }
     *passes = t;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_device_check(gcs_device* d, void* stream)
+{
+    if (!d) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    gcs::DeviceGuard guard(d->device);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(d->pinned, d->err, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return gcs::hip_fail(e, "gcs_device_check");
+    int flag;
+    std::memcpy(&flag, d->pinned, sizeof(int));
+    if (flag) {
+        e = hipMemsetAsync(d->err, 0, sizeof(int), s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        gcs::set_error("a sweep's tail kernel timed out at its grid barrier; its results are invalid");
+        return GCS_ESTATE;
+    }
     return GCS_OK;
 }
 

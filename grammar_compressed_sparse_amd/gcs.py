@@ -66,6 +66,8 @@ _lib.gcs_level_widths.argtypes = [_P, _P, _I64]
 _lib.gcs_export_grammar.argtypes = [_P] + [_P] * 9
 _lib.gcs_layout_counts.argtypes = [_P, _P]
 _lib.gcs_export_layout.argtypes = [_P] + [_P] * 6
+_lib.gcs_export_slices.argtypes = [_P, _P, _P]
+_lib.gcs_export_slices.restype = _st
 _lib.gcs_free_grammar.argtypes = [_P]
 _lib.gcs_free_grammar.restype = None
 _lib.gcs_device_layout.argtypes = [_P, ctypes.c_int, ctypes.POINTER(DevSizes)]
@@ -77,6 +79,8 @@ _lib.gcs_sweep_launches.restype = _I64
 _lib.gcs_profile_begin.argtypes = [_P, _I64]
 _lib.gcs_sweep_right_profiled.argtypes = [_P, _P, _P, _P]
 _lib.gcs_profile_end.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+_lib.gcs_device_check.argtypes = [_P, _P]
+_lib.gcs_device_check.restype = _st
 _lib.gcs_free_device.argtypes = [_P]
 _lib.gcs_free_device.restype = None
 for _f in ("gcs_build_grammar", "gcs_grammar_from_rules", "gcs_grammar_stats", "gcs_level_widths",
@@ -143,6 +147,9 @@ class Grammar:
                    epos=np.zeros(ne, np.int32), arena=arena, buf_a=ba, buf_b=bb)
         _check(_lib.gcs_export_layout(self._h, *[_ptr(out[k]) for k in (
             "level_meta", "child", "ptsrc", "erow", "eoff", "epos")]))
+        out["slices"] = np.zeros((nl, 3, 9), np.int64)
+        out["col_cut"] = np.zeros(9, np.int32)
+        _check(_lib.gcs_export_slices(self._h, _ptr(out["slices"]), _ptr(out["col_cut"])))
         return out
 
     def device_layout(self, policy: int) -> dict:
@@ -250,6 +257,10 @@ class Device:
 
     def bfs(self, sources, max_passes=1 << 16, stream=None):
         return bfs(self, sources, max_passes, stream)
+
+    def check(self, stream=None):
+        """gcs_device_check: synchronise and raise if a sweep failed on the device."""
+        _check(_lib.gcs_device_check(self._h, _stream_ptr(stream)))
 
     def sweep_launches(self) -> int:
         return int(_lib.gcs_sweep_launches(self._h))

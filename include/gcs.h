@@ -165,13 +165,21 @@ gcs_status gcs_layout_counts(const gcs_grammar* g, int64_t* counts8);
 gcs_status gcs_export_layout(const gcs_grammar* g, int64_t* level_meta, int32_t* child, int32_t* ptsrc,
                              int32_t* erow, int32_t* eoff, int32_t* epos);
 
+/* Column slices of the layout: every level is cut into 8 contiguous pieces by
+ * first-column thresholds col_cut[0..8] (slice x = first columns in
+ * [col_cut[x], col_cut[x+1])), one piece per XCD.  out[(k*3 + 0)*9 + x] =
+ * first binary node of slice x at level k (x = 8: end), [(k*3+1)*9 + x] the
+ * same for pass-through nodes, [(k*3+2)*9 + x] for emission groups (relative
+ * to the level's first group).  Either pointer may be NULL. */
+gcs_status gcs_export_slices(const gcs_grammar* g, int64_t* out, int32_t* col_cut);
+
 void gcs_free_grammar(gcs_grammar* g);
 
 /* ---- device ----------------------------------------------------------- */
 
 typedef struct {
     size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, terminals, V) */
-    size_t workspace_bytes; /* value arena [T | A | B] plus a 256-byte counter block                    */
+    size_t workspace_bytes; /* value arena [T | A | B], 8 x n_rows row accumulators, 256-byte counters  */
     int64_t x_len;          /* elements of x (= n_cols)                                                 */
     int64_t y_len;          /* elements of y (= n_rows)                                                 */
     int32_t x_elem_bytes;
@@ -190,9 +198,10 @@ gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* 
 gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
                       void* workspace_dev, size_t workspace_bytes, void* stream, gcs_device** out);
 
-/* y = M x under the uploaded policy: zero y, evaluate the terminal array,
- * then for k = 1..L evaluate level k and emit the roots of level k-1, and
- * finally emit level L (section 4.3, Listing 1).  x_dev holds x_len
+/* y = M x under the uploaded policy: evaluate the terminal array (and clear
+ * the row accumulators), then for k = 1..L evaluate level k and emit the
+ * roots of level k-1, then emit level L (section 4.3, Listing 1), and finally
+ * y[r] = the combination of row r's 8 slice accumulators.  x_dev holds x_len
  * elements, y_dev y_len elements, both device memory of the policy's types;
  * x is not modified.  Asynchronous on `stream`.  Calls on one device handle
  * share its workspace, so they must be ordered (same stream or synchronised). */
@@ -214,9 +223,10 @@ gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t n_sources,
 
 /* ---- profiling --------------------------------------------------------- */
 
-/* Kernel launches of one sweep: 1 (terminal array, zero y) + L (level k with
- * emission of level k-1) + 1 (emission of level L), minus launches with no
- * work (none when the matrix has nonzeros). */
+/* Kernel launches of one sweep: 1 (terminal array, clear accumulators), one
+ * per wide level k (level k with the emission of level k-1), and 1 persistent
+ * launch for the narrow levels, the emission of level L and the reduction of
+ * the slice accumulators into y. */
 int64_t gcs_sweep_launches(const gcs_device* d);
 
 /* Timing of sweeps with HIP events on the sweep's own stream, for
@@ -231,6 +241,13 @@ int64_t gcs_sweep_launches(const gcs_device* d);
 gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps);
 gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t* sweeps, int64_t* launches);
+
+/* Synchronises `stream` and reports whether any sweep since the last check
+ * failed on the device: the persistent kernel that evaluates the narrow top
+ * levels waits at a grid-wide barrier with a bounded wait (about a second),
+ * and flags the sweep instead of hanging if its workgroups were not all
+ * resident.  GCS_ESTATE (and the flag cleared) if so, GCS_OK otherwise. */
+gcs_status gcs_device_check(gcs_device* d, void* stream);
 
 void gcs_free_device(gcs_device* d);
 

@@ -142,18 +142,22 @@ def emulate_layout(lay, ex, x, op="plus", dtype=np.float64, poison=True):
         comb = np.bitwise_or
         bad = 0x80
     n = len(ex["c_off"]) - 1
-    y = np.zeros(n, dtype)
+    S = lay["slices"].shape[2] - 1
+    acc = np.zeros((S, n), dtype)  # per-slice row accumulators
     meta = lay["level_meta"]
     L = meta.shape[0] - 1
 
     def emit(level):
         nb_, npt_, co_, ro_, nr_, base_, g0, ng = meta[level]
-        for g in range(g0, g0 + ng):
-            e0, e1 = lay["eoff"][g], lay["eoff"][g + 1]
-            s = arena[lay["epos"][e0]]
-            for e in range(e0 + 1, e1):
-                s = comb(s, arena[lay["epos"][e]])
-            y[lay["erow"][g]] = comb(y[lay["erow"][g]], s)
+        gsl = lay["slices"][level, 2]
+        assert gsl[0] == 0 and gsl[S] == ng
+        for x in range(S):
+            for g in range(g0 + gsl[x], g0 + gsl[x + 1]):
+                e0, e1 = lay["eoff"][g], lay["eoff"][g + 1]
+                s = arena[lay["epos"][e0]]
+                for e in range(e0 + 1, e1):
+                    s = comb(s, arena[lay["epos"][e]])
+                acc[x, lay["erow"][g]] = comb(acc[x, lay["erow"][g]], s)
 
     for k in range(1, L + 2):
         if k <= L:
@@ -169,6 +173,9 @@ def emulate_layout(lay, ex, x, op="plus", dtype=np.float64, poison=True):
             arena[base + nb:base + nb + npt] = ptv
         else:
             emit(k - 1)
+    y = acc[0].copy()
+    for x in range(1, S):
+        y = comb(y, acc[x])
     return y
 
 

@@ -39,7 +39,7 @@ def _sweep(env, g, policy, x_np):
     dev = gcs.upload(g, policy)
     x = torch.from_numpy(np.ascontiguousarray(x_np)).to("cuda")
     y = dev.sweep_right(x)
-    torch.cuda.synchronize()
+    dev.check()  # synchronises; raises if the persistent tail kernel flagged a failure
     return y.cpu().numpy(), dev
 
 
@@ -142,6 +142,30 @@ def test_genotype_mid_tiles(env, oracle_mod, synth_mod, col_chunk, row_chunk):
     _rel_ok(y, yo, absum, 1e-5)
     y, _ = _sweep(env, g, gcs.PLUS_F64, x32.astype(np.float64))
     _rel_ok(y, yo, absum, 1e-12)
+
+
+@pytest.mark.parametrize("tail", [("256", "2"), ("8", "1"), ("64", "1000000"), ("2048", "1")])
+def test_tail_split_bit_identical(env, oracle_mod, synth_mod, c1, monkeypatch, tail):
+    """The persistent tail kernel (narrow levels behind grid barriers) gives the
+    same bits as one launch per level, whatever the split and the tail grid."""
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    x = synth_mod.normal(spec.n_cols, 303)
+    monkeypatch.setenv("GCS_TAIL_WGS", "256")
+    monkeypatch.setenv("GCS_TAIL_VB", "1")
+    ref, dev = _sweep(env, g, gcs.PLUS_F64, x)
+    n_ref = dev.sweep_launches()
+    monkeypatch.setenv("GCS_TAIL_WGS", tail[0])
+    monkeypatch.setenv("GCS_TAIL_VB", tail[1])
+    y, dev = _sweep(env, g, gcs.PLUS_F64, x)
+    _say(f"tail wgs={tail[0]} vb={tail[1]}: {dev.sweep_launches()} launches (reference {n_ref})")
+    assert np.array_equal(y, ref)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    _rel_ok(y, yo, absum, 1e-12)
+    xt = torch.from_numpy(x).cuda()
+    for _ in range(5):
+        assert np.array_equal(dev.sweep_right(xt).cpu().numpy(), ref)
+    dev.check()
 
 
 def test_random_values_many_distinct(env, oracle_mod):
