@@ -93,7 +93,72 @@ def csr_comparator(torch, rp, col, val, x, steps):
         return {"error": str(e)[:200]}
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "sweep.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
+    """Turn rocprofv3 CSV output (kernel trace stats; FETCH_SIZE and WRITE_SIZE
+    counter collections that include a known-size copy) into the text summary
+    under profiles/ and the traffic record bench.py reads."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        fs = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        return list(csv.DictReader(open(fs[0]))) if fs else []
+
+    stats = rows(kt_dir, "*kernel_stats.csv")
+    lines = ["# rocprofv3 summary: level_kernel on genotype_20000x100000_f32", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "## Kernel time (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20}
+    for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
+        cc = rows(d, "*counter_collection.csv")
+        # the calibration copies: the copy dispatches that moved copy_mib MiB
+        # (the first copy dispatches of the run, one per calibration copy)
+        copies = [float(r["Counter_Value"]) for r in cc if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        big = [v for v in copies if v > 0.25 * copy_mib * 1024]
+        lvl = [float(r["Counter_Value"]) * 1024 for r in cc if "level_kernel" in r["Kernel_Name"]]
+        rec[tag + "_kib_copy"] = sum(big) / len(big)
+        rec[tag + "_bytes_per_launch"] = sum(lvl) / max(len(lvl), 1)
+        rec[tag + "_launches"] = len(lvl)
+    scale_f = rec["copy_bytes"] / (rec["fetch_kib_copy"] * 1024)
+    scale_w = rec["copy_bytes"] / (rec["write_kib_copy"] * 1024)
+    rec["scale_fetch"], rec["scale_write"] = scale_f, scale_w
+    rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] * scale_f + rec["write_bytes_per_launch"] * scale_w
+    lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"- calibration: one copy dispatch of {rec['copy_bytes'] / 2**20:.0f} MiB read "
+              f"{rec['fetch_kib_copy']:.1f} KiB and wrote {rec['write_kib_copy']:.1f} KiB "
+              f"(scale {scale_f:.5f} / {scale_w:.5f})",
+              f"- level_kernel, mean over {rec['fetch_launches']} dispatches: FETCH "
+              f"{rec['fetch_bytes_per_launch'] / 1e6:.2f} MB, WRITE {rec['write_bytes_per_launch'] / 1e6:.2f} MB, "
+              f"traffic {rec['traffic_bytes_per_launch'] / 1e6:.2f} MB per launch (scaled)",
+              f"- kernel source sha256[:16] = {rec['source_sha256']}"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-rocprof":
+        # bench.py --summarize-rocprof KT_DIR FETCH_DIR WRITE_DIR OUT_MD COPY_MIB "command" ...
+        summarize_rocprof(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -102,6 +167,9 @@ def main():
     ap.add_argument("--col-chunk", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-csr", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 5 device-to-device copies of this many MiB (a known-size reference kernel "
+                         "for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the sweep is a single-GPU engine here (multi-GPU sharding is a "
@@ -111,6 +179,16 @@ def main():
     import torch
     import oracle
     from grammar_compressed_sparse_amd import gcs, synth
+
+    if args.calibrate_copy_mib:
+        nb = args.calibrate_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 5 copies of {args.calibrate_copy_mib} MiB ({nb} bytes read and written per copy)")
+        del src, dst
 
     wl = synth.WORKLOADS[args.workload]
     spec = wl["matrix"]
@@ -186,6 +264,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(rp, col, val, xs[0].cpu().numpy().astype(np.float64), nnz)
 
+    traffic = None  # HBM bytes per level_kernel launch from the committed counter profile, if still current
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("source_sha256") == kernel_source_hash() and args.workload == "genotype_20000x100000_f32":
+            traffic = rec["traffic_bytes_per_launch"]
     value = nnz * args.steps / elapsed
     out = {
         "metric": "nnz/s for y=Mx sweep; achieved HBM GB/s (% peak); device bytes vs CSR",
@@ -223,7 +307,7 @@ def main():
             "tail_bytes": float(lb_all[nwide:].sum()),
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "level_kernel (the wide levels of a sweep, one launch each)",
                      "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,

@@ -553,6 +553,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     auto* arena = (A*)d->arena;
     auto* acc = (A*)d->acc;
     auto* y = (typename P::Y*)yv;
+    // profiling: events[2i] before launch i, events[2i+1] right after it
     int64_t li = 0;
     auto mark = [&]() {
         if (ev) (void)hipEventRecord(ev[li++], s);
@@ -563,6 +564,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         leaf_kernel<P><<<std::max(1, ceil_div(std::max<int64_t>(d->alpha, n_acc), kBlock)), kBlock, 0, s>>>(
             d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha, acc,
             n_acc, d->barrier);
+        mark();
     }
     for (int64_t k = 1; k < d->tail_k0; ++k) {
         const LevelArgs& a = d->largs[k - 1];
@@ -570,6 +572,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         if (grid > 0) {
             mark();
             level_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(a, arena, acc);
+            mark();
         }
     }
     if (has_tail(d)) {
@@ -582,8 +585,8 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
                                                   dim3(kBlock), args, 0, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
+        mark();
     }
-    mark();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return hip_fail(err, "sweep launch");
     return GCS_OK;
@@ -812,7 +815,7 @@ extern "C" gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps)
     }
     gcs::DeviceGuard guard(d->device);
     release_events(d);
-    const int64_t per = gcs::count_launches(d) + 1;
+    const int64_t per = 2 * gcs::count_launches(d);
     d->events.resize((size_t)(per * max_sweeps));
     for (auto& e : d->events) {
         hipError_t err = hipEventCreate(&e);
@@ -839,7 +842,7 @@ extern "C" gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev,
         gcs::set_error("more sweeps than gcs_profile_begin reserved");
         return GCS_ERANGE;
     }
-    const int64_t per = gcs::count_launches(d) + 1;
+    const int64_t per = 2 * gcs::count_launches(d);
     gcs_status st = sweep_dispatch(d, x_dev, y_dev, stream, d->events.data() + per * d->prof_used);
     if (st == GCS_OK) d->prof_used++;
     return st;
@@ -853,7 +856,7 @@ extern "C" gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t c
         return GCS_ESTATE;
     }
     gcs::DeviceGuard guard(d->device);
-    const int64_t nl = gcs::count_launches(d), per = nl + 1;
+    const int64_t nl = gcs::count_launches(d), per = 2 * nl;
     *sweeps = d->prof_used;
     *launches = nl;
     if (cap < d->prof_used * nl || (cap > 0 && !launch_ms)) {
@@ -862,14 +865,14 @@ extern "C" gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t c
         return GCS_ERANGE;
     }
     for (int64_t s = 0; s < d->prof_used; ++s) {
-        hipError_t err = hipEventSynchronize(d->events[per * s + nl]);
+        hipError_t err = hipEventSynchronize(d->events[per * s + per - 1]);
         if (err != hipSuccess) {
             release_events(d);
             return gcs::hip_fail(err, "hipEventSynchronize");
         }
         for (int64_t i = 0; i < nl; ++i) {
             float ms = 0;
-            err = hipEventElapsedTime(&ms, d->events[per * s + i], d->events[per * s + i + 1]);
+            err = hipEventElapsedTime(&ms, d->events[per * s + 2 * i], d->events[per * s + 2 * i + 1]);
             if (err != hipSuccess) {
                 release_events(d);
                 return gcs::hip_fail(err, "hipEventElapsedTime");

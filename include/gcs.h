@@ -231,11 +231,11 @@ int64_t gcs_sweep_launches(const gcs_device* d);
 
 /* Timing of sweeps with HIP events on the sweep's own stream, for
  * benchmarking.  gcs_profile_begin reserves events for up to max_sweeps
- * sweeps; each gcs_sweep_right_profiled is gcs_sweep_right plus one event
- * before every launch and one after the last; gcs_profile_end synchronises
- * the events and writes launch_ms[s * launches + i] = time from the event
- * before launch i of sweep s to the next event (the launch's duration
- * including any gap before the next launch), then releases the events.
+ * sweeps; each gcs_sweep_right_profiled is gcs_sweep_right with an event
+ * recorded right before and right after every launch; gcs_profile_end
+ * synchronises the events and writes launch_ms[s * launches + i] = time
+ * between the two events around launch i of sweep s, then releases the
+ * events.
  * GCS_ERANGE if more than max_sweeps sweeps were profiled or cap is too
  * small; GCS_ESTATE without gcs_profile_begin. */
 gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps);
