@@ -257,6 +257,24 @@ def main():
                   "GBs": float(lb[k] / (lvl_ms[k] * 1e-3) / 1e9)} for k in range(nwide)]
     widest = int(np.argmax([p["width"] for p in per_level])) if per_level else 0
 
+    per_vector = None
+    if len(xs) > 1:
+        # multiply-many: one sweep per vector, latency of each measured with
+        # events on the sweep's stream (after the timed region)
+        lat = []
+        for xv in xs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dev.sweep_right(xv, y)
+            e1.record()
+            e1.synchronize()
+            lat.append(e0.elapsed_time(e1))
+        lat = np.array(lat)
+        per_vector = {"vectors": len(xs), "median_ms": float(np.median(lat)), "p90_ms": float(np.percentile(lat, 90)),
+                      "aggregate_nnz_per_s": float(nnz * len(xs) / (lat.sum() * 1e-3))}
+        log(f"per-vector latency over {len(xs)} vectors: median {per_vector['median_ms']:.3f} ms, "
+            f"p90 {per_vector['p90_ms']:.3f} ms")
+
     csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
     eng_bytes = dev.device_bytes + xs[0].numel() * elem + y.numel() * elem
     csr = None if args.no_csr else csr_comparator(torch, rp, col, val, xs[0], min(args.steps, 20))
@@ -289,6 +307,7 @@ def main():
             "n_rows": spec.n_rows, "n_cols": spec.n_cols, "nnz": nnz,
             "founders": spec.founders, "seg_mean": spec.seg_mean, "mu": spec.mu, "seed": spec.seed,
             "vectors": len(xs),
+            "multiply_many": per_vector,
             "grammar": {k: st[k] for k in ("n_rules", "n_passthrough", "depth", "max_width", "c_len",
                                            "n_terminals", "n_tiles", "n_emit_groups")},
             "build_s": build_s, "upload_s": upload_s,
