@@ -105,6 +105,7 @@ __device__ inline uint8_t xchg(uint8_t v, int m) { return (uint8_t)__shfl_xor((i
 
 constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
+constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
 template <class P>
@@ -145,14 +146,14 @@ struct LevelArgs {
 
 // One workgroup's share of a level launch: virtual block b of the grid.
 template <class P>
-__device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, typename P::A* __restrict__ arena,
-                                            typename P::A* __restrict__ acc)
+__device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32_t tid,
+                                            typename P::A* __restrict__ arena, typename P::A* __restrict__ acc)
 {
     using A = typename P::A;
     const int32_t part_bin = a.pb_bin * kSlices, part_pt = a.pb_pt * kSlices;
     if (b < part_bin) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
-        const int32_t t0 = a.bsl[x] + i * (kBlock * kBinItems) + threadIdx.x;
+        const int32_t t0 = a.bsl[x] + i * (kBlock * kBinItems) + tid;
         int2 c[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
@@ -172,7 +173,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, typen
     b -= part_bin;
     if (b < part_pt) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
-        const int32_t t0 = a.psl[x] + i * (kBlock * kBinItems) + threadIdx.x;
+        const int32_t t0 = a.psl[x] + i * (kBlock * kBinItems) + tid;
         int32_t src[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
@@ -196,7 +197,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, typen
     // accumulator of the row (each (slice, row) has one group per level and
     // levels are ordered launches, so a plain read-modify-write suffices)
     const int32_t x = b % kSlices, i = b / kSlices;
-    const int32_t gl = i * kBlock + threadIdx.x;
+    const int32_t gl = i * kBlock + tid;
     const int32_t team = 1 << a.team_log2;
     const int32_t g = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
     const bool valid = g < a.gsl[x + 1];
@@ -212,11 +213,16 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, typen
     }
 }
 
+// One wide level.  The grid is capped near the number of resident
+// workgroups; each workgroup strides over the level's virtual blocks.  The
+// stride (gridDim.x) is a multiple of kSlices, so a workgroup keeps serving
+// the same slice on the same XCD.
 template <class P>
 __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::A* __restrict__ arena,
                                                        typename P::A* __restrict__ acc)
 {
-    level_block<P>(a, blockIdx.x, arena, acc);
+    const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
+    for (int32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) level_block<P>(a, vb, threadIdx.x, arena, acc);
 }
 
 // Grid-wide barrier for the co-resident tail grid.  bar[0] counts arrivals
@@ -256,26 +262,104 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
     return ok != 0;
 }
 
-// The narrow levels k0..L (each with the emission of the level below), the
-// emission of level L and the final slice reduction, in one launch.  The grid
-// is a multiple of kSlices workgroups, so virtual block vb = blockIdx.x +
-// j * gridDim.x serves slice vb % kSlices = blockIdx.x % kSlices: every
-// workgroup keeps working on one slice, on one XCD.
+// The narrowest levels, run by one workgroup of kTailBlock lanes with
+// workgroup barriers only: binary nodes, pass-through nodes and the emission
+// of the level below as flat loops over the whole level (slices ignored; an
+// emission group's slice is looked up to address its accumulator).
 template <class P>
-__global__ __launch_bounds__(kBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t nent,
-                                                      typename P::A* __restrict__ arena,
-                                                      typename P::A* __restrict__ acc,
-                                                      typename P::Y* __restrict__ y, int32_t n_rows,
-                                                      unsigned* __restrict__ bar, int* __restrict__ err)
+__device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __restrict__ arena,
+                                           typename P::A* __restrict__ acc)
 {
-    for (int32_t li = 0; li < nent; ++li) {
+    using A = typename P::A;
+    const int32_t tid = threadIdx.x;
+    const int32_t nb = a.bsl[kSlices], npt = a.psl[kSlices];
+    for (int32_t t0 = tid; t0 < nb; t0 += kTailBlock * kBinItems) {
+        int2 c[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kTailBlock;
+            c[u] = t < nb ? a.child[t] : make_int2(0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kTailBlock;
+            const A v = P::comb(arena[c[u].x], arena[c[u].y]);
+            if (t < nb) arena[a.cur + t] = v;
+        }
+    }
+    for (int32_t t0 = tid; t0 < npt; t0 += kTailBlock * kBinItems) {
+        int32_t src[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kTailBlock;
+            src[u] = t < npt ? a.ptsrc[t] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * kTailBlock;
+            const A v = arena[src[u]];
+            if (t < npt) arena[a.cur + a.nb + t] = v;
+        }
+    }
+    const int32_t team = 1 << a.team_log2, ngrp = a.gsl[kSlices];
+    for (int32_t gl0 = 0; gl0 < (ngrp << a.team_log2); gl0 += kTailBlock) {
+        const int32_t gl = gl0 + tid;
+        const int32_t g = gl >> a.team_log2, sub = gl & (team - 1);
+        const bool valid = g < ngrp;
+        A s = P::ident();
+        if (valid) {
+            const int32_t e1 = a.eoff[g + 1];
+            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
+        }
+        for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+        if (valid && sub == 0) {
+            int x = 0;
+            while (g >= a.gsl[x + 1]) ++x;
+            A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
+            *r = P::comb(*r, s);
+        }
+    }
+}
+
+// Levels k0..L (each with the emission of the level below), the emission of
+// level L and the final slice reduction, in one cooperative launch of
+// workgroups with kTailBlock lanes.  Entries [0, n_multi) run on the whole
+// grid: the four 256-lane quarters of a workgroup take virtual blocks
+// blockIdx.x + (quarter + 4j) * gridDim.x, all of the same slice (gridDim.x
+// is a multiple of kSlices), so a workgroup stays on its slice's XCD; grid
+// barriers separate the entries.  Entries [n_multi, nent) are the narrowest
+// levels: workgroup 0 runs them alone with workgroup barriers while the
+// others wait at the next grid barrier.  Then every workgroup reduces
+// y[r] = acc[0][r] (+) ... (+) acc[7][r].
+template <class P>
+__global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t nent,
+                                                          int32_t n_multi, typename P::A* __restrict__ arena,
+                                                          typename P::A* __restrict__ acc,
+                                                          typename P::Y* __restrict__ y, int32_t n_rows,
+                                                          unsigned* __restrict__ bar, int* __restrict__ err)
+{
+    constexpr int Q = kTailBlock / kBlock;
+    const int32_t q = threadIdx.x / kBlock, ltid = threadIdx.x % kBlock;
+    unsigned round = 0;
+    for (int32_t li = 0; li < n_multi; ++li) {
         const LevelArgs& a = table[li];
         const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
-        for (int32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) level_block<P>(a, vb, arena, acc);
-        if (!grid_barrier(bar, (unsigned)(li + 1), err) && threadIdx.x == 0)
+        for (int32_t vb = blockIdx.x + q * gridDim.x; vb < nvb; vb += Q * gridDim.x)
+            level_block<P>(a, vb, ltid, arena, acc);
+        if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    for (int32_t r = blockIdx.x * kBlock + threadIdx.x; r < n_rows; r += gridDim.x * kBlock) {
+    if (n_multi < nent) {
+        if (blockIdx.x == 0) {
+            for (int32_t li = n_multi; li < nent; ++li) {
+                level_flat<P>(table[li], arena, acc);
+                __syncthreads();
+            }
+        }
+        if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int32_t r = blockIdx.x * kTailBlock + threadIdx.x; r < n_rows; r += gridDim.x * kTailBlock) {
         typename P::A s = acc[r];
 #pragma unroll
         for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
@@ -347,7 +431,9 @@ struct gcs_device {
     int* err;                      // set by the tail kernel if its barrier timed out
     std::vector<gcs::LevelArgs> largs;  // launch k = 1..L+1 at index k-1
     int64_t tail_k0 = 1, tail_nent = 0;  // levels tail_k0..L and the last emission run in the tail kernel
+    int64_t tail_multi = 0;              // of which the first tail_multi run on the whole tail grid
     int32_t tail_wgs = 0;
+    int64_t grid_max = 0;  // cap on workgroups of a wide level launch (multiple of kSlices)
     const gcs::LevelArgs* tail_table = nullptr;
     int64_t* pinned;
     // profiling
@@ -568,7 +654,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     }
     for (int64_t k = 1; k < d->tail_k0; ++k) {
         const LevelArgs& a = d->largs[k - 1];
-        const int64_t grid = vblocks(a);
+        const int64_t grid = std::min<int64_t>(vblocks(a), d->grid_max);
         if (grid > 0) {
             mark();
             level_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(a, arena, acc);
@@ -578,12 +664,12 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     if (has_tail(d)) {
         mark();
         const LevelArgs* table = d->tail_table;
-        int32_t nent = (int32_t)d->tail_nent, n_rows = (int32_t)d->n_rows;
+        int32_t nent = (int32_t)d->tail_nent, n_multi = (int32_t)d->tail_multi, n_rows = (int32_t)d->n_rows;
         unsigned* bar = d->barrier;
         int* errp = d->err;
-        void* args[] = {&table, &nent, &arena, &acc, &y, &n_rows, &bar, &errp};
+        void* args[] = {&table, &nent, &n_multi, &arena, &acc, &y, &n_rows, &bar, &errp};
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
-                                                  dim3(kBlock), args, 0, s);
+                                                  dim3(kTailBlock), args, 0, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
         mark();
     }
@@ -735,16 +821,27 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const char* v = std::getenv(name);
         return v ? std::atoi(v) : dflt;
     };
-    // 64 workgroups (8 per XCD) and at most 4 virtual blocks each per level
+    // 64 workgroups (8 per XCD), one virtual block per 256-lane quarter and level
     // measured best on MI355X for the tail (fewer arrivals per barrier round)
     d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
-    const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 4));
+    const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
+    d->grid_max = std::max(gcs::kSlices, env_int("GCS_GRID_MAX", 8 * std::max(dev_cu, 1)) / gcs::kSlices * gcs::kSlices);
     d->largs.resize((size_t)g.L + 1);
     for (int64_t k = 1; k <= g.L + 1; ++k) d->largs[k - 1] = gcs::make_args(d, k);
     d->tail_k0 = g.L + 1;
-    while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * d->tail_wgs) --d->tail_k0;
+    const int64_t quarters = gcs::kTailBlock / gcs::kBlock;
+    while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
     d->tail_nent = g.L + 2 - d->tail_k0;
+    // the narrowest entries at the end (work per entry within one workgroup's
+    // flat loops: binary + pass-through nodes and emission lanes) run on
+    // workgroup 0 alone
+    const int64_t flat_max = env_int("GCS_TAIL_FLAT", 4096);
+    auto flat_work = [&](const gcs::LevelArgs& a) {
+        return (int64_t)a.bsl[gcs::kSlices] + a.psl[gcs::kSlices] + ((int64_t)a.gsl[gcs::kSlices] << a.team_log2);
+    };
+    d->tail_multi = d->tail_nent;
+    while (d->tail_multi > 0 && flat_work(d->largs[d->tail_k0 - 1 + d->tail_multi - 1]) <= flat_max) --d->tail_multi;
     d->tail_table = (const gcs::LevelArgs*)(base + im.table) + (d->tail_k0 - 1);
     e = hipMemcpyAsync(base + im.table, d->largs.data(), d->largs.size() * sizeof(gcs::LevelArgs),
                        hipMemcpyHostToDevice, s);

@@ -144,7 +144,8 @@ def test_genotype_mid_tiles(env, oracle_mod, synth_mod, col_chunk, row_chunk):
     _rel_ok(y, yo, absum, 1e-12)
 
 
-@pytest.mark.parametrize("tail", [("256", "2"), ("8", "1"), ("64", "1000000"), ("2048", "1")])
+@pytest.mark.parametrize("tail", [("256", "2", "4096"), ("8", "1", "0"), ("64", "1000000", "0"),
+                                  ("2048", "1", "4096"), ("64", "4", "100000000"), ("16", "1000000", "100000")])
 def test_tail_split_bit_identical(env, oracle_mod, synth_mod, c1, monkeypatch, tail):
     """The persistent tail kernel (narrow levels behind grid barriers) gives the
     same bits as one launch per level, whatever the split and the tail grid."""
@@ -153,12 +154,14 @@ def test_tail_split_bit_identical(env, oracle_mod, synth_mod, c1, monkeypatch, t
     x = synth_mod.normal(spec.n_cols, 303)
     monkeypatch.setenv("GCS_TAIL_WGS", "256")
     monkeypatch.setenv("GCS_TAIL_VB", "1")
+    monkeypatch.setenv("GCS_TAIL_FLAT", "0")
     ref, dev = _sweep(env, g, gcs.PLUS_F64, x)
     n_ref = dev.sweep_launches()
     monkeypatch.setenv("GCS_TAIL_WGS", tail[0])
     monkeypatch.setenv("GCS_TAIL_VB", tail[1])
+    monkeypatch.setenv("GCS_TAIL_FLAT", tail[2])
     y, dev = _sweep(env, g, gcs.PLUS_F64, x)
-    _say(f"tail wgs={tail[0]} vb={tail[1]}: {dev.sweep_launches()} launches (reference {n_ref})")
+    _say(f"tail wgs={tail[0]} vb={tail[1]} flat={tail[2]}: {dev.sweep_launches()} launches (reference {n_ref})")
     assert np.array_equal(y, ref)
     yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
     _rel_ok(y, yo, absum, 1e-12)
