@@ -8,6 +8,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <numeric>
 #include <sched.h>
@@ -59,6 +60,17 @@ static double ms_since(std::chrono::steady_clock::time_point t0)
     return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
+// Phase timing of the builder on stderr when GCS_BUILD_TRACE is set.
+struct PhaseTrace {
+    bool on = std::getenv("GCS_BUILD_TRACE") != nullptr;
+    std::chrono::steady_clock::time_point t = std::chrono::steady_clock::now();
+    void mark(const char* what)
+    {
+        if (on) std::fprintf(stderr, "[gcs build] %-28s %9.1f ms\n", what, ms_since(t));
+        t = std::chrono::steady_clock::now();
+    }
+};
+
 // ---------------------------------------------------------------------------
 // levels, completion, layout
 // ---------------------------------------------------------------------------
@@ -81,9 +93,10 @@ static double ms_since(std::chrono::steady_clock::time_point t0)
 // the pass-through nodes of level k are the carried binary nodes of level k-1
 // merged with the continuing pass-through nodes of level k-1, two lists that
 // are already sorted by first column.
-gcs_status finish_layout(Grammar& g)
+gcs_status finish_layout(Grammar& g, int threads)
 {
     auto t0 = std::chrono::steady_clock::now();
+    PhaseTrace tr;
     const int64_t alpha = g.alpha(), R = g.nrules();
     if (alpha + R >= (int64_t)INT32_MAX) {
         set_error("grammar exceeds the 32-bit symbol space");
@@ -104,6 +117,7 @@ gcs_status finish_layout(Grammar& g)
         if (b >= alpha) g.plast[b - alpha] = std::max(g.plast[b - alpha], l);
     }
     g.L = L;
+    tr.mark("levels (Eq. 3.1)");
 
     // rules of each level, ordered by (first column, id)
     std::vector<int64_t> cnt_lvl((size_t)L + 2, 0);
@@ -117,13 +131,15 @@ gcs_status finish_layout(Grammar& g)
     }
     auto by_fc = [&](int32_t u, int32_t v) { return fc[u] != fc[v] ? fc[u] < fc[v] : u < v; };
     std::vector<int32_t> pos((size_t)R, 0);  // position within own level
-    for (int k = 1; k <= L; ++k) {
+    parallel_for(L, threads, [&](int64_t km1) {
+        const int k = (int)km1 + 1;
         auto b = order.begin() + lvl_start[k], e = order.begin() + lvl_start[k + 1];
         std::sort(b, e, by_fc);  // ids are unique: the order is total
         int32_t p = 0;
         for (auto it = b; it != e; ++it) pos[*it] = p++;
-    }
+    });
 
+    tr.mark("order levels by column");
     g.lv.assign((size_t)L + 1, Level{});
     g.lv[0] = Level{};
     g.wmax = 0;
@@ -156,6 +172,7 @@ gcs_status finish_layout(Grammar& g)
         g.wmax = std::max<int64_t>(g.wmax, nb_of[k] + npt_of[k]);
         pt_prev.swap(pt_cur);
     }
+    tr.mark("pass-through lists");
     auto align64 = [](int64_t v) { return (v + 63) & ~int64_t(63); };
     g.buf_a = align64(alpha);
     g.buf_b = g.buf_a + align64(g.wmax);
@@ -214,6 +231,7 @@ gcs_status finish_layout(Grammar& g)
         g.lv[0].bsl[x] = g.lv[0].psl[x] = 0;
     }
 
+    tr.mark("column slices");
     // children and pass-through sources
     g.child.resize((size_t)2 * R);
     g.ptsrc.resize((size_t)g.pt_total);
@@ -248,26 +266,53 @@ gcs_status finish_layout(Grammar& g)
     // root is emitted the moment its level is computed), grouped by (level,
     // slice of the symbol's first column, row), rows ascending, C order within
     // a group
+    tr.mark("children and sources");
     const int64_t n = g.n_rows;
     const int NB = (L + 1) * kSlices;
-    std::vector<int64_t> per_b((size_t)NB, 0), grp_b((size_t)NB, 0);
-    std::vector<int32_t> last_row((size_t)NB, -1);
-    auto bucket_of = [&](int32_t s) -> int {
-        if (s < alpha) return slice_of(g.tcol[s]);
-        return g.lvl[s - alpha] * kSlices + slice_of(fc[s - alpha]);
+    // per symbol: its emission bucket (level * kSlices + slice) and the arena
+    // offset of its value, so a C entry costs one lookup
+    struct SymInfo {
+        int32_t bucket, off;
     };
-    for (int64_t r = 0; r < n; ++r)
-        for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
-            int bk = bucket_of(g.c_sym[e]);
-            per_b[bk]++;
-            if (last_row[bk] != (int32_t)r) {
-                last_row[bk] = (int32_t)r;
-                grp_b[bk]++;
+    std::vector<SymInfo> sym((size_t)(alpha + R));
+    parallel_for((alpha + R + 65535) / 65536, threads, [&](int64_t b) {
+        for (int64_t s = b * 65536; s < std::min(alpha + R, (b + 1) * 65536); ++s) {
+            if (s < alpha) {
+                sym[s] = {slice_of(g.tcol[s]), (int32_t)s};
+            } else {
+                const int64_t v = s - alpha;
+                const int l = g.lvl[v];
+                sym[s] = {l * kSlices + slice_of(fc[v]), (int32_t)(g.lv[l].base + pos[v])};
             }
         }
+    });
+    tr.mark("emission: symbol table");
+    // row blocks processed in parallel: per block and bucket, count entries
+    // and groups (a row opens a group in every bucket it touches), then fill
+    // at offsets from a (bucket, block) prefix sum, so groups stay ordered by
+    // (level, slice, row)
+    const int64_t nblk = std::max<int64_t>(1, std::min<int64_t>((n + 4095) / 4096, 64 * (int64_t)threads));
+    auto blk_rows = [&](int64_t b) { return std::make_pair(n * b / nblk, n * (b + 1) / nblk); };
+    std::vector<int64_t> cnt_e((size_t)nblk * NB, 0), cnt_g((size_t)nblk * NB, 0);
+    parallel_for(nblk, threads, [&](int64_t b) {
+        int64_t* ce = &cnt_e[(size_t)b * NB];
+        int64_t* cg = &cnt_g[(size_t)b * NB];
+        std::vector<int32_t> seen_row((size_t)NB, -1);
+        auto [r0, r1] = blk_rows(b);
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
+                const int bk = sym[g.c_sym[e]].bucket;
+                ce[bk]++;
+                if (seen_row[bk] != (int32_t)r) {
+                    seen_row[bk] = (int32_t)r;
+                    cg[bk]++;
+                }
+            }
+    });
+    tr.mark("emission: count");
     const int64_t C = (int64_t)g.c_sym.size();
     int64_t G = 0;
-    for (int bk = 0; bk < NB; ++bk) G += grp_b[bk];
+    for (int64_t v : cnt_g) G += v;
     if (C >= (int64_t)INT32_MAX || G >= (int64_t)INT32_MAX) {
         set_error("C exceeds the 32-bit index space");
         return GCS_ERANGE;
@@ -275,7 +320,11 @@ gcs_status finish_layout(Grammar& g)
     g.erow.assign((size_t)G, 0);
     g.eoff.assign((size_t)G + 1, 0);
     g.epos.assign((size_t)C, 0);
-    std::vector<int64_t> gfill((size_t)NB), efill((size_t)NB);
+    if (tr.on) std::fprintf(stderr, "[gcs build] C = %lld, groups = %lld, blocks = %lld, buckets = %d\n", (long long)C,
+                            (long long)G, (long long)nblk, NB);
+    tr.mark("emission: allocate");
+    // offsets: bucket-major, block-minor
+    std::vector<int64_t> off_e((size_t)nblk * NB), off_g((size_t)nblk * NB);
     {
         int64_t go = 0, eo = 0;
         for (int l = 0; l <= L; ++l) {
@@ -283,30 +332,38 @@ gcs_status finish_layout(Grammar& g)
             for (int x = 0; x < kSlices; ++x) {
                 const int bk = l * kSlices + x;
                 g.lv[l].gsl[x] = go - g.lv[l].grp_off;
-                gfill[bk] = go;
-                efill[bk] = eo;
-                go += grp_b[bk];
-                eo += per_b[bk];
+                for (int64_t b = 0; b < nblk; ++b) {
+                    off_g[(size_t)b * NB + bk] = go;
+                    off_e[(size_t)b * NB + bk] = eo;
+                    go += cnt_g[(size_t)b * NB + bk];
+                    eo += cnt_e[(size_t)b * NB + bk];
+                }
             }
             g.lv[l].gsl[kSlices] = go - g.lv[l].grp_off;
             g.lv[l].ngrp = go - g.lv[l].grp_off;
         }
     }
-    std::fill(last_row.begin(), last_row.end(), -1);
-    for (int64_t r = 0; r < n; ++r)
-        for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
-            int32_t s = g.c_sym[e];
-            int bk = bucket_of(s);
-            int l = bk / kSlices;
-            if (last_row[bk] != (int32_t)r) {
-                last_row[bk] = (int32_t)r;
-                g.erow[gfill[bk]] = (int32_t)r;
-                g.eoff[gfill[bk]] = (int32_t)efill[bk];
-                gfill[bk]++;
+    tr.mark("emission: offsets");
+    parallel_for(nblk, threads, [&](int64_t b) {
+        int64_t* gf = &off_g[(size_t)b * NB];
+        int64_t* ef = &off_e[(size_t)b * NB];
+        std::vector<int32_t> seen_row((size_t)NB, -1);
+        auto [r0, r1] = blk_rows(b);
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t e = g.c_off[r]; e < g.c_off[r + 1]; ++e) {
+                const SymInfo si = sym[g.c_sym[e]];
+                const int bk = si.bucket;
+                if (seen_row[bk] != (int32_t)r) {
+                    seen_row[bk] = (int32_t)r;
+                    g.erow[gf[bk]] = (int32_t)r;
+                    g.eoff[gf[bk]] = (int32_t)ef[bk];
+                    gf[bk]++;
+                }
+                g.epos[ef[bk]++] = si.off;
             }
-            g.epos[efill[bk]++] = s < alpha ? s : (int32_t)(g.lv[l].base + pos[s - alpha]);
-        }
+    });
     g.eoff[G] = (int32_t)C;
+    tr.mark("emission groups");
     g.t_layer = ms_since(t0);
     return GCS_OK;
 }
@@ -477,6 +534,37 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
     const int64_t ncc = std::max<int64_t>(1, (mc + cc - 1) / cc), nrc = std::max<int64_t>(1, (n + rc - 1) / rc);
     const int64_t ntiles = ncc * nrc;
     g.n_tiles = ntiles;
+    // row order of the row tiles: natural, or grouped by similarity (rows
+    // ordered by two MinHash values of their column sets, so rows sharing
+    // many columns -- and hence pairs -- tend to land in the same tile)
+    std::vector<int32_t> perm((size_t)n), where((size_t)n);
+    for (int64_t r = 0; r < n; ++r) perm[r] = (int32_t)r;
+    if (opts && opts->row_order == GCS_ROWS_SIMILAR && nrc > 1) {
+        std::vector<uint64_t> h1((size_t)n), h2((size_t)n);
+        auto mix = [](uint64_t z) {
+            z += 0x9E3779B97F4A7C15ULL;
+            z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+            z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+            return z ^ (z >> 31);
+        };
+        parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
+            for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
+                uint64_t a = UINT64_MAX, c = UINT64_MAX;
+                for (int64_t k = m->row_ptr[r]; k < m->row_ptr[r + 1]; ++k) {
+                    a = std::min(a, mix((uint64_t)m->col[k] * 2 + 1));
+                    c = std::min(c, mix((uint64_t)m->col[k] * 2 + 2));
+                }
+                h1[r] = a;
+                h2[r] = c;
+            }
+        });
+        std::sort(perm.begin(), perm.end(), [&](int32_t u, int32_t v) {
+            if (h1[u] != h1[v]) return h1[u] < h1[v];
+            if (h2[u] != h2[v]) return h2[u] < h2[v];
+            return u < v;
+        });
+    }
+    for (int64_t i = 0; i < n; ++i) where[perm[i]] = (int32_t)i;
     std::vector<RePairResult> res((size_t)ntiles);
     std::atomic<int> fail{0};
     std::atomic<int64_t> nnz_total{0};
@@ -491,7 +579,8 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
         try {
             off.reserve((size_t)(r1 - r0 + 1));
             off.push_back(0);
-            for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t i = r0; i < r1; ++i) {
+                const int64_t r = perm[i];
                 const int32_t* cb_ = m->col + m->row_ptr[r];
                 const int32_t* ce_ = m->col + m->row_ptr[r + 1];
                 const int32_t* s = (ncc == 1) ? cb_ : std::lower_bound(cb_, ce_, c0);
@@ -548,14 +637,14 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
             for (size_t i = 0; i < res[t].row_len.size(); ++i) s[i + 1] = s[i] + res[t].row_len[i];
         }
         for (int64_t r = 0; r < n; ++r) {
-            int64_t rb = r / rc, ri = r - rb * rc, len = 0;
+            int64_t rb = where[r] / rc, ri = where[r] - rb * rc, len = 0;
             for (int64_t cb = 0; cb < ncc; ++cb) len += res[rb * ncc + cb].row_len[ri];
             g.c_off[r + 1] = g.c_off[r] + len;
         }
         g.c_sym.resize((size_t)g.c_off[n]);
         parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
             for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
-                int64_t rb = r / rc, ri = r - rb * rc, o = g.c_off[r];
+                int64_t rb = where[r] / rc, ri = where[r] - rb * rc, o = g.c_off[r];
                 for (int64_t cb = 0; cb < ncc; ++cb) {
                     const int64_t t = rb * ncc + cb;
                     const int32_t shift = (int32_t)rbase[t];
@@ -571,7 +660,7 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
         return GCS_ENOMEM;
     }
     g.t_repair = ms_since(t1);
-    return finish_layout(g);
+    return finish_layout(g, threads);
 }
 
 }  // namespace gcs
@@ -669,7 +758,7 @@ extern "C" gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, con
             len[i] = (rule_a[i] < n_terms ? 1 : len[rule_a[i] - n_terms]) +
                      (rule_b[i] < n_terms ? 1 : len[rule_b[i] - n_terms]);
         for (int64_t e = 0; e < C; ++e) g.nnz += c_sym[e] < n_terms ? 1 : len[c_sym[e] - n_terms];
-        gcs_status st = gcs::finish_layout(g);
+        gcs_status st = gcs::finish_layout(g, gcs::resolve_threads(0));
         if (st != GCS_OK) {
             delete h;
             return st;

@@ -68,7 +68,7 @@ struct Grammar {
 };
 
 // Levels, pass-through completion and layout from (tcol/tval, ra/rb, C).
-gcs_status finish_layout(Grammar& g);
+gcs_status finish_layout(Grammar& g, int threads);
 
 }  // namespace gcs
 

@@ -40,7 +40,7 @@ class CsrView(ctypes.Structure):
 
 class BuildOpts(ctypes.Structure):
     _fields_ = [("n_threads", ctypes.c_int32), ("col_chunk", ctypes.c_int32), ("row_chunk", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("row_order", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -169,7 +169,11 @@ class Grammar:
             pass
 
 
-def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0) -> Grammar:
+ROWS_NATURAL, ROWS_SIMILAR = 0, 1
+
+
+def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0,
+                  row_order=ROWS_NATURAL) -> Grammar:
     """gcs_build_grammar on a host CSR matrix (val: None = all ones, int8, or fp64)."""
     rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
     cl = np.ascontiguousarray(col, dtype=np.int32)
@@ -184,7 +188,7 @@ def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0,
         kind, vv = VAL_F64, np.ascontiguousarray(val, dtype=np.float64)
     view = CsrView(n, n_cols, rp.ctypes.data, cl.ctypes.data if cl.size else None, kind, 0,
                    vv.ctypes.data if vv is not None and vv.size else None)
-    opts = BuildOpts(n_threads, col_chunk, row_chunk, 0)
+    opts = BuildOpts(n_threads, col_chunk, row_chunk, row_order)
     h = _P()
     _check(_lib.gcs_build_grammar(ctypes.byref(view), ctypes.byref(opts), ctypes.byref(h)))
     return Grammar(h)

@@ -80,16 +80,25 @@ typedef struct {
     const void* val;
 } gcs_csr_view;
 
+/* Row order for row tiles. */
+typedef enum {
+    GCS_ROWS_NATURAL = 0, /* row tiles are consecutive rows                                    */
+    GCS_ROWS_SIMILAR = 1  /* rows ordered by two MinHash values of their column sets first,    */
+                          /* so rows that share many columns tend to share a tile              */
+} gcs_row_order;
+
 /* Builder options.  RePair runs independently on each tile of a
  * (row chunk x column chunk) partition; tiles run in parallel.  Column chunks
  * lose no rule sharing (terminals carry their column, so rules never span
- * two column ranges); they only cut pairs that straddle a chunk border.  The
- * pages' prior work partitions by row blocks (section 1). */
+ * two column ranges); they only cut pairs that straddle a chunk border.  Row
+ * chunks lose the sharing between rows of different tiles; the pages' prior
+ * work partitions by row blocks (section 1).  y is always in the input's row
+ * order. */
 typedef struct {
     int32_t n_threads; /* 0 = OMP_NUM_THREADS if set, else the CPUs of the affinity mask */
     int32_t col_chunk; /* columns per tile; 0 = all columns                               */
     int32_t row_chunk; /* rows per tile; 0 = all rows                                     */
-    int32_t reserved;
+    int32_t row_order; /* gcs_row_order: which rows share a row tile                      */
 } gcs_build_opts;
 
 /* Structural figures of a built grammar (section 4.4, Table 4.1 columns). */

@@ -258,3 +258,19 @@ def test_stored_zeros_dropped(gcs):
     rp = np.array([0, 3], np.int64)
     g = gcs.build_grammar(rp, np.array([0, 1, 2], np.int32), np.array([1.0, 0.0, 2.0]), n_cols=3)
     assert g.stats()["nnz"] == 2 and g.stats()["n_values"] == 2
+
+
+def test_similar_row_tiles_copy_graph(gcs, oracle_mod, synth_mod):
+    """Row tiles over a MinHash row order: still lossless, y in input row order."""
+    spec = synth_mod.GraphSpec(20_000, seed=8)
+    rp, col = synth_mod.copy_graph(spec)
+    g = gcs.build_grammar(rp, col, None, n_cols=spec.n, row_chunk=3000, row_order=gcs.ROWS_SIMILAR, n_threads=4)
+    assert g.stats()["n_tiles"] == 7
+    ex = _check_grammar(g, rp, col, None, single_tile=False)
+    xb = np.zeros(spec.n, np.uint8)
+    xb[synth_mod.sources(spec.n, 200, 3)] = 1
+    yb = H.emulate_layout(g.layout(), ex, xb, op="bool", dtype=np.uint8)
+    assert np.array_equal(yb, oracle_mod.spmv_bool(rp, col, xb))
+    nat = gcs.build_grammar(rp, col, None, n_cols=spec.n, row_chunk=3000)
+    # grouping similar rows keeps more of the sharing than consecutive blocks
+    assert g.stats()["c_len"] < nat.stats()["c_len"]
