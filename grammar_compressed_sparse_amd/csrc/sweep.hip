@@ -106,6 +106,8 @@ __device__ inline uint8_t xchg(uint8_t v, int m) { return (uint8_t)__shfl_xor((i
 constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
+constexpr size_t kFlatLdsBytes = 52 * 1024;  // LDS of the tail's single-workgroup phase: two level buffers
+constexpr size_t kFlatArgsBytes = 8 * 1024;  // and a copy of its levels' launch arguments
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
 template <class P>
@@ -138,11 +140,14 @@ struct LevelArgs {
     const int32_t* eoff;
     const int32_t* epos;
     int32_t cur, nb;       // arena offset of this level's buffer; binary node count
+    int32_t prev, alpha;   // arena offset of the level below; terminals (arena offsets below alpha)
     int32_t n_rows;        // stride of the per-slice row accumulators
     int32_t team_log2;     // lanes per emission group = 1 << team_log2 (<= 64)
     int32_t pb_bin, pb_pt, pb_emit;  // workgroups per slice in each part
     int32_t bsl[kSlices + 1], psl[kSlices + 1], gsl[kSlices + 1];
 };
+
+static_assert(sizeof(LevelArgs) % 4 == 0, "LevelArgs is copied as 32-bit words");
 
 // One workgroup's share of a level launch: virtual block b of the grid.
 template <class P>
@@ -263,16 +268,22 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
 }
 
 // The narrowest levels, run by one workgroup of kTailBlock lanes with
-// workgroup barriers only: binary nodes, pass-through nodes and the emission
-// of the level below as flat loops over the whole level (slices ignored; an
-// emission group's slice is looked up to address its accumulator).
+// workgroup barriers only, their values held in two LDS buffers (lprev: the
+// level below, lcur: this level) instead of the arena.  A child offset c
+// reads the terminal array (c < alpha) or the level below: from LDS when that
+// level was computed here too, from the arena when it came from the grid
+// phase.  Binary nodes, pass-through nodes and the emission of the level
+// below are flat loops over the whole level; an emission group's slice is
+// looked up to address its accumulator.
 template <class P>
-__device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __restrict__ arena,
+__device__ __forceinline__ void level_flat(const LevelArgs& a, const typename P::A* __restrict__ arena,
+                                           const typename P::A* lprev, bool prev_in_lds, typename P::A* lcur,
                                            typename P::A* __restrict__ acc)
 {
     using A = typename P::A;
     const int32_t tid = threadIdx.x;
     const int32_t nb = a.bsl[kSlices], npt = a.psl[kSlices];
+    auto val = [&](int32_t c) -> A { return (prev_in_lds && c >= a.alpha) ? lprev[c - a.prev] : arena[c]; };
     for (int32_t t0 = tid; t0 < nb; t0 += kTailBlock * kBinItems) {
         int2 c[kBinItems];
 #pragma unroll
@@ -283,8 +294,7 @@ __device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kTailBlock;
-            const A v = P::comb(arena[c[u].x], arena[c[u].y]);
-            if (t < nb) arena[a.cur + t] = v;
+            if (t < nb) lcur[t] = P::comb(val(c[u].x), val(c[u].y));
         }
     }
     for (int32_t t0 = tid; t0 < npt; t0 += kTailBlock * kBinItems) {
@@ -297,8 +307,7 @@ __device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kTailBlock;
-            const A v = arena[src[u]];
-            if (t < npt) arena[a.cur + a.nb + t] = v;
+            if (t < npt) lcur[nb + t] = val(src[u]);
         }
     }
     const int32_t team = 1 << a.team_log2, ngrp = a.gsl[kSlices];
@@ -309,16 +318,67 @@ __device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __
         A s = P::ident();
         if (valid) {
             const int32_t e1 = a.eoff[g + 1];
-            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
+            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, val(a.epos[e]));
         }
         for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
         if (valid && sub == 0) {
-            int x = 0;
-            while (g >= a.gsl[x + 1]) ++x;
+            int x = 0;  // slice of group g: gsl[x] <= g < gsl[x+1]
+#pragma unroll
+            for (int w = kSlices / 2; w > 0; w >>= 1)
+                if (g >= a.gsl[x + w]) x += w;
             A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
             *r = P::comb(*r, s);
         }
     }
+}
+
+// Brings what the narrow levels will read into the L2 before they start: one
+// load per 128-byte line of their index arrays, then the terminal values and
+// row accumulators those indices name.  Every later access of the phase then
+// hits the L2 instead of paying a trip to HBM per dependent step.
+__device__ __forceinline__ int32_t touch_lines(const int32_t* p, int64_t n, int32_t tid)
+{
+    int32_t s = 0;
+    for (int64_t i = (int64_t)tid * 32; i < n; i += (int64_t)kTailBlock * 32) s ^= p[i];
+    return s;
+}
+
+template <class P>
+__device__ __noinline__ void flat_prefetch(const LevelArgs* __restrict__ table, int32_t n_multi, int32_t nent,
+                                           const typename P::A* __restrict__ arena,
+                                           const typename P::A* __restrict__ acc)
+{
+    const int32_t tid = threadIdx.x;
+    int32_t sink = 0;
+    for (int32_t li = n_multi; li < nent; ++li) {
+        const LevelArgs& a = table[li];
+        const int32_t ng = a.gsl[kSlices];
+        sink ^= touch_lines((const int32_t*)a.child, 2 * (int64_t)a.bsl[kSlices], tid);
+        sink ^= touch_lines(a.ptsrc, a.psl[kSlices], tid);
+        sink ^= touch_lines(a.eoff, ng + 1, tid);
+        sink ^= touch_lines(a.erow, ng, tid);
+        if (ng) sink ^= touch_lines(a.epos + a.eoff[0], a.eoff[ng] - a.eoff[0], tid);
+    }
+    __syncthreads();
+    typename P::A vs = P::ident();
+    for (int32_t li = n_multi; li < nent; ++li) {
+        const LevelArgs& a = table[li];
+        for (int32_t t = tid; t < a.bsl[kSlices]; t += kTailBlock) {
+            const int2 c = a.child[t];
+            if (c.x < a.alpha) vs = P::comb(vs, arena[c.x]);
+            if (c.y < a.alpha) vs = P::comb(vs, arena[c.y]);
+        }
+        for (int32_t g = tid; g < a.gsl[kSlices]; g += kTailBlock) {
+            int x = 0;
+#pragma unroll
+            for (int w = kSlices / 2; w > 0; w >>= 1)
+                if (g >= a.gsl[x + w]) x += w;
+            vs = P::comb(vs, acc[(int64_t)x * a.n_rows + a.erow[g]]);
+        }
+    }
+    // keep the loads: a value no input produces
+    if (sink == 0x7fffffff && vs == P::ident() && tid == kTailBlock) ((int32_t*)arena)[0] = sink;
+    __syncthreads();
 }
 
 // Levels k0..L (each with the emission of the level below), the emission of
@@ -333,7 +393,8 @@ __device__ __forceinline__ void level_flat(const LevelArgs& a, typename P::A* __
 // y[r] = acc[0][r] (+) ... (+) acc[7][r].
 template <class P>
 __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t nent,
-                                                          int32_t n_multi, typename P::A* __restrict__ arena,
+                                                          int32_t n_multi, int32_t flat_cap,
+                                                          typename P::A* __restrict__ arena,
                                                           typename P::A* __restrict__ acc,
                                                           typename P::Y* __restrict__ y, int32_t n_rows,
                                                           unsigned* __restrict__ bar, int* __restrict__ err)
@@ -351,8 +412,21 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
     }
     if (n_multi < nent) {
         if (blockIdx.x == 0) {
+            extern __shared__ unsigned char flat_lds[];
+            typename P::A* lbuf[2] = {(typename P::A*)flat_lds, (typename P::A*)flat_lds + flat_cap};
+            // the narrow levels' launch arguments, copied to LDS once
+            LevelArgs* largs = (LevelArgs*)(flat_lds + kFlatLdsBytes);
+            const int32_t ncache = min(nent - n_multi, (int32_t)(kFlatArgsBytes / sizeof(LevelArgs)));
+            {
+                const int32_t words = ncache * (int32_t)(sizeof(LevelArgs) / 4);
+                const int32_t* src = (const int32_t*)(table + n_multi);
+                for (int32_t w = threadIdx.x; w < words; w += kTailBlock) ((int32_t*)largs)[w] = src[w];
+            }
+            flat_prefetch<P>(table, n_multi, nent, arena, acc);  // ends with a workgroup barrier
             for (int32_t li = n_multi; li < nent; ++li) {
-                level_flat<P>(table[li], arena, acc);
+                const int32_t j = li - n_multi;
+                const LevelArgs& a = j < ncache ? largs[j] : table[li];
+                level_flat<P>(a, arena, lbuf[(j + 1) & 1], j > 0, lbuf[j & 1], acc);
                 __syncthreads();
             }
         }
@@ -591,6 +665,7 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
         a.ptsrc = d->ptsrc + l.pt_off;
         a.nb = (int32_t)l.nb;
         a.cur = (int32_t)l.base;
+        a.prev = (int32_t)d->lv[k - 1].base;
         for (int x = 0; x <= kSlices; ++x) {
             a.bsl[x] = (int32_t)l.bsl[x];
             a.psl[x] = (int32_t)l.psl[x];
@@ -605,6 +680,8 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
     a.eoff = d->eoff + e.grp_off;
     a.epos = d->epos;
     a.n_rows = (int32_t)d->n_rows;
+    a.alpha = (int32_t)d->alpha;
+    if (k > d->L) a.prev = (int32_t)e.base;
     a.team_log2 = d->team_log2[k - 1];
     for (int x = 0; x <= kSlices; ++x) a.gsl[x] = (int32_t)e.gsl[x];
     for (int x = 0; x < kSlices; ++x) mg = std::max<int64_t>(mg, e.gsl[x + 1] - e.gsl[x]);
@@ -665,11 +742,12 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         mark();
         const LevelArgs* table = d->tail_table;
         int32_t nent = (int32_t)d->tail_nent, n_multi = (int32_t)d->tail_multi, n_rows = (int32_t)d->n_rows;
+        int32_t flat_cap = (int32_t)(kFlatLdsBytes / 2 / sizeof(A));
         unsigned* bar = d->barrier;
         int* errp = d->err;
-        void* args[] = {&table, &nent, &n_multi, &arena, &acc, &y, &n_rows, &bar, &errp};
+        void* args[] = {&table, &nent, &n_multi, &flat_cap, &arena, &acc, &y, &n_rows, &bar, &errp};
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
-                                                  dim3(kTailBlock), args, 0, s);
+                                                  dim3(kTailBlock), args, kFlatLdsBytes + kFlatArgsBytes, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
         mark();
     }
@@ -837,11 +915,34 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     // flat loops: binary + pass-through nodes and emission lanes) run on
     // workgroup 0 alone
     const int64_t flat_max = env_int("GCS_TAIL_FLAT", 4096);
-    auto flat_work = [&](const gcs::LevelArgs& a) {
-        return (int64_t)a.bsl[gcs::kSlices] + a.psl[gcs::kSlices] + ((int64_t)a.gsl[gcs::kSlices] << a.team_log2);
+    const int64_t flat_cap = (int64_t)(gcs::kFlatLdsBytes / 2 / gcs::elem_bytes(p));
+    auto flat_ok = [&](const gcs::LevelArgs& a) {
+        const int64_t w = (int64_t)a.bsl[gcs::kSlices] + a.psl[gcs::kSlices];
+        return w <= flat_cap && w + ((int64_t)a.gsl[gcs::kSlices] << a.team_log2) <= flat_max;
     };
     d->tail_multi = d->tail_nent;
-    while (d->tail_multi > 0 && flat_work(d->largs[d->tail_k0 - 1 + d->tail_multi - 1]) <= flat_max) --d->tail_multi;
+    while (d->tail_multi > 0 && flat_ok(d->largs[d->tail_k0 - 1 + d->tail_multi - 1])) --d->tail_multi;
+    // every level-below reference of a flat level after the first must land in
+    // its LDS buffer (true by construction; checked before anything runs)
+    for (int64_t j = d->tail_multi + 1; j < d->tail_nent; ++j) {
+        const int64_t k = d->tail_k0 + j;  // launch k: level k and the emission of level k-1
+        const gcs::Level& pl = g.lv[k - 1];
+        const int64_t lo = pl.base, hi = pl.base + pl.nb + pl.npt;
+        auto in_prev = [&](int64_t c) { return c < g.alpha() || (c >= lo && c < hi && c - lo < flat_cap); };
+        bool ok = true;
+        if (k <= g.L) {
+            const gcs::Level& l = g.lv[k];
+            for (int64_t t = 0; t < 2 * l.nb && ok; ++t) ok = in_prev(g.child[2 * l.child_off + t]);
+            for (int64_t t = 0; t < l.npt && ok; ++t) ok = in_prev(g.ptsrc[l.pt_off + t]);
+        }
+        for (int64_t gi = pl.grp_off; gi < pl.grp_off + pl.ngrp && ok; ++gi)
+            for (int32_t e = g.eoff[gi]; e < g.eoff[gi + 1] && ok; ++e) ok = in_prev(g.epos[e]);
+        if (!ok) {
+            delete d;
+            gcs::set_error("internal layout check failed: a narrow level reads outside its LDS buffer");
+            return GCS_ESTATE;
+        }
+    }
     d->tail_table = (const gcs::LevelArgs*)(base + im.table) + (d->tail_k0 - 1);
     e = hipMemcpyAsync(base + im.table, d->largs.data(), d->largs.size() * sizeof(gcs::LevelArgs),
                        hipMemcpyHostToDevice, s);
