@@ -397,7 +397,8 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
                                                           typename P::A* __restrict__ arena,
                                                           typename P::A* __restrict__ acc,
                                                           typename P::Y* __restrict__ y, int32_t n_rows,
-                                                          unsigned* __restrict__ bar, int* __restrict__ err)
+                                                          int32_t accumulate, unsigned* __restrict__ bar,
+                                                          int* __restrict__ err)
 {
     constexpr int Q = kTailBlock / kBlock;
     const int32_t q = threadIdx.x / kBlock, ltid = threadIdx.x % kBlock;
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
         typename P::A s = acc[r];
 #pragma unroll
         for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
-        y[r] = P::emit(P::yzero(), s);
+        y[r] = P::emit(accumulate ? y[r] : P::yzero(), s);
     }
 }
 
@@ -710,7 +711,8 @@ int64_t count_launches(const gcs_device* d)
 }
 
 template <class P>
-gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hipEvent_t* ev = nullptr)
+gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hipEvent_t* ev = nullptr,
+                     int32_t accumulate = 0)
 {
     using A = typename P::A;
     auto* arena = (A*)d->arena;
@@ -745,7 +747,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         int32_t flat_cap = (int32_t)(kFlatLdsBytes / 2 / sizeof(A));
         unsigned* bar = d->barrier;
         int* errp = d->err;
-        void* args[] = {&table, &nent, &n_multi, &flat_cap, &arena, &acc, &y, &n_rows, &bar, &errp};
+        void* args[] = {&table, &nent, &n_multi, &flat_cap, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
                                                   dim3(kTailBlock), args, kFlatLdsBytes + kFlatArgsBytes, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
@@ -967,7 +969,8 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     return GCS_OK;
 }
 
-static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, void* stream, hipEvent_t* ev)
+static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, void* stream, hipEvent_t* ev,
+                                 int32_t accumulate = 0)
 {
     if (!d || (d->n_cols > 0 && !x_dev) || (d->n_rows > 0 && !y_dev)) {
         gcs::set_error("invalid argument");
@@ -980,11 +983,11 @@ static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, 
     }
     hipStream_t s = (hipStream_t)stream;
     switch (d->policy) {
-    case GCS_PLUS_F64: return gcs::run_sweep<gcs::PolPlusF64>(d, x_dev, y_dev, s, ev);
-    case GCS_PLUS_F32: return gcs::run_sweep<gcs::PolPlusF32>(d, x_dev, y_dev, s, ev);
-    case GCS_PLUS_F32_ACC_F64: return gcs::run_sweep<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, s, ev);
-    case GCS_BOOL_OR: return gcs::run_sweep<gcs::PolBoolOr>(d, x_dev, y_dev, s, ev);
-    case GCS_PLUS_I64: return gcs::run_sweep<gcs::PolPlusI64>(d, x_dev, y_dev, s, ev);
+    case GCS_PLUS_F64: return gcs::run_sweep<gcs::PolPlusF64>(d, x_dev, y_dev, s, ev, accumulate);
+    case GCS_PLUS_F32: return gcs::run_sweep<gcs::PolPlusF32>(d, x_dev, y_dev, s, ev, accumulate);
+    case GCS_PLUS_F32_ACC_F64: return gcs::run_sweep<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, s, ev, accumulate);
+    case GCS_BOOL_OR: return gcs::run_sweep<gcs::PolBoolOr>(d, x_dev, y_dev, s, ev, accumulate);
+    case GCS_PLUS_I64: return gcs::run_sweep<gcs::PolPlusI64>(d, x_dev, y_dev, s, ev, accumulate);
     }
     gcs::set_error("corrupt device handle");
     return GCS_ESTATE;
@@ -993,6 +996,11 @@ static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, 
 extern "C" gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* stream)
 {
     return sweep_dispatch(d, x_dev, y_dev, stream, nullptr);
+}
+
+extern "C" gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void* y_dev, void* stream)
+{
+    return sweep_dispatch(d, x_dev, y_dev, stream, nullptr, 1);
 }
 
 extern "C" int64_t gcs_sweep_launches(const gcs_device* d) { return d ? gcs::count_launches(d) : 0; }

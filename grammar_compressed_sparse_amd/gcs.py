@@ -73,6 +73,7 @@ _lib.gcs_free_grammar.restype = None
 _lib.gcs_device_layout.argtypes = [_P, ctypes.c_int, ctypes.POINTER(DevSizes)]
 _lib.gcs_upload.argtypes = [_P, ctypes.c_int, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
 _lib.gcs_sweep_right.argtypes = [_P, _P, _P, _P]
+_lib.gcs_sweep_right_acc.argtypes = [_P, _P, _P, _P]
 _lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
@@ -85,7 +86,7 @@ _lib.gcs_free_device.argtypes = [_P]
 _lib.gcs_free_device.restype = None
 for _f in ("gcs_build_grammar", "gcs_grammar_from_rules", "gcs_grammar_stats", "gcs_level_widths",
            "gcs_export_grammar", "gcs_layout_counts", "gcs_export_layout", "gcs_device_layout", "gcs_upload",
-           "gcs_sweep_right", "gcs_bfs", "gcs_profile_begin", "gcs_sweep_right_profiled", "gcs_profile_end"):
+           "gcs_sweep_right", "gcs_sweep_right_acc", "gcs_bfs", "gcs_profile_begin", "gcs_sweep_right_profiled", "gcs_profile_end"):
     getattr(_lib, _f).restype = _st
 
 
@@ -259,6 +260,9 @@ class Device:
     def sweep_right(self, x, y=None, stream=None):
         return sweep_right(self, x, y, stream)
 
+    def sweep_right_acc(self, x, y, stream=None):
+        return sweep_right_acc(self, x, y, stream)
+
     def bfs(self, sources, max_passes=1 << 16, stream=None):
         return bfs(self, sources, max_passes, stream)
 
@@ -337,6 +341,16 @@ def sweep_right(dev: Device, x, y=None, stream=None):
     with torch.cuda.device(dev.device):
         _check(_lib.gcs_sweep_right(dev.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                     _stream_ptr(stream)))
+    return y
+
+
+def sweep_right_acc(dev: Device, x, y, stream=None):
+    """gcs_sweep_right_acc: y (+)= M x on the device (async on the stream)."""
+    _check_xy(dev, x, y)
+    torch = _torch()
+    with torch.cuda.device(dev.device):
+        _check(_lib.gcs_sweep_right_acc(dev.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                        _stream_ptr(stream)))
     return y
 
 

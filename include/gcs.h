@@ -216,6 +216,13 @@ gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, siz
  * share its workspace, so they must be ordered (same stream or synchronised). */
 gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 
+/* y (+)= M x: as gcs_sweep_right, but row r's result is combined into the
+ * existing y[r] (added; OR for the Boolean policy) instead of replacing it.
+ * Lets a matrix too large for one grammar be swept as independent column
+ * groups (each group its own grammar and upload, rules never spanning
+ * columns of two groups), accumulating into one y. */
+gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
+
 /* BFS fixpoint with the Boolean policy on a square matrix (section 5: one
  * Boolean pass is one frontier expansion; the fixpoint repeats it):
  *   f = visited = sources; repeat { y = M f; f = y AND NOT visited;
