@@ -101,10 +101,25 @@ __device__ inline float xchg(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline int64_t xchg(int64_t v, int m) { return __shfl_xor((long long)v, m, 64); }
 __device__ inline uint8_t xchg(uint8_t v, int m) { return (uint8_t)__shfl_xor((int)v, m, 64); }
 
+// An empty asm statement that takes v as an input: v must be computed before
+// this point on every lane, which keeps the compiler from sinking a lane's
+// independent loads into the masked store that consumes them (one load in
+// flight at a time instead of all of them).  Emits no instruction.
+template <class T>
+__device__ __forceinline__ void issue_before(const T& v)
+{
+    if constexpr (sizeof(T) == 8) {
+        asm volatile("" ::"v"(v));
+    } else {
+        asm volatile("" ::"v"((int32_t)v));
+    }
+}
+
 // ---------------------------------------------------------------- kernels
 
 constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
+constexpr int kEmitItems = 4;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
 constexpr size_t kFlatLdsBytes = 52 * 1024;  // LDS of the tail's single-workgroup phase: two level buffers
 constexpr size_t kFlatArgsBytes = 8 * 1024;  // and a copy of its levels' launch arguments
@@ -149,7 +164,48 @@ struct LevelArgs {
 
 static_assert(sizeof(LevelArgs) % 4 == 0, "LevelArgs is copied as 32-bit words");
 
+// One emission lane: combines the roots e0, e0 + team, ... below e1 of its
+// group in that order, kEmitItems independent loads per round (indices past
+// e1 are clamped to e1 - 1, the group's last root, and discarded).  A lane of
+// an invalid team, or one with no root, returns the identity.
+template <class P, class Val>
+__device__ __forceinline__ typename P::A emit_rounds(const int32_t* __restrict__ epos, int32_t e0, int32_t e1,
+                                                     int32_t team, bool valid, Val val)
+{
+    using A = typename P::A;
+    A s = P::ident();
+    int32_t e = e0;
+    do {
+        int32_t p[kEmitItems];
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) p[u] = epos[min(e + u * team, e1 - 1)];
+        A v[kEmitItems];
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) v[u] = val(p[u]);
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) issue_before(v[u]);
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u)
+            if (valid && e + u * team < e1) s = P::comb(s, v[u]);
+        e += kEmitItems * team;
+    } while (valid && e < e1);
+    return s;
+}
+
+// The fixed xor butterfly over a team of adjacent lanes (every lane of the
+// team ends with the same combination, in the same order on every run).
+template <class P>
+__device__ __forceinline__ typename P::A team_combine(typename P::A s, int32_t team)
+{
+    for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+    return s;
+}
+
 // One workgroup's share of a level launch: virtual block b of the grid.
+// Every load of a part is issued unconditionally (indices past the end of
+// the part are clamped to its last element, which exists because a block
+// with no element returns first), so a lane keeps all of its independent
+// gathers in flight at once; only the stores and the combines are masked.
 template <class P>
 __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32_t tid,
                                             typename P::A* __restrict__ arena, typename P::A* __restrict__ acc)
@@ -158,16 +214,17 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     const int32_t part_bin = a.pb_bin * kSlices, part_pt = a.pb_pt * kSlices;
     if (b < part_bin) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
-        const int32_t t0 = a.bsl[x] + i * (kBlock * kBinItems) + tid;
+        const int32_t first = a.bsl[x] + i * (kBlock * kBinItems);
+        if (first >= end) return;
+        const int32_t t0 = first + tid;
         int2 c[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kBlock;
-            c[u] = t < end ? a.child[t] : make_int2(0, 0);
-        }
+        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * kBlock, end - 1)];
         A v[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(arena[c[u].x], arena[c[u].y]);
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
@@ -178,16 +235,17 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     b -= part_bin;
     if (b < part_pt) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
-        const int32_t t0 = a.psl[x] + i * (kBlock * kBinItems) + tid;
+        const int32_t first = a.psl[x] + i * (kBlock * kBinItems);
+        if (first >= end) return;
+        const int32_t t0 = first + tid;
         int32_t src[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kBlock;
-            src[u] = t < end ? a.ptsrc[t] : 0;
-        }
+        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * kBlock, end - 1)];
         A v[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u]];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
@@ -197,29 +255,35 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     }
     b -= part_pt;
     // emission: a team of 2^team_log2 adjacent lanes per (slice, row) group;
-    // lanes stride over the group's roots, a fixed xor butterfly combines the
-    // team (deterministic), and the team's first lane updates the slice's
-    // accumulator of the row (each (slice, row) has one group per level and
-    // levels are ordered launches, so a plain read-modify-write suffices)
+    // lane sub of a team takes the group's roots sub, sub + team, ... in that
+    // order, kEmitItems of them per round as independent loads; a fixed xor
+    // butterfly combines the team (deterministic), and the team's first lane
+    // updates the slice's accumulator of the row (each (slice, row) has one
+    // group per level and levels are ordered launches, so a plain
+    // read-modify-write suffices).  Teams past the slice's last group read
+    // that group and discard it.
     const int32_t x = b % kSlices, i = b / kSlices;
+    const int32_t gend = a.gsl[x + 1];
+    const int32_t gfirst = a.gsl[x] + ((i * kBlock) >> a.team_log2);
+    if (gfirst >= gend) return;
     const int32_t gl = i * kBlock + tid;
     const int32_t team = 1 << a.team_log2;
-    const int32_t g = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
-    const bool valid = g < a.gsl[x + 1];
-    A s = P::ident();
-    if (valid) {
-        const int32_t e1 = a.eoff[g + 1];
-        for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, arena[a.epos[e]]);
-    }
-    for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+    const int32_t graw = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
+    const bool valid = graw < gend;
+    const int32_t g = valid ? graw : gend - 1;
+    const int32_t row = a.erow[g];
+    const int32_t e1 = a.eoff[g + 1];
+    const A s0 = emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, [&](int32_t c) { return arena[c]; });
+    const A s = team_combine<P>(s0, team);
     if (valid && sub == 0) {
-        A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
+        A* r = acc + (int64_t)x * a.n_rows + row;
         *r = P::comb(*r, s);
     }
 }
 
-// One wide level.  The grid is capped near the number of resident
-// workgroups; each workgroup strides over the level's virtual blocks.  The
+// One wide level.  By default the grid has one workgroup per virtual block
+// (measured faster on MI355X than a grid capped near the resident count);
+// with a cap, each workgroup strides over the level's virtual blocks.  The
 // stride (gridDim.x) is a multiple of kSlices, so a workgroup keeps serving
 // the same slice on the same XCD.
 template <class P>
@@ -284,49 +348,49 @@ __device__ __forceinline__ void level_flat(const LevelArgs& a, const typename P:
     const int32_t tid = threadIdx.x;
     const int32_t nb = a.bsl[kSlices], npt = a.psl[kSlices];
     auto val = [&](int32_t c) -> A { return (prev_in_lds && c >= a.alpha) ? lprev[c - a.prev] : arena[c]; };
+    // loads clamped into range and issued unconditionally, as in level_block
     for (int32_t t0 = tid; t0 < nb; t0 += kTailBlock * kBinItems) {
         int2 c[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kTailBlock;
-            c[u] = t < nb ? a.child[t] : make_int2(0, 0);
-        }
+        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * kTailBlock, nb - 1)];
+        A v[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(val(c[u].x), val(c[u].y));
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kTailBlock;
-            if (t < nb) lcur[t] = P::comb(val(c[u].x), val(c[u].y));
+            if (t < nb) lcur[t] = v[u];
         }
     }
     for (int32_t t0 = tid; t0 < npt; t0 += kTailBlock * kBinItems) {
         int32_t src[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kTailBlock;
-            src[u] = t < npt ? a.ptsrc[t] : 0;
-        }
+        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * kTailBlock, npt - 1)];
+        A v[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) v[u] = val(src[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kTailBlock;
-            if (t < npt) lcur[nb + t] = val(src[u]);
+            if (t < npt) lcur[nb + t] = v[u];
         }
     }
     const int32_t team = 1 << a.team_log2, ngrp = a.gsl[kSlices];
     for (int32_t gl0 = 0; gl0 < (ngrp << a.team_log2); gl0 += kTailBlock) {
         const int32_t gl = gl0 + tid;
-        const int32_t g = gl >> a.team_log2, sub = gl & (team - 1);
-        const bool valid = g < ngrp;
-        A s = P::ident();
-        if (valid) {
-            const int32_t e1 = a.eoff[g + 1];
-            for (int32_t e = a.eoff[g] + sub; e < e1; e += team) s = P::comb(s, val(a.epos[e]));
-        }
-        for (int32_t o = team >> 1; o > 0; o >>= 1) s = P::comb(s, xchg(s, o));
+        const int32_t graw = gl >> a.team_log2, sub = gl & (team - 1);
+        const bool valid = graw < ngrp;
+        const int32_t g = valid ? graw : ngrp - 1;
+        const int32_t row = a.erow[g];
+        const int32_t e1 = a.eoff[g + 1];
+        const A s0 = emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, val);
+        const A s = team_combine<P>(s0, team);
         if (valid && sub == 0) {
             int x = 0;  // slice of group g: gsl[x] <= g < gsl[x+1]
 #pragma unroll
             for (int w = kSlices / 2; w > 0; w >>= 1)
                 if (g >= a.gsl[x + w]) x += w;
-            A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
+            A* r = acc + (int64_t)x * a.n_rows + row;
             *r = P::comb(*r, s);
         }
     }
@@ -602,8 +666,10 @@ bool layout_in_bounds(const Grammar& g)
         po += l.npt;
     }
     if (2 * co != (int64_t)g.child.size() || po != (int64_t)g.ptsrc.size()) return false;
+    // every emission group holds at least one root (the kernels clamp a
+    // lane's root index to its group's last root)
     for (size_t i = 0; i + 1 < g.eoff.size(); ++i)
-        if (g.eoff[i] < 0 || g.eoff[i] > g.eoff[i + 1]) return false;
+        if (g.eoff[i] < 0 || g.eoff[i] >= g.eoff[i + 1]) return false;
     if (!g.eoff.empty() && g.eoff.back() != (int32_t)g.epos.size()) return false;
     for (int32_t e : g.epos)
         if (e < 0 || e >= arena) return false;
@@ -861,13 +927,16 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->alpha = g.alpha();
     d->L = g.L;
     d->lv = g.lv;
-    // emission team per level: about four roots per lane, at most one wave
+    // emission team per level: about GCS_EMIT_PER_LANE (default 4) roots per
+    // lane, at most one wave
+    const char* pl_env = std::getenv("GCS_EMIT_PER_LANE");
+    const double per_lane = pl_env ? std::max(0.5, std::atof(pl_env)) : 4.0;
     d->team_log2.assign(g.lv.size(), 0);
     for (size_t k = 0; k < g.lv.size(); ++k) {
         const gcs::Level& l = g.lv[k];
         if (l.ngrp == 0) continue;
         const int64_t roots = g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off];
-        const double per_lane = 4.0, mean = (double)roots / (double)l.ngrp;
+        const double mean = (double)roots / (double)l.ngrp;
         int t = 0;
         while (t < 6 && (double)(1 << t) * per_lane < mean && (l.ngrp << (t + 1)) < (int64_t)INT32_MAX - gcs::kBlock) ++t;
         d->team_log2[k] = t;
@@ -906,7 +975,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
-    d->grid_max = std::max(gcs::kSlices, env_int("GCS_GRID_MAX", 8 * std::max(dev_cu, 1)) / gcs::kSlices * gcs::kSlices);
+    // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
+    // the grid (then workgroups stride over the blocks)
+    d->grid_max = std::max(gcs::kSlices, env_int("GCS_GRID_MAX", INT32_MAX) / gcs::kSlices * gcs::kSlices);
     d->largs.resize((size_t)g.L + 1);
     for (int64_t k = 1; k <= g.L + 1; ++k) d->largs[k - 1] = gcs::make_args(d, k);
     d->tail_k0 = g.L + 1;
