@@ -31,6 +31,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "grammar.hpp"
@@ -121,8 +122,8 @@ constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kEmitItems = 4;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
-constexpr size_t kFlatLdsBytes = 52 * 1024;  // LDS of the tail's single-workgroup phase: two level buffers
-constexpr size_t kFlatArgsBytes = 8 * 1024;  // and a copy of its levels' launch arguments
+constexpr size_t kFlatLdsMax = 128 * 1024;  // LDS budget of the tail's single-workgroup phase
+constexpr int kFlatEntryWords = 8;  // per narrow launch in that phase's table
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
 template <class P>
@@ -168,8 +169,8 @@ static_assert(sizeof(LevelArgs) % 4 == 0, "LevelArgs is copied as 32-bit words")
 // group in that order, kEmitItems independent loads per round (indices past
 // e1 are clamped to e1 - 1, the group's last root, and discarded).  A lane of
 // an invalid team, or one with no root, returns the identity.
-template <class P, class Val>
-__device__ __forceinline__ typename P::A emit_rounds(const int32_t* __restrict__ epos, int32_t e0, int32_t e1,
+template <class P, class Idx, class Val>
+__device__ __forceinline__ typename P::A emit_rounds(const Idx* __restrict__ epos, int32_t e0, int32_t e1,
                                                      int32_t team, bool valid, Val val)
 {
     using A = typename P::A;
@@ -331,118 +332,112 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
     return ok != 0;
 }
 
-// The narrowest levels, run by one workgroup of kTailBlock lanes with
-// workgroup barriers only, their values held in two LDS buffers (lprev: the
-// level below, lcur: this level) instead of the arena.  A child offset c
-// reads the terminal array (c < alpha) or the level below: from LDS when that
-// level was computed here too, from the arena when it came from the grid
-// phase.  Binary nodes, pass-through nodes and the emission of the level
-// below are flat loops over the whole level; an emission group's slice is
-// looked up to address its accumulator.
+// The narrowest launches, run by one workgroup of kTailBlock lanes with
+// workgroup barriers only and everything they touch held in LDS.  The host
+// rewrites each of their value references (a child, a pass-through source, a
+// root) as a slot of one LDS value array: slots [0, n_stage) are staged from
+// the arena once (terminal values and the level the grid phase computed
+// last), and every narrow level owns the slots its nodes are written to.
+// Emission sums go to LDS slots (gsum) and are folded into the row
+// accumulators at the end, each accumulator taking its sums in level order:
+// the same operations in the same order as one read-modify-write per level.
+struct FlatArgs {
+    const int32_t* idx;        // LDS part: entry table, group offsets, u16 refs, u16 roots (idx_words words)
+    const int32_t* stage_src;  // arena offset staged into slot s, s < n_stage
+    const int32_t* fold_acc;   // accumulator index of fold i
+    const int32_t* fold_off;   // fold i takes gsum slots fold_list[fold_off[i] .. fold_off[i+1])
+    const int32_t* fold_list;
+    int32_t idx_words, n_ent, goff_word, refs_word, roots_word;
+    int32_t n_stage, n_fold;
+    int32_t vals_off, gsum_off;  // byte offsets of the value and gsum arrays in LDS
+};
+
+// for (i = tid; i < n; i += kTailBlock) op(i), four independent iterations at
+// a time: op(i, live) must only load when live is false (i is then clamped
+// to n - 1) and store when it is true
+template <class Op>
+__device__ __forceinline__ void block_rounds(int32_t n, int32_t tid, Op op)
+{
+    for (int32_t i0 = tid; i0 < n; i0 += 4 * kTailBlock) op(i0, min(i0 + kTailBlock, n - 1), min(i0 + 2 * kTailBlock, n - 1),
+                                                              min(i0 + 3 * kTailBlock, n - 1), i0 + kTailBlock < n,
+                                                              i0 + 2 * kTailBlock < n, i0 + 3 * kTailBlock < n);
+}
+
 template <class P>
-__device__ __forceinline__ void level_flat(const LevelArgs& a, const typename P::A* __restrict__ arena,
-                                           const typename P::A* lprev, bool prev_in_lds, typename P::A* lcur,
-                                           typename P::A* __restrict__ acc)
+__device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* __restrict__ arena,
+                                        typename P::A* __restrict__ acc)
 {
     using A = typename P::A;
+    extern __shared__ __align__(16) unsigned char flat_lds[];
     const int32_t tid = threadIdx.x;
-    const int32_t nb = a.bsl[kSlices], npt = a.psl[kSlices];
-    auto val = [&](int32_t c) -> A { return (prev_in_lds && c >= a.alpha) ? lprev[c - a.prev] : arena[c]; };
-    // loads clamped into range and issued unconditionally, as in level_block
-    for (int32_t t0 = tid; t0 < nb; t0 += kTailBlock * kBinItems) {
-        int2 c[kBinItems];
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * kTailBlock, nb - 1)];
-        A v[kBinItems];
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(val(c[u].x), val(c[u].y));
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kTailBlock;
-            if (t < nb) lcur[t] = v[u];
-        }
-    }
-    for (int32_t t0 = tid; t0 < npt; t0 += kTailBlock * kBinItems) {
-        int32_t src[kBinItems];
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * kTailBlock, npt - 1)];
-        A v[kBinItems];
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = val(src[u]);
-#pragma unroll
-        for (int u = 0; u < kBinItems; ++u) {
-            const int32_t t = t0 + u * kTailBlock;
-            if (t < npt) lcur[nb + t] = v[u];
-        }
-    }
-    const int32_t team = 1 << a.team_log2, ngrp = a.gsl[kSlices];
-    for (int32_t gl0 = 0; gl0 < (ngrp << a.team_log2); gl0 += kTailBlock) {
-        const int32_t gl = gl0 + tid;
-        const int32_t graw = gl >> a.team_log2, sub = gl & (team - 1);
-        const bool valid = graw < ngrp;
-        const int32_t g = valid ? graw : ngrp - 1;
-        const int32_t row = a.erow[g];
-        const int32_t e1 = a.eoff[g + 1];
-        const A s0 = emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, val);
-        const A s = team_combine<P>(s0, team);
-        if (valid && sub == 0) {
-            int x = 0;  // slice of group g: gsl[x] <= g < gsl[x+1]
-#pragma unroll
-            for (int w = kSlices / 2; w > 0; w >>= 1)
-                if (g >= a.gsl[x + w]) x += w;
-            A* r = acc + (int64_t)x * a.n_rows + row;
-            *r = P::comb(*r, s);
-        }
-    }
-}
-
-// Brings what the narrow levels will read into the L2 before they start: one
-// load per 128-byte line of their index arrays, then the terminal values and
-// row accumulators those indices name.  Every later access of the phase then
-// hits the L2 instead of paying a trip to HBM per dependent step.
-__device__ __forceinline__ int32_t touch_lines(const int32_t* p, int64_t n, int32_t tid)
-{
-    int32_t s = 0;
-    for (int64_t i = (int64_t)tid * 32; i < n; i += (int64_t)kTailBlock * 32) s ^= p[i];
-    return s;
-}
-
-template <class P>
-__device__ __noinline__ void flat_prefetch(const LevelArgs* __restrict__ table, int32_t n_multi, int32_t nent,
-                                           const typename P::A* __restrict__ arena,
-                                           const typename P::A* __restrict__ acc)
-{
-    const int32_t tid = threadIdx.x;
-    int32_t sink = 0;
-    for (int32_t li = n_multi; li < nent; ++li) {
-        const LevelArgs& a = table[li];
-        const int32_t ng = a.gsl[kSlices];
-        sink ^= touch_lines((const int32_t*)a.child, 2 * (int64_t)a.bsl[kSlices], tid);
-        sink ^= touch_lines(a.ptsrc, a.psl[kSlices], tid);
-        sink ^= touch_lines(a.eoff, ng + 1, tid);
-        sink ^= touch_lines(a.erow, ng, tid);
-        if (ng) sink ^= touch_lines(a.epos + a.eoff[0], a.eoff[ng] - a.eoff[0], tid);
+    int32_t* iw = (int32_t*)flat_lds;
+    A* vals = (A*)(flat_lds + f.vals_off);
+    A* gsum = (A*)(flat_lds + f.gsum_off);
+    // the index image (a multiple of four words) and the staged values
+    {
+        const int4* src = (const int4*)f.idx;
+        int4* dst = (int4*)iw;
+        block_rounds(f.idx_words / 4, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
+            const int4 v0 = src[i0], v1 = src[i1], v2 = src[i2], v3 = src[i3];
+            dst[i0] = v0;
+            if (l1) dst[i1] = v1;
+            if (l2) dst[i2] = v2;
+            if (l3) dst[i3] = v3;
+        });
+        block_rounds(f.n_stage, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
+            const A v0 = arena[f.stage_src[i0]], v1 = arena[f.stage_src[i1]];
+            const A v2 = arena[f.stage_src[i2]], v3 = arena[f.stage_src[i3]];
+            issue_before(v0);
+            issue_before(v1);
+            issue_before(v2);
+            issue_before(v3);
+            vals[i0] = v0;
+            if (l1) vals[i1] = v1;
+            if (l2) vals[i2] = v2;
+            if (l3) vals[i3] = v3;
+        });
     }
     __syncthreads();
-    typename P::A vs = P::ident();
-    for (int32_t li = n_multi; li < nent; ++li) {
-        const LevelArgs& a = table[li];
-        for (int32_t t = tid; t < a.bsl[kSlices]; t += kTailBlock) {
-            const int2 c = a.child[t];
-            if (c.x < a.alpha) vs = P::comb(vs, arena[c.x]);
-            if (c.y < a.alpha) vs = P::comb(vs, arena[c.y]);
+    const uint16_t* refs = (const uint16_t*)(iw + f.refs_word);
+    const uint16_t* roots = (const uint16_t*)(iw + f.roots_word);
+    const int32_t* goff = iw + f.goff_word;
+    auto val = [&](int32_t c) -> A { return vals[c]; };
+    for (int32_t j = 0; j < f.n_ent; ++j) {
+        const int32_t* e = iw + j * kFlatEntryWords;
+        const int32_t nb = e[0], npt = e[1], ng = e[2], tl = e[3], out = e[4], r0 = e[5], g0 = e[6], s0 = e[7];
+        // this level's nodes (slots out ..) from the level below; the emission
+        // of the level below reads other slots, so no barrier in between
+        for (int32_t t = tid; t < nb; t += kTailBlock)
+            vals[out + t] = P::comb(vals[refs[r0 + 2 * t]], vals[refs[r0 + 2 * t + 1]]);
+        for (int32_t t = tid; t < npt; t += kTailBlock) vals[out + nb + t] = vals[refs[r0 + 2 * nb + t]];
+        const int32_t team = 1 << tl;
+        for (int32_t gl0 = 0; gl0 < (ng << tl); gl0 += kTailBlock) {
+            const int32_t gl = gl0 + tid;
+            const int32_t graw = gl >> tl, sub = gl & (team - 1);
+            const bool valid = graw < ng;
+            const int32_t gg = valid ? graw : ng - 1;
+            const A s0v = emit_rounds<P>(roots, goff[g0 + gg] + sub, goff[g0 + gg + 1], team, valid, val);
+            const A sum = team_combine<P>(s0v, team);
+            if (valid && sub == 0) gsum[s0 + graw] = sum;
         }
-        for (int32_t g = tid; g < a.gsl[kSlices]; g += kTailBlock) {
-            int x = 0;
-#pragma unroll
-            for (int w = kSlices / 2; w > 0; w >>= 1)
-                if (g >= a.gsl[x + w]) x += w;
-            vs = P::comb(vs, acc[(int64_t)x * a.n_rows + a.erow[g]]);
-        }
+        __syncthreads();
     }
-    // keep the loads: a value no input produces
-    if (sink == 0x7fffffff && vs == P::ident() && tid == kTailBlock) ((int32_t*)arena)[0] = sink;
-    __syncthreads();
+    block_rounds(f.n_fold, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
+        const int32_t ai[4] = {f.fold_acc[i0], f.fold_acc[i1], f.fold_acc[i2], f.fold_acc[i3]};
+        const int32_t ii[4] = {i0, i1, i2, i3};
+        const bool live[4] = {true, l1, l2, l3};
+        A a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = acc[ai[u]];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) issue_before(a[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (!live[u]) continue;
+            for (int32_t k = f.fold_off[ii[u]]; k < f.fold_off[ii[u] + 1]; ++k) a[u] = P::comb(a[u], gsum[f.fold_list[k]]);
+            acc[ai[u]] = a[u];
+        }
+    });
 }
 
 // Levels k0..L (each with the emission of the level below), the emission of
@@ -451,14 +446,13 @@ __device__ __noinline__ void flat_prefetch(const LevelArgs* __restrict__ table, 
 // grid: the four 256-lane quarters of a workgroup take virtual blocks
 // blockIdx.x + (quarter + 4j) * gridDim.x, all of the same slice (gridDim.x
 // is a multiple of kSlices), so a workgroup stays on its slice's XCD; grid
-// barriers separate the entries.  Entries [n_multi, nent) are the narrowest
-// levels: workgroup 0 runs them alone with workgroup barriers while the
+// barriers separate the entries.  The remaining f.n_ent entries are the
+// narrowest levels: workgroup 0 runs them alone in LDS (flat_phase) while the
 // others wait at the next grid barrier.  Then every workgroup reduces
 // y[r] = acc[0][r] (+) ... (+) acc[7][r].
 template <class P>
-__global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t nent,
-                                                          int32_t n_multi, int32_t flat_cap,
-                                                          typename P::A* __restrict__ arena,
+__global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t n_multi,
+                                                          FlatArgs f, typename P::A* __restrict__ arena,
                                                           typename P::A* __restrict__ acc,
                                                           typename P::Y* __restrict__ y, int32_t n_rows,
                                                           int32_t accumulate, unsigned* __restrict__ bar,
@@ -475,26 +469,8 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
         if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (n_multi < nent) {
-        if (blockIdx.x == 0) {
-            extern __shared__ unsigned char flat_lds[];
-            typename P::A* lbuf[2] = {(typename P::A*)flat_lds, (typename P::A*)flat_lds + flat_cap};
-            // the narrow levels' launch arguments, copied to LDS once
-            LevelArgs* largs = (LevelArgs*)(flat_lds + kFlatLdsBytes);
-            const int32_t ncache = min(nent - n_multi, (int32_t)(kFlatArgsBytes / sizeof(LevelArgs)));
-            {
-                const int32_t words = ncache * (int32_t)(sizeof(LevelArgs) / 4);
-                const int32_t* src = (const int32_t*)(table + n_multi);
-                for (int32_t w = threadIdx.x; w < words; w += kTailBlock) ((int32_t*)largs)[w] = src[w];
-            }
-            flat_prefetch<P>(table, n_multi, nent, arena, acc);  // ends with a workgroup barrier
-            for (int32_t li = n_multi; li < nent; ++li) {
-                const int32_t j = li - n_multi;
-                const LevelArgs& a = j < ncache ? largs[j] : table[li];
-                level_flat<P>(a, arena, lbuf[(j + 1) & 1], j > 0, lbuf[j & 1], acc);
-                __syncthreads();
-            }
-        }
+    if (f.n_ent > 0) {
+        if (blockIdx.x == 0) flat_phase<P>(f, arena, acc);
         if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -574,6 +550,9 @@ struct gcs_device {
     int32_t tail_wgs = 0;
     int64_t grid_max = 0;  // cap on workgroups of a wide level launch (multiple of kSlices)
     const gcs::LevelArgs* tail_table = nullptr;
+    gcs::FlatArgs flat{};      // the narrowest tail launches, run in LDS by one workgroup
+    size_t flat_lds = 0;       // dynamic LDS bytes of the tail launch
+    bool flat_attr = false;    // the tail kernel's dynamic LDS limit has been raised
     int64_t* pinned;
     // profiling
     std::vector<hipEvent_t> events;
@@ -602,8 +581,25 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, table, total;
+    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, table, flat, total;
 };
+
+inline size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
+
+// Upper bound on the narrow launches' image (32-bit words): the LDS part is
+// at most kFlatLdsMax bytes and no larger than the grammar's own index
+// arrays with a table entry and one group offset per launch; staged slots
+// and emission sums are 16-bit indices (below 2^16) and at most all of the
+// arena and all groups; the fold lists hold one index per emission sum.
+size_t flat_section_words(const Grammar& g)
+{
+    const size_t G = g.erow.size(), C = g.epos.size();
+    const size_t lds = std::min(kFlatLdsMax / 4, (size_t)kFlatEntryWords * (g.L + 2) + G + g.L + 2 +
+                                                     (g.child.size() + g.ptsrc.size() + 1) / 2 + (C + 1) / 2 + 4);
+    const size_t stage = std::min<size_t>(65536, (size_t)g.arena);
+    const size_t sums = std::min<size_t>(65536, G);
+    return lds + stage + 3 * sums + 1;
+}
 
 Image image_layout(const Grammar& g, gcs_policy p)
 {
@@ -627,6 +623,8 @@ Image image_layout(const Grammar& g, gcs_policy p)
     o = al256(o + g.V.size() * v_bytes(p));
     m.table = o;
     o = al256(o + (size_t)(g.L + 1) * sizeof(LevelArgs));
+    m.flat = o;
+    o = al256(o + 4 * flat_section_words(g));
     m.total = o;
     return m;
 }
@@ -636,6 +634,181 @@ size_t acc_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)kSlices 
 size_t workspace_bytes(const Grammar& g, gcs_policy p) { return arena_bytes(g, p) + acc_bytes(g, p) + 256; }
 
 bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_PLUS_I64; }
+
+// The narrow launches' image, built at upload: tail entry j is launch
+// k = tail_k0 + j (level k when k <= L, and the emission of level k-1).
+struct FlatImage {
+    int64_t first = 0;              // tail entry of the first narrow launch
+    std::vector<int32_t> words;     // the section: LDS part, stage, fold_acc, fold_off, fold_list
+    FlatArgs args{};                // pointer members hold word offsets into the section until upload
+    size_t lds_bytes = 0;
+};
+
+// Picks the longest suffix of tail entries that fits: every entry's work
+// (nodes plus emission lanes) at most flat_max, all slots and sums below 2^16,
+// the LDS part within budget.  Then rewrites every reference as a slot.
+// Returns false (with the error set) only if a reference breaks the layering.
+bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budget, int64_t flat_max, FlatImage& fi)
+{
+    const int64_t nent = d->tail_nent, k0 = d->tail_k0, alpha = g.alpha();
+    auto width = [&](int64_t k) -> int64_t { return k >= 1 && k <= g.L ? g.lv[k].nb + g.lv[k].npt : 0; };
+    auto for_refs = [&](int64_t j, auto&& fn) {  // children, pass-through sources, roots, in that order
+        const int64_t k = k0 + j;
+        if (k <= g.L) {
+            const Level& l = g.lv[k];
+            for (int64_t t = 0; t < 2 * l.nb; ++t) fn(g.child[2 * l.child_off + t]);
+            for (int64_t t = 0; t < l.npt; ++t) fn(g.ptsrc[l.pt_off + t]);
+        }
+        const Level& pl = g.lv[k - 1];
+        for (int64_t e = g.eoff[pl.grp_off]; e < g.eoff[pl.grp_off + pl.ngrp]; ++e) fn(g.epos[e]);
+    };
+    // selection, from the last entry backwards
+    fi.first = nent;
+    {
+        std::vector<int32_t> terms;
+        int64_t produced = 0, sums = 0, nrefs = 0, nroots = 0, ngoff = 0;
+        for (int64_t j = nent - 1; j >= 0; --j) {
+            const int64_t k = k0 + j;
+            const Level& pl = g.lv[k - 1];
+            if (width(k) + ((int64_t)pl.ngrp << d->team_log2[k - 1]) > flat_max) break;
+            std::vector<int32_t> prev;
+            for_refs(j, [&](int32_t c) { (c < alpha ? terms : prev).push_back(c); });
+            std::sort(terms.begin(), terms.end());
+            terms.erase(std::unique(terms.begin(), terms.end()), terms.end());
+            std::sort(prev.begin(), prev.end());
+            prev.erase(std::unique(prev.begin(), prev.end()), prev.end());
+            produced += width(k);
+            sums += pl.ngrp;
+            nrefs += k <= g.L ? 2 * g.lv[k].nb + g.lv[k].npt : 0;
+            nroots += g.eoff[pl.grp_off + pl.ngrp] - g.eoff[pl.grp_off];
+            ngoff += pl.ngrp + 1;
+            const int64_t slots = (int64_t)terms.size() + (int64_t)prev.size() + produced;
+            const int64_t words = (kFlatEntryWords * (nent - j) + ngoff + (nrefs + 1) / 2 + (nroots + 1) / 2 + 3) / 4 * 4;
+            const size_t bytes = al16(4 * (size_t)words) + al16((size_t)slots * elem) + al16((size_t)sums * elem);
+            if (slots > 65535 || sums > 65535 || bytes > budget) break;
+            fi.first = j;
+        }
+    }
+    const int64_t f0 = fi.first, n_ent = nent - f0;
+    if (n_ent == 0) return true;
+    // stage slots: the terminals referenced, then the first narrow launch's
+    // references to the level the grid computed, each in increasing order
+    std::vector<int32_t> terms, prevs;
+    for (int64_t j = f0; j < nent; ++j)
+        for_refs(j, [&](int32_t c) {
+            if (c < alpha) terms.push_back(c);
+            else if (j == f0) prevs.push_back(c);
+        });
+    for (auto* v : {&terms, &prevs}) {
+        std::sort(v->begin(), v->end());
+        v->erase(std::unique(v->begin(), v->end()), v->end());
+    }
+    const int64_t n_stage = (int64_t)(terms.size() + prevs.size());
+    std::vector<int64_t> sb((size_t)g.L + 2, 0);  // first slot of level k's nodes
+    int64_t slot = n_stage;
+    for (int64_t j = f0; j < nent; ++j) {
+        sb[k0 + j] = slot;
+        slot += width(k0 + j);
+    }
+    const int64_t n_slots = slot;
+    bool ok = true;
+    auto map = [&](int32_t c, int64_t j) -> uint16_t {
+        int64_t r;
+        if (c < alpha) {
+            r = std::lower_bound(terms.begin(), terms.end(), c) - terms.begin();
+        } else if (j == f0) {
+            r = (int64_t)terms.size() + (std::lower_bound(prevs.begin(), prevs.end(), c) - prevs.begin());
+        } else {
+            const int64_t kb = k0 + j - 1, off = (int64_t)c - g.lv[kb].base;
+            if (off < 0 || off >= width(kb)) ok = false;
+            r = sb[kb] + off;
+        }
+        if (r < 0 || r >= n_slots) {
+            ok = false;
+            r = 0;
+        }
+        return (uint16_t)r;
+    };
+    std::vector<int32_t> ent, goff;
+    std::vector<uint16_t> refs, roots;
+    std::vector<std::pair<int32_t, int32_t>> folds;  // (accumulator, sum slot) in level order
+    int32_t sums = 0;
+    for (int64_t j = f0; j < nent; ++j) {
+        const int64_t k = k0 + j;
+        const Level& pl = g.lv[k - 1];
+        const int64_t nb = k <= g.L ? g.lv[k].nb : 0, npt = k <= g.L ? g.lv[k].npt : 0;
+        const int32_t e[kFlatEntryWords] = {(int32_t)nb, (int32_t)npt, (int32_t)pl.ngrp, d->team_log2[k - 1],
+                                            (int32_t)(k <= g.L ? sb[k] : 0), (int32_t)refs.size(),
+                                            (int32_t)goff.size(), sums};
+        ent.insert(ent.end(), e, e + kFlatEntryWords);
+        if (k <= g.L) {
+            const Level& l = g.lv[k];
+            for (int64_t t = 0; t < 2 * l.nb; ++t) refs.push_back(map(g.child[2 * l.child_off + t], j));
+            for (int64_t t = 0; t < l.npt; ++t) refs.push_back(map(g.ptsrc[l.pt_off + t], j));
+        }
+        goff.push_back((int32_t)roots.size());
+        int x = 0;
+        for (int64_t gi = 0; gi < pl.ngrp; ++gi) {
+            while (x < kSlices - 1 && gi >= pl.gsl[x + 1]) ++x;
+            const int64_t G = pl.grp_off + gi;
+            for (int32_t e2 = g.eoff[G]; e2 < g.eoff[G + 1]; ++e2) roots.push_back(map(g.epos[e2], j));
+            goff.push_back((int32_t)roots.size());
+            folds.push_back({(int32_t)(x * g.n_rows + g.erow[G]), sums + (int32_t)gi});
+        }
+        sums += (int32_t)pl.ngrp;
+    }
+    if (!ok) {
+        set_error("internal layout check failed: a narrow level reads outside the level below");
+        return false;
+    }
+    std::stable_sort(folds.begin(), folds.end(),
+                     [](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
+                         return a.first < b.first;
+                     });
+    FlatArgs& fa = fi.args;
+    std::vector<int32_t>& w = fi.words;
+    w = ent;
+    fa.goff_word = (int32_t)w.size();
+    w.insert(w.end(), goff.begin(), goff.end());
+    fa.refs_word = (int32_t)w.size();
+    w.resize(w.size() + (refs.size() + 1) / 2, 0);
+    std::memcpy(w.data() + fa.refs_word, refs.data(), refs.size() * 2);
+    fa.roots_word = (int32_t)w.size();
+    w.resize(w.size() + (roots.size() + 1) / 2, 0);
+    std::memcpy(w.data() + fa.roots_word, roots.data(), roots.size() * 2);
+    w.resize((w.size() + 3) / 4 * 4, 0);
+    fa.idx_words = (int32_t)w.size();
+    fa.n_ent = (int32_t)n_ent;
+    fa.n_stage = (int32_t)n_stage;
+    fa.vals_off = (int32_t)al16(4 * w.size());
+    fa.gsum_off = (int32_t)(fa.vals_off + al16((size_t)n_slots * elem));
+    fi.lds_bytes = fa.gsum_off + al16((size_t)sums * elem);
+    // global-only part; pointer members hold word offsets until upload
+    fa.stage_src = (const int32_t*)(uintptr_t)w.size();
+    w.insert(w.end(), terms.begin(), terms.end());
+    w.insert(w.end(), prevs.begin(), prevs.end());
+    std::vector<int32_t> facc, foff{0}, flist;
+    for (size_t i = 0; i < folds.size(); ++i) {
+        if (i == 0 || folds[i].first != folds[i - 1].first) {
+            if (i) foff.push_back((int32_t)flist.size());
+            facc.push_back(folds[i].first);
+        }
+        flist.push_back(folds[i].second);
+    }
+    if (!folds.empty()) foff.push_back((int32_t)flist.size());
+    fa.n_fold = (int32_t)facc.size();
+    fa.fold_acc = (const int32_t*)(uintptr_t)w.size();
+    w.insert(w.end(), facc.begin(), facc.end());
+    fa.fold_off = (const int32_t*)(uintptr_t)w.size();
+    w.insert(w.end(), foff.begin(), foff.end());
+    fa.fold_list = (const int32_t*)(uintptr_t)w.size();
+    w.insert(w.end(), flist.begin(), flist.end());
+    if (fi.lds_bytes > budget || w.size() > flat_section_words(g)) {
+        set_error("internal layout check failed: the narrow levels' image exceeds its bound");
+        return false;
+    }
+    return true;
+}
 
 // Every index a kernel dereferences must stay inside its buffer: children,
 // pass-through sources and emission positions inside the arena, emission rows
@@ -809,13 +982,19 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     if (has_tail(d)) {
         mark();
         const LevelArgs* table = d->tail_table;
-        int32_t nent = (int32_t)d->tail_nent, n_multi = (int32_t)d->tail_multi, n_rows = (int32_t)d->n_rows;
-        int32_t flat_cap = (int32_t)(kFlatLdsBytes / 2 / sizeof(A));
+        int32_t n_multi = (int32_t)d->tail_multi, n_rows = (int32_t)d->n_rows;
+        FlatArgs flat = d->flat;
         unsigned* bar = d->barrier;
         int* errp = d->err;
-        void* args[] = {&table, &nent, &n_multi, &flat_cap, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
+        if (d->flat_lds > 65536 && !d->flat_attr) {
+            hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&tail_kernel<P>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)d->flat_lds);
+            if (ea != hipSuccess) return hip_fail(ea, "hipFuncSetAttribute (tail LDS)");
+            d->flat_attr = true;
+        }
+        void* args[] = {&table, &n_multi, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
         hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
-                                                  dim3(kTailBlock), args, kFlatLdsBytes + kFlatArgsBytes, s);
+                                                  dim3(kTailBlock), args, d->flat_lds, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
         mark();
     }
@@ -984,36 +1163,33 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     const int64_t quarters = gcs::kTailBlock / gcs::kBlock;
     while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
     d->tail_nent = g.L + 2 - d->tail_k0;
-    // the narrowest entries at the end (work per entry within one workgroup's
-    // flat loops: binary + pass-through nodes and emission lanes) run on
-    // workgroup 0 alone
-    const int64_t flat_max = env_int("GCS_TAIL_FLAT", 4096);
-    const int64_t flat_cap = (int64_t)(gcs::kFlatLdsBytes / 2 / gcs::elem_bytes(p));
-    auto flat_ok = [&](const gcs::LevelArgs& a) {
-        const int64_t w = (int64_t)a.bsl[gcs::kSlices] + a.psl[gcs::kSlices];
-        return w <= flat_cap && w + ((int64_t)a.gsl[gcs::kSlices] << a.team_log2) <= flat_max;
-    };
-    d->tail_multi = d->tail_nent;
-    while (d->tail_multi > 0 && flat_ok(d->largs[d->tail_k0 - 1 + d->tail_multi - 1])) --d->tail_multi;
-    // every level-below reference of a flat level after the first must land in
-    // its LDS buffer (true by construction; checked before anything runs)
-    for (int64_t j = d->tail_multi + 1; j < d->tail_nent; ++j) {
-        const int64_t k = d->tail_k0 + j;  // launch k: level k and the emission of level k-1
-        const gcs::Level& pl = g.lv[k - 1];
-        const int64_t lo = pl.base, hi = pl.base + pl.nb + pl.npt;
-        auto in_prev = [&](int64_t c) { return c < g.alpha() || (c >= lo && c < hi && c - lo < flat_cap); };
-        bool ok = true;
-        if (k <= g.L) {
-            const gcs::Level& l = g.lv[k];
-            for (int64_t t = 0; t < 2 * l.nb && ok; ++t) ok = in_prev(g.child[2 * l.child_off + t]);
-            for (int64_t t = 0; t < l.npt && ok; ++t) ok = in_prev(g.ptsrc[l.pt_off + t]);
-        }
-        for (int64_t gi = pl.grp_off; gi < pl.grp_off + pl.ngrp && ok; ++gi)
-            for (int32_t e = g.eoff[gi]; e < g.eoff[gi + 1] && ok; ++e) ok = in_prev(g.epos[e]);
-        if (!ok) {
+    // the narrowest entries at the end run on workgroup 0 alone, in LDS: as
+    // many as fit its budget, each with at most GCS_TAIL_FLAT work items
+    {
+        int max_lds = 0;
+        (void)hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 1024));
+        gcs::FlatImage fi;
+        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), fi)) {
             delete d;
-            gcs::set_error("internal layout check failed: a narrow level reads outside its LDS buffer");
             return GCS_ESTATE;
+        }
+        d->tail_multi = fi.first;
+        d->flat = fi.args;
+        d->flat_lds = fi.args.n_ent > 0 ? fi.lds_bytes : 0;
+        const int32_t* sec = (const int32_t*)(base + im.flat);
+        d->flat.idx = sec;
+        d->flat.stage_src = sec + (uintptr_t)fi.args.stage_src;
+        d->flat.fold_acc = sec + (uintptr_t)fi.args.fold_acc;
+        d->flat.fold_off = sec + (uintptr_t)fi.args.fold_off;
+        d->flat.fold_list = sec + (uintptr_t)fi.args.fold_list;
+        if (!fi.words.empty()) {
+            e = hipMemcpyAsync(base + im.flat, fi.words.data(), fi.words.size() * 4, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+            if (e != hipSuccess) {
+                delete d;
+                return gcs::hip_fail(e, "hipMemcpyAsync (narrow levels)");
+            }
         }
     }
     d->tail_table = (const gcs::LevelArgs*)(base + im.table) + (d->tail_k0 - 1);
