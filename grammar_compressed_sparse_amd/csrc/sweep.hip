@@ -122,7 +122,7 @@ constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kEmitItems = 4;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
-constexpr size_t kFlatLdsMax = 128 * 1024;  // LDS budget of the tail's single-workgroup phase
+constexpr size_t kFlatLdsMax = 160 * 1024;  // LDS cap of the tail's single-workgroup phase
 constexpr int kFlatEntryWords = 8;  // per narrow launch in that phase's table
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
@@ -272,14 +272,15 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     const int32_t graw = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
     const bool valid = graw < gend;
     const int32_t g = valid ? graw : gend - 1;
-    const int32_t row = a.erow[g];
+    // the accumulator is read beside the roots (its address needs only the
+    // group's row), not after the team has combined them
+    A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
+    const A old = *r;
     const int32_t e1 = a.eoff[g + 1];
     const A s0 = emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, [&](int32_t c) { return arena[c]; });
+    issue_before(old);
     const A s = team_combine<P>(s0, team);
-    if (valid && sub == 0) {
-        A* r = acc + (int64_t)x * a.n_rows + row;
-        *r = P::comb(*r, s);
-    }
+    if (valid && sub == 0) *r = P::comb(old, s);
 }
 
 // One wide level.  By default the grid has one workgroup per virtual block
@@ -332,29 +333,26 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
     return ok != 0;
 }
 
-// The narrowest launches, run by one workgroup of kTailBlock lanes with
+// The narrowest launches, run by one extra workgroup of kTailBlock lanes with
 // workgroup barriers only and everything they touch held in LDS.  The host
 // rewrites each of their value references (a child, a pass-through source, a
 // root) as a slot of one LDS value array: slots [0, n_stage) are staged from
-// the arena once (terminal values and the level the grid phase computed
-// last), and every narrow level owns the slots its nodes are written to.
-// Emission sums go to LDS slots (gsum) and are folded into the row
-// accumulators at the end, each accumulator taking its sums in level order:
-// the same operations in the same order as one read-modify-write per level.
+// the arena (the n_terms terminal values first, then values of the level the
+// grid computed last), and every narrow level owns the slots its nodes are
+// written to.  Emission sums go to LDS slots (gsum); at the end each touched
+// row accumulator takes its sums in level order (fold lists): the same
+// operations in the same order as one read-modify-write per level.
 struct FlatArgs {
-    const int32_t* idx;        // LDS part: entry table, group offsets, u16 refs, u16 roots (idx_words words)
-    const int32_t* stage_src;  // arena offset staged into slot s, s < n_stage
-    const int32_t* fold_acc;   // accumulator index of fold i
-    const int32_t* fold_off;   // fold i takes gsum slots fold_list[fold_off[i] .. fold_off[i+1])
-    const int32_t* fold_list;
-    int32_t idx_words, n_ent, goff_word, refs_word, roots_word;
-    int32_t n_stage, n_fold;
-    int32_t vals_off, gsum_off;  // byte offsets of the value and gsum arrays in LDS
+    const int32_t* idx;  // the LDS image, idx_words 32-bit words (a multiple of four)
+    int32_t idx_words, n_ent, n_stage, n_terms, n_fold;
+    // word offsets in the image: entry table at 0, then these arrays
+    int32_t goff_word, stage_word, facc_word, foff_word, refs_word, roots_word, flist_word;
+    int32_t vals_off, gsum_off, accv_off;  // byte offsets of the value, sum and accumulator arrays in LDS
 };
 
 // for (i = tid; i < n; i += kTailBlock) op(i), four independent iterations at
-// a time: op(i, live) must only load when live is false (i is then clamped
-// to n - 1) and store when it is true
+// a time: op(i0..i3, live1..live3) must only load when live is false (i is
+// then clamped to n - 1) and store when it is true
 template <class Op>
 __device__ __forceinline__ void block_rounds(int32_t n, int32_t tid, Op op)
 {
@@ -363,6 +361,51 @@ __device__ __forceinline__ void block_rounds(int32_t n, int32_t tid, Op op)
                                                               i0 + 2 * kTailBlock < n, i0 + 3 * kTailBlock < n);
 }
 
+// vals[i] = arena[stage[i]] for i in [lo, hi)
+template <class A>
+__device__ __forceinline__ void stage_values(const int32_t* stage, const A* __restrict__ arena, A* vals, int32_t lo,
+                                             int32_t hi, int32_t tid)
+{
+    block_rounds(hi - lo, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
+        const A v0 = arena[stage[lo + i0]], v1 = arena[stage[lo + i1]];
+        const A v2 = arena[stage[lo + i2]], v3 = arena[stage[lo + i3]];
+        issue_before(v0);
+        issue_before(v1);
+        issue_before(v2);
+        issue_before(v3);
+        vals[lo + i0] = v0;
+        if (l1) vals[lo + i1] = v1;
+        if (l2) vals[lo + i2] = v2;
+        if (l3) vals[lo + i3] = v3;
+    });
+}
+
+// Before the grid levels finish: the image into LDS and the terminal values
+// (complete since the leaf launch).
+template <class P>
+__device__ __noinline__ void flat_prefetch(const FlatArgs f, const typename P::A* __restrict__ arena)
+{
+    using A = typename P::A;
+    extern __shared__ __align__(16) unsigned char flat_lds[];
+    const int32_t tid = threadIdx.x;
+    int32_t* iw = (int32_t*)flat_lds;
+    const int4* src = (const int4*)f.idx;
+    int4* dst = (int4*)iw;
+    block_rounds(f.idx_words / 4, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
+        const int4 v0 = src[i0], v1 = src[i1], v2 = src[i2], v3 = src[i3];
+        dst[i0] = v0;
+        if (l1) dst[i1] = v1;
+        if (l2) dst[i2] = v2;
+        if (l3) dst[i3] = v3;
+    });
+    // the stage indices straight from the image in global memory (the LDS
+    // copy is not yet visible to other lanes)
+    stage_values<A>(f.idx + f.stage_word, arena, (A*)(flat_lds + f.vals_off), 0, f.n_terms, tid);
+    __syncthreads();
+}
+
+// After the grid levels: their values, the accumulators to fold, the narrow
+// levels, the folds.
 template <class P>
 __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* __restrict__ arena,
                                         typename P::A* __restrict__ acc)
@@ -370,33 +413,13 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
     using A = typename P::A;
     extern __shared__ __align__(16) unsigned char flat_lds[];
     const int32_t tid = threadIdx.x;
-    int32_t* iw = (int32_t*)flat_lds;
+    const int32_t* iw = (const int32_t*)flat_lds;
     A* vals = (A*)(flat_lds + f.vals_off);
     A* gsum = (A*)(flat_lds + f.gsum_off);
-    // the index image (a multiple of four words) and the staged values
-    {
-        const int4* src = (const int4*)f.idx;
-        int4* dst = (int4*)iw;
-        block_rounds(f.idx_words / 4, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
-            const int4 v0 = src[i0], v1 = src[i1], v2 = src[i2], v3 = src[i3];
-            dst[i0] = v0;
-            if (l1) dst[i1] = v1;
-            if (l2) dst[i2] = v2;
-            if (l3) dst[i3] = v3;
-        });
-        block_rounds(f.n_stage, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
-            const A v0 = arena[f.stage_src[i0]], v1 = arena[f.stage_src[i1]];
-            const A v2 = arena[f.stage_src[i2]], v3 = arena[f.stage_src[i3]];
-            issue_before(v0);
-            issue_before(v1);
-            issue_before(v2);
-            issue_before(v3);
-            vals[i0] = v0;
-            if (l1) vals[i1] = v1;
-            if (l2) vals[i2] = v2;
-            if (l3) vals[i3] = v3;
-        });
-    }
+    A* accv = (A*)(flat_lds + f.accv_off);
+    const int32_t* facc = iw + f.facc_word;
+    stage_values<A>(iw + f.stage_word, arena, vals, f.n_terms, f.n_stage, tid);
+    stage_values<A>(facc, acc, accv, 0, f.n_fold, tid);
     __syncthreads();
     const uint16_t* refs = (const uint16_t*)(iw + f.refs_word);
     const uint16_t* roots = (const uint16_t*)(iw + f.roots_word);
@@ -416,43 +439,36 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
             const int32_t graw = gl >> tl, sub = gl & (team - 1);
             const bool valid = graw < ng;
             const int32_t gg = valid ? graw : ng - 1;
-            const A s0v = emit_rounds<P>(roots, goff[g0 + gg] + sub, goff[g0 + gg + 1], team, valid, val);
-            const A sum = team_combine<P>(s0v, team);
+            const A part = emit_rounds<P>(roots, goff[g0 + gg] + sub, goff[g0 + gg + 1], team, valid, val);
+            const A sum = team_combine<P>(part, team);
             if (valid && sub == 0) gsum[s0 + graw] = sum;
         }
         __syncthreads();
     }
-    block_rounds(f.n_fold, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
-        const int32_t ai[4] = {f.fold_acc[i0], f.fold_acc[i1], f.fold_acc[i2], f.fold_acc[i3]};
-        const int32_t ii[4] = {i0, i1, i2, i3};
-        const bool live[4] = {true, l1, l2, l3};
-        A a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = acc[ai[u]];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) issue_before(a[u]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (!live[u]) continue;
-            for (int32_t k = f.fold_off[ii[u]]; k < f.fold_off[ii[u] + 1]; ++k) a[u] = P::comb(a[u], gsum[f.fold_list[k]]);
-            acc[ai[u]] = a[u];
-        }
-    });
+    const int32_t* foff = iw + f.foff_word;
+    const uint16_t* flist = (const uint16_t*)(iw + f.flist_word);
+    for (int32_t i = tid; i < f.n_fold; i += kTailBlock) {
+        A a = accv[i];
+        for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
+        acc[facc[i]] = a;
+    }
 }
 
 // Levels k0..L (each with the emission of the level below), the emission of
 // level L and the final slice reduction, in one cooperative launch of
-// workgroups with kTailBlock lanes.  Entries [0, n_multi) run on the whole
-// grid: the four 256-lane quarters of a workgroup take virtual blocks
-// blockIdx.x + (quarter + 4j) * gridDim.x, all of the same slice (gridDim.x
-// is a multiple of kSlices), so a workgroup stays on its slice's XCD; grid
-// barriers separate the entries.  The remaining f.n_ent entries are the
-// narrowest levels: workgroup 0 runs them alone in LDS (flat_phase) while the
-// others wait at the next grid barrier.  Then every workgroup reduces
+// workgroups with kTailBlock lanes.  Entries [0, n_multi) run on the first
+// n_grid workgroups (a multiple of kSlices): the four 256-lane quarters of a
+// workgroup take virtual blocks blockIdx.x + (quarter + 4j) * n_grid, all of
+// the same slice, so a workgroup stays on its slice's XCD; grid barriers
+// separate the entries.  The f.n_ent narrowest levels run on one more
+// workgroup (blockIdx.x == n_grid), in LDS, which loads its image while the
+// others work and only joins their barriers; the others wait for it at the
+// next grid barrier.  Then every workgroup reduces
 // y[r] = acc[0][r] (+) ... (+) acc[7][r].
 template <class P>
 __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __restrict__ table, int32_t n_multi,
-                                                          FlatArgs f, typename P::A* __restrict__ arena,
+                                                          int32_t n_grid, FlatArgs f,
+                                                          typename P::A* __restrict__ arena,
                                                           typename P::A* __restrict__ acc,
                                                           typename P::Y* __restrict__ y, int32_t n_rows,
                                                           int32_t accumulate, unsigned* __restrict__ bar,
@@ -460,17 +476,21 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
 {
     constexpr int Q = kTailBlock / kBlock;
     const int32_t q = threadIdx.x / kBlock, ltid = threadIdx.x % kBlock;
+    const bool flat_wg = f.n_ent > 0 && (int32_t)blockIdx.x == n_grid;
+    if (flat_wg) flat_prefetch<P>(f, arena);
     unsigned round = 0;
     for (int32_t li = 0; li < n_multi; ++li) {
-        const LevelArgs& a = table[li];
-        const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
-        for (int32_t vb = blockIdx.x + q * gridDim.x; vb < nvb; vb += Q * gridDim.x)
-            level_block<P>(a, vb, ltid, arena, acc);
+        if (!flat_wg) {
+            const LevelArgs& a = table[li];
+            const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
+            for (int32_t vb = blockIdx.x + q * n_grid; vb < nvb; vb += Q * n_grid)
+                level_block<P>(a, vb, ltid, arena, acc);
+        }
         if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (f.n_ent > 0) {
-        if (blockIdx.x == 0) flat_phase<P>(f, arena, acc);
+        if (flat_wg) flat_phase<P>(f, arena, acc);
         if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -586,19 +606,17 @@ struct Image {
 
 inline size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
 
-// Upper bound on the narrow launches' image (32-bit words): the LDS part is
-// at most kFlatLdsMax bytes and no larger than the grammar's own index
-// arrays with a table entry and one group offset per launch; staged slots
-// and emission sums are 16-bit indices (below 2^16) and at most all of the
-// arena and all groups; the fold lists hold one index per emission sum.
+// Upper bound on the narrow launches' image (32-bit words, all of it loaded
+// into LDS): at most kFlatLdsMax bytes, and no more than a table entry and a
+// group offset per launch, every staged slot (at most the terminals and the
+// arena), three fold words per emission group and the grammar's own indices
+// as 16-bit slots.
 size_t flat_section_words(const Grammar& g)
 {
     const size_t G = g.erow.size(), C = g.epos.size();
-    const size_t lds = std::min(kFlatLdsMax / 4, (size_t)kFlatEntryWords * (g.L + 2) + G + g.L + 2 +
-                                                     (g.child.size() + g.ptsrc.size() + 1) / 2 + (C + 1) / 2 + 4);
-    const size_t stage = std::min<size_t>(65536, (size_t)g.arena);
-    const size_t sums = std::min<size_t>(65536, G);
-    return lds + stage + 3 * sums + 1;
+    const size_t bound = (size_t)kFlatEntryWords * (g.L + 2) + G + g.L + 2 + (size_t)g.arena + 3 * G + 1 +
+                         (g.child.size() + g.ptsrc.size() + 1) / 2 + (C + 1) / 2 + 8;
+    return std::min(kFlatLdsMax / 4, bound);
 }
 
 Image image_layout(const Grammar& g, gcs_policy p)
@@ -639,8 +657,8 @@ bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_PLUS_I64; }
 // k = tail_k0 + j (level k when k <= L, and the emission of level k-1).
 struct FlatImage {
     int64_t first = 0;              // tail entry of the first narrow launch
-    std::vector<int32_t> words;     // the section: LDS part, stage, fold_acc, fold_off, fold_list
-    FlatArgs args{};                // pointer members hold word offsets into the section until upload
+    std::vector<int32_t> words;     // the image (loaded whole into LDS)
+    FlatArgs args{};                // idx is set at upload
     size_t lds_bytes = 0;
 };
 
@@ -682,9 +700,12 @@ bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budge
             nrefs += k <= g.L ? 2 * g.lv[k].nb + g.lv[k].npt : 0;
             nroots += g.eoff[pl.grp_off + pl.ngrp] - g.eoff[pl.grp_off];
             ngoff += pl.ngrp + 1;
-            const int64_t slots = (int64_t)terms.size() + (int64_t)prev.size() + produced;
-            const int64_t words = (kFlatEntryWords * (nent - j) + ngoff + (nrefs + 1) / 2 + (nroots + 1) / 2 + 3) / 4 * 4;
-            const size_t bytes = al16(4 * (size_t)words) + al16((size_t)slots * elem) + al16((size_t)sums * elem);
+            const int64_t staged = (int64_t)terms.size() + (int64_t)prev.size(), slots = staged + produced;
+            // folds: at most one per emission sum (accumulator index, offset,
+            // 16-bit list entry and the accumulator value itself)
+            const int64_t words = (kFlatEntryWords * (nent - j) + ngoff + staged + 2 * sums + 1 + (nrefs + 1) / 2 +
+                                   (nroots + 1) / 2 + (sums + 1) / 2 + 3) / 4 * 4;
+            const size_t bytes = al16(4 * (size_t)words) + al16((size_t)slots * elem) + 2 * al16((size_t)sums * elem);
             if (slots > 65535 || sums > 65535 || bytes > budget) break;
             fi.first = j;
         }
@@ -765,44 +786,49 @@ bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budge
                      [](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
                          return a.first < b.first;
                      });
-    FlatArgs& fa = fi.args;
-    std::vector<int32_t>& w = fi.words;
-    w = ent;
-    fa.goff_word = (int32_t)w.size();
-    w.insert(w.end(), goff.begin(), goff.end());
-    fa.refs_word = (int32_t)w.size();
-    w.resize(w.size() + (refs.size() + 1) / 2, 0);
-    std::memcpy(w.data() + fa.refs_word, refs.data(), refs.size() * 2);
-    fa.roots_word = (int32_t)w.size();
-    w.resize(w.size() + (roots.size() + 1) / 2, 0);
-    std::memcpy(w.data() + fa.roots_word, roots.data(), roots.size() * 2);
-    w.resize((w.size() + 3) / 4 * 4, 0);
-    fa.idx_words = (int32_t)w.size();
-    fa.n_ent = (int32_t)n_ent;
-    fa.n_stage = (int32_t)n_stage;
-    fa.vals_off = (int32_t)al16(4 * w.size());
-    fa.gsum_off = (int32_t)(fa.vals_off + al16((size_t)n_slots * elem));
-    fi.lds_bytes = fa.gsum_off + al16((size_t)sums * elem);
-    // global-only part; pointer members hold word offsets until upload
-    fa.stage_src = (const int32_t*)(uintptr_t)w.size();
-    w.insert(w.end(), terms.begin(), terms.end());
-    w.insert(w.end(), prevs.begin(), prevs.end());
-    std::vector<int32_t> facc, foff{0}, flist;
+    std::vector<int32_t> facc, foff{0};
+    std::vector<uint16_t> flist;
     for (size_t i = 0; i < folds.size(); ++i) {
         if (i == 0 || folds[i].first != folds[i - 1].first) {
             if (i) foff.push_back((int32_t)flist.size());
             facc.push_back(folds[i].first);
         }
-        flist.push_back(folds[i].second);
+        flist.push_back((uint16_t)folds[i].second);
     }
     if (!folds.empty()) foff.push_back((int32_t)flist.size());
+    FlatArgs& fa = fi.args;
+    std::vector<int32_t>& w = fi.words;
+    auto put = [&](const std::vector<int32_t>& v) {
+        const int32_t at = (int32_t)w.size();
+        w.insert(w.end(), v.begin(), v.end());
+        return at;
+    };
+    auto put16 = [&](const std::vector<uint16_t>& v) {
+        const int32_t at = (int32_t)w.size();
+        w.resize(w.size() + (v.size() + 1) / 2, 0);
+        if (!v.empty()) std::memcpy(w.data() + at, v.data(), v.size() * 2);
+        return at;
+    };
+    std::vector<int32_t> stage(terms);
+    stage.insert(stage.end(), prevs.begin(), prevs.end());
+    w = ent;
+    fa.goff_word = put(goff);
+    fa.stage_word = put(stage);
+    fa.facc_word = put(facc);
+    fa.foff_word = put(foff);
+    fa.refs_word = put16(refs);
+    fa.roots_word = put16(roots);
+    fa.flist_word = put16(flist);
+    w.resize((w.size() + 3) / 4 * 4, 0);
+    fa.idx_words = (int32_t)w.size();
+    fa.n_ent = (int32_t)n_ent;
+    fa.n_stage = (int32_t)n_stage;
+    fa.n_terms = (int32_t)terms.size();
     fa.n_fold = (int32_t)facc.size();
-    fa.fold_acc = (const int32_t*)(uintptr_t)w.size();
-    w.insert(w.end(), facc.begin(), facc.end());
-    fa.fold_off = (const int32_t*)(uintptr_t)w.size();
-    w.insert(w.end(), foff.begin(), foff.end());
-    fa.fold_list = (const int32_t*)(uintptr_t)w.size();
-    w.insert(w.end(), flist.begin(), flist.end());
+    fa.vals_off = (int32_t)al16(4 * w.size());
+    fa.gsum_off = (int32_t)(fa.vals_off + al16((size_t)n_slots * elem));
+    fa.accv_off = (int32_t)(fa.gsum_off + al16((size_t)sums * elem));
+    fi.lds_bytes = fa.accv_off + al16((size_t)fa.n_fold * elem);
     if (fi.lds_bytes > budget || w.size() > flat_section_words(g)) {
         set_error("internal layout check failed: the narrow levels' image exceeds its bound");
         return false;
@@ -992,8 +1018,10 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             if (ea != hipSuccess) return hip_fail(ea, "hipFuncSetAttribute (tail LDS)");
             d->flat_attr = true;
         }
-        void* args[] = {&table, &n_multi, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
-        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(d->tail_wgs),
+        int32_t n_grid = d->tail_wgs;
+        void* args[] = {&table, &n_multi, &n_grid, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
+        const unsigned wgs = (unsigned)d->tail_wgs + (flat.n_ent > 0 ? 1u : 0u);
+        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(wgs),
                                                   dim3(kTailBlock), args, d->flat_lds, s);
         if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
         mark();
@@ -1151,7 +1179,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     };
     // 64 workgroups (8 per XCD), one virtual block per 256-lane quarter and level
     // measured best on MI355X for the tail (fewer arrivals per barrier round)
-    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu, gcs::kSlices)) /
+    // (at most one fewer than the compute units: the narrow levels' workgroup
+    // joins the cooperative grid, and each of these workgroups needs a CU)
+    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu - 1, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
     // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
@@ -1168,7 +1198,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     {
         int max_lds = 0;
         (void)hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-        const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 1024));
+        const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 2048));
         gcs::FlatImage fi;
         if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), fi)) {
             delete d;
@@ -1177,12 +1207,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         d->tail_multi = fi.first;
         d->flat = fi.args;
         d->flat_lds = fi.args.n_ent > 0 ? fi.lds_bytes : 0;
-        const int32_t* sec = (const int32_t*)(base + im.flat);
-        d->flat.idx = sec;
-        d->flat.stage_src = sec + (uintptr_t)fi.args.stage_src;
-        d->flat.fold_acc = sec + (uintptr_t)fi.args.fold_acc;
-        d->flat.fold_off = sec + (uintptr_t)fi.args.fold_off;
-        d->flat.fold_list = sec + (uintptr_t)fi.args.fold_list;
+        d->flat.idx = (const int32_t*)(base + im.flat);
         if (!fi.words.empty()) {
             e = hipMemcpyAsync(base + im.flat, fi.words.data(), fi.words.size() * 4, hipMemcpyHostToDevice, s);
             if (e == hipSuccess) e = hipStreamSynchronize(s);
