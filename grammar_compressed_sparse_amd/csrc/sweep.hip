@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <utility>
@@ -124,6 +125,7 @@ constexpr int kEmitItems = 4;  // roots per emission lane loaded before the firs
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
 constexpr size_t kFlatLdsMax = 160 * 1024;  // LDS cap of the tail's single-workgroup phase
 constexpr int kFlatEntryWords = 8;  // per narrow launch in that phase's table
+constexpr int kStageItems = 8;  // loads per lane in flight while that phase stages its values
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
 
 template <class P>
@@ -418,8 +420,30 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
     A* gsum = (A*)(flat_lds + f.gsum_off);
     A* accv = (A*)(flat_lds + f.accv_off);
     const int32_t* facc = iw + f.facc_word;
-    stage_values<A>(iw + f.stage_word, arena, vals, f.n_terms, f.n_stage, tid);
-    stage_values<A>(facc, acc, accv, 0, f.n_fold, tid);
+    // one gather round for the grid's last level and the accumulators to
+    // fold: item i < n_prev stages slot n_terms + i, the rest accumulators
+    {
+        const int32_t* stage = iw + f.stage_word;
+        const int32_t n_prev = f.n_stage - f.n_terms, n = n_prev + f.n_fold;
+        for (int32_t i0 = tid; i0 < n; i0 += kStageItems * kTailBlock) {
+            A v[kStageItems];
+#pragma unroll
+            for (int u = 0; u < kStageItems; ++u) {
+                const int32_t i = min(i0 + u * kTailBlock, n - 1);
+                v[u] = i < n_prev ? arena[stage[f.n_terms + i]] : acc[facc[i - n_prev]];
+            }
+#pragma unroll
+            for (int u = 0; u < kStageItems; ++u) issue_before(v[u]);
+#pragma unroll
+            for (int u = 0; u < kStageItems; ++u) {
+                const int32_t i = i0 + u * kTailBlock;
+                if (i < n) {
+                    if (i < n_prev) vals[f.n_terms + i] = v[u];
+                    else accv[i - n_prev] = v[u];
+                }
+            }
+        }
+    }
     __syncthreads();
     const uint16_t* refs = (const uint16_t*)(iw + f.refs_word);
     const uint16_t* roots = (const uint16_t*)(iw + f.roots_word);
@@ -1177,11 +1201,12 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const char* v = std::getenv(name);
         return v ? std::atoi(v) : dflt;
     };
-    // 64 workgroups (8 per XCD), one virtual block per 256-lane quarter and level
-    // measured best on MI355X for the tail (fewer arrivals per barrier round)
+    // 16 workgroups (2 per XCD), one virtual block per 256-lane quarter and
+    // level: measured best on MI355X for the tail (fewer arrivals per barrier
+    // round; the wider levels this leaves out run faster as launches)
     // (at most one fewer than the compute units: the narrow levels' workgroup
     // joins the cooperative grid, and each of these workgroups needs a CU)
-    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 64), std::max(dev_cu - 1, gcs::kSlices)) /
+    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 16), std::max(dev_cu - 1, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
     // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
@@ -1208,6 +1233,14 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         d->flat = fi.args;
         d->flat_lds = fi.args.n_ent > 0 ? fi.lds_bytes : 0;
         d->flat.idx = (const int32_t*)(base + im.flat);
+        if (std::getenv("GCS_UPLOAD_TRACE"))
+            std::fprintf(stderr,
+                         "[gcs upload] levels %lld: wide launches 1..%lld, tail grid %d workgroups over %lld "
+                         "launches, narrow launches %d in LDS (%zu bytes: %d image words, %d staged of which %d "
+                         "terminals, %d folds)\n",
+                         (long long)g.L, (long long)d->tail_k0 - 1, d->tail_wgs, (long long)d->tail_multi,
+                         fi.args.n_ent, d->flat_lds, fi.args.idx_words, fi.args.n_stage, fi.args.n_terms,
+                         fi.args.n_fold);
         if (!fi.words.empty()) {
             e = hipMemcpyAsync(base + im.flat, fi.words.data(), fi.words.size() * 4, hipMemcpyHostToDevice, s);
             if (e == hipSuccess) e = hipStreamSynchronize(s);
