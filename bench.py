@@ -300,16 +300,25 @@ def main():
     for i in range(args.warmup):
         dev.sweep_right(xs[i % len(xs)], y)
     torch.cuda.synchronize()
-    dev.profile_begin(args.steps)
+    # timed region: K sweeps, each with one pair of HIP events (on the sweep's
+    # stream) around its wide level launches, the dominant kernel
+    dev.profile_begin(args.steps, gcs.PROFILE_LEVEL_SPAN)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         dev.sweep_right_profiled(xs[i % len(xs)], y)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    launch_ms = dev.profile_end()  # (steps, launches)
+    span_ms = float(dev.profile_end()[:, 0].mean())
     dev.check()
     ms_per_step = elapsed * 1e3 / args.steps
+    # breakdown (after the timed region): events around every launch, which
+    # add a gap between launches, so these sum to more than a clean sweep
+    dev.profile_begin(args.steps, gcs.PROFILE_LAUNCHES)
+    for i in range(args.steps):
+        dev.sweep_right_profiled(xs[i % len(xs)], y)
+    launch_ms = dev.profile_end()  # (steps, launches)
+    dev.check()
     L = st["depth"]
     # launch 0 = terminal array, 1..k0-1 = wide levels (each with the emission
     # of the level below), last = the persistent tail (levels k0..L, the last
@@ -319,7 +328,7 @@ def main():
     tail_ms = float(launch_ms[:, -1].mean())
     lb_all = level_bytes(lay, elem, elem)
     lb = lb_all[:nwide]
-    achieved = lb.sum() / (lvl_ms.sum() * 1e-3) / 1e9
+    achieved = lb.sum() / (span_ms * 1e-3) / 1e9
     per_level = [{"k": k + 1, "width": int(lay["level_meta"][k + 1][0] + lay["level_meta"][k + 1][1]),
                   "bytes": int(lb[k]), "us": float(lvl_ms[k] * 1e3),
                   "GBs": float(lb[k] / (lvl_ms[k] * 1e-3) / 1e9)} for k in range(nwide)]
@@ -387,7 +396,8 @@ def main():
             "csr_rocsparse": csr,
             "per_level_widest": per_level[widest] if per_level else None,
             "wide_levels": nwide,
-            "level_us_total": float(lvl_ms.sum() * 1e3),
+            "level_span_us": span_ms * 1e3,
+            "level_us_total_launch_events": float(lvl_ms.sum() * 1e3),
             "leaf_us": float(launch_ms[:, 0].mean() * 1e3),
             "tail_us": tail_ms * 1e3,
             "tail_levels": L - nwide,
@@ -395,7 +405,10 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "level_kernel (the wide levels of a sweep, one launch each)",
+                     "kernel": "level_kernel (the wide levels of a sweep, one launch each; timed from before the "
+                               "first to after the last, gaps between launches included)",
+                     "launches": int(nwide), "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
+                     "bytes_per_launch_avg": float(lb.sum() / max(nwide, 1)),
                      "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,
     }

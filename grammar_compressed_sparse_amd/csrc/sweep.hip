@@ -602,6 +602,7 @@ struct gcs_device {
     std::vector<hipEvent_t> events;
     int64_t prof_max = 0, prof_used = 0;
     bool profiling = false;
+    int32_t prof_mode = GCS_PROFILE_LAUNCHES;
 };
 
 namespace gcs {
@@ -1001,16 +1002,17 @@ int64_t count_launches(const gcs_device* d)
 
 template <class P>
 gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hipEvent_t* ev = nullptr,
-                     int32_t accumulate = 0)
+                     int32_t accumulate = 0, bool span = false)
 {
     using A = typename P::A;
     auto* arena = (A*)d->arena;
     auto* acc = (A*)d->acc;
     auto* y = (typename P::Y*)yv;
-    // profiling: events[2i] before launch i, events[2i+1] right after it
+    // profiling: events[2i] before launch i, events[2i+1] right after it; or
+    // (span) events[0] before the first wide level launch, events[1] after the last
     int64_t li = 0;
     auto mark = [&]() {
-        if (ev) (void)hipEventRecord(ev[li++], s);
+        if (ev && !span) (void)hipEventRecord(ev[li++], s);
     };
     const int32_t n_acc = (int32_t)(kSlices * d->n_rows);
     if (has_leaf(d)) {
@@ -1020,6 +1022,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             n_acc, d->barrier);
         mark();
     }
+    if (ev && span) (void)hipEventRecord(ev[0], s);
     for (int64_t k = 1; k < d->tail_k0; ++k) {
         const LevelArgs& a = d->largs[k - 1];
         const int64_t grid = std::min<int64_t>(vblocks(a), d->grid_max);
@@ -1029,6 +1032,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             mark();
         }
     }
+    if (ev && span) (void)hipEventRecord(ev[1], s);
     if (has_tail(d)) {
         mark();
         const LevelArgs* table = d->tail_table;
@@ -1275,7 +1279,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
 }
 
 static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, void* stream, hipEvent_t* ev,
-                                 int32_t accumulate = 0)
+                                 int32_t accumulate = 0, bool span = false)
 {
     if (!d || (d->n_cols > 0 && !x_dev) || (d->n_rows > 0 && !y_dev)) {
         gcs::set_error("invalid argument");
@@ -1288,11 +1292,11 @@ static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, 
     }
     hipStream_t s = (hipStream_t)stream;
     switch (d->policy) {
-    case GCS_PLUS_F64: return gcs::run_sweep<gcs::PolPlusF64>(d, x_dev, y_dev, s, ev, accumulate);
-    case GCS_PLUS_F32: return gcs::run_sweep<gcs::PolPlusF32>(d, x_dev, y_dev, s, ev, accumulate);
-    case GCS_PLUS_F32_ACC_F64: return gcs::run_sweep<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, s, ev, accumulate);
-    case GCS_BOOL_OR: return gcs::run_sweep<gcs::PolBoolOr>(d, x_dev, y_dev, s, ev, accumulate);
-    case GCS_PLUS_I64: return gcs::run_sweep<gcs::PolPlusI64>(d, x_dev, y_dev, s, ev, accumulate);
+    case GCS_PLUS_F64: return gcs::run_sweep<gcs::PolPlusF64>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_PLUS_F32: return gcs::run_sweep<gcs::PolPlusF32>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_PLUS_F32_ACC_F64: return gcs::run_sweep<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_BOOL_OR: return gcs::run_sweep<gcs::PolBoolOr>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_PLUS_I64: return gcs::run_sweep<gcs::PolPlusI64>(d, x_dev, y_dev, s, ev, accumulate, span);
     }
     gcs::set_error("corrupt device handle");
     return GCS_ESTATE;
@@ -1318,15 +1322,22 @@ static void release_events(gcs_device* d)
     d->prof_max = d->prof_used = 0;
 }
 
-extern "C" gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps)
+// events per profiled sweep and timings per sweep
+static int64_t prof_pairs(const gcs_device* d)
 {
-    if (!d || max_sweeps <= 0) {
+    return d->prof_mode == GCS_PROFILE_LEVEL_SPAN ? 1 : gcs::count_launches(d);
+}
+
+extern "C" gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps, int32_t mode)
+{
+    if (!d || max_sweeps <= 0 || (mode != GCS_PROFILE_LAUNCHES && mode != GCS_PROFILE_LEVEL_SPAN)) {
         gcs::set_error("invalid argument");
         return GCS_EINVAL;
     }
     gcs::DeviceGuard guard(d->device);
     release_events(d);
-    const int64_t per = 2 * gcs::count_launches(d);
+    d->prof_mode = mode;
+    const int64_t per = 2 * prof_pairs(d);
     d->events.resize((size_t)(per * max_sweeps));
     for (auto& e : d->events) {
         hipError_t err = hipEventCreate(&e);
@@ -1353,8 +1364,9 @@ extern "C" gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev,
         gcs::set_error("more sweeps than gcs_profile_begin reserved");
         return GCS_ERANGE;
     }
-    const int64_t per = 2 * gcs::count_launches(d);
-    gcs_status st = sweep_dispatch(d, x_dev, y_dev, stream, d->events.data() + per * d->prof_used);
+    const int64_t per = 2 * prof_pairs(d);
+    gcs_status st = sweep_dispatch(d, x_dev, y_dev, stream, d->events.data() + per * d->prof_used, 0,
+                                   d->prof_mode == GCS_PROFILE_LEVEL_SPAN);
     if (st == GCS_OK) d->prof_used++;
     return st;
 }
@@ -1367,7 +1379,7 @@ extern "C" gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t c
         return GCS_ESTATE;
     }
     gcs::DeviceGuard guard(d->device);
-    const int64_t nl = gcs::count_launches(d), per = 2 * nl;
+    const int64_t nl = prof_pairs(d), per = 2 * nl;
     *sweeps = d->prof_used;
     *launches = nl;
     if (cap < d->prof_used * nl || (cap > 0 && !launch_ms)) {

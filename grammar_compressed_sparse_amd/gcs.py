@@ -23,6 +23,7 @@ _lib = ctypes.CDLL(_SO)
 PLUS_F64, PLUS_F32, PLUS_F32_ACC_F64, BOOL_OR, PLUS_I64 = range(5)
 POLICY_NAMES = {"f64": PLUS_F64, "f32": PLUS_F32, "f32_acc_f64": PLUS_F32_ACC_F64, "bool": BOOL_OR, "i64": PLUS_I64}
 VAL_ONES, VAL_I8, VAL_F64 = 0, 1, 2
+PROFILE_LAUNCHES, PROFILE_LEVEL_SPAN = 0, 1  # gcs_profile_mode
 _STATUS = {0: "GCS_OK", -1: "GCS_EINVAL", -2: "GCS_ENOMEM", -3: "GCS_EHIP", -4: "GCS_ERANGE", -5: "GCS_ESTATE"}
 
 
@@ -77,7 +78,7 @@ _lib.gcs_sweep_right_acc.argtypes = [_P, _P, _P, _P]
 _lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
-_lib.gcs_profile_begin.argtypes = [_P, _I64]
+_lib.gcs_profile_begin.argtypes = [_P, _I64, ctypes.c_int32]
 _lib.gcs_sweep_right_profiled.argtypes = [_P, _P, _P, _P]
 _lib.gcs_profile_end.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
 _lib.gcs_device_check.argtypes = [_P, _P]
@@ -273,8 +274,10 @@ class Device:
     def sweep_launches(self) -> int:
         return int(_lib.gcs_sweep_launches(self._h))
 
-    def profile_begin(self, max_sweeps: int):
-        _check(_lib.gcs_profile_begin(self._h, max_sweeps))
+    def profile_begin(self, max_sweeps: int, mode: int = 0):
+        """mode PROFILE_LAUNCHES: events around every launch; PROFILE_LEVEL_SPAN:
+        one pair around the wide level launches of each sweep."""
+        _check(_lib.gcs_profile_begin(self._h, max_sweeps, mode))
 
     def sweep_right_profiled(self, x, y, stream=None):
         _check_xy(self, x, y)
@@ -283,7 +286,7 @@ class Device:
         return y
 
     def profile_end(self) -> np.ndarray:
-        """Per-launch durations (ms), shape (sweeps, launches)."""
+        """Durations (ms), shape (sweeps, launches), or (sweeps, 1) for the span mode."""
         cap = 1 << 22
         buf = np.zeros(cap, np.float32)
         ns, nl = _I64(0), _I64(0)

@@ -245,16 +245,24 @@ gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t n_sources,
  * the slice accumulators into y. */
 int64_t gcs_sweep_launches(const gcs_device* d);
 
+/* What a profiled sweep times. */
+typedef enum {
+    GCS_PROFILE_LAUNCHES = 0,   /* every launch: an event right before and right after each */
+    GCS_PROFILE_LEVEL_SPAN = 1  /* the wide level launches together: one event right before the
+                                   first and one right after the last (two events per sweep) */
+} gcs_profile_mode;
+
 /* Timing of sweeps with HIP events on the sweep's own stream, for
  * benchmarking.  gcs_profile_begin reserves events for up to max_sweeps
- * sweeps; each gcs_sweep_right_profiled is gcs_sweep_right with an event
- * recorded right before and right after every launch; gcs_profile_end
- * synchronises the events and writes launch_ms[s * launches + i] = time
- * between the two events around launch i of sweep s, then releases the
- * events.
- * GCS_ERANGE if more than max_sweeps sweeps were profiled or cap is too
- * small; GCS_ESTATE without gcs_profile_begin. */
-gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps);
+ * sweeps in the given mode; each gcs_sweep_right_profiled is gcs_sweep_right
+ * with those events recorded; gcs_profile_end synchronises the events and
+ * writes launch_ms[s * launches + i] = time between the i-th pair of events of
+ * sweep s (launches = gcs_sweep_launches for GCS_PROFILE_LAUNCHES, 1 for
+ * GCS_PROFILE_LEVEL_SPAN: 0 ms when the sweep has no wide level launch), then
+ * releases the events.
+ * GCS_EINVAL for an unknown mode; GCS_ERANGE if more than max_sweeps sweeps
+ * were profiled or cap is too small; GCS_ESTATE without gcs_profile_begin. */
+gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps, int32_t mode);
 gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t* sweeps, int64_t* launches);
 
