@@ -526,6 +526,125 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
     }
 }
 
+// ---------------------------------------------------------------- batched right product
+
+// Y = M X for B vectors at once (X: m x B and Y: n x B, row-major).  Every
+// value becomes a row of B values (terminal array, arena and accumulators
+// scaled by B), a node's B values adjacent, so the lanes of a node gather
+// consecutive addresses: at B = 32 in fp32 one cache line serves a whole
+// node.  Lanes come in groups of VB = 2^vb_log2 >= B (lane b of a group
+// takes vector b; lanes b >= B compute vector B-1 again and store nothing);
+// a 256-lane block takes 256 / VB nodes, or emission groups, at a time.
+// Same grammar, slices and emission groups as the single-vector sweep; every
+// level is its own launch.
+constexpr int kMaxBatch = 64;
+
+struct BatchArgs {
+    LevelArgs a;                     // the level's launch arguments (pointers, counts, slices)
+    int32_t B, vb_log2;              // vectors; lanes per node = 1 << vb_log2
+    int32_t pb_bin, pb_pt, pb_emit;  // workgroups per slice in each part at this width
+};
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void leaf_batch_kernel(const int32_t* __restrict__ tcol,
+                                                            const int32_t* __restrict__ tval,
+                                                            const typename P::W* __restrict__ V,
+                                                            const typename P::X* __restrict__ X,
+                                                            typename P::A* __restrict__ T, int64_t alpha, int32_t B,
+                                                            typename P::A* __restrict__ acc, int64_t n_acc)
+{
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < alpha * B; i += stride) {
+        const int64_t p = i / B, b = i - p * B;
+        T[i] = P::leaf(V[tval[p]], X[(int64_t)tcol[p] * B + b]);
+    }
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n_acc; i += stride) acc[i] = P::ident();
+}
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typename P::A* __restrict__ arena,
+                                                             typename P::A* __restrict__ acc)
+{
+    using A = typename P::A;
+    const LevelArgs& a = ba.a;
+    const int64_t B = ba.B;
+    const int32_t tid = threadIdx.x, per = kBlock >> ba.vb_log2, slot = tid >> ba.vb_log2;
+    const int32_t lane_b = tid & ((1 << ba.vb_log2) - 1);
+    const bool live = lane_b < ba.B;
+    const int64_t vb = min(lane_b, ba.B - 1);  // the vector this lane gathers
+    int32_t b = blockIdx.x;
+    const int32_t part_bin = ba.pb_bin * kSlices, part_pt = ba.pb_pt * kSlices;
+    if (b < part_bin) {
+        const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
+        const int32_t first = a.bsl[x] + i * (per * kBinItems);
+        if (first >= end) return;
+        const int32_t t0 = first + slot;
+        int2 c[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
+        A v[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(arena[c[u].x * B + vb], arena[c[u].y * B + vb]);
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * per;
+            if (t < end && live) arena[(int64_t)(a.cur + t) * B + vb] = v[u];
+        }
+        return;
+    }
+    b -= part_bin;
+    if (b < part_pt) {
+        const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
+        const int32_t first = a.psl[x] + i * (per * kBinItems);
+        if (first >= end) return;
+        const int32_t t0 = first + slot;
+        int32_t src[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
+        A v[kBinItems];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u] * B + vb];
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
+#pragma unroll
+        for (int u = 0; u < kBinItems; ++u) {
+            const int32_t t = t0 + u * per;
+            if (t < end && live) arena[(int64_t)(a.cur + a.nb + t) * B + vb] = v[u];
+        }
+        return;
+    }
+    b -= part_pt;
+    // emission: the lanes of a group each combine the group's roots in C
+    // order for their vector, then update the slice accumulator of the row
+    const int32_t x = b % kSlices, i = b / kSlices, gend = a.gsl[x + 1];
+    const int32_t gfirst = a.gsl[x] + i * per;
+    if (gfirst >= gend) return;
+    const int32_t graw = gfirst + slot;
+    const bool valid = graw < gend;
+    const int32_t g = valid ? graw : gend - 1;
+    A* r = acc + ((int64_t)x * a.n_rows + a.erow[g]) * B + vb;
+    const A old = *r;
+    const int32_t e1 = a.eoff[g + 1];
+    const A s = emit_rounds<P>(a.epos, a.eoff[g], e1, 1, valid, [&](int32_t c) { return arena[c * B + vb]; });
+    issue_before(old);
+    if (valid && live) *r = P::comb(old, s);
+}
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void reduce_batch_kernel(const typename P::A* __restrict__ acc,
+                                                              typename P::Y* __restrict__ Y, int64_t n, int32_t accumulate)
+{
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        typename P::A s = acc[i];
+#pragma unroll
+        for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n + i]);
+        Y[i] = P::emit(accumulate ? Y[i] : P::yzero(), s);
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void bfs_clear_kernel(uint8_t* __restrict__ f, uint8_t* __restrict__ vis,
                                                            int64_t n, unsigned long long* __restrict__ cnt)
 {
@@ -577,6 +696,7 @@ struct gcs_device {
     gcs_policy policy;
     int device;
     int64_t n_rows, n_cols, alpha, L;
+    int64_t arena_len = 0;  // values in the arena (terminals and both level buffers)
     std::vector<gcs::Level> lv;
     std::vector<int32_t> team_log2;  // per level: lanes per emission group
     const int2* child;
@@ -677,6 +797,13 @@ size_t acc_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)kSlices 
 size_t workspace_bytes(const Grammar& g, gcs_policy p) { return arena_bytes(g, p) + acc_bytes(g, p) + 256; }
 
 bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_PLUS_I64; }
+
+// batch workspace: [arena x B | kSlices x n_rows x B accumulators]
+size_t batch_arena_bytes(int64_t arena, gcs_policy p, int64_t B) { return al256((size_t)(arena * B) * elem_bytes(p)); }
+size_t batch_workspace_bytes(int64_t arena, int64_t n_rows, gcs_policy p, int64_t B)
+{
+    return batch_arena_bytes(arena, p, B) + al256((size_t)(kSlices * n_rows * B) * elem_bytes(p));
+}
 
 // The narrow launches' image, built at upload: tail entry j is launch
 // k = tail_k0 + j (level k when k <= L, and the emission of level k-1).
@@ -1059,6 +1186,51 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     return GCS_OK;
 }
 
+// Y = M X for B vectors: leaf, one launch per level k = 1..L+1 (level k and
+// the emission of level k-1), slice reduction into Y.
+template <class P>
+gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, void* ws, int32_t accumulate,
+                           hipStream_t s)
+{
+    using A = typename P::A;
+    auto* arena = (A*)ws;
+    auto* acc = (A*)((unsigned char*)ws + batch_arena_bytes(d->arena_len, d->policy, B));
+    int vb_log2 = 0;
+    while ((1 << vb_log2) < B) ++vb_log2;
+    const int32_t per = kBlock >> vb_log2;
+    const int64_t n_acc = (int64_t)kSlices * d->n_rows * B;
+    const int64_t leaf_items = std::max<int64_t>(d->alpha * B, n_acc);
+    const int64_t grid_leaf = std::min<int64_t>(std::max<int64_t>(1, (leaf_items + kBlock - 1) / kBlock), 1 << 16);
+    leaf_batch_kernel<P><<<(int32_t)grid_leaf, kBlock, 0, s>>>(d->tcol, d->tval, (const typename P::W*)d->V,
+                                                                (const typename P::X*)xv, arena, d->alpha, B, acc,
+                                                                n_acc);
+    for (int64_t k = 1; k <= d->L + 1; ++k) {
+        BatchArgs ba{};
+        ba.a = d->largs[k - 1];
+        ba.B = B;
+        ba.vb_log2 = vb_log2;
+        int64_t mb = 0, mp = 0, mg = 0;
+        for (int x = 0; x < kSlices; ++x) {
+            mb = std::max<int64_t>(mb, ba.a.bsl[x + 1] - ba.a.bsl[x]);
+            mp = std::max<int64_t>(mp, ba.a.psl[x + 1] - ba.a.psl[x]);
+            mg = std::max<int64_t>(mg, ba.a.gsl[x + 1] - ba.a.gsl[x]);
+        }
+        ba.pb_bin = ceil_div(mb, per * kBinItems);
+        ba.pb_pt = ceil_div(mp, per * kBinItems);
+        ba.pb_emit = ceil_div(mg, per);
+        const int64_t grid = (int64_t)kSlices * (ba.pb_bin + ba.pb_pt + ba.pb_emit);
+        if (grid > 0) level_batch_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc);
+    }
+    const int64_t n = d->n_rows * B;
+    if (n > 0) {
+        const int64_t grid = std::min<int64_t>((n + kBlock - 1) / kBlock, 1 << 16);
+        reduce_batch_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(acc, (typename P::Y*)yv, n, accumulate);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return hip_fail(err, "batched sweep launch");
+    return GCS_OK;
+}
+
 }  // namespace
 }  // namespace gcs
 
@@ -1161,6 +1333,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->n_cols = g.n_cols;
     d->alpha = g.alpha();
     d->L = g.L;
+    d->arena_len = g.arena;
     d->lv = g.lv;
     // emission team per level: about GCS_EMIT_PER_LANE (default 4) roots per
     // lane, at most one wave
@@ -1310,6 +1483,51 @@ extern "C" gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_
 extern "C" gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void* y_dev, void* stream)
 {
     return sweep_dispatch(d, x_dev, y_dev, stream, nullptr, 1);
+}
+
+extern "C" gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, size_t* bytes)
+{
+    if (!d || !bytes || nvec < 1 || nvec > gcs::kMaxBatch) {
+        gcs::set_error("invalid argument (nvec must be in 1..64)");
+        return GCS_EINVAL;
+    }
+    *bytes = gcs::batch_workspace_bytes(d->arena_len, d->n_rows, d->policy, nvec);
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec,
+                                            void* workspace_dev, size_t workspace_bytes, int32_t accumulate,
+                                            void* stream)
+{
+    if (!d || nvec < 1 || nvec > gcs::kMaxBatch || (d->n_cols > 0 && !x_dev) || (d->n_rows > 0 && !y_dev) ||
+        !workspace_dev) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    if ((uintptr_t)workspace_dev & 255) {
+        gcs::set_error("the batch workspace must be 256-byte aligned");
+        return GCS_EINVAL;
+    }
+    if (workspace_bytes < gcs::batch_workspace_bytes(d->arena_len, d->n_rows, d->policy, nvec)) {
+        gcs::set_error("batch workspace smaller than gcs_batch_workspace_bytes reports");
+        return GCS_EINVAL;
+    }
+    gcs::DeviceGuard guard(d->device);
+    if (!guard.ok) {
+        gcs::set_error("cannot select the upload's device");
+        return GCS_EHIP;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    switch (d->policy) {
+    case GCS_PLUS_F64: return gcs::run_sweep_batch<gcs::PolPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_PLUS_F32: return gcs::run_sweep_batch<gcs::PolPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_PLUS_F32_ACC_F64:
+        return gcs::run_sweep_batch<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_BOOL_OR: return gcs::run_sweep_batch<gcs::PolBoolOr>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_PLUS_I64: return gcs::run_sweep_batch<gcs::PolPlusI64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    }
+    gcs::set_error("invalid policy");
+    return GCS_EINVAL;
 }
 
 extern "C" int64_t gcs_sweep_launches(const gcs_device* d) { return d ? gcs::count_launches(d) : 0; }

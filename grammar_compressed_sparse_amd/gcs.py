@@ -76,6 +76,8 @@ _lib.gcs_upload.argtypes = [_P, ctypes.c_int, _P, ctypes.c_size_t, _P, ctypes.c_
 _lib.gcs_sweep_right.argtypes = [_P, _P, _P, _P]
 _lib.gcs_sweep_right_acc.argtypes = [_P, _P, _P, _P]
 _lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
+_lib.gcs_batch_workspace_bytes.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+_lib.gcs_sweep_right_batch.argtypes = [_P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
 _lib.gcs_profile_begin.argtypes = [_P, _I64, ctypes.c_int32]
@@ -87,7 +89,8 @@ _lib.gcs_free_device.argtypes = [_P]
 _lib.gcs_free_device.restype = None
 for _f in ("gcs_build_grammar", "gcs_grammar_from_rules", "gcs_grammar_stats", "gcs_level_widths",
            "gcs_export_grammar", "gcs_layout_counts", "gcs_export_layout", "gcs_device_layout", "gcs_upload",
-           "gcs_sweep_right", "gcs_sweep_right_acc", "gcs_bfs", "gcs_profile_begin", "gcs_sweep_right_profiled", "gcs_profile_end"):
+           "gcs_sweep_right", "gcs_sweep_right_acc", "gcs_bfs", "gcs_profile_begin", "gcs_sweep_right_profiled", "gcs_profile_end",
+           "gcs_batch_workspace_bytes", "gcs_sweep_right_batch"):
     getattr(_lib, _f).restype = _st
 
 
@@ -264,6 +267,14 @@ class Device:
     def sweep_right_acc(self, x, y, stream=None):
         return sweep_right_acc(self, x, y, stream)
 
+    def sweep_right_batch(self, X, Y=None, accumulate=False, stream=None):
+        return sweep_right_batch(self, X, Y, accumulate, stream)
+
+    def batch_workspace_bytes(self, nvec: int) -> int:
+        n = ctypes.c_size_t(0)
+        _check(_lib.gcs_batch_workspace_bytes(self._h, nvec, ctypes.byref(n)))
+        return int(n.value)
+
     def bfs(self, sources, max_passes=1 << 16, stream=None):
         return bfs(self, sources, max_passes, stream)
 
@@ -355,6 +366,34 @@ def sweep_right_acc(dev: Device, x, y, stream=None):
         _check(_lib.gcs_sweep_right_acc(dev.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                         _stream_ptr(stream)))
     return y
+
+
+def sweep_right_batch(dev: Device, X, Y=None, accumulate=False, stream=None):
+    """gcs_sweep_right_batch: Y = M X (or Y (+)= M X) for X of shape (x_len, B),
+    B in 1..64, row-major; the batch workspace is a torch buffer kept on the
+    device object (one per B) and reused by later calls."""
+    torch = _torch()
+    if not dev.handle:
+        raise GcsError(-5, "device handle already freed")
+    if X.dim() != 2 or X.shape[0] != dev.sizes["x_len"] or X.dtype != dev.x_dtype or not X.is_contiguous() \
+            or X.device != dev.device:
+        raise GcsError(-1, f"X must be a contiguous {dev.x_dtype} tensor of shape ({dev.sizes['x_len']}, B) on "
+                           f"{dev.device}")
+    B = int(X.shape[1])
+    if Y is None:
+        Y = torch.empty((dev.sizes["y_len"], B), dtype=dev.y_dtype, device=dev.device)
+    if tuple(Y.shape) != (dev.sizes["y_len"], B) or Y.dtype != dev.y_dtype or not Y.is_contiguous() \
+            or Y.device != dev.device:
+        raise GcsError(-1, f"Y must be a contiguous {dev.y_dtype} tensor of shape ({dev.sizes['y_len']}, {B})")
+    ws = dev.__dict__.setdefault("_batch_ws", {})
+    if B not in ws:
+        ws[B] = torch.empty(max(dev.batch_workspace_bytes(B), 1), dtype=torch.uint8, device=dev.device)
+    w = ws[B]
+    with torch.cuda.device(dev.device):
+        _check(_lib.gcs_sweep_right_batch(dev.handle, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
+                                          B, ctypes.c_void_p(w.data_ptr()), w.numel(), int(bool(accumulate)),
+                                          _stream_ptr(stream)))
+    return Y
 
 
 def bfs(dev: Device, sources, max_passes=1 << 16, stream=None):

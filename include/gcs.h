@@ -203,7 +203,8 @@ gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* 
  * image into grammar_dev (>= grammar_bytes, 256-byte aligned) on `stream`;
  * workspace_dev (>= workspace_bytes, 256-byte aligned) is the value arena.
  * Both stay owned by the caller.  The grammar object may be freed after this
- * call returns.  The copy is complete when the stream reaches it. */
+ * call returns.  The call synchronises `stream`: the copy is complete when it
+ * returns. */
 gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
                       void* workspace_dev, size_t workspace_bytes, void* stream, gcs_device** out);
 
@@ -222,6 +223,25 @@ gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* 
  * groups (each group its own grammar and upload, rules never spanning
  * columns of two groups), accumulating into one y. */
 gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
+
+/* Batched right product Y = M X (section 4.4, "Batched evaluation (SpMM)";
+ * appendix A): nvec vectors (1..64) in one sweep
+ * over the uploaded grammar.  X is x_len x nvec and Y is y_len x nvec, both
+ * row-major device arrays of the policy's x and y types (X[j * nvec + b] is
+ * entry j of vector b); Y = M X, or Y (+)= M X when accumulate is nonzero.
+ * Every value of the sweep becomes a row of nvec values, so the terminal
+ * array, the level buffers and the slice accumulators live in a separate,
+ * caller-owned batch workspace of at least gcs_batch_workspace_bytes(d, nvec)
+ * bytes (256-byte aligned; (alpha + 2 w*) * nvec values plus
+ * 8 * y_len * nvec accumulators).  Column b of Y equals gcs_sweep_right on
+ * column b of X up to the order of floating-point additions within a row's
+ * emission (bit-exact for the Boolean and int64 policies).  Asynchronous on
+ * `stream`; calls sharing one workspace must be ordered.
+ * GCS_EINVAL for a null handle or buffer, nvec outside 1..64, or a workspace
+ * that is misaligned or too small. */
+gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, size_t* bytes);
+gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, void* workspace_dev,
+                                 size_t workspace_bytes, int32_t accumulate, void* stream);
 
 /* BFS fixpoint with the Boolean policy on a square matrix (section 5: one
  * Boolean pass is one frontier expansion; the fixpoint repeats it):
