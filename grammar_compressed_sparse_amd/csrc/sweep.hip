@@ -561,17 +561,53 @@ __global__ __launch_bounds__(kBlock) void leaf_batch_kernel(const int32_t* __res
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n_acc; i += stride) acc[i] = P::ident();
 }
 
-template <class P>
-__global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typename P::A* __restrict__ arena,
-                                                             typename P::A* __restrict__ acc)
+// VW adjacent values of a node's row, loaded and stored as one access of
+// VW * sizeof(A) <= 16 bytes (the row and the lane's offset in it are
+// multiples of that size)
+template <class A, int VW>
+struct alignas(sizeof(A) * VW) Row {
+    A v[VW];
+};
+
+template <class P, int VW>
+__device__ __forceinline__ Row<typename P::A, VW> comb_row(const Row<typename P::A, VW>& a,
+                                                           const Row<typename P::A, VW>& b)
+{
+    Row<typename P::A, VW> r;
+#pragma unroll
+    for (int i = 0; i < VW; ++i) r.v[i] = P::comb(a.v[i], b.v[i]);
+    return r;
+}
+
+template <class T>
+__device__ __forceinline__ void issue_before_row(const T& r)
+{
+    static_assert(sizeof(T) % 4 == 0 || sizeof(T) < 4, "row size");
+    if constexpr (sizeof(T) >= 4) {
+        const int32_t* w = (const int32_t*)&r;
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"v"(w[i]));
+    } else {
+        issue_before(r.v[0]);
+    }
+}
+
+// One level of the batched sweep; each lane takes VW consecutive vectors of
+// a node (vb_log2 counts lanes per node: 2^vb_log2 >= B / VW).
+template <class P, int VW>
+__global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typename P::A* __restrict__ arena_a,
+                                                             typename P::A* __restrict__ acc_a)
 {
     using A = typename P::A;
+    using R = Row<A, VW>;
+    R* __restrict__ arena = (R*)arena_a;
+    R* __restrict__ acc = (R*)acc_a;
     const LevelArgs& a = ba.a;
-    const int64_t B = ba.B;
+    const int64_t W = ba.B / VW;  // Row elements per node
     const int32_t tid = threadIdx.x, per = kBlock >> ba.vb_log2, slot = tid >> ba.vb_log2;
-    const int32_t lane_b = tid & ((1 << ba.vb_log2) - 1);
-    const bool live = lane_b < ba.B;
-    const int64_t vb = min(lane_b, ba.B - 1);  // the vector this lane gathers
+    const int32_t lane_w = tid & ((1 << ba.vb_log2) - 1);
+    const bool live = lane_w < W;
+    const int64_t vw = min((int64_t)lane_w, W - 1);  // the row element this lane gathers
     int32_t b = blockIdx.x;
     const int32_t part_bin = ba.pb_bin * kSlices, part_pt = ba.pb_pt * kSlices;
     if (b < part_bin) {
@@ -582,15 +618,15 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         int2 c[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
-        A v[kBinItems];
+        R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(arena[c[u].x * B + vb], arena[c[u].y * B + vb]);
+        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(arena[c[u].x * W + vw], arena[c[u].y * W + vw]);
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
-            if (t < end && live) arena[(int64_t)(a.cur + t) * B + vb] = v[u];
+            if (t < end && live) arena[(int64_t)(a.cur + t) * W + vw] = v[u];
         }
         return;
     }
@@ -603,33 +639,50 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         int32_t src[kBinItems];
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
-        A v[kBinItems];
+        R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u] * B + vb];
+        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u] * W + vw];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
-            if (t < end && live) arena[(int64_t)(a.cur + a.nb + t) * B + vb] = v[u];
+            if (t < end && live) arena[(int64_t)(a.cur + a.nb + t) * W + vw] = v[u];
         }
         return;
     }
     b -= part_pt;
     // emission: the lanes of a group each combine the group's roots in C
-    // order for their vector, then update the slice accumulator of the row
+    // order for their vectors, then update the slice accumulator of the row
     const int32_t x = b % kSlices, i = b / kSlices, gend = a.gsl[x + 1];
     const int32_t gfirst = a.gsl[x] + i * per;
     if (gfirst >= gend) return;
     const int32_t graw = gfirst + slot;
     const bool valid = graw < gend;
     const int32_t g = valid ? graw : gend - 1;
-    A* r = acc + ((int64_t)x * a.n_rows + a.erow[g]) * B + vb;
-    const A old = *r;
-    const int32_t e1 = a.eoff[g + 1];
-    const A s = emit_rounds<P>(a.epos, a.eoff[g], e1, 1, valid, [&](int32_t c) { return arena[c * B + vb]; });
-    issue_before(old);
-    if (valid && live) *r = P::comb(old, s);
+    R* r = acc + ((int64_t)x * a.n_rows + a.erow[g]) * W + vw;
+    const R old = *r;
+    const int32_t e0 = a.eoff[g], e1 = a.eoff[g + 1];
+    R s;
+#pragma unroll
+    for (int k = 0; k < VW; ++k) s.v[k] = P::ident();
+    int32_t e = e0;
+    do {
+        int32_t p[kEmitItems];
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) p[u] = a.epos[min(e + u, e1 - 1)];
+        R v[kEmitItems];
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) v[u] = arena[p[u] * W + vw];
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u) issue_before_row(v[u]);
+#pragma unroll
+        for (int u = 0; u < kEmitItems; ++u)
+            if (e + u < e1) s = comb_row<P, VW>(s, v[u]);
+        e += kEmitItems;
+    } while (valid && e < e1);
+    issue_before_row(old);
+    if (valid && live) *r = comb_row<P, VW>(old, s);
 }
 
 template <class P>
@@ -1195,8 +1248,11 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
     using A = typename P::A;
     auto* arena = (A*)ws;
     auto* acc = (A*)((unsigned char*)ws + batch_arena_bytes(d->arena_len, d->policy, B));
+    // widest access of at most 16 bytes that divides the row
+    int VW = 1;
+    while (VW * 2 * (int)sizeof(A) <= 16 && B % (VW * 2) == 0) VW *= 2;
     int vb_log2 = 0;
-    while ((1 << vb_log2) < B) ++vb_log2;
+    while ((1 << vb_log2) < B / VW) ++vb_log2;
     const int32_t per = kBlock >> vb_log2;
     const int64_t n_acc = (int64_t)kSlices * d->n_rows * B;
     const int64_t leaf_items = std::max<int64_t>(d->alpha * B, n_acc);
@@ -1219,7 +1275,14 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
         ba.pb_pt = ceil_div(mp, per * kBinItems);
         ba.pb_emit = ceil_div(mg, per);
         const int64_t grid = (int64_t)kSlices * (ba.pb_bin + ba.pb_pt + ba.pb_emit);
-        if (grid > 0) level_batch_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc);
+        if (grid <= 0) continue;
+        switch (VW) {
+        case 1: level_batch_kernel<P, 1><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+        case 2: level_batch_kernel<P, 2><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+        case 4: level_batch_kernel<P, 4><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+        case 8: level_batch_kernel<P, 8><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+        default: level_batch_kernel<P, 16><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+        }
     }
     const int64_t n = d->n_rows * B;
     if (n > 0) {
