@@ -93,6 +93,67 @@ def csr_comparator(torch, rp, col, val, x, steps):
         return {"error": str(e)[:200]}
 
 
+def bench_batched(torch, gcs, oracle, synth, dev, lay, rp, col, val, spec, elem, xdt, batches, steps):
+    """Batched right product Y = M X (B vectors per sweep) on the same upload:
+    sampled rows of two columns checked against the oracle, then K timed
+    sweeps; algorithmic bytes = the per-level formula with B-wide values, plus
+    the leaf (descriptors, x rows, terminal rows) and the slice reduction.
+    rocSPARSE SpMM (torch.sparse.mm on a CSR tensor) at the same B is context."""
+    nnz = int(rp[-1])
+    n, m = spec.n_rows, spec.n_cols
+    alpha = int(lay["alpha"])
+    rows = np.unique(np.concatenate([np.arange(0, n, max(1, n // 256)), [n - 1]]))
+    crow = torch.from_numpy(rp.astype(np.int32)).cuda()
+    A = torch.sparse_csr_tensor(crow, torch.from_numpy(col).cuda(), torch.from_numpy(val.astype(xdt)).cuda(),
+                                size=(n, m))
+    out = []
+    for B in batches:
+        X = torch.from_numpy(np.stack([synth.normal(m, 7000 + b) for b in range(B)], axis=1).astype(xdt)).cuda()
+        Y = dev.sweep_right_batch(X)
+        dev.check()
+        Yh = Y.cpu().numpy()
+        worst = 0.0
+        for b in (0, B - 1):
+            yo, absum = oracle.spmv_f64_rows(rows, rp, col, val, X[:, b].cpu().numpy().astype(np.float64))
+            worst = max(worst, float(np.max(np.abs(Yh[rows, b].astype(np.float64) - yo) / np.maximum(absum, 1e-300))))
+        tol = 1e-5 if elem == 4 else 1e-12
+        if worst > tol:
+            raise SystemExit(f"batched sweep (B={B}) disagrees with the oracle: {worst:.2e}")
+        for _ in range(3):
+            dev.sweep_right_batch(X, Y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dev.sweep_right_batch(X, Y)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        sv = B * elem
+        meta, eoff = lay["level_meta"], lay["eoff"]
+        L = meta.shape[0] - 1
+        g0, ng = int(meta[L][6]), int(meta[L][7])
+        last_emit = 8 * ng + 4 * int(eoff[g0 + ng] - eoff[g0]) + 2 * sv * ng if ng else 0
+        # levels and emissions, then the leaf (descriptors, x rows, terminal
+        # rows), the accumulator clear and the slice reduction into Y
+        alg = float(level_bytes(lay, sv, sv).sum() + last_emit + alpha * (8 + sv) + m * sv + 8 * n * sv +
+                    9 * n * sv)
+        Z = torch.sparse.mm(A, X)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            Z = torch.sparse.mm(A, X)
+        torch.cuda.synchronize()
+        ms_csr = (time.perf_counter() - t0) * 1e3 / 3
+        del Z, X, Y
+        out.append({"B": B, "ms_per_sweep": ms, "ms_per_vector": ms / B, "nnz_per_s": nnz * B / (ms * 1e-3),
+                    "alg_bytes_per_sweep": alg, "achieved_GBs": alg / (ms * 1e-3) / 1e9,
+                    "frac_hbm_peak": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "max_rel_err_sampled": worst,
+                    "workspace_bytes": dev.batch_workspace_bytes(B), "rocsparse_spmm_ms": ms_csr})
+        log(f"batched B={B}: {ms:.3f} ms per sweep ({ms / B:.4f} ms per vector), rocSPARSE SpMM {ms_csr:.3f} ms")
+    del A, crow
+    torch.cuda.empty_cache()
+    return out
+
+
 KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "sweep.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
 
@@ -235,6 +296,8 @@ def main():
     ap.add_argument("--col-chunk", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-csr", action="store_true")
+    ap.add_argument("--batches", default="32,64",
+                    help="batched sweeps (Y = M X) to time after the headline, comma-separated B; empty: none")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run 5 device-to-device copies of this many MiB (a known-size reference kernel "
                          "for hardware traffic counters)")
@@ -355,6 +418,10 @@ def main():
     csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
     eng_bytes = dev.device_bytes + xs[0].numel() * elem + y.numel() * elem
     csr = None if args.no_csr else csr_comparator(torch, rp, col, val, xs[0], min(args.steps, 20))
+    batched = None
+    if args.batches:
+        batched = bench_batched(torch, gcs, oracle, synth, dev, lay, rp, col, val, spec, elem, xdt,
+                                [int(b) for b in args.batches.split(",")], min(args.steps, 20))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(rp, col, val, xs[0].cpu().numpy().astype(np.float64), nnz)
@@ -394,6 +461,7 @@ def main():
             "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
             "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
             "csr_rocsparse": csr,
+            "batched": batched,
             "per_level_widest": per_level[widest] if per_level else None,
             "wide_levels": nwide,
             "level_span_us": span_ms * 1e3,

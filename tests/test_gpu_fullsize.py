@@ -86,3 +86,19 @@ def test_fullsize_multiply_many(big, oracle_mod, synth_mod):
         worst = max(worst, _rows_ok(y.cpu().numpy(), sub, oracle_mod, rp, col, val, x.astype(np.float64), 1e-5))
     dev.check()
     _say(f"32 vectors: {sub.size} sampled rows each, max rel err {worst:.2e}")
+
+
+def test_fullsize_batch32(big, oracle_mod, synth_mod):
+    """Batched Y = M X with 32 fp32 vectors in one sweep: sampled rows of
+    every column against the oracle."""
+    torch, gcs, spec, rp, col, val, g, rows = big
+    dev = gcs.upload(g, gcs.PLUS_F32)
+    X = np.stack([synth_mod.normal(spec.n_cols, s) for s in range(301, 333)], axis=1).astype(np.float32)
+    Y = dev.sweep_right_batch(torch.from_numpy(X).cuda())
+    dev.check()
+    Yh = Y.cpu().numpy()
+    sub = rows[::4]
+    worst = 0.0
+    for b in range(32):
+        worst = max(worst, _rows_ok(Yh[:, b], sub, oracle_mod, rp, col, val, X[:, b].astype(np.float64), 1e-5))
+    _say(f"batched B=32: {sub.size} sampled rows per column, max rel err {worst:.2e}")
