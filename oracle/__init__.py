@@ -52,6 +52,8 @@ def _load():
         lib.oracle_spmv_f64_rows.argtypes = [P, I64, P, P, I32, P, P, P, P]
         lib.oracle_spmv_i64.argtypes = [I64, P, P, I32, P, P, P]
         lib.oracle_spmv_bool.argtypes = [I64, P, P, P, P]
+        lib.oracle_spmv_min_plus_f32.argtypes = [I64, P, P, I32, P, P, P]
+        lib.oracle_spmv_min_plus_f64.argtypes = [I64, P, P, I32, P, P, P]
         lib.oracle_bfs.argtypes = [I64, P, P, P, I64, P, P, I64]
         lib.oracle_bfs.restype = I64
         lib.oracle_num_threads.restype = I32
@@ -139,6 +141,22 @@ def spmv_bool(row_ptr, col, x):
     xx = np.ascontiguousarray(np.asarray(x) != 0, dtype=np.uint8)
     y = np.empty(n, np.uint8)
     lib.oracle_spmv_bool(n, _p(rp), _p(cl), _p(xx), _p(y))
+    return y
+
+
+def spmv_min_plus(row_ptr, col, val, x, dtype=np.float32):
+    """Tropical y[r] = min over the stored entries of row r of (M[r][j] + x[j]),
+    +inf for an empty row; every addition in ``dtype`` (float32 or float64)."""
+    lib = _load()
+    rp, cl = _csr(row_ptr, col)
+    n = rp.shape[0] - 1
+    kind, vp, keep = _vals(val)
+    dt = np.dtype(dtype)
+    xx = np.ascontiguousarray(x, dtype=dt)
+    y = np.empty(n, dt)
+    f = lib.oracle_spmv_min_plus_f32 if dt == np.float32 else lib.oracle_spmv_min_plus_f64
+    f(n, _p(rp), _p(cl), kind, vp, _p(xx), _p(y))
+    del keep
     return y
 
 

@@ -15,7 +15,13 @@
  *     (section 5);
  *   - BFS fixpoint: repeat f <- (M f) AND NOT visited, visited <- visited OR f
  *     until f is empty (section 5 names one Boolean pass as one frontier
- *     expansion; iterating it to the fixpoint is the plain reading).
+ *     expansion; iterating it to the fixpoint is the plain reading);
+ *   - tropical (min, +): y[r] = min_{j : M[r][j] stored} (M[r][j] + x[j]),
+ *     +infinity for a row without stored entries (section 5: combine = min,
+ *     leaf = +, identity +infinity; one pass is one Bellman-Ford
+ *     relaxation).  Each term is a single addition in the precision of the
+ *     policy (fp32: the fp32 value plus x[j], rounded to fp32), so the
+ *     minimum is exact in any order.
  *
  * Plus-times sums are accumulated in fp64 with Neumaier's compensated
  * summation (Neumaier 1974, "Rundungsfehleranalyse einiger Verfahren zur
@@ -26,6 +32,7 @@
  * Matrix values: kind 0 = every stored entry is 1, kind 1 = int8 values,
  * kind 2 = fp64 values.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -116,6 +123,34 @@ void oracle_spmv_bool(int64_t n, const int64_t* row_ptr, const int32_t* col,
  * every executed pass (the last one is 0).  Returns the number of passes, or
  * -1 if max_passes was reached first.
  */
+void oracle_spmv_min_plus_f32(int64_t n, const int64_t* row_ptr, const int32_t* col, int kind, const void* val,
+                              const float* x, float* y)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < n; ++r) {
+        float m = INFINITY;
+        for (int64_t k = row_ptr[r]; k < row_ptr[r + 1]; ++k) {
+            const float t = (float)entry(kind, val, k) + x[col[k]];
+            if (t < m) m = t;
+        }
+        y[r] = m;
+    }
+}
+
+void oracle_spmv_min_plus_f64(int64_t n, const int64_t* row_ptr, const int32_t* col, int kind, const void* val,
+                              const double* x, double* y)
+{
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < n; ++r) {
+        double m = INFINITY;
+        for (int64_t k = row_ptr[r]; k < row_ptr[r + 1]; ++k) {
+            const double t = entry(kind, val, k) + x[col[k]];
+            if (t < m) m = t;
+        }
+        y[r] = m;
+    }
+}
+
 int64_t oracle_bfs(int64_t n, const int64_t* row_ptr, const int32_t* col, const int64_t* sources,
                    int64_t nsrc, uint8_t* visited, int64_t* new_counts, int64_t max_passes)
 {

@@ -140,3 +140,66 @@ def test_bfs_vs_warshall(oracle_mod, seed):
     vis, counts = oracle_mod.bfs(rp, col, srcs)
     assert sorted(np.nonzero(vis)[0].tolist()) == oracle_mod.reverse_reachable(adj, srcs)
     assert counts[-1] == 0 and counts.sum() + len(srcs) == vis.sum()
+
+
+def _random_csr(rng, n, m, p_row_empty=0.2, max_deg=6):
+    rows = []
+    for _ in range(n):
+        k = 0 if rng.random() < p_row_empty else rng.randint(1, max_deg)
+        rows.append(sorted(rng.sample(range(m), min(k, m))))
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    col = np.array([j for r in rows for j in r], np.int32)
+    return rows, rp, col
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_min_plus_brute_force(oracle_mod, seed):
+    """Tropical pass written out term by term (section 5: combine = min,
+    leaf = value + x[j], identity +inf), in fp64 (Python floats) and in fp32
+    (numpy float32 scalars), against the oracle: bit-exact."""
+    rng = random.Random(seed)
+    n, m = 37, 23
+    rows, rp, col = _random_csr(rng, n, m)
+    val = np.array([rng.choice([-2.5, -1.0, 0.0, 0.125, 1.0, 3.75, 1e-3, 7.0]) for _ in range(col.size)])
+    x = [rng.uniform(-5, 5) for _ in range(m)]
+    y64 = oracle_mod.spmv_min_plus(rp, col, val, np.array(x), np.float64)
+    y32 = oracle_mod.spmv_min_plus(rp, col, val, np.array(x, np.float32), np.float32)
+    k = 0
+    for r, cols in enumerate(rows):
+        best64, best32 = float("inf"), np.float32(np.inf)
+        for j in cols:
+            t64 = float(val[k]) + x[j]
+            t32 = np.float32(val[k]) + np.float32(x[j])
+            best64 = t64 if t64 < best64 else best64
+            best32 = t32 if t32 < best32 else best32
+            k += 1
+        assert y64[r] == best64
+        assert y32[r] == best32 and y32.dtype == np.float32
+
+
+def test_min_plus_path_distances(oracle_mod):
+    """Relaxing to the fixpoint on a path (out-list of i is {i+1}, unit
+    weights) from node n-1 gives the closed-form distance n-1-i."""
+    n = 30
+    rp = np.arange(n + 1, dtype=np.int64).clip(max=n - 1)
+    col = np.arange(1, n, dtype=np.int32)
+    d = np.full(n, np.inf)
+    d[n - 1] = 0.0
+    for _ in range(n):
+        d = np.minimum(d, oracle_mod.spmv_min_plus(rp, col, None, d, np.float64))
+    assert np.array_equal(d, np.arange(n - 1, -1, -1, dtype=np.float64))
+
+
+def test_min_plus_reduces_to_boolean(oracle_mod):
+    """With zero weights and x in {0, +inf}, y[r] = 0 exactly where the
+    Boolean pass of (x == 0) is 1, +inf elsewhere (empty rows included)."""
+    rng = random.Random(9)
+    n, m = 60, 40
+    rows, rp, col = _random_csr(rng, n, m)
+    xb = np.array([rng.random() < 0.3 for _ in range(m)], np.uint8)
+    x = np.where(xb == 1, 0.0, np.inf)
+    y = oracle_mod.spmv_min_plus(rp, col, np.zeros(col.size), x, np.float64)
+    yb = oracle_mod.spmv_bool(rp, col, xb)
+    assert np.array_equal(y == 0.0, yb == 1)
+    assert np.all(np.isinf(y[yb == 0]))
