@@ -97,6 +97,32 @@ struct PolPlusI64 {
     __device__ static A ident() { return 0; }
 };
 
+// tropical (min, +): leaf = matrix value + x[j], combine = min, identity
+// +infinity (section 5); exact, since min never rounds and every sum is
+// formed once, in the leaf
+struct PolMinPlusF32 {
+    using X = float;
+    using A = float;
+    using Y = float;
+    using W = float;
+    __device__ static A leaf(W v, X x) { return v + x; }
+    __device__ static A comb(A a, A b) { return b < a ? b : a; }
+    __device__ static Y emit(Y y, A s) { return s < y ? s : y; }
+    __device__ static Y yzero() { return __builtin_huge_valf(); }
+    __device__ static A ident() { return __builtin_huge_valf(); }
+};
+struct PolMinPlusF64 {
+    using X = double;
+    using A = double;
+    using Y = double;
+    using W = double;
+    __device__ static A leaf(W v, X x) { return v + x; }
+    __device__ static A comb(A a, A b) { return b < a ? b : a; }
+    __device__ static Y emit(Y y, A s) { return s < y ? s : y; }
+    __device__ static Y yzero() { return __builtin_huge_val(); }
+    __device__ static A ident() { return __builtin_huge_val(); }
+};
+
 // lane exchange inside a wave for every arena type
 __device__ inline double xchg(double v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline float xchg(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -789,6 +815,8 @@ size_t elem_bytes(gcs_policy p)
     case GCS_PLUS_F32_ACC_F64: return 8;
     case GCS_BOOL_OR: return 1;
     case GCS_PLUS_I64: return 8;
+    case GCS_MIN_PLUS_F32: return 4;
+    case GCS_MIN_PLUS_F64: return 8;
     }
     return 0;
 }
@@ -849,7 +877,7 @@ size_t arena_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)g.aren
 size_t acc_bytes(const Grammar& g, gcs_policy p) { return al256((size_t)kSlices * g.n_rows * elem_bytes(p)); }
 size_t workspace_bytes(const Grammar& g, gcs_policy p) { return arena_bytes(g, p) + acc_bytes(g, p) + 256; }
 
-bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_PLUS_I64; }
+bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_MIN_PLUS_F64; }
 
 // batch workspace: [arena x B | kSlices x n_rows x B accumulators]
 size_t batch_arena_bytes(int64_t arena, gcs_policy p, int64_t B) { return al256((size_t)(arena * B) * elem_bytes(p)); }
@@ -1352,12 +1380,14 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         unsigned char* o = vbuf.data() + i * gcs::v_bytes(p);
         switch (p) {
         case GCS_PLUS_F64:
-        case GCS_PLUS_F32_ACC_F64: {
+        case GCS_PLUS_F32_ACC_F64:
+        case GCS_MIN_PLUS_F64: {
             double v = g.V[i];
             std::memcpy(o, &v, 8);
             break;
         }
-        case GCS_PLUS_F32: {
+        case GCS_PLUS_F32:
+        case GCS_MIN_PLUS_F32: {
             float v = (float)g.V[i];
             std::memcpy(o, &v, 4);
             break;
@@ -1533,6 +1563,8 @@ static gcs_status sweep_dispatch(gcs_device* d, const void* x_dev, void* y_dev, 
     case GCS_PLUS_F32_ACC_F64: return gcs::run_sweep<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, s, ev, accumulate, span);
     case GCS_BOOL_OR: return gcs::run_sweep<gcs::PolBoolOr>(d, x_dev, y_dev, s, ev, accumulate, span);
     case GCS_PLUS_I64: return gcs::run_sweep<gcs::PolPlusI64>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_MIN_PLUS_F32: return gcs::run_sweep<gcs::PolMinPlusF32>(d, x_dev, y_dev, s, ev, accumulate, span);
+    case GCS_MIN_PLUS_F64: return gcs::run_sweep<gcs::PolMinPlusF64>(d, x_dev, y_dev, s, ev, accumulate, span);
     }
     gcs::set_error("corrupt device handle");
     return GCS_ESTATE;
@@ -1588,6 +1620,10 @@ extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, vo
         return gcs::run_sweep_batch<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
     case GCS_BOOL_OR: return gcs::run_sweep_batch<gcs::PolBoolOr>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
     case GCS_PLUS_I64: return gcs::run_sweep_batch<gcs::PolPlusI64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_MIN_PLUS_F32:
+        return gcs::run_sweep_batch<gcs::PolMinPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_MIN_PLUS_F64:
+        return gcs::run_sweep_batch<gcs::PolMinPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
     }
     gcs::set_error("invalid policy");
     return GCS_EINVAL;

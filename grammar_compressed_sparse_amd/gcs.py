@@ -20,8 +20,9 @@ if not os.path.exists(_SO):
 _lib = ctypes.CDLL(_SO)
 
 # policies (gcs_policy)
-PLUS_F64, PLUS_F32, PLUS_F32_ACC_F64, BOOL_OR, PLUS_I64 = range(5)
-POLICY_NAMES = {"f64": PLUS_F64, "f32": PLUS_F32, "f32_acc_f64": PLUS_F32_ACC_F64, "bool": BOOL_OR, "i64": PLUS_I64}
+PLUS_F64, PLUS_F32, PLUS_F32_ACC_F64, BOOL_OR, PLUS_I64, MIN_PLUS_F32, MIN_PLUS_F64 = range(7)
+POLICY_NAMES = {"f64": PLUS_F64, "f32": PLUS_F32, "f32_acc_f64": PLUS_F32_ACC_F64, "bool": BOOL_OR, "i64": PLUS_I64,
+                "min_plus_f32": MIN_PLUS_F32, "min_plus_f64": MIN_PLUS_F64}
 VAL_ONES, VAL_I8, VAL_F64 = 0, 1, 2
 PROFILE_LAUNCHES, PROFILE_LEVEL_SPAN = 0, 1  # gcs_profile_mode
 _STATUS = {0: "GCS_OK", -1: "GCS_EINVAL", -2: "GCS_ENOMEM", -3: "GCS_EHIP", -4: "GCS_ERANGE", -5: "GCS_ESTATE"}
@@ -224,9 +225,9 @@ def _torch():
 
 
 _X_DTYPES = {PLUS_F64: "float64", PLUS_F32: "float32", PLUS_F32_ACC_F64: "float32", BOOL_OR: "uint8",
-             PLUS_I64: "int64"}
+             PLUS_I64: "int64", MIN_PLUS_F32: "float32", MIN_PLUS_F64: "float64"}
 _Y_DTYPES = {PLUS_F64: "float64", PLUS_F32: "float32", PLUS_F32_ACC_F64: "float64", BOOL_OR: "uint8",
-             PLUS_I64: "int64"}
+             PLUS_I64: "int64", MIN_PLUS_F32: "float32", MIN_PLUS_F64: "float64"}
 
 
 def _stream_ptr(stream):

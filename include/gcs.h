@@ -51,13 +51,19 @@ typedef enum {
  *   GCS_PLUS_F32          x float,   y float;   T and buffers float
  *   GCS_PLUS_F32_ACC_F64  x float,   y double;  T and buffers double
  *   GCS_BOOL_OR           x uint8 0/1, y uint8 0/1; leaf = x[j], combine = OR
- *   GCS_PLUS_I64          x int64,   y int64; matrix values must be integers  */
+ *   GCS_PLUS_I64          x int64,   y int64; matrix values must be integers
+ *   GCS_MIN_PLUS_F32      x float,   y float;  tropical: leaf = M[r][j] + x[j],
+ *                         combine = min, +infinity for a row with no entry
+ *                         (one Bellman-Ford relaxation per pass)
+ *   GCS_MIN_PLUS_F64      as GCS_MIN_PLUS_F32 in double  */
 typedef enum {
     GCS_PLUS_F64 = 0,
     GCS_PLUS_F32 = 1,
     GCS_PLUS_F32_ACC_F64 = 2,
     GCS_BOOL_OR = 3,
-    GCS_PLUS_I64 = 4
+    GCS_PLUS_I64 = 4,
+    GCS_MIN_PLUS_F32 = 5,
+    GCS_MIN_PLUS_F64 = 6
 } gcs_policy;
 
 /* Value array of a CSR input. */
