@@ -215,6 +215,50 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     print("\n".join(lines))
 
 
+def bench_tropical(args, torch, gcs, oracle, g, rp, col, spec, src, vis_o, counts_o):
+    """Tropical (min, +) policy with unit weights on the same graph: K timed
+    single passes from d0 (0 at the sources, +inf elsewhere), one checked
+    bit for bit against the oracle, then Bellman-Ford d <- min(d, M d) to the
+    fixpoint, whose distances must be the oracle BFS's levels."""
+    nnz = int(rp[-1])
+    dev = gcs.upload(g, gcs.MIN_PLUS_F32)
+    d0 = torch.full((spec.n,), float("inf"), dtype=torch.float32, device="cuda")
+    d0[torch.from_numpy(src).cuda()] = 0
+    y = dev.new_y()
+    for _ in range(max(args.warmup, 1)):
+        dev.sweep_right(d0, y)
+    dev.check()
+    if not np.array_equal(y.cpu().numpy(), oracle.spmv_min_plus(rp, col, None, d0.cpu().numpy(), np.float32)):
+        raise SystemExit("tropical pass disagrees with the oracle")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dev.sweep_right(d0, y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    t0 = time.perf_counter()
+    d, passes = d0, 0
+    while True:
+        nd = torch.minimum(d, dev.sweep_right(d, y))
+        passes += 1
+        if torch.equal(nd, d):
+            break
+        d = nd
+    torch.cuda.synchronize()
+    bf_s = time.perf_counter() - t0
+    dev.check()
+    dh = d.cpu().numpy()
+    hist = np.bincount(dh[np.isfinite(dh)].astype(np.int64))
+    if not (np.array_equal(np.isfinite(dh), vis_o.astype(bool)) and
+            np.array_equal(hist[1:], counts_o[:len(hist) - 1])):
+        raise SystemExit("Bellman-Ford distances disagree with the oracle BFS levels")
+    out = {"ms_per_pass": ms, "nnz_per_s": nnz / (ms * 1e-3), "bellman_ford_passes": passes,
+           "bellman_ford_s": bf_s, "max_distance": int(len(hist) - 1)}
+    log(f"tropical: {ms:.2f} ms per pass; Bellman-Ford fixpoint in {passes} passes, {bf_s:.2f} s")
+    dev.free()
+    return out
+
+
 def bench_graph(args, wl, spec):
     """Boolean policy on the copy-model digraph: K single passes y = M f from
     the seeded sources (edges/s per pass), then the BFS fixpoint, with the
@@ -235,7 +279,6 @@ def bench_graph(args, wl, spec):
     log(f"grammar built in {build_s:.1f}s: {st}")
     src = synth.sources(spec.n, wl["n_sources"], wl["source_seed"])
     dev = gcs.upload(g, gcs.BOOL_OR)
-    del g
     f = torch.zeros(spec.n, dtype=torch.uint8, device="cuda")
     f[torch.from_numpy(src).cuda()] = 1
     y = dev.new_y()
@@ -262,6 +305,8 @@ def bench_graph(args, wl, spec):
     bfs_cpu_s = time.perf_counter() - t
     if not (np.array_equal(counts, counts_o) and np.array_equal(vis.cpu().numpy(), vis_o)):
         raise SystemExit("BFS disagrees with the oracle")
+    tropical = bench_tropical(args, torch, gcs, oracle, g, rp, col, spec, src, vis_o, counts_o)
+    del g
     dev_bytes = dev.device_bytes + 2 * spec.n
     csr_bytes = 4 * nnz + 4 * (spec.n + 1) + 2 * spec.n
     out = {
@@ -274,7 +319,7 @@ def bench_graph(args, wl, spec):
                                                   "n_terminals", "n_tiles", "n_emit_groups")},
                    "build_s": build_s, "bfs_passes": len(counts), "bfs_s": bfs_s, "visited": int(vis_o.sum()),
                    "device_bytes": dev_bytes, "csr_bytes_analytic": csr_bytes,
-                   "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes},
+                   "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes, "tropical": tropical},
         "roofline": None,
         "cpu_baseline": {"value": nnz * len(counts_o) / bfs_cpu_s, "unit": "nnz/s", "cores": oracle.num_threads(),
                          "kind": "oracle", "sample": f"the oracle's BFS fixpoint ({len(counts_o)} Boolean passes "
