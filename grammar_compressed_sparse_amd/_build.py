@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libgcs.so")
 OBJ = os.path.join(PKG, "_build")
 
-HOST_SOURCES = ["builder.cpp", "repair.cpp"]
+HOST_SOURCES = ["builder.cpp", "repair.cpp", "serialize.cpp"]
 DEVICE_SOURCES = ["sweep.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

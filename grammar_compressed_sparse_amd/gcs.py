@@ -70,6 +70,10 @@ _lib.gcs_layout_counts.argtypes = [_P, _P]
 _lib.gcs_export_layout.argtypes = [_P] + [_P] * 6
 _lib.gcs_export_slices.argtypes = [_P, _P, _P]
 _lib.gcs_export_slices.restype = _st
+_lib.gcs_save_grammar.argtypes = [_P, ctypes.c_char_p]
+_lib.gcs_save_grammar.restype = _st
+_lib.gcs_load_grammar.argtypes = [ctypes.c_char_p, ctypes.POINTER(_P)]
+_lib.gcs_load_grammar.restype = _st
 _lib.gcs_free_grammar.argtypes = [_P]
 _lib.gcs_free_grammar.restype = None
 _lib.gcs_device_layout.argtypes = [_P, ctypes.c_int, ctypes.POINTER(DevSizes)]
@@ -121,6 +125,10 @@ class Grammar:
     @property
     def handle(self):
         return self._h
+
+    def save(self, path):
+        """gcs_save_grammar: write this grammar to ``path`` (load_grammar reads it back)."""
+        _check(_lib.gcs_save_grammar(self._h, os.fsencode(path)))
 
     def stats(self) -> dict:
         s = Stats()
@@ -176,6 +184,13 @@ class Grammar:
 
 
 ROWS_NATURAL, ROWS_SIMILAR = 0, 1
+
+
+def load_grammar(path) -> Grammar:
+    """gcs_load_grammar: a grammar saved by Grammar.save."""
+    h = _P()
+    _check(_lib.gcs_load_grammar(os.fsencode(path), ctypes.byref(h)))
+    return Grammar(h)
 
 
 def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0,

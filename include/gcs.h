@@ -201,6 +201,18 @@ typedef struct {
     int32_t y_elem_bytes;
 } gcs_dev_sizes;
 
+/* Serialized grammar (section 5, Table 5.1 reports its size; section 7,
+ * item 2: construction is a one-time offline cost): gcs_save_grammar writes
+ * everything the upload and the inspection calls need to `path` (one binary
+ * file, little-endian, ending in a checksum); gcs_load_grammar reads it back
+ * into a new grammar owned by the caller (free with gcs_free_grammar) that
+ * behaves exactly like the one saved.  GCS_EINVAL if the file cannot be
+ * opened or written, is not a grammar file, comes from an incompatible
+ * version, is truncated, fails its checksum or has inconsistent sizes
+ * (gcs_last_error says which); GCS_ENOMEM if memory runs out. */
+gcs_status gcs_save_grammar(const gcs_grammar* g, const char* path);
+gcs_status gcs_load_grammar(const char* path, gcs_grammar** out);
+
 /* Sizes for a policy.  GCS_EINVAL for GCS_PLUS_I64 when V has non-integral
  * values; GCS_ERANGE if the arena exceeds 2^31 - 1 elements. */
 gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* out);

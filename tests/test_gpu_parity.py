@@ -245,3 +245,21 @@ def test_abi_errors_on_device(env):
         dev.sweep_right(torch.zeros(2, dtype=torch.float64, device="cuda"))  # wrong dtype
     with pytest.raises(gcs.GcsError, match="ESTATE"):
         dev.bfs([0])  # not Boolean (matrix is 1x2 and policy fp32)
+
+
+def test_loaded_grammar_sweeps_identically(env, synth_mod, c1, tmp_path):
+    """A grammar saved and loaded back (gcs_save_grammar / gcs_load_grammar)
+    gives the same bits as the one it was saved from: single and batched."""
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    g.save(tmp_path / "c1.gcs")
+    h = gcs.load_grammar(tmp_path / "c1.gcs")
+    x = synth_mod.normal(spec.n_cols, 404)
+    ya, _ = _sweep(env, g, gcs.PLUS_F64, x)
+    yb, _ = _sweep(env, h, gcs.PLUS_F64, x)
+    assert np.array_equal(ya, yb)
+    X = torch.from_numpy(np.stack([synth_mod.normal(spec.n_cols, 405 + b) for b in range(4)], axis=1)).cuda()
+    da, db = gcs.upload(g, gcs.PLUS_F64), gcs.upload(h, gcs.PLUS_F64)
+    assert torch.equal(da.sweep_right_batch(X), db.sweep_right_batch(X))
+    da.check()
+    db.check()
