@@ -569,6 +569,11 @@ struct BatchArgs {
     LevelArgs a;                     // the level's launch arguments (pointers, counts, slices)
     int32_t B, vb_log2;              // vectors; lanes per node = 1 << vb_log2
     int32_t pb_bin, pb_pt, pb_emit;  // workgroups per slice in each part at this width
+    // leaves evaluated in the sweep: a reference c < leaf_alpha is computed as
+    // V[tval[c]] (x) X[tcol[c]] instead of read; arena rows start at node tbase
+    int32_t leaf_alpha, tbase;
+    const int32_t *tcol, *tval;
+    const void *V, *X;
 };
 
 template <class P>
@@ -634,6 +639,18 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     const int32_t lane_w = tid & ((1 << ba.vb_log2) - 1);
     const bool live = lane_w < W;
     const int64_t vw = min((int64_t)lane_w, W - 1);  // the row element this lane gathers
+    // the row element of reference c: a stored value, or a leaf computed in
+    // place (same arithmetic as the leaf kernel)
+    auto fetch = [&](int32_t c) -> R {
+        if (c >= ba.leaf_alpha) return arena[(int64_t)(c - ba.tbase) * W + vw];
+        using XR = Row<typename P::X, VW>;
+        const typename P::W v = ((const typename P::W*)ba.V)[ba.tval[c]];
+        const XR xr = ((const XR*)ba.X)[(int64_t)ba.tcol[c] * W + vw];
+        R r;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) r.v[k] = P::leaf(v, xr.v[k]);
+        return r;
+    };
     int32_t b = blockIdx.x;
     const int32_t part_bin = ba.pb_bin * kSlices, part_pt = ba.pb_pt * kSlices;
     if (b < part_bin) {
@@ -646,13 +663,13 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
         R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(arena[c[u].x * W + vw], arena[c[u].y * W + vw]);
+        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(fetch(c[u].x), fetch(c[u].y));
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
-            if (t < end && live) arena[(int64_t)(a.cur + t) * W + vw] = v[u];
+            if (t < end && live) arena[(int64_t)(a.cur + t - ba.tbase) * W + vw] = v[u];
         }
         return;
     }
@@ -667,13 +684,13 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
         R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u] * W + vw];
+        for (int u = 0; u < kBinItems; ++u) v[u] = fetch(src[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
-            if (t < end && live) arena[(int64_t)(a.cur + a.nb + t) * W + vw] = v[u];
+            if (t < end && live) arena[(int64_t)(a.cur + a.nb + t - ba.tbase) * W + vw] = v[u];
         }
         return;
     }
@@ -699,7 +716,7 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         for (int u = 0; u < kEmitItems; ++u) p[u] = a.epos[min(e + u, e1 - 1)];
         R v[kEmitItems];
 #pragma unroll
-        for (int u = 0; u < kEmitItems; ++u) v[u] = arena[p[u] * W + vw];
+        for (int u = 0; u < kEmitItems; ++u) v[u] = fetch(p[u]);
 #pragma unroll
         for (int u = 0; u < kEmitItems; ++u) issue_before_row(v[u]);
 #pragma unroll
@@ -881,9 +898,15 @@ bool valid_policy(int p) { return p >= GCS_PLUS_F64 && p <= GCS_MIN_PLUS_F64; }
 
 // batch workspace: [arena x B | kSlices x n_rows x B accumulators]
 size_t batch_arena_bytes(int64_t arena, gcs_policy p, int64_t B) { return al256((size_t)(arena * B) * elem_bytes(p)); }
-size_t batch_workspace_bytes(int64_t arena, int64_t n_rows, gcs_policy p, int64_t B)
+// rows of the batch arena: all of it, or without the terminal array when the
+// leaves are evaluated in the sweep
+int64_t batch_arena_rows(const gcs_device* d, int32_t flags)
 {
-    return batch_arena_bytes(arena, p, B) + al256((size_t)(kSlices * n_rows * B) * elem_bytes(p));
+    return (flags & GCS_BATCH_LEAVES_IN_SWEEP) ? d->arena_len - d->alpha : d->arena_len;
+}
+size_t batch_workspace_bytes(int64_t arena_rows, int64_t n_rows, gcs_policy p, int64_t B)
+{
+    return batch_arena_bytes(arena_rows, p, B) + al256((size_t)(kSlices * n_rows * B) * elem_bytes(p));
 }
 
 // The narrow launches' image, built at upload: tail entry j is launch
@@ -1270,12 +1293,14 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
 // Y = M X for B vectors: leaf, one launch per level k = 1..L+1 (level k and
 // the emission of level k-1), slice reduction into Y.
 template <class P>
-gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, void* ws, int32_t accumulate,
+gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, void* ws, int32_t flags,
                            hipStream_t s)
 {
     using A = typename P::A;
+    const bool leaves = (flags & GCS_BATCH_LEAVES_IN_SWEEP) != 0;
+    const int32_t accumulate = (flags & GCS_BATCH_ACCUMULATE) ? 1 : 0;
     auto* arena = (A*)ws;
-    auto* acc = (A*)((unsigned char*)ws + batch_arena_bytes(d->arena_len, d->policy, B));
+    auto* acc = (A*)((unsigned char*)ws + batch_arena_bytes(batch_arena_rows(d, flags), d->policy, B));
     // widest access of at most 16 bytes that divides the row
     int VW = 1;
     while (VW * 2 * (int)sizeof(A) <= 16 && B % (VW * 2) == 0) VW *= 2;
@@ -1283,16 +1308,25 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
     while ((1 << vb_log2) < B / VW) ++vb_log2;
     const int32_t per = kBlock >> vb_log2;
     const int64_t n_acc = (int64_t)kSlices * d->n_rows * B;
-    const int64_t leaf_items = std::max<int64_t>(d->alpha * B, n_acc);
+    // the terminal array (unless the leaves are evaluated in the sweep) and
+    // the accumulator clear
+    const int64_t t_rows = leaves ? 0 : d->alpha;
+    const int64_t leaf_items = std::max<int64_t>(t_rows * B, n_acc);
     const int64_t grid_leaf = std::min<int64_t>(std::max<int64_t>(1, (leaf_items + kBlock - 1) / kBlock), 1 << 16);
     leaf_batch_kernel<P><<<(int32_t)grid_leaf, kBlock, 0, s>>>(d->tcol, d->tval, (const typename P::W*)d->V,
-                                                                (const typename P::X*)xv, arena, d->alpha, B, acc,
+                                                                (const typename P::X*)xv, arena, t_rows, B, acc,
                                                                 n_acc);
     for (int64_t k = 1; k <= d->L + 1; ++k) {
         BatchArgs ba{};
         ba.a = d->largs[k - 1];
         ba.B = B;
         ba.vb_log2 = vb_log2;
+        ba.leaf_alpha = leaves ? (int32_t)d->alpha : 0;
+        ba.tbase = leaves ? (int32_t)d->alpha : 0;
+        ba.tcol = d->tcol;
+        ba.tval = d->tval;
+        ba.V = d->V;
+        ba.X = xv;
         int64_t mb = 0, mp = 0, mg = 0;
         for (int x = 0; x < kSlices; ++x) {
             mb = std::max<int64_t>(mb, ba.a.bsl[x + 1] - ba.a.bsl[x]);
@@ -1580,22 +1614,27 @@ extern "C" gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void
     return sweep_dispatch(d, x_dev, y_dev, stream, nullptr, 1);
 }
 
-extern "C" gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, size_t* bytes)
+static bool batch_flags_ok(int32_t flags)
 {
-    if (!d || !bytes || nvec < 1 || nvec > gcs::kMaxBatch) {
-        gcs::set_error("invalid argument (nvec must be in 1..64)");
+    return (flags & ~(GCS_BATCH_ACCUMULATE | GCS_BATCH_LEAVES_IN_SWEEP)) == 0;
+}
+
+extern "C" gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, int32_t flags, size_t* bytes)
+{
+    if (!d || !bytes || nvec < 1 || nvec > gcs::kMaxBatch || !batch_flags_ok(flags)) {
+        gcs::set_error("invalid argument (nvec must be in 1..64, flags known)");
         return GCS_EINVAL;
     }
-    *bytes = gcs::batch_workspace_bytes(d->arena_len, d->n_rows, d->policy, nvec);
+    *bytes = gcs::batch_workspace_bytes(gcs::batch_arena_rows(d, flags), d->n_rows, d->policy, nvec);
     return GCS_OK;
 }
 
 extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec,
-                                            void* workspace_dev, size_t workspace_bytes, int32_t accumulate,
+                                            void* workspace_dev, size_t workspace_bytes, int32_t flags,
                                             void* stream)
 {
-    if (!d || nvec < 1 || nvec > gcs::kMaxBatch || (d->n_cols > 0 && !x_dev) || (d->n_rows > 0 && !y_dev) ||
-        !workspace_dev) {
+    if (!d || nvec < 1 || nvec > gcs::kMaxBatch || !batch_flags_ok(flags) || (d->n_cols > 0 && !x_dev) ||
+        (d->n_rows > 0 && !y_dev) || !workspace_dev) {
         gcs::set_error("invalid argument");
         return GCS_EINVAL;
     }
@@ -1603,7 +1642,7 @@ extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, vo
         gcs::set_error("the batch workspace must be 256-byte aligned");
         return GCS_EINVAL;
     }
-    if (workspace_bytes < gcs::batch_workspace_bytes(d->arena_len, d->n_rows, d->policy, nvec)) {
+    if (workspace_bytes < gcs::batch_workspace_bytes(gcs::batch_arena_rows(d, flags), d->n_rows, d->policy, nvec)) {
         gcs::set_error("batch workspace smaller than gcs_batch_workspace_bytes reports");
         return GCS_EINVAL;
     }
@@ -1614,16 +1653,16 @@ extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, vo
     }
     hipStream_t s = (hipStream_t)stream;
     switch (d->policy) {
-    case GCS_PLUS_F64: return gcs::run_sweep_batch<gcs::PolPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
-    case GCS_PLUS_F32: return gcs::run_sweep_batch<gcs::PolPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+    case GCS_PLUS_F64: return gcs::run_sweep_batch<gcs::PolPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
+    case GCS_PLUS_F32: return gcs::run_sweep_batch<gcs::PolPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
     case GCS_PLUS_F32_ACC_F64:
-        return gcs::run_sweep_batch<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
-    case GCS_BOOL_OR: return gcs::run_sweep_batch<gcs::PolBoolOr>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
-    case GCS_PLUS_I64: return gcs::run_sweep_batch<gcs::PolPlusI64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+        return gcs::run_sweep_batch<gcs::PolPlusF32AccF64>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
+    case GCS_BOOL_OR: return gcs::run_sweep_batch<gcs::PolBoolOr>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
+    case GCS_PLUS_I64: return gcs::run_sweep_batch<gcs::PolPlusI64>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
     case GCS_MIN_PLUS_F32:
-        return gcs::run_sweep_batch<gcs::PolMinPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+        return gcs::run_sweep_batch<gcs::PolMinPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
     case GCS_MIN_PLUS_F64:
-        return gcs::run_sweep_batch<gcs::PolMinPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, accumulate, s);
+        return gcs::run_sweep_batch<gcs::PolMinPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
     }
     gcs::set_error("invalid policy");
     return GCS_EINVAL;

@@ -25,6 +25,7 @@ POLICY_NAMES = {"f64": PLUS_F64, "f32": PLUS_F32, "f32_acc_f64": PLUS_F32_ACC_F6
                 "min_plus_f32": MIN_PLUS_F32, "min_plus_f64": MIN_PLUS_F64}
 VAL_ONES, VAL_I8, VAL_F64 = 0, 1, 2
 PROFILE_LAUNCHES, PROFILE_LEVEL_SPAN = 0, 1  # gcs_profile_mode
+BATCH_ACCUMULATE, BATCH_LEAVES_IN_SWEEP = 1, 2  # gcs_sweep_right_batch flags
 _STATUS = {0: "GCS_OK", -1: "GCS_EINVAL", -2: "GCS_ENOMEM", -3: "GCS_EHIP", -4: "GCS_ERANGE", -5: "GCS_ESTATE"}
 
 
@@ -81,7 +82,7 @@ _lib.gcs_upload.argtypes = [_P, ctypes.c_int, _P, ctypes.c_size_t, _P, ctypes.c_
 _lib.gcs_sweep_right.argtypes = [_P, _P, _P, _P]
 _lib.gcs_sweep_right_acc.argtypes = [_P, _P, _P, _P]
 _lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
-_lib.gcs_batch_workspace_bytes.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+_lib.gcs_batch_workspace_bytes.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.gcs_sweep_right_batch.argtypes = [_P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
@@ -283,12 +284,13 @@ class Device:
     def sweep_right_acc(self, x, y, stream=None):
         return sweep_right_acc(self, x, y, stream)
 
-    def sweep_right_batch(self, X, Y=None, accumulate=False, stream=None):
-        return sweep_right_batch(self, X, Y, accumulate, stream)
+    def sweep_right_batch(self, X, Y=None, accumulate=False, leaves_in_sweep=False, stream=None):
+        return sweep_right_batch(self, X, Y, accumulate, leaves_in_sweep, stream)
 
-    def batch_workspace_bytes(self, nvec: int) -> int:
+    def batch_workspace_bytes(self, nvec: int, leaves_in_sweep=False) -> int:
         n = ctypes.c_size_t(0)
-        _check(_lib.gcs_batch_workspace_bytes(self._h, nvec, ctypes.byref(n)))
+        flags = BATCH_LEAVES_IN_SWEEP if leaves_in_sweep else 0
+        _check(_lib.gcs_batch_workspace_bytes(self._h, nvec, flags, ctypes.byref(n)))
         return int(n.value)
 
     def bfs(self, sources, max_passes=1 << 16, stream=None):
@@ -384,10 +386,11 @@ def sweep_right_acc(dev: Device, x, y, stream=None):
     return y
 
 
-def sweep_right_batch(dev: Device, X, Y=None, accumulate=False, stream=None):
+def sweep_right_batch(dev: Device, X, Y=None, accumulate=False, leaves_in_sweep=False, stream=None):
     """gcs_sweep_right_batch: Y = M X (or Y (+)= M X) for X of shape (x_len, B),
-    B in 1..64, row-major; the batch workspace is a torch buffer kept on the
-    device object (one per B) and reused by later calls."""
+    B in 1..64, row-major; with leaves_in_sweep no terminal array is kept.  The
+    batch workspace is a torch buffer kept on the device object (one per B and
+    mode) and reused by later calls."""
     torch = _torch()
     if not dev.handle:
         raise GcsError(-5, "device handle already freed")
@@ -401,14 +404,16 @@ def sweep_right_batch(dev: Device, X, Y=None, accumulate=False, stream=None):
     if tuple(Y.shape) != (dev.sizes["y_len"], B) or Y.dtype != dev.y_dtype or not Y.is_contiguous() \
             or Y.device != dev.device:
         raise GcsError(-1, f"Y must be a contiguous {dev.y_dtype} tensor of shape ({dev.sizes['y_len']}, {B})")
+    flags = (BATCH_ACCUMULATE if accumulate else 0) | (BATCH_LEAVES_IN_SWEEP if leaves_in_sweep else 0)
     ws = dev.__dict__.setdefault("_batch_ws", {})
-    if B not in ws:
-        ws[B] = torch.empty(max(dev.batch_workspace_bytes(B), 1), dtype=torch.uint8, device=dev.device)
-    w = ws[B]
+    key = (B, bool(leaves_in_sweep))
+    if key not in ws:
+        ws[key] = torch.empty(max(dev.batch_workspace_bytes(B, leaves_in_sweep), 1), dtype=torch.uint8,
+                              device=dev.device)
+    w = ws[key]
     with torch.cuda.device(dev.device):
         _check(_lib.gcs_sweep_right_batch(dev.handle, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
-                                          B, ctypes.c_void_p(w.data_ptr()), w.numel(), int(bool(accumulate)),
-                                          _stream_ptr(stream)))
+                                          B, ctypes.c_void_p(w.data_ptr()), w.numel(), flags, _stream_ptr(stream)))
     return Y
 
 

@@ -243,23 +243,32 @@ gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* 
 gcs_status gcs_sweep_right_acc(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 
 /* Batched right product Y = M X (section 4.4, "Batched evaluation (SpMM)";
- * appendix A): nvec vectors (1..64) in one sweep
- * over the uploaded grammar.  X is x_len x nvec and Y is y_len x nvec, both
- * row-major device arrays of the policy's x and y types (X[j * nvec + b] is
- * entry j of vector b); Y = M X, or Y (+)= M X when accumulate is nonzero.
- * Every value of the sweep becomes a row of nvec values, so the terminal
- * array, the level buffers and the slice accumulators live in a separate,
- * caller-owned batch workspace of at least gcs_batch_workspace_bytes(d, nvec)
- * bytes (256-byte aligned; (alpha + 2 w*) * nvec values plus
- * 8 * y_len * nvec accumulators).  Column b of Y equals gcs_sweep_right on
- * column b of X up to the order of floating-point additions within a row's
- * emission (bit-exact for the Boolean and int64 policies).  Asynchronous on
- * `stream`; calls sharing one workspace must be ordered.
- * GCS_EINVAL for a null handle or buffer, nvec outside 1..64, or a workspace
- * that is misaligned or too small. */
-gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, size_t* bytes);
+ * appendix A): nvec vectors (1..64) in one sweep over the uploaded grammar.
+ * X is x_len x nvec and Y is y_len x nvec, both row-major device arrays of the
+ * policy's x and y types (X[j * nvec + b] is entry j of vector b).  Every
+ * value of the sweep becomes a row of nvec values, so the level buffers, the
+ * slice accumulators and (unless leaves are evaluated in the sweep) the
+ * terminal array live in a separate, caller-owned batch workspace of at least
+ * gcs_batch_workspace_bytes(d, nvec, flags) bytes, 256-byte aligned:
+ * (alpha + 2 w*) * nvec values, or 2 w* * nvec with
+ * GCS_BATCH_LEAVES_IN_SWEEP, plus 8 * y_len * nvec accumulators.
+ * Flags:
+ *   GCS_BATCH_ACCUMULATE       Y (+)= M X instead of Y = M X
+ *   GCS_BATCH_LEAVES_IN_SWEEP  no terminal array: a reference to terminal
+ *                              <l, j> computes V[l] (x) X[j] where it is read
+ *                              (section 7 item 3 names the Theta(alpha B)
+ *                              terminal array as the cost this removes);
+ *                              same results, bit for bit
+ * Column b of Y equals gcs_sweep_right on column b of X up to the order of
+ * floating-point additions within a row's emission (bit-exact for the
+ * Boolean, int64 and tropical policies).  Asynchronous on `stream`; calls
+ * sharing one workspace must be ordered.
+ * GCS_EINVAL for a null handle or buffer, nvec outside 1..64, unknown flags,
+ * or a workspace that is misaligned or too small. */
+enum { GCS_BATCH_ACCUMULATE = 1, GCS_BATCH_LEAVES_IN_SWEEP = 2 };
+gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, int32_t flags, size_t* bytes);
 gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, void* workspace_dev,
-                                 size_t workspace_bytes, int32_t accumulate, void* stream);
+                                 size_t workspace_bytes, int32_t flags, void* stream);
 
 /* BFS fixpoint with the Boolean policy on a square matrix (section 5: one
  * Boolean pass is one frontier expansion; the fixpoint repeats it):

@@ -198,3 +198,50 @@ def test_batch_abi_errors(env, c1):
     assert st == -1  # GCS_EINVAL: workspace too small, nothing launched
     with pytest.raises(gcs.GcsError):
         dev.sweep_right_batch(torch.zeros((spec.n_cols + 1, 4), dtype=torch.float64, device="cuda"))
+
+
+@pytest.mark.parametrize("pol,dt,B", [("f64", np.float64, 1), ("f64", np.float64, 8), ("f32", np.float32, 32),
+                                      ("i64", np.int64, 5), ("bool", np.uint8, 64), ("min_plus_f32", np.float32, 4),
+                                      ("f32_acc_f64", np.float32, 6)])
+def test_batch_leaves_in_sweep(env, synth_mod, c1, pol, dt, B):
+    """GCS_BATCH_LEAVES_IN_SWEEP (no terminal array) gives the same bits as the
+    sweep with the terminal array, in a workspace smaller by alpha rows."""
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+    rng = np.random.default_rng(B)
+    if dt == np.uint8:
+        X = (rng.random((spec.n_cols, B)) < 0.05).astype(np.uint8)
+    elif dt == np.int64:
+        X = rng.integers(-1000, 1000, (spec.n_cols, B))
+    else:
+        X = rng.standard_normal((spec.n_cols, B)).astype(dt)
+    Xt = torch.from_numpy(X).cuda()
+    Ya = dev.sweep_right_batch(Xt)
+    Yb = dev.sweep_right_batch(Xt, leaves_in_sweep=True)
+    dev.check()
+    assert torch.equal(Ya, Yb)
+    alpha = g.stats()["n_terminals"]
+    elem = {np.float64: 8, np.float32: 4, np.int64: 8, np.uint8: 1}[dt]
+    if pol == "f32_acc_f64":
+        elem = 8
+    saved = dev.batch_workspace_bytes(B) - dev.batch_workspace_bytes(B, leaves_in_sweep=True)
+    assert abs(saved - alpha * B * elem) < 512
+
+
+def test_batch_leaves_in_sweep_graph(env, oracle_mod, synth_mod):
+    torch, gcs = env
+    spec = synth_mod.GraphSpec(300_000, seed=55)
+    rp, col = synth_mod.copy_graph(spec)
+    g = gcs.build_grammar(rp, col, None, n_cols=spec.n)
+    dev = gcs.upload(g, gcs.BOOL_OR)
+    Xb = np.zeros((spec.n, 32), np.uint8)
+    for b in range(32):
+        Xb[synth_mod.sources(spec.n, 4, 700 + b), b] = 1
+    Y = dev.sweep_right_batch(torch.from_numpy(Xb).cuda(), leaves_in_sweep=True)
+    dev.check()
+    Y = Y.cpu().numpy()
+    for b in range(32):
+        assert np.array_equal(Y[:, b], oracle_mod.spmv_bool(rp, col, np.ascontiguousarray(Xb[:, b])))
+    with pytest.raises(gcs.GcsError):  # unknown flag bit
+        gcs._check(gcs._lib.gcs_batch_workspace_bytes(dev.handle, 4, 4, None))
