@@ -136,6 +136,18 @@ def bench_batched(torch, gcs, oracle, synth, dev, lay, rp, col, val, spec, elem,
         # rows), the accumulator clear and the slice reduction into Y
         alg = float(level_bytes(lay, sv, sv).sum() + last_emit + alpha * (8 + sv) + m * sv + 8 * n * sv +
                     9 * n * sv)
+        # the same sweep without a terminal array (leaves evaluated in place)
+        Yl = dev.sweep_right_batch(X, leaves_in_sweep=True)
+        dev.check()
+        if not torch.equal(Yl, Y):
+            raise SystemExit(f"batched sweep with leaves in the sweep (B={B}) differs")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dev.sweep_right_batch(X, Yl, leaves_in_sweep=True)
+        torch.cuda.synchronize()
+        ms_leaves = (time.perf_counter() - t0) * 1e3 / steps
+        del Yl
         Z = torch.sparse.mm(A, X)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -147,7 +159,9 @@ def bench_batched(torch, gcs, oracle, synth, dev, lay, rp, col, val, spec, elem,
         out.append({"B": B, "ms_per_sweep": ms, "ms_per_vector": ms / B, "nnz_per_s": nnz * B / (ms * 1e-3),
                     "alg_bytes_per_sweep": alg, "achieved_GBs": alg / (ms * 1e-3) / 1e9,
                     "frac_hbm_peak": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "max_rel_err_sampled": worst,
-                    "workspace_bytes": dev.batch_workspace_bytes(B), "rocsparse_spmm_ms": ms_csr})
+                    "workspace_bytes": dev.batch_workspace_bytes(B), "rocsparse_spmm_ms": ms_csr,
+                    "leaves_in_sweep": {"ms_per_sweep": ms_leaves,
+                                        "workspace_bytes": dev.batch_workspace_bytes(B, leaves_in_sweep=True)}})
         log(f"batched B={B}: {ms:.3f} ms per sweep ({ms / B:.4f} ms per vector), rocSPARSE SpMM {ms_csr:.3f} ms")
     del A, crow
     torch.cuda.empty_cache()

@@ -625,7 +625,7 @@ __device__ __forceinline__ void issue_before_row(const T& r)
 
 // One level of the batched sweep; each lane takes VW consecutive vectors of
 // a node (vb_log2 counts lanes per node: 2^vb_log2 >= B / VW).
-template <class P, int VW>
+template <class P, int VW, bool LEAVES>
 __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typename P::A* __restrict__ arena_a,
                                                              typename P::A* __restrict__ acc_a)
 {
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     // the row element of reference c: a stored value, or a leaf computed in
     // place (same arithmetic as the leaf kernel)
     auto fetch = [&](int32_t c) -> R {
-        if (c >= ba.leaf_alpha) return arena[(int64_t)(c - ba.tbase) * W + vw];
+        if (!LEAVES || c >= ba.leaf_alpha) return arena[(int64_t)(c - ba.tbase) * W + vw];
         using XR = Row<typename P::X, VW>;
         const typename P::W v = ((const typename P::W*)ba.V)[ba.tval[c]];
         const XR xr = ((const XR*)ba.X)[(int64_t)ba.tcol[c] * W + vw];
@@ -1290,6 +1290,19 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     return GCS_OK;
 }
 
+template <class P, bool LEAVES>
+void launch_level_batch(int VW, int64_t grid, const BatchArgs& ba, typename P::A* arena, typename P::A* acc,
+                        hipStream_t s)
+{
+    switch (VW) {
+    case 1: level_batch_kernel<P, 1, LEAVES><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+    case 2: level_batch_kernel<P, 2, LEAVES><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+    case 4: level_batch_kernel<P, 4, LEAVES><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+    case 8: level_batch_kernel<P, 8, LEAVES><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+    default: level_batch_kernel<P, 16, LEAVES><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
+    }
+}
+
 // Y = M X for B vectors: leaf, one launch per level k = 1..L+1 (level k and
 // the emission of level k-1), slice reduction into Y.
 template <class P>
@@ -1338,13 +1351,8 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
         ba.pb_emit = ceil_div(mg, per);
         const int64_t grid = (int64_t)kSlices * (ba.pb_bin + ba.pb_pt + ba.pb_emit);
         if (grid <= 0) continue;
-        switch (VW) {
-        case 1: level_batch_kernel<P, 1><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
-        case 2: level_batch_kernel<P, 2><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
-        case 4: level_batch_kernel<P, 4><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
-        case 8: level_batch_kernel<P, 8><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
-        default: level_batch_kernel<P, 16><<<(int32_t)grid, kBlock, 0, s>>>(ba, arena, acc); break;
-        }
+        if (leaves) launch_level_batch<P, true>(VW, grid, ba, arena, acc, s);
+        else launch_level_batch<P, false>(VW, grid, ba, arena, acc, s);
     }
     const int64_t n = d->n_rows * B;
     if (n > 0) {
