@@ -55,6 +55,9 @@ def level_bytes(lay, elem, yelem):
 
 
 def cpu_baseline(rp, col, val, x64, nnz, budget_s=10.0):
+    """The oracle (fp64 compensated CSR SpMV) on all host cores over the full
+    matrix for about budget_s, then on one core over a row sample of about a
+    fifth of that time (context: the single-thread rate)."""
     import oracle
     passes, t0 = 0, time.perf_counter()
     while True:
@@ -63,8 +66,25 @@ def cpu_baseline(rp, col, val, x64, nnz, budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= 50:
             break
-    return {"value": nnz * passes / el, "unit": "nnz/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the full matrix, {passes} fp64 compensated CSR passes ({el:.1f} s)"}
+    cores = oracle.num_threads()
+    out = {"value": nnz * passes / el, "unit": "nnz/s", "cores": cores, "kind": "oracle",
+           "sample": f"the full matrix, {passes} fp64 compensated CSR passes ({el:.1f} s)"}
+    # one core: every k-th row, sized to about budget_s / 5 at the single-thread rate
+    n = rp.shape[0] - 1
+    per_core = nnz * passes / el / max(cores, 1)
+    k = max(1, int(np.ceil(nnz / (per_core * budget_s / 5))))
+    rows = np.arange(0, n, k)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.spmv_f64_rows(rows, rp, col, val, x64)
+        el1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
+    nnz1 = int((rp[rows + 1] - rp[rows]).sum())
+    out["one_core"] = {"value": nnz1 / el1, "unit": "nnz/s",
+                       "sample": f"rows 0, {k}, {2 * k}, ... ({rows.size} rows, {nnz1} nonzeros, {el1:.1f} s)"}
+    return out
 
 
 def csr_comparator(torch, rp, col, val, x, steps):
@@ -431,9 +451,23 @@ def main():
         dev.sweep_right_profiled(xs[i % len(xs)], y)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    span_ms = float(dev.profile_end()[:, 0].mean())
+    spans = dev.profile_end()[:, 0]
+    span_ms = float(spans.mean())
     dev.check()
     ms_per_step = elapsed * 1e3 / args.steps
+    # sustained: back-to-back sweeps for at least 1.5 s (after the timed region)
+    torch.cuda.synchronize()
+    t0, sweeps = time.perf_counter(), 0
+    while True:
+        for i in range(50):
+            dev.sweep_right(xs[i % len(xs)], y)
+        sweeps += 50
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= 1.5:
+            break
+    sustained = {"seconds": time.perf_counter() - t0, "sweeps": sweeps}
+    sustained["nnz_per_s"] = nnz * sweeps / sustained["seconds"]
+    dev.check()
     # breakdown (after the timed region): events around every launch, which
     # add a gap between launches, so these sum to more than a clean sweep
     dev.profile_begin(args.steps, gcs.PROFILE_LAUNCHES)
@@ -524,6 +558,8 @@ def main():
             "per_level_widest": per_level[widest] if per_level else None,
             "wide_levels": nwide,
             "level_span_us": span_ms * 1e3,
+            "level_span_us_median": float(np.median(spans) * 1e3),
+            "sustained": sustained,
             "level_us_total_launch_events": float(lvl_ms.sum() * 1e3),
             "leaf_us": float(launch_ms[:, 0].mean() * 1e3),
             "tail_us": tail_ms * 1e3,
