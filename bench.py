@@ -571,6 +571,7 @@ def main():
                      "kernel": "level_kernel (the wide levels of a sweep, one launch each; timed from before the "
                                "first to after the last, gaps between launches included)",
                      "launches": int(nwide), "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
+                     "achieved_from_traffic": (traffic / (span_ms * 1e-3 / max(nwide, 1)) / 1e9) if traffic else None,
                      "bytes_per_launch_avg": float(lb.sum() / max(nwide, 1)),
                      "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,
