@@ -233,7 +233,7 @@ static gcs_status load_grammar(const char* path, gcs_grammar** out)
     // count fails here instead of allocating)
     const uint64_t big = (uint64_t)1 << 40;
     std::vector<int64_t> lvw;
-    bool ok = r.array(g.V, 1 << 24) && r.array(g.tcol, (uint64_t)g.arena) && r.array(g.tval, g.tcol.size()) &&
+    bool ok = r.array(g.V, (uint64_t)g.nnz + 1) && r.array(g.tcol, (uint64_t)g.arena) && r.array(g.tval, g.tcol.size()) &&
               r.array(g.ra, big) && r.array(g.rb, g.ra.size()) && r.array(g.c_off, (uint64_t)g.n_rows + 1) &&
               r.array(g.c_sym, big) && r.array(g.lvl, g.ra.size()) && r.array(g.plast, g.ra.size()) &&
               r.array(lvw, (uint64_t)(L + 1) * gcs::kLevelWords) && r.array(g.child, 2 * g.ra.size()) &&

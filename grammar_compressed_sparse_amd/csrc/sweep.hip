@@ -812,7 +812,8 @@ struct gcs_device {
     const gcs::LevelArgs* tail_table = nullptr;
     gcs::FlatArgs flat{};      // the narrowest tail launches, run in LDS by one workgroup
     size_t flat_lds = 0;       // dynamic LDS bytes of the tail launch
-    bool flat_attr = false;    // the tail kernel's dynamic LDS limit has been raised
+    size_t flat_budget = 0;    // LDS budget of that phase on this device (the same for every handle)
+    bool flat_attr = false;    // the tail kernel's dynamic LDS limit has been raised to flat_budget
     int64_t* pinned;
     // profiling
     std::vector<hipEvent_t> events;
@@ -1271,9 +1272,11 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         FlatArgs flat = d->flat;
         unsigned* bar = d->barrier;
         int* errp = d->err;
+        // the limit is a property of the kernel, shared by every handle: all
+        // of them raise it to the same device budget (never lower it)
         if (d->flat_lds > 65536 && !d->flat_attr) {
             hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&tail_kernel<P>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)d->flat_lds);
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)d->flat_budget);
             if (ea != hipSuccess) return hip_fail(ea, "hipFuncSetAttribute (tail LDS)");
             d->flat_attr = true;
         }
@@ -1536,6 +1539,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         int max_lds = 0;
         (void)hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 2048));
+        d->flat_budget = budget;
         gcs::FlatImage fi;
         if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), fi)) {
             delete d;

@@ -263,3 +263,27 @@ def test_loaded_grammar_sweeps_identically(env, synth_mod, c1, tmp_path):
     assert torch.equal(da.sweep_right_batch(X), db.sweep_right_batch(X))
     da.check()
     db.check()
+
+
+def test_handles_with_different_lds_images_interleave(env, oracle_mod, synth_mod, c1, monkeypatch):
+    """Uploads whose narrow-level LDS images differ in size sweep in any
+    interleaving (the kernel's dynamic-LDS limit is shared by all handles)."""
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    x = synth_mod.normal(spec.n_cols, 406)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    devs = []
+    for wgs, vb, flat in (("8", "1000000", "100000000"), ("16", "1", "4096"), ("8", "4", "2048")):
+        monkeypatch.setenv("GCS_TAIL_WGS", wgs)
+        monkeypatch.setenv("GCS_TAIL_VB", vb)
+        monkeypatch.setenv("GCS_TAIL_FLAT", flat)
+        devs.append(gcs.upload(g, gcs.PLUS_F64))
+    xt = torch.from_numpy(x).cuda()
+    ref = None
+    for d in devs + devs[::-1] + devs:
+        y = d.sweep_right(xt).cpu().numpy()
+        d.check()
+        _rel_ok(y, yo, absum, 1e-12)
+        if ref is None:
+            ref = y
+        assert np.array_equal(y, ref)
