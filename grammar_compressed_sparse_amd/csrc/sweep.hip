@@ -123,6 +123,15 @@ struct PolMinPlusF64 {
     __device__ static A ident() { return __builtin_huge_val(); }
 };
 
+// Policies whose emission is an idempotent store: OR never needs the value
+// already in y, so a lane whose partial OR is 1 stores 1 into y[row] and
+// every racing writer writes the same byte (the result is the same in any
+// order).  Their sweep has no slice accumulators and no final reduction.
+template <class P>
+constexpr bool kDirectEmit = false;
+template <>
+constexpr bool kDirectEmit<PolBoolOr> = true;
+
 // lane exchange inside a wave for every arena type
 __device__ inline double xchg(double v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline float xchg(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -300,6 +309,13 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     const int32_t graw = a.gsl[x] + (gl >> a.team_log2), sub = gl & (team - 1);
     const bool valid = graw < gend;
     const int32_t g = valid ? graw : gend - 1;
+    if constexpr (kDirectEmit<P>) {
+        // acc is y itself: store 1 where this lane's roots OR to 1
+        const A part = emit_rounds<P>(a.epos, a.eoff[g] + sub, a.eoff[g + 1], team, valid,
+                                      [&](int32_t c) { return arena[c]; });
+        if (valid && part) acc[a.erow[g]] = 1;
+        return;
+    }
     // the accumulator is read beside the roots (its address needs only the
     // group's row), not after the team has combined them
     A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
@@ -450,7 +466,7 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
     // fold: item i < n_prev stages slot n_terms + i, the rest accumulators
     {
         const int32_t* stage = iw + f.stage_word;
-        const int32_t n_prev = f.n_stage - f.n_terms, n = n_prev + f.n_fold;
+        const int32_t n_prev = f.n_stage - f.n_terms, n = n_prev + (kDirectEmit<P> ? 0 : f.n_fold);
         for (int32_t i0 = tid; i0 < n; i0 += kStageItems * kTailBlock) {
             A v[kStageItems];
 #pragma unroll
@@ -498,9 +514,16 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
     const int32_t* foff = iw + f.foff_word;
     const uint16_t* flist = (const uint16_t*)(iw + f.flist_word);
     for (int32_t i = tid; i < f.n_fold; i += kTailBlock) {
-        A a = accv[i];
-        for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
-        acc[facc[i]] = a;
+        if constexpr (kDirectEmit<P>) {
+            // fold i is a row of y: set it if any of its sums is set
+            A a = P::ident();
+            for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
+            if (a) acc[facc[i]] = 1;
+        } else {
+            A a = accv[i];
+            for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
+            acc[facc[i]] = a;
+        }
     }
 }
 
@@ -544,11 +567,13 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
         if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    for (int32_t r = blockIdx.x * kTailBlock + threadIdx.x; r < n_rows; r += gridDim.x * kTailBlock) {
-        typename P::A s = acc[r];
+    if constexpr (!kDirectEmit<P>) {
+        for (int32_t r = blockIdx.x * kTailBlock + threadIdx.x; r < n_rows; r += gridDim.x * kTailBlock) {
+            typename P::A s = acc[r];
 #pragma unroll
-        for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
-        y[r] = P::emit(accumulate ? y[r] : P::yzero(), s);
+            for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
+            y[r] = P::emit(accumulate ? y[r] : P::yzero(), s);
+        }
     }
 }
 
@@ -923,7 +948,8 @@ struct FlatImage {
 // (nodes plus emission lanes) at most flat_max, all slots and sums below 2^16,
 // the LDS part within budget.  Then rewrites every reference as a slot.
 // Returns false (with the error set) only if a reference breaks the layering.
-bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budget, int64_t flat_max, FlatImage& fi)
+bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budget, int64_t flat_max, bool direct,
+                FlatImage& fi)
 {
     const int64_t nent = d->tail_nent, k0 = d->tail_k0, alpha = g.alpha();
     auto width = [&](int64_t k) -> int64_t { return k >= 1 && k <= g.L ? g.lv[k].nb + g.lv[k].npt : 0; };
@@ -1031,7 +1057,9 @@ bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budge
             const int64_t G = pl.grp_off + gi;
             for (int32_t e2 = g.eoff[G]; e2 < g.eoff[G + 1]; ++e2) roots.push_back(map(g.epos[e2], j));
             goff.push_back((int32_t)roots.size());
-            folds.push_back({(int32_t)(x * g.n_rows + g.erow[G]), sums + (int32_t)gi});
+            // fold key: the row's slice accumulator, or the row of y itself
+            // for a direct (idempotent) emission
+            folds.push_back({(int32_t)(direct ? g.erow[G] : x * g.n_rows + g.erow[G]), sums + (int32_t)gi});
         }
         sums += (int32_t)pl.ngrp;
     }
@@ -1238,15 +1266,17 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
 {
     using A = typename P::A;
     auto* arena = (A*)d->arena;
-    auto* acc = (A*)d->acc;
     auto* y = (typename P::Y*)yv;
+    // direct emission writes y itself (cleared by the leaf launch unless
+    // accumulating); otherwise the slice accumulators, reduced into y at the end
+    auto* acc = kDirectEmit<P> ? (A*)yv : (A*)d->acc;
     // profiling: events[2i] before launch i, events[2i+1] right after it; or
     // (span) events[0] before the first wide level launch, events[1] after the last
     int64_t li = 0;
     auto mark = [&]() {
         if (ev && !span) (void)hipEventRecord(ev[li++], s);
     };
-    const int32_t n_acc = (int32_t)(kSlices * d->n_rows);
+    const int32_t n_acc = kDirectEmit<P> ? (accumulate ? 0 : (int32_t)d->n_rows) : (int32_t)(kSlices * d->n_rows);
     if (has_leaf(d)) {
         mark();
         leaf_kernel<P><<<std::max(1, ceil_div(std::max<int64_t>(d->alpha, n_acc), kBlock)), kBlock, 0, s>>>(
@@ -1541,7 +1571,8 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 2048));
         d->flat_budget = budget;
         gcs::FlatImage fi;
-        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), fi)) {
+        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), p == GCS_BOOL_OR,
+                             fi)) {
             delete d;
             return GCS_ESTATE;
         }
