@@ -123,14 +123,40 @@ struct PolMinPlusF64 {
     __device__ static A ident() { return __builtin_huge_val(); }
 };
 
-// Policies whose emission is an idempotent store: OR never needs the value
-// already in y, so a lane whose partial OR is 1 stores 1 into y[row] and
-// every racing writer writes the same byte (the result is the same in any
-// order).  Their sweep has no slice accumulators and no final reduction.
+// Policies whose emission goes straight into y because the combination is
+// idempotent and exact, so its result does not depend on the order of the
+// writers: OR (a lane whose partial OR is 1 stores 1; racing writers write
+// the same byte) and min (an atomic minimum).  Their sweep has no slice
+// accumulators and no final reduction.  direct(p, v) folds a lane's partial
+// v into *p; the identity is a no-op.
 template <class P>
 constexpr bool kDirectEmit = false;
 template <>
 constexpr bool kDirectEmit<PolBoolOr> = true;
+template <>
+constexpr bool kDirectEmit<PolMinPlusF32> = true;
+template <>
+constexpr bool kDirectEmit<PolMinPlusF64> = true;
+
+__device__ __forceinline__ void direct(uint8_t* p, uint8_t v)
+{
+    if (v) *p = 1;
+}
+// IEEE order of non-negative floats is the order of their bits as signed
+// integers, and of negative floats the reverse order of their bits as
+// unsigned integers, so min is an integer min or an unsigned max
+__device__ __forceinline__ void direct(float* p, float v)
+{
+    if (!(v < __builtin_huge_valf())) return;
+    if (v >= 0.0f) atomicMin((int*)p, __float_as_int(v));
+    else atomicMax((unsigned int*)p, __float_as_uint(v));
+}
+__device__ __forceinline__ void direct(double* p, double v)
+{
+    if (!(v < __builtin_huge_val())) return;
+    if (v >= 0.0) atomicMin((long long*)p, __double_as_longlong(v));
+    else atomicMax((unsigned long long*)p, (unsigned long long)__double_as_longlong(v));
+}
 
 // lane exchange inside a wave for every arena type
 __device__ inline double xchg(double v, int m) { return __shfl_xor(v, m, 64); }
@@ -313,7 +339,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
         // acc is y itself: store 1 where this lane's roots OR to 1
         const A part = emit_rounds<P>(a.epos, a.eoff[g] + sub, a.eoff[g + 1], team, valid,
                                       [&](int32_t c) { return arena[c]; });
-        if (valid && part) acc[a.erow[g]] = 1;
+        if (valid) direct(acc + a.erow[g], part);
         return;
     }
     // the accumulator is read beside the roots (its address needs only the
@@ -515,10 +541,10 @@ __device__ __noinline__ void flat_phase(const FlatArgs f, const typename P::A* _
     const uint16_t* flist = (const uint16_t*)(iw + f.flist_word);
     for (int32_t i = tid; i < f.n_fold; i += kTailBlock) {
         if constexpr (kDirectEmit<P>) {
-            // fold i is a row of y: set it if any of its sums is set
+            // fold i is a row of y: fold its sums into it
             A a = P::ident();
             for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
-            if (a) acc[facc[i]] = 1;
+            direct(acc + facc[i], a);
         } else {
             A a = accv[i];
             for (int32_t k = foff[i]; k < foff[i + 1]; ++k) a = P::comb(a, gsum[flist[k]]);
@@ -728,8 +754,10 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     const int32_t graw = gfirst + slot;
     const bool valid = graw < gend;
     const int32_t g = valid ? graw : gend - 1;
-    R* r = acc + ((int64_t)x * a.n_rows + a.erow[g]) * W + vw;
-    const R old = *r;
+    // direct policies: acc is Y itself (no slices)
+    R* r = acc + ((kDirectEmit<P> ? 0 : (int64_t)x * a.n_rows) + a.erow[g]) * W + vw;
+    R old;
+    if constexpr (!kDirectEmit<P>) old = *r;
     const int32_t e0 = a.eoff[g], e1 = a.eoff[g + 1];
     R s;
 #pragma unroll
@@ -749,8 +777,14 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
             if (e + u < e1) s = comb_row<P, VW>(s, v[u]);
         e += kEmitItems;
     } while (valid && e < e1);
-    issue_before_row(old);
-    if (valid && live) *r = comb_row<P, VW>(old, s);
+    if constexpr (kDirectEmit<P>) {
+        if (valid && live)
+#pragma unroll
+            for (int k = 0; k < VW; ++k) direct(&r->v[k], s.v[k]);
+    } else {
+        issue_before_row(old);
+        if (valid && live) *r = comb_row<P, VW>(old, s);
+    }
 }
 
 template <class P>
@@ -1346,14 +1380,16 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
     const bool leaves = (flags & GCS_BATCH_LEAVES_IN_SWEEP) != 0;
     const int32_t accumulate = (flags & GCS_BATCH_ACCUMULATE) ? 1 : 0;
     auto* arena = (A*)ws;
-    auto* acc = (A*)((unsigned char*)ws + batch_arena_bytes(batch_arena_rows(d, flags), d->policy, B));
+    // direct policies emit into Y itself (cleared here unless accumulating)
+    auto* acc = kDirectEmit<P> ? (A*)yv
+                               : (A*)((unsigned char*)ws + batch_arena_bytes(batch_arena_rows(d, flags), d->policy, B));
     // widest access of at most 16 bytes that divides the row
     int VW = 1;
     while (VW * 2 * (int)sizeof(A) <= 16 && B % (VW * 2) == 0) VW *= 2;
     int vb_log2 = 0;
     while ((1 << vb_log2) < B / VW) ++vb_log2;
     const int32_t per = kBlock >> vb_log2;
-    const int64_t n_acc = (int64_t)kSlices * d->n_rows * B;
+    const int64_t n_acc = kDirectEmit<P> ? (accumulate ? 0 : d->n_rows * B) : (int64_t)kSlices * d->n_rows * B;
     // the terminal array (unless the leaves are evaluated in the sweep) and
     // the accumulator clear
     const int64_t t_rows = leaves ? 0 : d->alpha;
@@ -1388,7 +1424,7 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
         else launch_level_batch<P, false>(VW, grid, ba, arena, acc, s);
     }
     const int64_t n = d->n_rows * B;
-    if (n > 0) {
+    if (n > 0 && !kDirectEmit<P>) {
         const int64_t grid = std::min<int64_t>((n + kBlock - 1) / kBlock, 1 << 16);
         reduce_batch_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(acc, (typename P::Y*)yv, n, accumulate);
     }
@@ -1571,8 +1607,8 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 2048));
         d->flat_budget = budget;
         gcs::FlatImage fi;
-        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), p == GCS_BOOL_OR,
-                             fi)) {
+        const bool direct = p == GCS_BOOL_OR || p == GCS_MIN_PLUS_F32 || p == GCS_MIN_PLUS_F64;
+        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), direct, fi)) {
             delete d;
             return GCS_ESTATE;
         }
