@@ -234,6 +234,21 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     scale_w = rec["copy_bytes"] / (rec["write_kib_copy"] * 1024)
     rec["scale_fetch"], rec["scale_write"] = scale_f, scale_w
     rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] * scale_f + rec["write_bytes_per_launch"] * scale_w
+    # the batched level kernel (context): mean scaled HBM bytes per dispatch
+    # and the summed bytes and kernel time over all of its dispatches
+    bt = {}
+    for tag, d, sc in (("fetch", fetch_dir, scale_f), ("write", write_dir, scale_w)):
+        cc = rows(d, "*counter_collection.csv")
+        v = [float(r["Counter_Value"]) * 1024 * sc for r in cc if "level_batch_kernel" in r["Kernel_Name"]]
+        bt[tag] = (sum(v), len(v))
+    kt_batch = [r for r in stats if "level_batch_kernel" in r["Name"]]
+    if bt["fetch"][1] and kt_batch:
+        total_ns = sum(float(r["TotalDurationNs"]) for r in kt_batch)
+        calls = sum(int(r["Calls"]) for r in kt_batch)
+        per = (bt["fetch"][0] / bt["fetch"][1] + bt["write"][0] / max(bt["write"][1], 1))
+        rec["batch_traffic_bytes_per_dispatch"] = per
+        rec["batch_kernel_avg_ns"] = total_ns / calls
+        rec["batch_traffic_GBs"] = per / (total_ns / calls)
     lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"- calibration: one copy dispatch of {rec['copy_bytes'] / 2**20:.0f} MiB read "
               f"{rec['fetch_kib_copy']:.1f} KiB and wrote {rec['write_kib_copy']:.1f} KiB "
@@ -242,6 +257,10 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
               f"{rec['fetch_bytes_per_launch'] / 1e6:.2f} MB, WRITE {rec['write_bytes_per_launch'] / 1e6:.2f} MB, "
               f"traffic {rec['traffic_bytes_per_launch'] / 1e6:.2f} MB per launch (scaled)",
               f"- kernel source sha256[:16] = {rec['source_sha256']}"]
+    if "batch_traffic_GBs" in rec:
+        lines += [f"- level_batch_kernel (batched sweeps of the same run): {rec['batch_traffic_bytes_per_dispatch'] / 1e6:.2f} "
+                  f"MB of HBM traffic per dispatch on average, {rec['batch_kernel_avg_ns'] / 1e3:.1f} us average "
+                  f"duration: {rec['batch_traffic_GBs']:.0f} GB/s measured"]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(TRAFFIC_FILE, "w") as f:
