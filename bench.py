@@ -523,10 +523,14 @@ def main():
     elem = 4 if wl["dtype"] == "f32" else 8
 
     torch.cuda.init()
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     t = time.perf_counter()
     dev = gcs.upload(g, policy)
     torch.cuda.synchronize()
     upload_s = time.perf_counter() - t
+    upload_peak = torch.cuda.max_memory_allocated() - mem0  # cross-check of the footprint
     xs = [torch.from_numpy(synth.normal(spec.n_cols, s).astype(xdt)).cuda() for s in wl["x_seeds"]]
     y = dev.new_y()
     log(f"uploaded {dev.device_bytes / 1e6:.1f} MB in {upload_s:.2f}s; {dev.sweep_launches()} launches per sweep")
@@ -664,6 +668,7 @@ def main():
             "grammar_bytes_per_s": (8 * st["n_rules"] + 8 * st["n_emit_groups"] + 4 * st["c_len"] +
                                     8 * st["n_terminals"]) / (ms_per_step * 1e-3),
             "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
+            "upload_bytes_torch_peak": int(upload_peak),
             "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
             "csr_rocsparse": csr,
             "batched": batched,
