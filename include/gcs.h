@@ -118,7 +118,7 @@ typedef struct {
     int64_t max_width;     /* w*: widest completed level (= streaming buffer)   */
     int64_t c_len;         /* |C|: symbols of the final sequence                */
     int64_t n_tiles;       /* RePair tiles                                       */
-    int64_t n_emit_groups; /* (row, level) emission groups                      */
+    int64_t n_emit_groups; /* (level, slice, row) emission groups               */
     double t_csrv_ms;      /* CSRV encoding                                      */
     double t_repair_ms;    /* RePair (all tiles, wall time)                      */
     double t_layer_ms;     /* levels + completion + bucketing + layout ("+pt")  */
@@ -193,7 +193,8 @@ void gcs_free_grammar(gcs_grammar* g);
 /* ---- device ----------------------------------------------------------- */
 
 typedef struct {
-    size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, terminals, V) */
+    size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, terminals, V,
+                               launch table, narrow levels' LDS image) */
     size_t workspace_bytes; /* value arena [T | A | B], 8 x n_rows row accumulators, 256-byte counters  */
     int64_t x_len;          /* elements of x (= n_cols)                                                 */
     int64_t y_len;          /* elements of y (= n_rows)                                                 */
@@ -229,14 +230,18 @@ gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, siz
 /* y = M x under the uploaded policy: evaluate the terminal array (and clear
  * the row accumulators), then for k = 1..L evaluate level k and emit the
  * roots of level k-1, then emit level L (section 4.3, Listing 1), and finally
- * y[r] = the combination of row r's 8 slice accumulators.  x_dev holds x_len
- * elements, y_dev y_len elements, both device memory of the policy's types;
- * x is not modified.  Asynchronous on `stream`.  Calls on one device handle
- * share its workspace, so they must be ordered (same stream or synchronised). */
+ * y[r] = the combination of row r's 8 slice accumulators.  The Boolean and
+ * tropical policies emit straight into y instead (OR and min do not depend on
+ * the order of the writers): y is cleared first and there are no
+ * accumulators.  x_dev holds x_len elements, y_dev y_len elements, both
+ * device memory of the policy's types; x is not modified.  Asynchronous on
+ * `stream`.  Calls on one device handle share its workspace, so they must be
+ * ordered (same stream or synchronised). */
 gcs_status gcs_sweep_right(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 
 /* y (+)= M x: as gcs_sweep_right, but row r's result is combined into the
- * existing y[r] (added; OR for the Boolean policy) instead of replacing it.
+ * existing y[r] (added; OR for the Boolean policy, min for the tropical ones)
+ * instead of replacing it.
  * Lets a matrix too large for one grammar be swept as independent column
  * groups (each group its own grammar and upload, rules never spanning
  * columns of two groups), accumulating into one y. */
