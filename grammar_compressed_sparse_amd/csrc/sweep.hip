@@ -1161,6 +1161,18 @@ bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budge
 bool layout_in_bounds(const Grammar& g)
 {
     const int64_t arena = g.arena, alpha = g.alpha();
+    // sizes inside the 32-bit index space and the level table complete
+    if ((int64_t)g.lv.size() != (int64_t)g.L + 1 || alpha > arena || g.epos.size() >= (size_t)INT32_MAX ||
+        g.erow.size() >= (size_t)INT32_MAX || g.child.size() >= (size_t)INT32_MAX ||
+        g.ptsrc.size() >= (size_t)INT32_MAX || g.eoff.size() != g.erow.size() + 1)
+        return false;
+    // each level's emission groups follow the previous level's, ending at the last group
+    int64_t go = 0;
+    for (int k = 0; k <= g.L; ++k) {
+        if (g.lv[k].grp_off != go || g.lv[k].ngrp < 0) return false;
+        go += g.lv[k].ngrp;
+    }
+    if (go != (int64_t)g.erow.size()) return false;
     for (int32_t c : g.child)
         if (c < 0 || c >= arena) return false;
     for (int32_t c : g.ptsrc)

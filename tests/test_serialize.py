@@ -87,3 +87,54 @@ def test_damaged_files_refused(gcs, synth_mod, tmp_path):
         gcs.load_grammar(tmp_path / "does_not_exist.gcs")
     with pytest.raises(gcs.GcsError):
         g.save(tmp_path / "no_such_dir" / "g.gcs")
+
+
+def _checksum(data: bytes) -> int:
+    """The file's trailing checksum (multiply-xorshift over 8-byte words,
+    a partial last word zero-padded), restated to forge consistent files."""
+    M = (1 << 64) - 1
+    h = 0x9E3779B97F4A7C15
+
+    def mix(h, w):
+        h ^= (w + 0x9E3779B97F4A7C15 + ((h << 6) & M) + (h >> 2)) & M
+        h = (h * 0xBF58476D1CE4E5B9) & M
+        return h ^ (h >> 31)
+
+    n = len(data) // 8 * 8
+    for w in np.frombuffer(data[:n], dtype="<u8").tolist():
+        h = mix(h, w)
+    if len(data) > n:
+        h = mix(h, int.from_bytes(data[n:] + b"\0" * (8 - len(data) + n), "little"))
+    return h
+
+
+def test_upload_refuses_a_forged_layout(gcs, synth_mod, tmp_path):
+    """A file with a valid checksum but a child index outside the arena loads,
+    and the upload's bounds check refuses it before touching a device."""
+    import ctypes
+    spec = synth_mod.GenotypeSpec(60, 500, 4, 50.0, 0.01, seed=4)
+    rp, col, val = synth_mod.genotype(spec)
+    g = gcs.build_grammar(rp, col, val, n_cols=spec.n_cols)
+    assert g.stats()["n_rules"] > 0
+    path = tmp_path / "g.gcs"
+    g.save(path)
+    blob = bytearray(path.read_bytes())
+    assert _checksum(bytes(blob[:-8])) == int.from_bytes(blob[-8:], "little")
+    # walk to the child array: header 8 + 16, scalars 80, col_cut 36, times 24
+    off = 8 + 16 + 80 + 36 + 24
+    sizes = [8, 4, 4, 4, 4, 8, 4, 4, 4, 8]  # V tcol tval ra rb c_off c_sym lvl plast levels
+    for sz in sizes:
+        n = int.from_bytes(blob[off:off + 8], "little")
+        off += 8 + n * sz
+    n_child = int.from_bytes(blob[off:off + 8], "little")
+    assert n_child == 2 * g.stats()["n_rules"]
+    blob[off + 8:off + 12] = (1 << 30).to_bytes(4, "little")
+    body = bytes(blob[:-8])
+    blob[-8:] = _checksum(body).to_bytes(8, "little")
+    bad = tmp_path / "forged.gcs"
+    bad.write_bytes(bytes(blob))
+    h = gcs.load_grammar(bad)
+    out = ctypes.c_void_p()
+    st = gcs._lib.gcs_upload(h.handle, gcs.PLUS_F64, ctypes.c_void_p(1 << 20), 1 << 40, ctypes.c_void_p(1 << 21),
+                             1 << 40, None, ctypes.byref(out))
+    assert st == -5 and b"layout check" in gcs._lib.gcs_last_error()
