@@ -188,7 +188,7 @@ def bench_batched(torch, gcs, oracle, synth, dev, lay, rp, col, val, spec, elem,
     return out
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "sweep.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "kernels.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
 
 
