@@ -1,0 +1,101 @@
+"""Degenerate shapes and accumulate mode for every kind of emission (slice
+accumulators: fp64; direct into y: Boolean and tropical), single-vector and
+batched, against the oracle (small integers and exact semirings: exact)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    from grammar_compressed_sparse_amd import gcs
+    return torch, gcs
+
+
+def _matrix(case):
+    if case == "identity":
+        n = m = 700
+        return n, m, np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32)
+    if case == "spine":
+        n, m = 5, 300
+        return n, m, np.arange(n + 1, dtype=np.int64) * m, np.tile(np.arange(m, dtype=np.int32), n)
+    if case == "empty_rows":
+        n, m = 100, 10
+        rp = np.zeros(n + 1, np.int64)
+        rp[51:] = 3
+        return n, m, rp, np.array([1, 4, 9], np.int32)
+    if case == "no_rows":
+        return 0, 10, np.zeros(1, np.int64), np.zeros(0, np.int32)
+    n, m = 10, 0  # no columns
+    return n, m, np.zeros(n + 1, np.int64), np.zeros(0, np.int32)
+
+
+def _x(pol, m, seed):
+    rng = np.random.default_rng(seed)
+    if pol == "bool":
+        return (rng.random(m) < 0.3).astype(np.uint8)
+    return (np.arange(m) % 13 - 6 + seed).astype(np.float64)
+
+
+def _ref(oracle_mod, pol, rp, col, x):
+    if pol == "bool":
+        return oracle_mod.spmv_bool(rp, col, x)
+    if pol == "min_plus_f64":
+        return oracle_mod.spmv_min_plus(rp, col, None, x, np.float64)
+    return oracle_mod.spmv_f64(rp, col, None, x)[0]
+
+
+@pytest.mark.parametrize("case", ["identity", "spine", "empty_rows", "no_rows", "no_cols"])
+@pytest.mark.parametrize("pol", ["f64", "bool", "min_plus_f64"])
+def test_edges_single_and_batched(env, oracle_mod, case, pol):
+    torch, gcs = env
+    n, m, rp, col = _matrix(case)
+    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+    x = _x(pol, m, 1)
+    y = dev.sweep_right(torch.from_numpy(x).cuda())
+    dev.check()
+    assert y.shape == (n,) and np.array_equal(y.cpu().numpy(), _ref(oracle_mod, pol, rp, col, x))
+    X = np.stack([_x(pol, m, s) for s in range(3)], axis=1)
+    Y = dev.sweep_right_batch(torch.from_numpy(np.ascontiguousarray(X)).cuda())
+    dev.check()
+    assert Y.shape == (n, 3)
+    for b in range(3):
+        assert np.array_equal(Y[:, b].cpu().numpy(), _ref(oracle_mod, pol, rp, col, np.ascontiguousarray(X[:, b])))
+
+
+@pytest.mark.parametrize("pol", ["bool", "min_plus_f64", "f64"])
+def test_accumulate_every_emission_kind(env, oracle_mod, synth_mod, pol):
+    """y (+)= M x: added for fp64, OR for Boolean, min for tropical, single
+    and batched, on the 512 x 4096 genotype's column pattern."""
+    torch, gcs = env
+    spec = synth_mod.GENOTYPE_512x4096
+    rp, col, _ = synth_mod.genotype(spec)
+    g = gcs.build_grammar(rp, col, None, n_cols=spec.n_cols)
+    dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+    x = _x(pol, spec.n_cols, 3)
+    y0 = _x(pol, spec.n_rows, 4)
+    yt = torch.from_numpy(y0.copy()).cuda()
+    dev.sweep_right_acc(torch.from_numpy(x).cuda(), yt)
+    dev.check()
+    ref = _ref(oracle_mod, pol, rp, col, x)
+    if pol == "bool":
+        expect = y0 | ref
+    elif pol == "min_plus_f64":
+        expect = np.minimum(y0, ref)
+    else:
+        expect = y0 + ref
+    assert np.array_equal(yt.cpu().numpy(), expect)
+    X = np.stack([_x(pol, spec.n_cols, 5 + b) for b in range(2)], axis=1)
+    Y0 = np.stack([_x(pol, spec.n_rows, 7 + b) for b in range(2)], axis=1)
+    Yt = torch.from_numpy(np.ascontiguousarray(Y0)).cuda()
+    dev.sweep_right_batch(torch.from_numpy(np.ascontiguousarray(X)).cuda(), Yt, accumulate=True)
+    dev.check()
+    for b in range(2):
+        ref = _ref(oracle_mod, pol, rp, col, np.ascontiguousarray(X[:, b]))
+        y0b = Y0[:, b]
+        expect = y0b | ref if pol == "bool" else (np.minimum(y0b, ref) if pol == "min_plus_f64" else y0b + ref)
+        assert np.array_equal(Yt[:, b].cpu().numpy(), expect)
