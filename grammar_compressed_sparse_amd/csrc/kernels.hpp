@@ -147,6 +147,30 @@ __device__ __forceinline__ void direct(double* p, double v)
     else atomicMax((unsigned long long*)p, (unsigned long long)__double_as_longlong(v));
 }
 
+// The Boolean sweep keeps its terminals one bit each: terminal c is bit c % 8
+// of byte c / 8 of T (the leaf launch packs 64 of them per wave with a
+// ballot).  The terminal array is most of what a Boolean sweep gathers from;
+// packed, it is an eighth of the size and an XCD's share of it stays in that
+// XCD's L2.  Level values stay one byte each (0 or 1), and the packed words,
+// ceil(alpha / 64) * 8 bytes, end before the level buffers, which start at
+// alpha rounded up to a multiple of 64.
+template <class P>
+constexpr bool kBitTerms = false;
+template <>
+constexpr bool kBitTerms<PolBoolOr> = true;
+
+// the value of arena reference c (terminals below alpha)
+template <class P>
+__device__ __forceinline__ typename P::A fetch(const typename P::A* __restrict__ arena, int32_t c, int32_t alpha)
+{
+    if constexpr (kBitTerms<P>) {
+        const bool t = c < alpha;
+        return (typename P::A)((arena[t ? c >> 3 : c] >> (t ? c & 7 : 0)) & 1);
+    } else {
+        return arena[c];
+    }
+}
+
 // lane exchange inside a wave for every arena type
 __device__ inline double xchg(double v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline float xchg(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -188,7 +212,14 @@ __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict_
                                                       unsigned* __restrict__ barrier)
 {
     const int32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (i < alpha) T[i] = P::leaf(V[tval[i]], x[tcol[i]]);
+    if constexpr (kBitTerms<P>) {
+        // every lane of the wave takes part in the ballot; lane i of the wave
+        // gives bit i of the word of terminals i0 .. i0 + 63 (i0 = i - lane)
+        const uint64_t w = __ballot(i < alpha && P::leaf(V[tval[i]], x[tcol[i]]));
+        if ((threadIdx.x & 63) == 0 && i < alpha) ((uint64_t*)T)[i >> 6] = w;
+    } else {
+        if (i < alpha) T[i] = P::leaf(V[tval[i]], x[tcol[i]]);
+    }
     if (i < n_acc) acc[i] = P::ident();
     if (i == 0) {  // the tail kernel's grid barrier counts rounds from 0 in every sweep
         barrier[0] = 0;
@@ -275,7 +306,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
         for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * kBlock, end - 1)];
         A v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(arena[c[u].x], arena[c[u].y]);
+        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(fetch<P>(arena, c[u].x, a.alpha), fetch<P>(arena, c[u].y, a.alpha));
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
@@ -296,7 +327,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
         for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * kBlock, end - 1)];
         A v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = arena[src[u]];
+        for (int u = 0; u < kBinItems; ++u) v[u] = fetch<P>(arena, src[u], a.alpha);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
@@ -327,7 +358,7 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     if constexpr (kDirectEmit<P>) {
         // acc is y itself: store 1 where this lane's roots OR to 1
         const A part = emit_rounds<P>(a.epos, a.eoff[g] + sub, a.eoff[g + 1], team, valid,
-                                      [&](int32_t c) { return arena[c]; });
+                                      [&](int32_t c) { return fetch<P>(arena, c, a.alpha); });
         if (valid) direct(acc + a.erow[g], part);
         return;
     }
@@ -336,7 +367,8 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     A* r = acc + (int64_t)x * a.n_rows + a.erow[g];
     const A old = *r;
     const int32_t e1 = a.eoff[g + 1];
-    const A s0 = emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, [&](int32_t c) { return arena[c]; });
+    const A s0 =
+        emit_rounds<P>(a.epos, a.eoff[g] + sub, e1, team, valid, [&](int32_t c) { return fetch<P>(arena, c, a.alpha); });
     issue_before(old);
     const A s = team_combine<P>(s0, team);
     if (valid && sub == 0) *r = P::comb(old, s);
@@ -404,6 +436,7 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
 struct FlatArgs {
     const int32_t* idx;  // the LDS image, idx_words 32-bit words (a multiple of four)
     int32_t idx_words, n_ent, n_stage, n_terms, n_fold;
+    int32_t alpha;  // terminals: arena references below alpha
     // word offsets in the image: entry table at 0, then these arrays
     int32_t goff_word, stage_word, facc_word, foff_word, refs_word, roots_word, flist_word;
     int32_t vals_off, gsum_off, accv_off;  // byte offsets of the value, sum and accumulator arrays in LDS
@@ -420,14 +453,15 @@ __device__ __forceinline__ void block_rounds(int32_t n, int32_t tid, Op op)
                                                               i0 + 2 * kTailBlock < n, i0 + 3 * kTailBlock < n);
 }
 
-// vals[i] = arena[stage[i]] for i in [lo, hi)
-template <class A>
-__device__ __forceinline__ void stage_values(const int32_t* stage, const A* __restrict__ arena, A* vals, int32_t lo,
-                                             int32_t hi, int32_t tid)
+// vals[i] = the value of arena reference stage[i], for i in [lo, hi)
+template <class P>
+__device__ __forceinline__ void stage_values(const int32_t* stage, const typename P::A* __restrict__ arena,
+                                             typename P::A* vals, int32_t lo, int32_t hi, int32_t alpha, int32_t tid)
 {
+    using A = typename P::A;
     block_rounds(hi - lo, tid, [&](int32_t i0, int32_t i1, int32_t i2, int32_t i3, bool l1, bool l2, bool l3) {
-        const A v0 = arena[stage[lo + i0]], v1 = arena[stage[lo + i1]];
-        const A v2 = arena[stage[lo + i2]], v3 = arena[stage[lo + i3]];
+        const A v0 = fetch<P>(arena, stage[lo + i0], alpha), v1 = fetch<P>(arena, stage[lo + i1], alpha);
+        const A v2 = fetch<P>(arena, stage[lo + i2], alpha), v3 = fetch<P>(arena, stage[lo + i3], alpha);
         issue_before(v0);
         issue_before(v1);
         issue_before(v2);
@@ -459,7 +493,7 @@ __device__ __noinline__ void flat_prefetch(const FlatArgs f, const typename P::A
     });
     // the stage indices straight from the image in global memory (the LDS
     // copy is not yet visible to other lanes)
-    stage_values<A>(f.idx + f.stage_word, arena, (A*)(flat_lds + f.vals_off), 0, f.n_terms, tid);
+    stage_values<P>(f.idx + f.stage_word, arena, (A*)(flat_lds + f.vals_off), 0, f.n_terms, f.alpha, tid);
     __syncthreads();
 }
 

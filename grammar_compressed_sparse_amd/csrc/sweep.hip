@@ -320,6 +320,7 @@ bool build_flat(const Grammar& g, const gcs_device* d, size_t elem, size_t budge
     fa.n_ent = (int32_t)n_ent;
     fa.n_stage = (int32_t)n_stage;
     fa.n_terms = (int32_t)terms.size();
+    fa.alpha = (int32_t)alpha;
     fa.n_fold = (int32_t)facc.size();
     fa.vals_off = (int32_t)al16(4 * w.size());
     fa.gsum_off = (int32_t)(fa.vals_off + al16((size_t)n_slots * elem));
@@ -367,7 +368,9 @@ bool layout_in_bounds(const Grammar& g)
     if (g.n_rows * kSlices >= (int64_t)INT32_MAX) return false;
     for (int k = 1; k <= g.L; ++k) {
         const Level& l = g.lv[k];
-        if (l.base < 0 || l.base + l.nb + l.npt > arena) return false;
+        // level buffers start past the terminals rounded up to 64 (room for
+        // the Boolean sweep's packed terminal words)
+        if (l.base < ((alpha + 63) & ~int64_t(63)) || l.base + l.nb + l.npt > arena) return false;
         if (l.child_off != co || l.pt_off != po) return false;
         co += l.nb;
         po += l.npt;
