@@ -195,7 +195,7 @@ __device__ __forceinline__ void issue_before(const T& v)
 
 constexpr int kBlock = 256;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
-constexpr int kEmitItems = 4;  // roots per emission lane loaded before the first combine
+constexpr int kEmitItems = 2;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
 constexpr size_t kFlatLdsMax = 160 * 1024;  // LDS cap of the tail's single-workgroup phase
 constexpr int kFlatEntryWords = 8;  // per narrow launch in that phase's table
@@ -356,10 +356,12 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     const bool valid = graw < gend;
     const int32_t g = valid ? graw : gend - 1;
     if constexpr (kDirectEmit<P>) {
-        // acc is y itself: store 1 where this lane's roots OR to 1
+        // acc is y itself: the team's first lane folds the team's combination
+        // into the row (one store or atomic per group, not one per lane)
         const A part = emit_rounds<P>(a.epos, a.eoff[g] + sub, a.eoff[g + 1], team, valid,
                                       [&](int32_t c) { return fetch<P>(arena, c, a.alpha); });
-        if (valid) direct(acc + a.erow[g], part);
+        const A s = team_combine<P>(part, team);
+        if (valid && sub == 0) direct(acc + a.erow[g], s);
         return;
     }
     // the accumulator is read beside the roots (its address needs only the
@@ -638,6 +640,7 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
 // Same grammar, slices and emission groups as the single-vector sweep; every
 // level is its own launch.
 constexpr int kMaxBatch = 64;
+constexpr int kBatchEmitItems = 4;  // roots per emission lane loaded before the first combine
 
 struct BatchArgs {
     LevelArgs a;                     // the level's launch arguments (pointers, counts, slices)
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     const int64_t vw = min((int64_t)lane_w, W - 1);  // the row element this lane gathers
     // the row element of reference c: a stored value, or a leaf computed in
     // place (same arithmetic as the leaf kernel)
-    auto fetch = [&](int32_t c) -> R {
+    auto row_of = [&](int32_t c) -> R {
         if (!LEAVES || c >= ba.leaf_alpha) return arena[(int64_t)(c - ba.tbase) * W + vw];
         using XR = Row<typename P::X, VW>;
         const typename P::W v = ((const typename P::W*)ba.V)[ba.tval[c]];
@@ -737,7 +740,7 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
         R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(fetch(c[u].x), fetch(c[u].y));
+        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(row_of(c[u].x), row_of(c[u].y));
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
@@ -758,7 +761,7 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
         for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
         R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBinItems; ++u) v[u] = fetch(src[u]);
+        for (int u = 0; u < kBinItems; ++u) v[u] = row_of(src[u]);
 #pragma unroll
         for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
@@ -787,18 +790,18 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     for (int k = 0; k < VW; ++k) s.v[k] = P::ident();
     int32_t e = e0;
     do {
-        int32_t p[kEmitItems];
+        int32_t p[kBatchEmitItems];
 #pragma unroll
-        for (int u = 0; u < kEmitItems; ++u) p[u] = a.epos[min(e + u, e1 - 1)];
-        R v[kEmitItems];
+        for (int u = 0; u < kBatchEmitItems; ++u) p[u] = a.epos[min(e + u, e1 - 1)];
+        R v[kBatchEmitItems];
 #pragma unroll
-        for (int u = 0; u < kEmitItems; ++u) v[u] = fetch(p[u]);
+        for (int u = 0; u < kBatchEmitItems; ++u) v[u] = row_of(p[u]);
 #pragma unroll
-        for (int u = 0; u < kEmitItems; ++u) issue_before_row(v[u]);
+        for (int u = 0; u < kBatchEmitItems; ++u) issue_before_row(v[u]);
 #pragma unroll
-        for (int u = 0; u < kEmitItems; ++u)
+        for (int u = 0; u < kBatchEmitItems; ++u)
             if (e + u < e1) s = comb_row<P, VW>(s, v[u]);
-        e += kEmitItems;
+        e += kBatchEmitItems;
     } while (valid && e < e1);
     if constexpr (kDirectEmit<P>) {
         if (valid && live)

@@ -74,6 +74,20 @@ size_t elem_bytes(gcs_policy p)
     }
     return 0;
 }
+// the policy's emission goes straight into y (no slice accumulators)
+bool direct_emit(gcs_policy p)
+{
+    switch (p) {
+    case GCS_PLUS_F64: return kDirectEmit<PolPlusF64>;
+    case GCS_PLUS_F32: return kDirectEmit<PolPlusF32>;
+    case GCS_PLUS_F32_ACC_F64: return kDirectEmit<PolPlusF32AccF64>;
+    case GCS_BOOL_OR: return kDirectEmit<PolBoolOr>;
+    case GCS_PLUS_I64: return kDirectEmit<PolPlusI64>;
+    case GCS_MIN_PLUS_F32: return kDirectEmit<PolMinPlusF32>;
+    case GCS_MIN_PLUS_F64: return kDirectEmit<PolMinPlusF64>;
+    }
+    return false;
+}
 size_t x_bytes(gcs_policy p) { return p == GCS_PLUS_F32 || p == GCS_PLUS_F32_ACC_F64 ? 4 : elem_bytes(p); }
 size_t y_bytes(gcs_policy p) { return elem_bytes(p); }
 size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
@@ -799,8 +813,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const size_t budget = std::min(gcs::kFlatLdsMax, (size_t)std::max(0, max_lds - 2048));
         d->flat_budget = budget;
         gcs::FlatImage fi;
-        const bool direct = p == GCS_BOOL_OR || p == GCS_MIN_PLUS_F32 || p == GCS_MIN_PLUS_F64;
-        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), direct, fi)) {
+        if (!gcs::build_flat(g, d, gcs::elem_bytes(p), budget, env_int("GCS_TAIL_FLAT", 4096), gcs::direct_emit(p), fi)) {
             delete d;
             return GCS_ESTATE;
         }
