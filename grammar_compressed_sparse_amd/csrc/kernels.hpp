@@ -201,6 +201,8 @@ constexpr size_t kFlatLdsMax = 160 * 1024;  // LDS cap of the tail's single-work
 constexpr int kFlatEntryWords = 8;  // per narrow launch in that phase's table
 constexpr int kStageItems = 8;  // loads per lane in flight while that phase stages its values
 constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words past the arrival counter
+constexpr int kStreamItems = 4;  // roots per lane and round of a stream emission block
+constexpr int kStreamCap = kBlock * kStreamItems;  // roots per round, and the most groups of a stream chunk
 
 template <class P>
 __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict__ tcol,
@@ -238,12 +240,15 @@ struct LevelArgs {
     const int32_t* erow;   // emission groups of the previous level
     const int32_t* eoff;
     const int32_t* epos;
+    const int32_t* chunk;  // stream emission: first group of each chunk of the previous level
     int32_t cur, nb;       // arena offset of this level's buffer; binary node count
     int32_t prev, alpha;   // arena offset of the level below; terminals (arena offsets below alpha)
     int32_t n_rows;        // stride of the per-slice row accumulators
     int32_t team_log2;     // lanes per emission group = 1 << team_log2 (<= 64)
     int32_t pb_bin, pb_pt, pb_emit;  // workgroups per slice in each part
     int32_t bsl[kSlices + 1], psl[kSlices + 1], gsl[kSlices + 1];
+    int32_t stream;              // emission by chunks (stream_block) instead of teams
+    int32_t csl[kSlices + 1];    // chunks of each slice (indices into chunk)
 };
 
 static_assert(sizeof(LevelArgs) % 4 == 0, "LevelArgs is copied as 32-bit words");
@@ -376,6 +381,81 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     if (valid && sub == 0) *r = P::comb(old, s);
 }
 
+// Stream emission, for levels whose groups are short and uneven (a team per
+// group leaves most lanes of a wave idle while its longest group finishes).
+// The host cuts each slice's groups into chunks of consecutive groups with at
+// most kStreamCap roots and kStreamCap groups (a longer group is a chunk of
+// its own).  A block takes one chunk and works in rounds of kStreamCap roots:
+// each lane loads kStreamItems of the round's roots (consecutive lanes read
+// consecutive roots) and puts their values in LDS; then lane j folds the part
+// of the chunk's groups j, j + kBlock, ... that falls in the round, left to
+// right, and keeps its partials for the next round.  Used only where the
+// level's team has one or two lanes, and folded in that team's order: roots
+// 0, 1, 2, ... for one lane; for two, roots 0, 2, 4, ... and 1, 3, 5, ...
+// apart, then the two partials combined as the team's butterfly does.  So
+// the bits do not depend on the mode, and the accumulator still takes one
+// read-modify-write per (slice, row) and level.
+template <class P>
+__device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int32_t tid,
+                                             typename P::A* __restrict__ arena, typename P::A* __restrict__ acc)
+{
+    using A = typename P::A;
+    constexpr int Q = kStreamCap / kBlock;  // groups per lane, at most
+    __shared__ A win[kStreamCap];
+    const int32_t x = b % kSlices, ci = a.csl[x] + b / kSlices;
+    if (ci >= a.csl[x + 1]) return;  // the same for the whole block
+    const int32_t g0 = a.chunk[ci], g1 = ci + 1 < a.csl[x + 1] ? a.chunk[ci + 1] : a.gsl[x + 1];
+    const int32_t r0 = a.eoff[g0], r1 = a.eoff[g1];
+    const int32_t odd = a.team_log2;  // 1: a two-lane team's order (roots at odd places apart)
+    int32_t lo[Q], hi[Q], row[Q];
+    A s0[Q], s1[Q], old[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int32_t g = g0 + tid + q * kBlock, gg = min(g, g1 - 1);
+        lo[q] = a.eoff[gg];
+        hi[q] = g < g1 ? a.eoff[gg + 1] : lo[q];
+        row[q] = a.erow[gg];
+        s0[q] = P::ident();
+        s1[q] = P::ident();
+    }
+    if constexpr (!kDirectEmit<P>) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) old[q] = acc[(int64_t)x * a.n_rows + row[q]];
+    }
+    for (int32_t rb = r0; rb < r1; rb += kStreamCap) {
+        const int32_t n = min(kStreamCap, r1 - rb);
+        int32_t p[kStreamItems];
+#pragma unroll
+        for (int u = 0; u < kStreamItems; ++u) p[u] = a.epos[rb + min(tid + u * kBlock, n - 1)];
+        A v[kStreamItems];
+#pragma unroll
+        for (int u = 0; u < kStreamItems; ++u) v[u] = fetch<P>(arena, p[u], a.alpha);
+#pragma unroll
+        for (int u = 0; u < kStreamItems; ++u) win[tid + u * kBlock] = v[u];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int32_t e1 = min(hi[q], rb + n);
+            for (int32_t e = max(lo[q], rb); e < e1; ++e) {
+                const A v = win[e - rb];
+                if ((e - lo[q]) & odd) s1[q] = P::comb(s1[q], v);
+                else s0[q] = P::comb(s0[q], v);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (g0 + tid + q * kBlock >= g1) continue;
+        const A sum = odd ? P::comb(s0[q], s1[q]) : s0[q];
+        if constexpr (kDirectEmit<P>) {
+            direct(acc + row[q], sum);
+        } else {
+            acc[(int64_t)x * a.n_rows + row[q]] = P::comb(old[q], sum);
+        }
+    }
+}
+
 // One wide level.  By default the grid has one workgroup per virtual block
 // (measured faster on MI355X than a grid capped near the resident count);
 // with a cap, each workgroup strides over the level's virtual blocks.  The
@@ -385,8 +465,11 @@ template <class P>
 __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::A* __restrict__ arena,
                                                        typename P::A* __restrict__ acc)
 {
-    const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit);
-    for (int32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) level_block<P>(a, vb, threadIdx.x, arena, acc);
+    const int32_t nvb = kSlices * (a.pb_bin + a.pb_pt + a.pb_emit), nodes = kSlices * (a.pb_bin + a.pb_pt);
+    for (int32_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+        if (a.stream && vb >= nodes) stream_block<P>(a, vb - nodes, threadIdx.x, arena, acc);
+        else level_block<P>(a, vb, threadIdx.x, arena, acc);
+    }
 }
 
 // Grid-wide barrier for the co-resident tail grid.  bar[0] counts arrivals

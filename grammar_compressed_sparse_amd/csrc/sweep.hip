@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -41,6 +42,9 @@ struct gcs_device {
     unsigned* barrier;             // tail grid barrier counter
     int* err;                      // set by the tail kernel if its barrier timed out
     std::vector<gcs::LevelArgs> largs;  // launch k = 1..L+1 at index k-1
+    const int32_t* chunk = nullptr;     // stream emission chunks of every level (grammar image)
+    std::vector<int64_t> chunk_off;     // per level: first entry of its chunks
+    std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;  // per level: chunks of each slice
     int64_t tail_k0 = 1, tail_nent = 0;  // levels tail_k0..L and the last emission run in the tail kernel
     int64_t tail_multi = 0;              // of which the first tail_multi run on the whole tail grid
     int32_t tail_wgs = 0;
@@ -95,8 +99,48 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, tcol, tval, V, table, flat, total;
+    size_t child, ptsrc, erow, eoff, epos, chunk, tcol, tval, V, table, flat, total;
 };
+
+// Stream emission chunks (see stream_block): per level and slice, runs of
+// consecutive groups with at most kStreamCap roots (a longer group alone)
+// and at most kStreamCap groups; an entry is the level-relative index of a
+// chunk's first group.  Every chunk but a slice's last was closed either by
+// the group limit or because it and the next chunk hold more than kStreamCap
+// roots together, which bounds the count by chunk_bound.
+size_t chunk_bound(const Grammar& g)
+{
+    const size_t G = g.erow.size(), C = g.epos.size(), K = kStreamCap;
+    return (G + K - 1) / K + 2 * ((C + K - 1) / K) + (size_t)kSlices * (g.L + 1) + 1;
+}
+
+void build_chunks(const Grammar& g, std::vector<int32_t>& chunk, std::vector<int64_t>& off,
+                  std::vector<std::array<int32_t, kSlices + 1>>& sl)
+{
+    chunk.clear();
+    off.assign((size_t)g.L + 1, 0);
+    sl.assign((size_t)g.L + 1, {});
+    for (int64_t k = 0; k <= g.L; ++k) {
+        const Level& l = g.lv[k];
+        off[k] = (int64_t)chunk.size();
+        for (int x = 0; x < kSlices; ++x) {
+            sl[k][x] = (int32_t)((int64_t)chunk.size() - off[k]);
+            int64_t gi = l.gsl[x];
+            while (gi < l.gsl[x + 1]) {
+                chunk.push_back((int32_t)gi);
+                int64_t roots = 0, cnt = 0;
+                while (gi < l.gsl[x + 1] && cnt < kStreamCap) {
+                    const int64_t len = g.eoff[l.grp_off + gi + 1] - g.eoff[l.grp_off + gi];
+                    if (cnt > 0 && roots + len > kStreamCap) break;
+                    roots += len;
+                    ++cnt;
+                    ++gi;
+                }
+            }
+        }
+        sl[k][kSlices] = (int32_t)((int64_t)chunk.size() - off[k]);
+    }
+}
 
 inline size_t al16(size_t v) { return (v + 15) & ~size_t(15); }
 
@@ -127,6 +171,8 @@ Image image_layout(const Grammar& g, gcs_policy p)
     o = al256(o + g.eoff.size() * 4);
     m.epos = o;
     o = al256(o + g.epos.size() * 4);
+    m.chunk = o;
+    o = al256(o + chunk_bound(g) * 4);
     m.tcol = o;
     o = al256(o + g.tcol.size() * 4);
     m.tval = o;
@@ -470,6 +516,8 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
     a.erow = d->erow + e.grp_off;
     a.eoff = d->eoff + e.grp_off;
     a.epos = d->epos;
+    a.chunk = d->chunk + d->chunk_off[k - 1];
+    for (int x = 0; x <= kSlices; ++x) a.csl[x] = d->chunk_sl[k - 1][x];
     a.n_rows = (int32_t)d->n_rows;
     a.alpha = (int32_t)d->alpha;
     if (k > d->L) a.prev = (int32_t)e.base;
@@ -480,6 +528,22 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
     a.pb_pt = ceil_div(mp, kBlock * kBinItems);
     a.pb_emit = ceil_div(mg << a.team_log2, kBlock);
     return a;
+}
+
+// Stream emission can replace a team of one or two lanes (stream_block folds
+// in their order).  By default it does where the groups are that short and
+// the level has enough chunks to fill the device: on MI355X it took the
+// launch emitting the copy graph's 1.7e8 groups of bare terminals from 6.62
+// to 5.47 ms, but slowed levels of a few dozen chunks (too few workgroups,
+// each with a longer chain of dependent steps) from 7.5 to 9.8 us.
+constexpr int64_t kStreamMinChunks = 2048;
+bool stream_capable(const gcs_device* d, int64_t k) { return d->team_log2[k] <= 1; }
+bool prefer_stream(const gcs_device* d, const Grammar& g, int64_t k)
+{
+    const Level& l = g.lv[k];
+    if (l.ngrp == 0 || !stream_capable(d, k)) return false;
+    const int64_t roots = g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off];
+    return roots <= 8 * l.ngrp && d->chunk_sl[k][kSlices] >= kStreamMinChunks;
 }
 
 bool has_tail(const gcs_device* d)
@@ -717,6 +781,14 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         }
         }
     }
+    std::vector<int32_t> chunk;
+    std::vector<int64_t> chunk_off;
+    std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;
+    gcs::build_chunks(g, chunk, chunk_off, chunk_sl);
+    if (chunk.size() > gcs::chunk_bound(g)) {
+        gcs::set_error("internal error: more emission chunks than the image holds");
+        return GCS_ESTATE;
+    }
     auto* base = (unsigned char*)grammar_dev;
     struct Sec {
         size_t off;
@@ -725,7 +797,8 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     } secs[] = {
         {im.child, g.child.data(), g.child.size() * 4}, {im.ptsrc, g.ptsrc.data(), g.ptsrc.size() * 4},
         {im.erow, g.erow.data(), g.erow.size() * 4},    {im.eoff, g.eoff.data(), g.eoff.size() * 4},
-        {im.epos, g.epos.data(), g.epos.size() * 4},    {im.tcol, g.tcol.data(), g.tcol.size() * 4},
+        {im.epos, g.epos.data(), g.epos.size() * 4},    {im.chunk, chunk.data(), chunk.size() * 4},
+        {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
     };
     for (const Sec& c : secs) {
@@ -764,6 +837,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->erow = (const int32_t*)(base + im.erow);
     d->eoff = (const int32_t*)(base + im.eoff);
     d->epos = (const int32_t*)(base + im.epos);
+    d->chunk = (const int32_t*)(base + im.chunk);
+    d->chunk_off = std::move(chunk_off);
+    d->chunk_sl = std::move(chunk_sl);
     d->tcol = (const int32_t*)(base + im.tcol);
     d->tval = (const int32_t*)(base + im.tval);
     d->V = base + im.V;
@@ -805,6 +881,27 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     const int64_t quarters = gcs::kTailBlock / gcs::kBlock;
     while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
     d->tail_nent = g.L + 2 - d->tail_k0;
+    // emission mode of each wide launch: chunks where the groups are short
+    // and uneven, teams elsewhere (GCS_EMIT_STREAM = 0 keeps teams, 1 takes
+    // chunks wherever the team has at most two lanes; the bits are the same)
+    {
+        const int forced = env_int("GCS_EMIT_STREAM", -1);
+        for (int64_t k = 1; k < d->tail_k0; ++k) {
+            gcs::LevelArgs& a = d->largs[k - 1];
+            const bool st = forced >= 0 ? forced != 0 && gcs::stream_capable(d, k - 1) : gcs::prefer_stream(d, g, k - 1);
+            if (!st) continue;
+            a.stream = 1;
+            int32_t mc = 0;
+            for (int x = 0; x < gcs::kSlices; ++x) mc = std::max(mc, a.csl[x + 1] - a.csl[x]);
+            a.pb_emit = mc;
+        }
+        if (std::getenv("GCS_UPLOAD_TRACE")) {
+            int n_stream = 0;
+            for (int64_t k = 1; k < d->tail_k0; ++k) n_stream += d->largs[k - 1].stream != 0;
+            std::fprintf(stderr, "[gcs upload] stream emission in %d of %lld wide launches\n", n_stream,
+                         (long long)d->tail_k0 - 1);
+        }
+    }
     // the narrowest entries at the end run on workgroup 0 alone, in LDS: as
     // many as fit its budget, each with at most GCS_TAIL_FLAT work items
     {

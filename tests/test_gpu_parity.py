@@ -287,3 +287,53 @@ def test_handles_with_different_lds_images_interleave(env, oracle_mod, synth_mod
         if ref is None:
             ref = y
         assert np.array_equal(y, ref)
+
+
+@pytest.fixture(scope="module")
+def graph300k(env, synth_mod):
+    torch, gcs = env
+    spec = synth_mod.GraphSpec(300_000, seed=55)
+    rp, col = synth_mod.copy_graph(spec)
+    return spec, gcs.build_grammar(rp, col, None, n_cols=spec.n)
+
+
+def _stream_launches(gcs, g, policy, capfd):
+    capfd.readouterr()
+    dev = gcs.upload(g, policy)
+    err = capfd.readouterr().err
+    n = [int(l.split("stream emission in ")[1].split()[0]) for l in err.splitlines() if "stream emission in" in l]
+    assert len(n) == 1, err
+    return dev, n[0]
+
+
+@pytest.mark.parametrize("pol", ["f64", "f32", "f32_acc_f64", "i64", "bool", "min_plus_f32"])
+def test_stream_emission_bit_identical(env, graph300k, monkeypatch, capfd, pol):
+    """Emission by chunks (stream_block) and by teams give the same bits:
+    chunks forced wherever a level's team has at most two lanes, teams
+    forced everywhere, and the default choice, on the 3e5-node copy graph
+    (whose short groups take chunks by default) for every kind of policy."""
+    torch, gcs = env
+    spec, g = graph300k
+    policy = gcs.POLICY_NAMES[pol]
+    rng = np.random.default_rng(77)
+    x = {"bool": (rng.random(spec.n) < 0.2).astype(np.uint8),
+         "i64": rng.integers(-5, 6, spec.n).astype(np.int64),
+         "f32": rng.standard_normal(spec.n).astype(np.float32),
+         "f32_acc_f64": rng.standard_normal(spec.n).astype(np.float32)}.get(pol, rng.standard_normal(spec.n))
+    if pol == "min_plus_f32":
+        x = x.astype(np.float32)
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    ys, used = {}, {}
+    for mode in ("default", "0", "1"):
+        if mode == "default":
+            monkeypatch.delenv("GCS_EMIT_STREAM", raising=False)
+        else:
+            monkeypatch.setenv("GCS_EMIT_STREAM", mode)
+        dev, used[mode] = _stream_launches(gcs, g, policy, capfd)
+        y = dev.sweep_right(torch.from_numpy(x).cuda())
+        dev.check()
+        ys[mode] = y.cpu().numpy()
+        dev.free()
+    _say(f"{pol}: stream launches default {used['default']}, forced {used['1']}")
+    assert used["0"] == 0 and used["default"] > 0 and used["1"] >= used["default"]
+    assert np.array_equal(ys["0"], ys["default"]) and np.array_equal(ys["1"], ys["default"])
