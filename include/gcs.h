@@ -193,8 +193,8 @@ void gcs_free_grammar(gcs_grammar* g);
 /* ---- device ----------------------------------------------------------- */
 
 typedef struct {
-    size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, terminals, V,
-                               launch table, narrow levels' LDS image) */
+    size_t grammar_bytes;   /* read-only grammar image (child indices, pass-through sources, emit lists, emission
+                               chunk table, terminals, V, launch table, narrow levels' LDS image) */
     size_t workspace_bytes; /* value arena [T | A | B], 8 x n_rows row accumulators, 256-byte counters  */
     int64_t x_len;          /* elements of x (= n_cols)                                                 */
     int64_t y_len;          /* elements of y (= n_rows)                                                 */
