@@ -198,6 +198,27 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def copy_achievable_gbs(torch, mib=2048, reps=10):
+    """Achievable HBM bandwidth on this device: a device-to-device copy of
+    `mib` MiB (read + written bytes / time, HIP events, after two warm-up
+    copies), the practical ceiling beside the 8 TB/s specification."""
+    src = torch.empty(mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)  # 4-byte elements, vectorized copy
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbs = 2 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"achievable copy bandwidth: {gbs:.0f} GB/s ({mib} MiB device-to-device)")
+    return gbs
+
+
 def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     """Turn rocprofv3 CSV output (kernel trace stats; FETCH_SIZE and WRITE_SIZE
     counter collections that include a known-size copy) into the text summary
@@ -634,6 +655,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(rp, col, val, xs[0].cpu().numpy().astype(np.float64), nnz)
 
+    copy_gbs = copy_achievable_gbs(torch)
     traffic = None  # HBM bytes per level_kernel launch from the committed counter profile, if still current
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -689,6 +711,7 @@ def main():
                      "launches": int(max(nwide, 1)),
                      "launch_avg_us": span_ms * 1e3 / nwide if nwide > 0 else tail_ms * 1e3,
                      "achieved_from_traffic": (traffic / (span_ms * 1e-3 / max(nwide, 1)) / 1e9) if traffic else None,
+                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
                      "bytes_per_launch_avg": float(lb.sum() / nwide if nwide > 0 else lb_all.sum()),
                      "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,

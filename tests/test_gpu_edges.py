@@ -99,3 +99,52 @@ def test_accumulate_every_emission_kind(env, oracle_mod, synth_mod, pol):
         y0b = Y0[:, b]
         expect = y0b | ref if pol == "bool" else (np.minimum(y0b, ref) if pol == "min_plus_f64" else y0b + ref)
         assert np.array_equal(Yt[:, b].cpu().numpy(), expect)
+
+
+def _long_group_matrix():
+    """4000 short random rows (3 columns) and 3 rows of 20000 random columns
+    out of 100000: the long rows' bare terminals form (row, slice) groups of
+    about 2400 roots, longer than one chunk round, while the level's mean
+    stays below 8 roots per group (a two-lane team)."""
+    rng = np.random.default_rng(2024)
+    m = 100_000
+    rows = [np.sort(rng.choice(m, 3, replace=False)) for _ in range(4000)]
+    for i in (10, 2000, 3999):
+        rows[i] = np.sort(rng.choice(m, 20_000, replace=False))
+    rp = np.zeros(len(rows) + 1, np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    return len(rows), m, rp, np.concatenate(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("pol", ["f64", "i64", "bool", "min_plus_f64"])
+def test_stream_emission_long_groups(env, oracle_mod, monkeypatch, capfd, pol):
+    """Chunked emission over groups longer than one round (1024 roots) keeps
+    each group's partials across rounds: forced chunks equal forced teams bit
+    for bit and the oracle (fp64 within 1e-12 of the row's absolute sum)."""
+    torch, gcs = env
+    n, m, rp, col = _long_group_matrix()
+    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    rng = np.random.default_rng(5)
+    x = {"bool": (rng.random(m) < 0.01).astype(np.uint8), "i64": rng.integers(-9, 10, m).astype(np.int64)}.get(
+        pol, rng.standard_normal(m))
+    ys, used = {}, {}
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    monkeypatch.setenv("GCS_TAIL_WGS", "8")  # keep the level-1 launch out of the tail
+    for mode in ("0", "1"):
+        monkeypatch.setenv("GCS_EMIT_STREAM", mode)
+        capfd.readouterr()
+        dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+        err = capfd.readouterr().err
+        used[mode] = [int(l.split("stream emission in ")[1].split()[0]) for l in err.splitlines()
+                      if "stream emission in" in l]
+        y = dev.sweep_right(torch.from_numpy(x).cuda())
+        dev.check()
+        ys[mode] = y.cpu().numpy()
+        dev.free()
+    assert used["0"] == [0] and used["1"][0] >= 1, used
+    assert np.array_equal(ys["0"], ys["1"])
+    if pol == "f64":
+        yo, absum = oracle_mod.spmv_f64(rp, col, None, x)
+        assert np.all(np.abs(ys["1"] - yo) <= 1e-12 * absum)
+    else:
+        assert np.array_equal(ys["1"], _ref(oracle_mod, pol, rp, col, x))
