@@ -219,6 +219,66 @@ def copy_achievable_gbs(torch, mib=2048, reps=10):
     return gbs
 
 
+def sweep_breakdown(trace, pol):
+    """Lines describing the launches of one sweep of policy `pol` (leaf_kernel
+    up to the tail_kernel) in a rocprofv3 kernel trace, averaged over the
+    sweeps of the run that have the usual number of launches."""
+    trace = sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
+    sweeps, cur = [], None
+    for r in trace:
+        n = r["Kernel_Name"]
+        if pol not in n:
+            continue
+        short = n.split("(")[0].split("<")[0].replace("void ", "").replace("gcs::", "")
+        if short == "leaf_kernel":
+            cur = []
+            sweeps.append(cur)
+        if cur is not None:
+            cur.append((short, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    sweeps = [sw for sw in sweeps if sw and sw[-1][0] == "tail_kernel"]
+    if not sweeps:
+        return []
+    nl = int(np.median([len(sw) for sw in sweeps]))
+    sweeps = [sw for sw in sweeps if len(sw) == nl]
+    dur = np.array([[(e - b) / 1e3 for _, b, e in sw] for sw in sweeps])
+    span = np.array([(sw[-1][2] - sw[0][1]) / 1e3 for sw in sweeps])
+    mean = dur.mean(axis=0)
+    return ["", f"## One sweep of {pol} ({len(sweeps)} sweeps of {nl} launches)", "",
+            f"- per sweep (medians): kernel time {np.median(dur.sum(axis=1)):.1f} us, first launch start to last "
+            f"launch end {np.median(span):.1f} us",
+            "- mean duration per launch, us: leaf " + f"{mean[0]:.1f}; levels 1-8: " +
+            " ".join(f"{v:.1f}" for v in mean[1:min(9, nl - 1)]) +
+            f"; remaining {max(nl - 10, 0)} wide launches {mean[9:nl - 1].sum():.1f} in total; tail {mean[-1]:.1f}"]
+
+
+def summarize_kernel_trace(kt_dir, out_md, title, commands, policies=("PolBoolOr", "PolMinPlusF32")):
+    """Text summary of a rocprofv3 kernel trace (no counters): the kernel time
+    table and, per policy, the launches of one sweep (leaf_kernel up to the
+    tail_kernel) averaged over the sweeps of the run."""
+    import csv
+    import glob
+
+    def rows(pat):
+        fs = glob.glob(os.path.join(kt_dir, "**", pat), recursive=True)
+        return list(csv.DictReader(open(fs[0]))) if fs else []
+
+    stats = rows("*kernel_stats.csv")
+    lines = [f"# rocprofv3 summary: {title}", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "## Kernel time (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats[:14]:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    trace = rows("*kernel_trace.csv")
+    for pol in policies:
+        lines += sweep_breakdown(trace, pol)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     """Turn rocprofv3 CSV output (kernel trace stats; FETCH_SIZE and WRITE_SIZE
     counter collections that include a known-size copy) into the text summary
@@ -240,6 +300,7 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
         name = r["Name"].split("(")[0].replace("void ", "")
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += sweep_breakdown(rows(kt_dir, "*kernel_trace.csv"), "PolPlusF32")
     rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20}
     for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
         cc = rows(d, "*counter_collection.csv")
@@ -483,6 +544,10 @@ def bench_graph(args, wl, spec):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-kernel-trace":
+        # bench.py --summarize-kernel-trace KT_DIR OUT_MD TITLE "command" ...
+        summarize_kernel_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-rocprof":
         # bench.py --summarize-rocprof KT_DIR FETCH_DIR WRITE_DIR OUT_MD COPY_MIB "command" ...
         summarize_rocprof(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7:])
