@@ -522,6 +522,11 @@ def bench_graph(args, wl, spec):
         raise SystemExit("BFS disagrees with the oracle")
     tropical = bench_tropical(args, torch, gcs, oracle, g, rp, col, spec, src, vis_o, counts_o)
     del g
+    # context: rocSPARSE fp32 CSR SpMV (unit values) on the same graph and frontier
+    csr = None
+    if not args.no_csr:
+        csr = csr_comparator(torch, rp, col, np.ones(nnz, np.float32), f.float(), min(args.steps, 20))
+        log(f"rocSPARSE fp32 CSR SpMV on the graph: {csr}")
     dev_bytes = dev.device_bytes + 2 * spec.n
     csr_bytes = 4 * nnz + 4 * (spec.n + 1) + 2 * spec.n
     out = {
@@ -534,7 +539,8 @@ def bench_graph(args, wl, spec):
                                                   "n_terminals", "n_tiles", "n_emit_groups")},
                    "build_s": build_s, "bfs_passes": len(counts), "bfs_s": bfs_s, "visited": int(vis_o.sum()),
                    "device_bytes": dev_bytes, "csr_bytes_analytic": csr_bytes,
-                   "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes, "tropical": tropical},
+                   "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes, "tropical": tropical,
+                   "csr_rocsparse_fp32": csr},
         "roofline": None,
         "cpu_baseline": {"value": nnz * len(counts_o) / bfs_cpu_s, "unit": "nnz/s", "cores": oracle.num_threads(),
                          "kind": "oracle", "sample": f"the oracle's BFS fixpoint ({len(counts_o)} Boolean passes "
