@@ -8,16 +8,17 @@
 //
 // A sweep: leaf_kernel (terminal array T, clears the row accumulators),
 // level_kernel once per wide level k (binary nodes and pass-through copies of
-// level k, emission of level k-1 into per-slice row accumulators), then one
-// cooperative tail_kernel for the narrow top levels, the last emission and
-// the reduction of the slice accumulators into y.  Child, source and root
-// indices are absolute arena offsets ([T | buffer A | buffer B], level parity
-// applied), so a node reads arena[c] whether c is a terminal or a node of the
-// level below.  Every part of a level is cut into kSlices column slices and
-// workgroup b serves slice b % kSlices, which keeps a slice on one XCD and
-// its gathers in that XCD's L2.  Emission is deterministic (each (level,
-// slice, row) group is combined by one team in a fixed order); the Boolean
-// and tropical policies emit straight into y instead.
+// level k, emission of level k-1 into per-slice row accumulators, by teams
+// or by chunks of short groups), then one cooperative tail_kernel for the
+// narrow top levels, the last emission and the reduction of the slice
+// accumulators into y.  Child, source and root indices are absolute arena
+// offsets ([T | buffer A | buffer B], level parity applied), so one read,
+// fetch(arena, c), serves a terminal and a node of the level below alike
+// (the Boolean policy keeps terminals as bits).  Every part of a level is cut
+// into kSlices column slices and workgroup b serves slice b % kSlices, which
+// keeps a slice on one XCD and its gathers in that XCD's L2.  Emission is
+// deterministic (each (level, slice, row) group is combined in a fixed
+// order); the Boolean and tropical policies emit straight into y instead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -460,7 +461,10 @@ __device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int3
 // (measured faster on MI355X than a grid capped near the resident count);
 // with a cap, each workgroup strides over the level's virtual blocks.  The
 // stride (gridDim.x) is a multiple of kSlices, so a workgroup keeps serving
-// the same slice on the same XCD.
+// the same slice on the same XCD.  The emission part runs by teams
+// (level_block) or, where the host chose it, by chunks (stream_block); a
+// virtual block is the same for all lanes of a workgroup, so the chunk path's
+// workgroup barriers are reached by every lane.
 template <class P>
 __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::A* __restrict__ arena,
                                                        typename P::A* __restrict__ acc)

@@ -5,8 +5,8 @@
 //
 // Device memory (all owned by the caller):
 //   grammar image  child pairs | pass-through sources | emission groups
-//                  (erow, eoff, epos) | terminal descriptors | V | launch
-//                  table | narrow levels' LDS image
+//                  (erow, eoff, epos) | emission chunks | terminal
+//                  descriptors | V | launch table | narrow levels' LDS image
 //   workspace      value arena [T (alpha) | buffer A | buffer B] | slice
 //                  accumulators | counters
 //   batch workspace (batched sweeps only, per call)
