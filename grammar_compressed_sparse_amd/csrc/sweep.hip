@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -43,6 +44,8 @@ struct gcs_device {
     int* err;                      // set by the tail kernel if its barrier timed out
     std::vector<gcs::LevelArgs> largs;  // launch k = 1..L+1 at index k-1
     const int32_t* chunk = nullptr;     // stream emission chunks of every level (grammar image)
+    int32_t l0_sub = 1;                 // level 0's emission cut into this many sub-slices per slice
+    const int32_t *l0row = nullptr, *l0off = nullptr;  // its groups then (rows, root offsets)
     std::vector<int64_t> chunk_off;     // per level: first entry of its chunks
     std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;  // per level: chunks of each slice
     int64_t tail_k0 = 1, tail_nent = 0;  // levels tail_k0..L and the last emission run in the tail kernel
@@ -99,8 +102,163 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, chunk, tcol, tval, V, table, flat, total;
+    size_t child, ptsrc, erow, eoff, epos, chunk, l0row, l0off, tcol, tval, V, table, flat, total;
 };
+
+// roots emitted at level k (the same whether or not level 0's groups are cut)
+inline int64_t level_roots(const Grammar& g, int64_t k)
+{
+    const Level& l = g.lv[k];
+    return l.ngrp > 0 ? g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off] : 0;
+}
+
+// ------------------------------------------------ level-0 emission by sub-slice
+//
+// The emission of level 0 gathers bare terminals: for a large terminal array
+// each slice's share of T (alpha * value bytes / 8) exceeds the 4 MB L2 of
+// its XCD, and a slice's groups, taken in row order, gather from all of it.
+// For the direct policies (whose emission may write a row more than once)
+// the upload cuts every level-0 group further by column sub-slice, S equal
+// parts of the slice's terminal range, and orders a slice's new groups by
+// (sub-slice, row): the workgroups of an XCD then gather from one window of
+// about kLevel0Window bytes at a time.  The permuted roots take the place of
+// level 0's roots in the uploaded root list; the new rows and offsets are
+// their own image section (the grammar's own level-0 groups stay unused).
+// Measured on MI355X, tropical fp32 on the 5e7-node copy graph (25 MB of T
+// per slice): the launch emitting level 0 takes 14.0 ms uncut, 6.95 / 6.68 /
+// 6.50 ms cut into 8 / 13 / 24 sub-slices when few x[j] are finite, and
+// 9.8 / 10.1 / 11.0 ms into 4 / 8 / 10 when all are (every group then ends
+// in an atomic, and more sub-slices mean more groups); a 3 MB window is the
+// compromise.
+constexpr double kLevel0Window = 3.0 * 1024 * 1024;
+constexpr int32_t kLevel0MaxSplit = 64;
+
+// sub-slices per slice for level 0's emission: GCS_LEVEL0_SPLIT forces a
+// count (1: none); otherwise enough for a window of kLevel0Window bytes of T
+// (Boolean terminals are bits), direct policies only
+int32_t level0_subslices(const Grammar& g, gcs_policy p)
+{
+    if (!direct_emit(p) || g.lv.empty() || g.lv[0].ngrp == 0) return 1;
+    if (const char* e = std::getenv("GCS_LEVEL0_SPLIT")) return std::max(1, std::min(kLevel0MaxSplit, std::atoi(e)));
+    const double term_bytes = p == GCS_BOOL_OR ? 0.125 : (double)elem_bytes(p);
+    const double per_slice = (double)g.alpha() * term_bytes / kSlices;
+    return (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
+}
+
+// first terminal of each column slice (terminals are sorted by column)
+std::array<int64_t, kSlices + 1> slice_terms(const Grammar& g)
+{
+    std::array<int64_t, kSlices + 1> t0{};
+    for (int x = 0; x <= kSlices; ++x)
+        t0[x] = x == kSlices ? g.alpha()
+                             : std::lower_bound(g.tcol.begin(), g.tcol.end(), g.col_cut[x]) - g.tcol.begin();
+    return t0;
+}
+
+inline int32_t sub_of(int64_t t, int x, const std::array<int64_t, kSlices + 1>& t0, int32_t S)
+{
+    const int64_t n = t0[x + 1] - t0[x];
+    const int64_t sub = n > 0 ? (t - t0[x]) * S / n : 0;
+    return (int32_t)std::max<int64_t>(0, std::min<int64_t>(S - 1, sub));
+}
+
+// For each slice x, calls fn(x) on a thread of its own.
+template <class Fn>
+void per_slice(Fn fn)
+{
+    std::vector<std::thread> th;
+    for (int x = 0; x < kSlices; ++x) th.emplace_back(fn, x);
+    for (auto& t : th) t.join();
+}
+
+// Level-0 groups after the cut: one per run of equal sub-slice inside a group.
+int64_t level0_split_groups(const Grammar& g, int32_t S)
+{
+    const Level& l = g.lv[0];
+    if (S <= 1) return l.ngrp;
+    const auto t0 = slice_terms(g);
+    std::array<int64_t, kSlices> n{};
+    per_slice([&](int x) {
+        int64_t c = 0;
+        for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
+            int32_t prev = -1;
+            for (int64_t e = g.eoff[l.grp_off + gi]; e < g.eoff[l.grp_off + gi + 1]; ++e) {
+                const int32_t s = sub_of(g.epos[e], x, t0, S);
+                c += s != prev;
+                prev = s;
+            }
+        }
+        n[x] = c;
+    });
+    int64_t total = 0;
+    for (int64_t c : n) total += c;
+    return total;
+}
+
+struct Level0Split {
+    int32_t S = 1;
+    std::vector<int32_t> row, off;  // per new group: its row; root offsets (ngrp + 1 entries)
+    std::vector<int32_t> pos;       // level 0's roots in the new order (root list positions [0, pos.size()))
+    int64_t gsl[kSlices + 1] = {};  // new groups of each slice
+};
+
+// The cut itself: per slice, runs counted per sub-slice, then placed
+// sub-slice major, each sub-slice's runs in the grammar's group (row) order.
+void level0_split(const Grammar& g, int32_t S, Level0Split& out)
+{
+    const Level& l = g.lv[0];
+    const auto t0 = slice_terms(g);
+    const int64_t r0 = g.eoff[l.grp_off], r1 = g.eoff[l.grp_off + l.ngrp];
+    out.S = S;
+    std::array<std::vector<int64_t>, kSlices> ng, nr;
+    per_slice([&](int x) {
+        ng[x].assign(S, 0);
+        nr[x].assign(S, 0);
+        for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
+            int32_t prev = -1;
+            for (int64_t e = g.eoff[l.grp_off + gi]; e < g.eoff[l.grp_off + gi + 1]; ++e) {
+                const int32_t s = sub_of(g.epos[e], x, t0, S);
+                ng[x][s] += s != prev;
+                nr[x][s] += 1;
+                prev = s;
+            }
+        }
+    });
+    std::array<int64_t, kSlices + 1> gbase{};
+    for (int x = 0; x < kSlices; ++x) {
+        int64_t c = 0;
+        for (int64_t v : ng[x]) c += v;
+        gbase[x + 1] = gbase[x] + c;
+    }
+    for (int x = 0; x <= kSlices; ++x) out.gsl[x] = gbase[x];
+    out.row.assign((size_t)gbase[kSlices], 0);
+    out.off.assign((size_t)gbase[kSlices] + 1, 0);
+    out.pos.assign((size_t)(r1 - r0), 0);
+    out.off[gbase[kSlices]] = (int32_t)r1;
+    per_slice([&](int x) {
+        std::vector<int64_t> gs(S), rs(S);
+        int64_t gacc = gbase[x], racc = g.eoff[l.grp_off + l.gsl[x]];
+        for (int32_t s = 0; s < S; ++s) {
+            gs[s] = gacc;
+            rs[s] = racc;
+            gacc += ng[x][s];
+            racc += nr[x][s];
+        }
+        for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
+            const int64_t e0 = g.eoff[l.grp_off + gi], e1 = g.eoff[l.grp_off + gi + 1];
+            int64_t e = e0;
+            while (e < e1) {
+                const int32_t s = sub_of(g.epos[e], x, t0, S);
+                const int64_t gn = gs[s]++;
+                out.row[gn] = g.erow[l.grp_off + gi];
+                out.off[gn] = (int32_t)rs[s];
+                do {
+                    out.pos[rs[s]++ - r0] = g.epos[e++];
+                } while (e < e1 && sub_of(g.epos[e], x, t0, S) == s);
+            }
+        }
+    });
+}
 
 // Stream emission chunks (see stream_block): per level and slice, runs of
 // consecutive groups with at most kStreamCap roots (a longer group alone)
@@ -108,13 +266,15 @@ struct Image {
 // chunk's first group.  Every chunk but a slice's last was closed either by
 // the group limit or because it and the next chunk hold more than kStreamCap
 // roots together, which bounds the count by chunk_bound.
-size_t chunk_bound(const Grammar& g)
+size_t chunk_bound(const Grammar& g, int64_t g0_split)
 {
-    const size_t G = g.erow.size(), C = g.epos.size(), K = kStreamCap;
+    // g0_split: level 0's group count after a sub-slice cut (the larger count bounds both)
+    const size_t G = g.erow.size() - (size_t)g.lv[0].ngrp + (size_t)std::max<int64_t>(g0_split, g.lv[0].ngrp);
+    const size_t C = g.epos.size(), K = kStreamCap;
     return (G + K - 1) / K + 2 * ((C + K - 1) / K) + (size_t)kSlices * (g.L + 1) + 1;
 }
 
-void build_chunks(const Grammar& g, std::vector<int32_t>& chunk, std::vector<int64_t>& off,
+void build_chunks(const Grammar& g, const Level0Split* l0, std::vector<int32_t>& chunk, std::vector<int64_t>& off,
                   std::vector<std::array<int32_t, kSlices + 1>>& sl)
 {
     chunk.clear();
@@ -122,15 +282,19 @@ void build_chunks(const Grammar& g, std::vector<int32_t>& chunk, std::vector<int
     sl.assign((size_t)g.L + 1, {});
     for (int64_t k = 0; k <= g.L; ++k) {
         const Level& l = g.lv[k];
+        // level 0 after a sub-slice cut: its own groups and root offsets
+        const bool cut = k == 0 && l0 && l0->S > 1;
+        const int32_t* eo = cut ? l0->off.data() : g.eoff.data() + l.grp_off;
+        const int64_t* gsl = cut ? l0->gsl : l.gsl;
         off[k] = (int64_t)chunk.size();
         for (int x = 0; x < kSlices; ++x) {
             sl[k][x] = (int32_t)((int64_t)chunk.size() - off[k]);
-            int64_t gi = l.gsl[x];
-            while (gi < l.gsl[x + 1]) {
+            int64_t gi = gsl[x];
+            while (gi < gsl[x + 1]) {
                 chunk.push_back((int32_t)gi);
                 int64_t roots = 0, cnt = 0;
-                while (gi < l.gsl[x + 1] && cnt < kStreamCap) {
-                    const int64_t len = g.eoff[l.grp_off + gi + 1] - g.eoff[l.grp_off + gi];
+                while (gi < gsl[x + 1] && cnt < kStreamCap) {
+                    const int64_t len = eo[gi + 1] - eo[gi];
                     if (cnt > 0 && roots + len > kStreamCap) break;
                     roots += len;
                     ++cnt;
@@ -159,6 +323,8 @@ size_t flat_section_words(const Grammar& g)
 
 Image image_layout(const Grammar& g, gcs_policy p)
 {
+    const int32_t S = level0_subslices(g, p);
+    const int64_t g0 = S > 1 ? level0_split_groups(g, S) : 0;
     Image m{};
     size_t o = 0;
     m.child = o;
@@ -172,7 +338,11 @@ Image image_layout(const Grammar& g, gcs_policy p)
     m.epos = o;
     o = al256(o + g.epos.size() * 4);
     m.chunk = o;
-    o = al256(o + chunk_bound(g) * 4);
+    o = al256(o + chunk_bound(g, g0) * 4);
+    m.l0row = o;
+    o = al256(o + (S > 1 ? (size_t)g0 * 4 : 0));
+    m.l0off = o;
+    o = al256(o + (S > 1 ? (size_t)(g0 + 1) * 4 : 0));
     m.tcol = o;
     o = al256(o + g.tcol.size() * 4);
     m.tval = o;
@@ -515,6 +685,10 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
     const Level& e = d->lv[k - 1];
     a.erow = d->erow + e.grp_off;
     a.eoff = d->eoff + e.grp_off;
+    if (k == 1 && d->l0_sub > 1) {  // level 0's groups cut by sub-slice
+        a.erow = d->l0row;
+        a.eoff = d->l0off;
+    }
     a.epos = d->epos;
     a.chunk = d->chunk + d->chunk_off[k - 1];
     for (int x = 0; x <= kSlices; ++x) a.csl[x] = d->chunk_sl[k - 1][x];
@@ -540,10 +714,9 @@ constexpr int64_t kStreamMinChunks = 2048;
 bool stream_capable(const gcs_device* d, int64_t k) { return d->team_log2[k] <= 1; }
 bool prefer_stream(const gcs_device* d, const Grammar& g, int64_t k)
 {
-    const Level& l = g.lv[k];
-    if (l.ngrp == 0 || !stream_capable(d, k)) return false;
-    const int64_t roots = g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off];
-    return roots <= 8 * l.ngrp && d->chunk_sl[k][kSlices] >= kStreamMinChunks;
+    const int64_t ngrp = d->lv[k].ngrp;  // the device's view (level 0 possibly cut)
+    if (ngrp == 0 || !stream_capable(d, k)) return false;
+    return level_roots(g, k) <= 8 * ngrp && d->chunk_sl[k][kSlices] >= kStreamMinChunks;
 }
 
 bool has_tail(const gcs_device* d)
@@ -781,11 +954,21 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         }
         }
     }
+    // level 0's emission cut by column sub-slice (direct policies, large T)
+    gcs::Level0Split l0;
+    const int32_t l0_sub = gcs::level0_subslices(g, p);
+    if (l0_sub > 1) gcs::level0_split(g, l0_sub, l0);
+    const int64_t r0 = g.lv[0].ngrp > 0 ? g.eoff[g.lv[0].grp_off + g.lv[0].ngrp] : 0;  // level 0's roots: [0, r0)
+    if (l0.S > 1 && ((int64_t)l0.pos.size() != r0 || g.lv[0].grp_off != 0 ||
+                     im.l0off - im.l0row < l0.row.size() * 4)) {
+        gcs::set_error("internal error: level-0 sub-slice cut does not match the image");
+        return GCS_ESTATE;
+    }
     std::vector<int32_t> chunk;
     std::vector<int64_t> chunk_off;
     std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;
-    gcs::build_chunks(g, chunk, chunk_off, chunk_sl);
-    if (chunk.size() > gcs::chunk_bound(g)) {
+    gcs::build_chunks(g, &l0, chunk, chunk_off, chunk_sl);
+    if (chunk.size() > gcs::chunk_bound(g, l0.S > 1 ? (int64_t)l0.row.size() : 0)) {
         gcs::set_error("internal error: more emission chunks than the image holds");
         return GCS_ESTATE;
     }
@@ -797,7 +980,11 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     } secs[] = {
         {im.child, g.child.data(), g.child.size() * 4}, {im.ptsrc, g.ptsrc.data(), g.ptsrc.size() * 4},
         {im.erow, g.erow.data(), g.erow.size() * 4},    {im.eoff, g.eoff.data(), g.eoff.size() * 4},
-        {im.epos, g.epos.data(), g.epos.size() * 4},    {im.chunk, chunk.data(), chunk.size() * 4},
+        // the root list, level 0's part in the sub-slice order when cut
+        {im.epos, l0.S > 1 ? l0.pos.data() : g.epos.data(), (size_t)r0 * 4},
+        {im.epos + (size_t)r0 * 4, g.epos.data() + r0, (g.epos.size() - (size_t)r0) * 4},
+        {im.chunk, chunk.data(), chunk.size() * 4},
+        {im.l0row, l0.row.data(), l0.row.size() * 4},   {im.l0off, l0.off.data(), l0.off.size() * 4},
         {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
     };
@@ -818,15 +1005,22 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->L = g.L;
     d->arena_len = g.arena;
     d->lv = g.lv;
+    if (l0.S > 1) {  // the device's view of level 0: the cut groups
+        d->lv[0].ngrp = (int64_t)l0.row.size();
+        for (int x = 0; x <= gcs::kSlices; ++x) d->lv[0].gsl[x] = l0.gsl[x];
+        d->l0_sub = l0.S;
+        d->l0row = (const int32_t*)(base + im.l0row);
+        d->l0off = (const int32_t*)(base + im.l0off);
+    }
     // emission team per level: about GCS_EMIT_PER_LANE (default 4) roots per
     // lane, at most one wave
     const char* pl_env = std::getenv("GCS_EMIT_PER_LANE");
     const double per_lane = pl_env ? std::max(0.5, std::atof(pl_env)) : 4.0;
     d->team_log2.assign(g.lv.size(), 0);
     for (size_t k = 0; k < g.lv.size(); ++k) {
-        const gcs::Level& l = g.lv[k];
+        const gcs::Level& l = d->lv[k];
         if (l.ngrp == 0) continue;
-        const int64_t roots = g.eoff[l.grp_off + l.ngrp] - g.eoff[l.grp_off];
+        const int64_t roots = gcs::level_roots(g, (int64_t)k);
         const double mean = (double)roots / (double)l.ngrp;
         int t = 0;
         while (t < 6 && (double)(1 << t) * per_lane < mean && (l.ngrp << (t + 1)) < (int64_t)INT32_MAX - gcs::kBlock) ++t;
@@ -880,6 +1074,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tail_k0 = g.L + 1;
     const int64_t quarters = gcs::kTailBlock / gcs::kBlock;
     while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
+    // level 0's cut groups are emitted by a wide launch only (the narrow
+    // levels' LDS image is built from the grammar's own groups)
+    if (d->l0_sub > 1) d->tail_k0 = std::max<int64_t>(d->tail_k0, 2);
     d->tail_nent = g.L + 2 - d->tail_k0;
     // emission mode of each wide launch: chunks where the groups are short
     // and uneven, teams elsewhere (GCS_EMIT_STREAM = 0 keeps teams, 1 takes
@@ -900,6 +1097,8 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
             for (int64_t k = 1; k < d->tail_k0; ++k) n_stream += d->largs[k - 1].stream != 0;
             std::fprintf(stderr, "[gcs upload] stream emission in %d of %lld wide launches\n", n_stream,
                          (long long)d->tail_k0 - 1);
+            std::fprintf(stderr, "[gcs upload] level-0 emission in %d sub-slices per slice (%lld groups, %lld before)\n",
+                         d->l0_sub, (long long)d->lv[0].ngrp, (long long)g.lv[0].ngrp);
         }
     }
     // the narrowest entries at the end run on workgroup 0 alone, in LDS: as

@@ -337,3 +337,38 @@ def test_stream_emission_bit_identical(env, graph300k, monkeypatch, capfd, pol):
     _say(f"{pol}: stream launches default {used['default']}, forced {used['1']}")
     assert used["0"] == 0 and used["default"] > 0 and used["1"] >= used["default"]
     assert np.array_equal(ys["0"], ys["default"]) and np.array_equal(ys["1"], ys["default"])
+
+
+@pytest.mark.parametrize("pol", ["bool", "min_plus_f32", "min_plus_f64"])
+def test_level0_subslice_cut_identical(env, oracle_mod, synth_mod, graph300k, monkeypatch, capfd, pol):
+    """Level-0 emission groups cut by column sub-slice (direct policies)
+    give the same y as the grammar's own groups and as the oracle, single
+    and batched, for several cut counts."""
+    torch, gcs = env
+    spec, g = graph300k
+    rp, col = synth_mod.copy_graph(spec)
+    rng = np.random.default_rng(91)
+    if pol == "bool":
+        x = (rng.random(spec.n) < 0.1).astype(np.uint8)
+        ref = oracle_mod.spmv_bool(rp, col, x)
+    else:
+        dt = np.float32 if pol == "min_plus_f32" else np.float64
+        x = (rng.random(spec.n) * 20).astype(dt)
+        x[rng.random(spec.n) < 0.5] = np.inf
+        ref = oracle_mod.spmv_min_plus(rp, col, None, x, dt)
+    X = np.ascontiguousarray(np.stack([x, x[::-1].copy()], axis=1))
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    for cut in ("1", "3", "16"):
+        monkeypatch.setenv("GCS_LEVEL0_SPLIT", cut)
+        capfd.readouterr()
+        dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+        err = capfd.readouterr().err
+        sub = [int(l.split("level-0 emission in ")[1].split()[0]) for l in err.splitlines() if "level-0 emission in" in l]
+        assert sub == [int(cut)], err
+        y = dev.sweep_right(torch.from_numpy(x).cuda())
+        Y = dev.sweep_right_batch(torch.from_numpy(X).cuda())
+        dev.check()
+        _say(f"{pol} cut {cut}: {err.strip().splitlines()[-1]}")
+        assert np.array_equal(y.cpu().numpy(), ref)
+        assert np.array_equal(Y[:, 0].cpu().numpy(), ref)
+        dev.free()
