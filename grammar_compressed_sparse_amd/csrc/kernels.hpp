@@ -457,6 +457,77 @@ __device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int3
     }
 }
 
+// Level-0 emission of the Boolean policy from LDS.  Level 0's roots are bare
+// terminals, one bit each in T; with level 0's groups cut by column
+// sub-slice, a run of consecutive groups of one sub-slice reads its roots
+// from a window of at most kWinBytes of T.  A workgroup of kWinBlock lanes
+// copies its chunk's window into LDS once (16-byte loads), then:
+//  - a run of short groups (at most kWinLong roots each): lane j takes
+//    groups j, j + kWinBlock, ..., kWinQ of them at a time with all their
+//    index loads issued together, ORs each group's bits from LDS (its first
+//    root first, the rest only while the OR is 0) and stores 1 into its row;
+//  - a long group (one per chunk): the lanes stride over its roots and the
+//    workgroup ORs their bits.
+// A root then costs its 4-byte index in a streamed list instead of an L2
+// request of its own.  Workgroup b takes chunk b: a chunk touches HBM only
+// to stream its lists and load its window once, so it gains nothing from
+// its slice's XCD, and the slices' level-0 work differs.
+constexpr int kWinBlock = 1024;
+constexpr int kWinQ = 8;                  // groups per lane in flight
+constexpr int kWinLong = 64;              // longer groups get a chunk (and the whole workgroup) of their own
+constexpr int32_t kWinBytes = 60 * 1024;  // LDS window: bytes of packed terminals, a multiple of 16
+
+struct WinArgs {
+    // per chunk: first group, end group (-1: one long group), window [b0, b1)
+    // in bytes of T (multiples of 16)
+    const int4* chunk;
+    const int32_t* erow;  // level 0's (cut) groups
+    const int32_t* eoff;
+    const int32_t* epos;
+    int32_t n_chunks;
+};
+
+template <class P>
+__global__ __launch_bounds__(kWinBlock) void window_emit_kernel(WinArgs w, const typename P::A* __restrict__ T,
+                                                                typename P::Y* __restrict__ y)
+{
+    static_assert(kBitTerms<P> && kDirectEmit<P>, "window emission reads terminal bits and stores into y");
+    extern __shared__ __align__(16) unsigned char win[];
+    const int4 ch = w.chunk[blockIdx.x];
+    const int4* src = (const int4*)(T + ch.z);
+    int4* dst = (int4*)win;
+    for (int32_t i = threadIdx.x; i < (ch.w - ch.z) / 16; i += kWinBlock) dst[i] = src[i];
+    __syncthreads();
+    auto bit = [&](int32_t t) -> uint32_t { return (win[(t >> 3) - ch.z] >> (t & 7)) & 1u; };
+    if (ch.y < 0) {  // one long group
+        const int32_t e0 = w.eoff[ch.x], e1 = w.eoff[ch.x + 1];
+        uint32_t v = 0;
+        for (int32_t e = e0 + threadIdx.x; e < e1; e += kWinBlock) v |= bit(w.epos[e]);
+        if (__syncthreads_or((int)v) && threadIdx.x == 0) y[w.erow[ch.x]] = 1;
+        return;
+    }
+    for (int32_t base = ch.x; base < ch.y; base += kWinQ * kWinBlock) {
+        int32_t e0[kWinQ], e1[kWinQ], row[kWinQ];
+#pragma unroll
+        for (int q = 0; q < kWinQ; ++q) {
+            const int32_t gi = min(base + threadIdx.x + q * kWinBlock, ch.y - 1);
+            e0[q] = w.eoff[gi];
+            e1[q] = w.eoff[gi + 1];
+            row[q] = w.erow[gi];
+        }
+        int32_t t[kWinQ];
+#pragma unroll
+        for (int q = 0; q < kWinQ; ++q) t[q] = w.epos[e0[q]];  // every group has a root
+#pragma unroll
+        for (int q = 0; q < kWinQ; ++q) {
+            if (base + threadIdx.x + q * kWinBlock >= ch.y) continue;
+            uint32_t v = bit(t[q]);
+            for (int32_t e = e0[q] + 1; e < e1[q] && !v; ++e) v = bit(w.epos[e]);
+            if (v) y[row[q]] = 1;
+        }
+    }
+}
+
 // One wide level.  By default the grid has one workgroup per virtual block
 // (measured faster on MI355X than a grid capped near the resident count);
 // with a cap, each workgroup strides over the level's virtual blocks.  The

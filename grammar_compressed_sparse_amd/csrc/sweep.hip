@@ -44,7 +44,13 @@ struct gcs_device {
     int* err;                      // set by the tail kernel if its barrier timed out
     std::vector<gcs::LevelArgs> largs;  // launch k = 1..L+1 at index k-1
     const int32_t* chunk = nullptr;     // stream emission chunks of every level (grammar image)
-    int32_t l0_sub = 1;                 // level 0's emission cut into this many sub-slices per slice
+    bool l0_on = false;                 // level 0's emission groups cut by sub-slice
+    int64_t grp_skip = 0;               // groups not uploaded at the start of erow / eoff (level 0's when cut)
+    int32_t l0_sub = 1;                 // into this many sub-slices per slice
+    bool win_on = false;                // Boolean level-0 emission by window_emit_kernel
+    gcs::WinArgs win{};
+    int32_t win_grid = 0;
+    size_t win_lds = 0;
     const int32_t *l0row = nullptr, *l0off = nullptr;  // its groups then (rows, root offsets)
     std::vector<int64_t> chunk_off;     // per level: first entry of its chunks
     std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;  // per level: chunks of each slice
@@ -102,7 +108,7 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, chunk, l0row, l0off, tcol, tval, V, table, flat, total;
+    size_t child, ptsrc, erow, eoff, epos, chunk, l0row, l0off, wchunk, tcol, tval, V, table, flat, total;
 };
 
 // roots emitted at level k (the same whether or not level 0's groups are cut)
@@ -131,19 +137,8 @@ inline int64_t level_roots(const Grammar& g, int64_t k)
 // in an atomic, and more sub-slices mean more groups); a 3 MB window is the
 // compromise.
 constexpr double kLevel0Window = 3.0 * 1024 * 1024;
+constexpr double kWinTarget = 40.0 * 1024;  // Boolean LDS window target (window_emit_kernel)
 constexpr int32_t kLevel0MaxSplit = 64;
-
-// sub-slices per slice for level 0's emission: GCS_LEVEL0_SPLIT forces a
-// count (1: none); otherwise enough for a window of kLevel0Window bytes of T
-// (Boolean terminals are bits), direct policies only
-int32_t level0_subslices(const Grammar& g, gcs_policy p)
-{
-    if (!direct_emit(p) || g.lv.empty() || g.lv[0].ngrp == 0) return 1;
-    if (const char* e = std::getenv("GCS_LEVEL0_SPLIT")) return std::max(1, std::min(kLevel0MaxSplit, std::atoi(e)));
-    const double term_bytes = p == GCS_BOOL_OR ? 0.125 : (double)elem_bytes(p);
-    const double per_slice = (double)g.alpha() * term_bytes / kSlices;
-    return (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
-}
 
 // first terminal of each column slice (terminals are sorted by column)
 std::array<int64_t, kSlices + 1> slice_terms(const Grammar& g)
@@ -162,6 +157,49 @@ inline int32_t sub_of(int64_t t, int x, const std::array<int64_t, kSlices + 1>& 
     return (int32_t)std::max<int64_t>(0, std::min<int64_t>(S - 1, sub));
 }
 
+// How level 0's emission is organized on upload.  Tropical policies: cut
+// into S sub-slices per slice when a slice's share of T exceeds
+// kLevel0Window.  Boolean: cut so that every sub-slice's bits fit one LDS
+// window, emitted by window_emit_kernel (its terminals are bits, so S is
+// small: 13 for 5e7 terminals).  GCS_LEVEL0_SPLIT=S forces a count (0: no
+// cut); GCS_LEVEL0_WINDOW=0 keeps the Boolean emission in the level kernel.
+struct Level0Plan {
+    bool cut = false;     // level 0's groups are cut by sub-slice
+    int32_t S = 1;        // sub-slices per slice
+    bool window = false;  // Boolean level-0 emission from LDS windows
+};
+
+Level0Plan level0_plan(const Grammar& g, gcs_policy p)
+{
+    Level0Plan pl;
+    if (!direct_emit(p) || g.lv.empty() || g.lv[0].ngrp == 0) return pl;
+    const char* ew = std::getenv("GCS_LEVEL0_WINDOW");
+    pl.window = p == GCS_BOOL_OR && !(ew && std::atoi(ew) == 0);
+    // the largest slice's share of T (slices are weighted quantiles of the
+    // first column, so their terminal counts differ)
+    const double term_bytes = p == GCS_BOOL_OR ? 0.125 : (double)elem_bytes(p);
+    const auto t0 = slice_terms(g);
+    int64_t widest = 0;
+    for (int x = 0; x < kSlices; ++x) widest = std::max(widest, t0[x + 1] - t0[x]);
+    const double per_slice = (double)widest * term_bytes;
+    if (const char* e = std::getenv("GCS_LEVEL0_SPLIT")) {
+        pl.S = std::max(0, std::min(kLevel0MaxSplit, std::atoi(e)));
+        pl.cut = pl.S >= 1;
+        pl.S = std::max(1, pl.S);
+    } else if (pl.window) {
+        // the widest slice's terminals in windows of about kWinTarget bytes
+        // (at most kWinBytes with alignment; smaller windows measured faster:
+        // the copy graph's level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB)
+        pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kWinTarget)));
+        pl.cut = true;
+    } else {
+        pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
+        pl.cut = pl.S > 1;
+    }
+    pl.window = pl.window && pl.cut;
+    return pl;
+}
+
 // For each slice x, calls fn(x) on a thread of its own.
 template <class Fn>
 void per_slice(Fn fn)
@@ -171,35 +209,49 @@ void per_slice(Fn fn)
     for (auto& t : th) t.join();
 }
 
-// Level-0 groups after the cut: one per run of equal sub-slice inside a group.
-int64_t level0_split_groups(const Grammar& g, int32_t S)
+// Level-0 groups after the cut (one per run of equal sub-slice inside a
+// group), and (*n_long) how many of them have more than kWinLong roots.
+int64_t level0_split_groups(const Grammar& g, int32_t S, int64_t* n_long = nullptr)
 {
     const Level& l = g.lv[0];
-    if (S <= 1) return l.ngrp;
     const auto t0 = slice_terms(g);
-    std::array<int64_t, kSlices> n{};
+    std::array<int64_t, kSlices> n{}, nl{};
     per_slice([&](int x) {
-        int64_t c = 0;
+        int64_t c = 0, cl = 0;
         for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
             int32_t prev = -1;
+            int64_t run = 0;
             for (int64_t e = g.eoff[l.grp_off + gi]; e < g.eoff[l.grp_off + gi + 1]; ++e) {
                 const int32_t s = sub_of(g.epos[e], x, t0, S);
-                c += s != prev;
+                if (s != prev) {
+                    cl += run > kWinLong;
+                    run = 0;
+                    ++c;
+                }
+                ++run;
                 prev = s;
             }
+            cl += run > kWinLong;
         }
         n[x] = c;
+        nl[x] = cl;
     });
-    int64_t total = 0;
-    for (int64_t c : n) total += c;
+    int64_t total = 0, tl = 0;
+    for (int x = 0; x < kSlices; ++x) {
+        total += n[x];
+        tl += nl[x];
+    }
+    if (n_long) *n_long = tl;
     return total;
 }
 
 struct Level0Split {
+    bool on = false;
     int32_t S = 1;
     std::vector<int32_t> row, off;  // per new group: its row; root offsets (ngrp + 1 entries)
     std::vector<int32_t> pos;       // level 0's roots in the new order (root list positions [0, pos.size()))
     int64_t gsl[kSlices + 1] = {};  // new groups of each slice
+    std::vector<int64_t> sgs;       // first new group of (slice x, sub-slice s) at x * S + s; kSlices * S + 1 entries
 };
 
 // The cut itself: per slice, runs counted per sub-slice, then placed
@@ -209,7 +261,9 @@ void level0_split(const Grammar& g, int32_t S, Level0Split& out)
     const Level& l = g.lv[0];
     const auto t0 = slice_terms(g);
     const int64_t r0 = g.eoff[l.grp_off], r1 = g.eoff[l.grp_off + l.ngrp];
+    out.on = true;
     out.S = S;
+    out.sgs.assign((size_t)kSlices * S + 1, 0);
     std::array<std::vector<int64_t>, kSlices> ng, nr;
     per_slice([&](int x) {
         ng[x].assign(S, 0);
@@ -235,12 +289,14 @@ void level0_split(const Grammar& g, int32_t S, Level0Split& out)
     out.off.assign((size_t)gbase[kSlices] + 1, 0);
     out.pos.assign((size_t)(r1 - r0), 0);
     out.off[gbase[kSlices]] = (int32_t)r1;
+    out.sgs[(size_t)kSlices * S] = gbase[kSlices];
     per_slice([&](int x) {
         std::vector<int64_t> gs(S), rs(S);
         int64_t gacc = gbase[x], racc = g.eoff[l.grp_off + l.gsl[x]];
         for (int32_t s = 0; s < S; ++s) {
             gs[s] = gacc;
             rs[s] = racc;
+            out.sgs[(size_t)x * S + s] = gacc;
             gacc += ng[x][s];
             racc += nr[x][s];
         }
@@ -258,6 +314,55 @@ void level0_split(const Grammar& g, int32_t S, Level0Split& out)
             }
         }
     });
+}
+
+// Window chunks of a Boolean level 0 after its cut, per slice and
+// sub-slice: each group of more than kWinLong roots alone (end -1), the
+// groups between them in runs of at most run_groups; each chunk with the
+// 16-byte aligned range of T bytes its roots' bits lie in.  False if a range
+// exceeds kWinBytes.
+size_t window_chunk_bound(int64_t groups, int64_t n_long, int32_t S)
+{
+    return (size_t)(groups / (kWinQ * kWinBlock) + 2 * (n_long + (int64_t)kSlices * S) + 2);
+}
+
+bool build_window_chunks(const Level0Split& l0, int64_t run_groups, std::vector<int4>& wch,
+                         int32_t wsl[kSlices + 1])
+{
+    wch.clear();
+    const int32_t S = l0.S;
+    auto push = [&](int64_t g0, int64_t g1, bool alone) {
+        int64_t tmin = INT64_MAX, tmax = -1;
+        for (int64_t e = l0.off[g0]; e < l0.off[g1]; ++e) {
+            tmin = std::min<int64_t>(tmin, l0.pos[e]);
+            tmax = std::max<int64_t>(tmax, l0.pos[e]);
+        }
+        const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
+        if (b1 - b0 > kWinBytes) return false;
+        wch.push_back(make_int4((int32_t)g0, alone ? -1 : (int32_t)g1, (int32_t)b0, (int32_t)b1));
+        return true;
+    };
+    for (int x = 0; x < kSlices; ++x) {
+        wsl[x] = (int32_t)wch.size();
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t ge = l0.sgs[(size_t)x * S + s + 1];
+            int64_t run0 = l0.sgs[(size_t)x * S + s];
+            for (int64_t gi = run0; gi <= ge; ++gi) {
+                const bool end = gi == ge;
+                const bool longg = !end && l0.off[gi + 1] - l0.off[gi] > kWinLong;
+                if (end || longg || gi - run0 == run_groups) {
+                    if (gi > run0 && !push(run0, gi, false)) return false;
+                    run0 = gi;
+                }
+                if (longg) {
+                    if (!push(gi, gi + 1, true)) return false;
+                    run0 = gi + 1;
+                }
+            }
+        }
+    }
+    wsl[kSlices] = (int32_t)wch.size();
+    return true;
 }
 
 // Stream emission chunks (see stream_block): per level and slice, runs of
@@ -283,7 +388,7 @@ void build_chunks(const Grammar& g, const Level0Split* l0, std::vector<int32_t>&
     for (int64_t k = 0; k <= g.L; ++k) {
         const Level& l = g.lv[k];
         // level 0 after a sub-slice cut: its own groups and root offsets
-        const bool cut = k == 0 && l0 && l0->S > 1;
+        const bool cut = k == 0 && l0 && l0->on;
         const int32_t* eo = cut ? l0->off.data() : g.eoff.data() + l.grp_off;
         const int64_t* gsl = cut ? l0->gsl : l.gsl;
         off[k] = (int64_t)chunk.size();
@@ -323,26 +428,32 @@ size_t flat_section_words(const Grammar& g)
 
 Image image_layout(const Grammar& g, gcs_policy p)
 {
-    const int32_t S = level0_subslices(g, p);
-    const int64_t g0 = S > 1 ? level0_split_groups(g, S) : 0;
+    const Level0Plan pl = level0_plan(g, p);
+    int64_t n_long = 0;
+    const int64_t g0 = pl.cut ? level0_split_groups(g, pl.S, &n_long) : 0;
     Image m{};
     size_t o = 0;
     m.child = o;
     o = al256(o + g.child.size() * 4);
     m.ptsrc = o;
     o = al256(o + g.ptsrc.size() * 4);
+    // when level 0's groups are cut, the grammar's own level-0 groups are not
+    // uploaded: the sections start at level 1's first group
+    const size_t skip = pl.cut ? (size_t)g.lv[0].ngrp : 0;
     m.erow = o;
-    o = al256(o + g.erow.size() * 4);
+    o = al256(o + (g.erow.size() - skip) * 4);
     m.eoff = o;
-    o = al256(o + g.eoff.size() * 4);
+    o = al256(o + (g.eoff.size() - skip) * 4);
     m.epos = o;
     o = al256(o + g.epos.size() * 4);
     m.chunk = o;
     o = al256(o + chunk_bound(g, g0) * 4);
     m.l0row = o;
-    o = al256(o + (S > 1 ? (size_t)g0 * 4 : 0));
+    o = al256(o + (pl.cut ? (size_t)g0 * 4 : 0));
     m.l0off = o;
-    o = al256(o + (S > 1 ? (size_t)(g0 + 1) * 4 : 0));
+    o = al256(o + (pl.cut ? (size_t)(g0 + 1) * 4 : 0));
+    m.wchunk = o;
+    o = al256(o + (pl.window ? window_chunk_bound(g0, n_long, pl.S) * sizeof(int4) : 0));
     m.tcol = o;
     o = al256(o + g.tcol.size() * 4);
     m.tval = o;
@@ -683,11 +794,12 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
         }
     }
     const Level& e = d->lv[k - 1];
-    a.erow = d->erow + e.grp_off;
-    a.eoff = d->eoff + e.grp_off;
-    if (k == 1 && d->l0_sub > 1) {  // level 0's groups cut by sub-slice
+    if (k == 1 && d->l0_on) {  // level 0's groups cut by sub-slice
         a.erow = d->l0row;
         a.eoff = d->l0off;
+    } else {  // the uploaded sections begin at group grp_skip
+        a.erow = d->erow + (e.grp_off - d->grp_skip);
+        a.eoff = d->eoff + (e.grp_off - d->grp_skip);
     }
     a.epos = d->epos;
     a.chunk = d->chunk + d->chunk_off[k - 1];
@@ -734,6 +846,7 @@ int64_t count_launches(const gcs_device* d)
 {
     int64_t c = has_leaf(d) ? 1 : 0;
     for (int64_t k = 1; k < d->tail_k0; ++k) c += vblocks(d->largs[k - 1]) > 0;
+    c += d->win_on ? 1 : 0;
     return c + (has_tail(d) ? 1 : 0);
 }
 
@@ -769,6 +882,13 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             mark();
             level_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(a, arena, acc);
             mark();
+        }
+        if constexpr (kBitTerms<P>) {
+            if (k == 1 && d->win_on) {  // level 0's emission from LDS windows of T
+                mark();
+                window_emit_kernel<P><<<d->win_grid, kWinBlock, d->win_lds, s>>>(d->win, arena, y);
+                mark();
+            }
         }
     }
     if (ev && span) (void)hipEventRecord(ev[1], s);
@@ -954,21 +1074,35 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         }
         }
     }
-    // level 0's emission cut by column sub-slice (direct policies, large T)
+    // level 0's emission cut by column sub-slice (direct policies, large T;
+    // Boolean: LDS windows)
     gcs::Level0Split l0;
-    const int32_t l0_sub = gcs::level0_subslices(g, p);
-    if (l0_sub > 1) gcs::level0_split(g, l0_sub, l0);
+    const gcs::Level0Plan l0_plan = gcs::level0_plan(g, p);
+    if (l0_plan.cut) gcs::level0_split(g, l0_plan.S, l0);
     const int64_t r0 = g.lv[0].ngrp > 0 ? g.eoff[g.lv[0].grp_off + g.lv[0].ngrp] : 0;  // level 0's roots: [0, r0)
-    if (l0.S > 1 && ((int64_t)l0.pos.size() != r0 || g.lv[0].grp_off != 0 ||
-                     im.l0off - im.l0row < l0.row.size() * 4)) {
+    if (l0.on && ((int64_t)l0.pos.size() != r0 || g.lv[0].grp_off != 0 ||
+                  im.l0off - im.l0row < l0.row.size() * 4)) {
         gcs::set_error("internal error: level-0 sub-slice cut does not match the image");
         return GCS_ESTATE;
     }
+    std::vector<int4> wch;
+    int32_t wsl[gcs::kSlices + 1] = {};
+    // runs of about an 8192th of the groups: many chunks per workgroup slot
+    // of the device (balance), each still loading its window once
+    const int64_t run_groups = std::max<int64_t>(gcs::kWinQ * gcs::kWinBlock, (int64_t)l0.row.size() / 8192);
+    bool win_on = l0_plan.window && gcs::build_window_chunks(l0, run_groups, wch, wsl) && !wch.empty();
+    int64_t n_long = 0;
+    for (size_t gi = 0; win_on && gi + 1 < l0.off.size(); ++gi) n_long += l0.off[gi + 1] - l0.off[gi] > gcs::kWinLong;
+    if (win_on && wch.size() > gcs::window_chunk_bound((int64_t)l0.row.size(), n_long, l0.S)) {
+        gcs::set_error("internal error: more window chunks than the image holds");
+        return GCS_ESTATE;
+    }
+    const size_t skip0 = l0.on ? (size_t)g.lv[0].ngrp : 0;  // the grammar's level-0 groups, not uploaded when cut
     std::vector<int32_t> chunk;
     std::vector<int64_t> chunk_off;
     std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;
     gcs::build_chunks(g, &l0, chunk, chunk_off, chunk_sl);
-    if (chunk.size() > gcs::chunk_bound(g, l0.S > 1 ? (int64_t)l0.row.size() : 0)) {
+    if (chunk.size() > gcs::chunk_bound(g, l0.on ? (int64_t)l0.row.size() : 0)) {
         gcs::set_error("internal error: more emission chunks than the image holds");
         return GCS_ESTATE;
     }
@@ -979,12 +1113,14 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         size_t bytes;
     } secs[] = {
         {im.child, g.child.data(), g.child.size() * 4}, {im.ptsrc, g.ptsrc.data(), g.ptsrc.size() * 4},
-        {im.erow, g.erow.data(), g.erow.size() * 4},    {im.eoff, g.eoff.data(), g.eoff.size() * 4},
+        {im.erow, g.erow.data() + skip0, (g.erow.size() - skip0) * 4},
+        {im.eoff, g.eoff.data() + skip0, (g.eoff.size() - skip0) * 4},
         // the root list, level 0's part in the sub-slice order when cut
-        {im.epos, l0.S > 1 ? l0.pos.data() : g.epos.data(), (size_t)r0 * 4},
+        {im.epos, l0.on ? l0.pos.data() : g.epos.data(), (size_t)r0 * 4},
         {im.epos + (size_t)r0 * 4, g.epos.data() + r0, (g.epos.size() - (size_t)r0) * 4},
         {im.chunk, chunk.data(), chunk.size() * 4},
         {im.l0row, l0.row.data(), l0.row.size() * 4},   {im.l0off, l0.off.data(), l0.off.size() * 4},
+        {im.wchunk, wch.data(), win_on ? wch.size() * sizeof(int4) : 0},
         {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
     };
@@ -1005,12 +1141,25 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->L = g.L;
     d->arena_len = g.arena;
     d->lv = g.lv;
-    if (l0.S > 1) {  // the device's view of level 0: the cut groups
+    if (l0.on) {  // the device's view of level 0: the cut groups
         d->lv[0].ngrp = (int64_t)l0.row.size();
         for (int x = 0; x <= gcs::kSlices; ++x) d->lv[0].gsl[x] = l0.gsl[x];
+        d->l0_on = true;
         d->l0_sub = l0.S;
         d->l0row = (const int32_t*)(base + im.l0row);
         d->l0off = (const int32_t*)(base + im.l0off);
+    }
+    if (win_on) {
+        d->win_on = true;
+        d->win.chunk = (const int4*)(base + im.wchunk);
+        d->win.erow = d->l0row;
+        d->win.eoff = d->l0off;
+        d->win.epos = (const int32_t*)(base + im.epos);
+        d->win.n_chunks = (int32_t)wch.size();
+        d->win_grid = (int32_t)wch.size();
+        int32_t mb = 0;
+        for (const int4& c : wch) mb = std::max(mb, c.w - c.z);
+        d->win_lds = (size_t)std::max(mb, 16);
     }
     // emission team per level: about GCS_EMIT_PER_LANE (default 4) roots per
     // lane, at most one wave
@@ -1028,8 +1177,11 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     }
     d->child = (const int2*)(base + im.child);
     d->ptsrc = (const int32_t*)(base + im.ptsrc);
+    // group g of the grammar at erow + (g - grp_skip): when level 0 is cut,
+    // the sections begin at level 1's first group
     d->erow = (const int32_t*)(base + im.erow);
     d->eoff = (const int32_t*)(base + im.eoff);
+    d->grp_skip = (int64_t)skip0;
     d->epos = (const int32_t*)(base + im.epos);
     d->chunk = (const int32_t*)(base + im.chunk);
     d->chunk_off = std::move(chunk_off);
@@ -1076,7 +1228,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
     // level 0's cut groups are emitted by a wide launch only (the narrow
     // levels' LDS image is built from the grammar's own groups)
-    if (d->l0_sub > 1) d->tail_k0 = std::max<int64_t>(d->tail_k0, 2);
+    if (d->l0_on) d->tail_k0 = std::max<int64_t>(d->tail_k0, 2);
     d->tail_nent = g.L + 2 - d->tail_k0;
     // emission mode of each wide launch: chunks where the groups are short
     // and uneven, teams elsewhere (GCS_EMIT_STREAM = 0 keeps teams, 1 takes
@@ -1092,13 +1244,20 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
             for (int x = 0; x < gcs::kSlices; ++x) mc = std::max(mc, a.csl[x + 1] - a.csl[x]);
             a.pb_emit = mc;
         }
+        if (d->win_on) {  // launch 1's emission runs in window_emit_kernel
+            d->largs[0].stream = 0;
+            d->largs[0].pb_emit = 0;
+        }
         if (std::getenv("GCS_UPLOAD_TRACE")) {
             int n_stream = 0;
             for (int64_t k = 1; k < d->tail_k0; ++k) n_stream += d->largs[k - 1].stream != 0;
             std::fprintf(stderr, "[gcs upload] stream emission in %d of %lld wide launches\n", n_stream,
                          (long long)d->tail_k0 - 1);
-            std::fprintf(stderr, "[gcs upload] level-0 emission in %d sub-slices per slice (%lld groups, %lld before)\n",
-                         d->l0_sub, (long long)d->lv[0].ngrp, (long long)g.lv[0].ngrp);
+            std::fprintf(stderr,
+                         "[gcs upload] level-0 emission in %d sub-slices per slice (%lld groups, %lld before); "
+                         "LDS windows %d (%d chunks, %zu bytes)\n",
+                         d->l0_on ? d->l0_sub : 0, (long long)d->lv[0].ngrp, (long long)g.lv[0].ngrp, (int)d->win_on,
+                         d->win_on ? d->win.n_chunks : 0, d->win_lds);
         }
     }
     // the narrowest entries at the end run on workgroup 0 alone, in LDS: as

@@ -130,6 +130,7 @@ def test_stream_emission_long_groups(env, oracle_mod, monkeypatch, capfd, pol):
     ys, used = {}, {}
     monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
     monkeypatch.setenv("GCS_TAIL_WGS", "8")  # keep the level-1 launch out of the tail
+    monkeypatch.setenv("GCS_LEVEL0_WINDOW", "0")  # Boolean level 0 through the level kernel
     for mode in ("0", "1"):
         monkeypatch.setenv("GCS_EMIT_STREAM", mode)
         capfd.readouterr()
@@ -148,3 +149,54 @@ def test_stream_emission_long_groups(env, oracle_mod, monkeypatch, capfd, pol):
         assert np.all(np.abs(ys["1"] - yo) <= 1e-12 * absum)
     else:
         assert np.array_equal(ys["1"], _ref(oracle_mod, pol, rp, col, x))
+
+
+def _window_matrix():
+    """2000 short random rows over 400000 columns and two rows of 200000
+    random columns: a long row's bare terminals in one slice (about 25000)
+    exceed a window chunk's 16384 roots."""
+    rng = np.random.default_rng(404)
+    m = 400_000
+    rows = [np.sort(rng.choice(m, 1 + i % 7, replace=False)) for i in range(2000)]
+    for i in (5, 1999):
+        rows[i] = np.sort(rng.choice(m, 200_000, replace=False))
+    rp = np.zeros(len(rows) + 1, np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    return len(rows), m, rp, np.concatenate(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("split", [None, "1", "5"])
+def test_boolean_window_emission(env, oracle_mod, monkeypatch, capfd, split):
+    """Boolean level-0 emission from LDS windows of the bit-packed terminals
+    (default, and with 1 and 5 sub-slices) equals the level-kernel emission
+    without a cut and the oracle, overwrite and accumulate, including a group
+    longer than one window chunk."""
+    torch, gcs = env
+    n, m, rp, col = _window_matrix()
+    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    rng = np.random.default_rng(6)
+    x = (rng.random(m) < 0.002).astype(np.uint8)
+    y0 = (rng.random(n) < 0.3).astype(np.uint8)
+    ref = oracle_mod.spmv_bool(rp, col, x)
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    ys = {}
+    for mode in ("plain", "window"):
+        if mode == "plain":
+            monkeypatch.setenv("GCS_LEVEL0_SPLIT", "0")
+        elif split is None:
+            monkeypatch.delenv("GCS_LEVEL0_SPLIT", raising=False)
+        else:
+            monkeypatch.setenv("GCS_LEVEL0_SPLIT", split)
+        capfd.readouterr()
+        dev = gcs.upload(g, gcs.BOOL_OR)
+        err = capfd.readouterr().err
+        line = [l for l in err.splitlines() if "LDS windows" in l]
+        assert len(line) == 1 and line[0].split("LDS windows ")[1].startswith("1" if mode == "window" else "0"), err
+        y = dev.sweep_right(torch.from_numpy(x).cuda())
+        ya = torch.from_numpy(y0.copy()).cuda()
+        dev.sweep_right_acc(torch.from_numpy(x).cuda(), ya)
+        dev.check()
+        ys[mode] = (y.cpu().numpy(), ya.cpu().numpy())
+        dev.free()
+    assert np.array_equal(ys["window"][0], ref) and np.array_equal(ys["plain"][0], ref)
+    assert np.array_equal(ys["window"][1], y0 | ref) and np.array_equal(ys["plain"][1], y0 | ref)

@@ -323,6 +323,7 @@ def test_stream_emission_bit_identical(env, graph300k, monkeypatch, capfd, pol):
     if pol == "min_plus_f32":
         x = x.astype(np.float32)
     monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    monkeypatch.setenv("GCS_LEVEL0_WINDOW", "0")  # Boolean level 0 through the level kernel
     ys, used = {}, {}
     for mode in ("default", "0", "1"):
         if mode == "default":
