@@ -235,6 +235,27 @@ def test_bfs_copy_graph(env, oracle_mod, synth_mod):
     assert np.array_equal(y, oracle_mod.spmv_bool(rp, col, xb))
 
 
+def test_bfs_pass_cap_and_repeat(env, oracle_mod, synth_mod, graph300k):
+    """The BFS fixpoint refuses to run past its pass cap (GCS_ERANGE after
+    exactly cap passes), and the same handle then runs the whole fixpoint
+    again, twice, with the oracle's counts (no state is left between
+    fixpoints)."""
+    torch, gcs = env
+    spec, g = graph300k
+    rp, col = synth_mod.copy_graph(spec)
+    src = synth_mod.sources(spec.n, 16, 501)
+    vis_o, counts_o = oracle_mod.bfs(rp, col, src)
+    dev = gcs.upload(g, gcs.BOOL_OR)
+    assert len(counts_o) > 3
+    with pytest.raises(gcs.GcsError, match="ERANGE|more passes"):
+        dev.bfs(src, max_passes=2)
+    for _ in range(2):
+        vis, counts = dev.bfs(src)
+        assert np.array_equal(counts, counts_o) and np.array_equal(vis.cpu().numpy(), vis_o)
+    vis, counts = dev.bfs(src, max_passes=len(counts_o))  # exactly enough passes
+    assert np.array_equal(counts, counts_o)
+
+
 def test_abi_errors_on_device(env):
     torch, gcs = env
     g = gcs.build_grammar(np.array([0, 2], np.int64), np.array([0, 1], np.int32), None, n_cols=2)
