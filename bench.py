@@ -345,10 +345,12 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20}
     for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
         cc = rows(d, "*counter_collection.csv")
-        # the calibration copies: the copy dispatches that moved copy_mib MiB
-        # (the first copy dispatches of the run, one per calibration copy)
-        copies = [float(r["Counter_Value"]) for r in cc if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
-        big = [v for v in copies if v > 0.25 * copy_mib * 1024]
+        # the calibration copies: the first five large copy dispatches of the
+        # run (issued before anything else; later large copies, such as the
+        # achievable-bandwidth copy, are not of the calibrated size)
+        cc_sorted = sorted(cc, key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in cc_sorted if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        big = [v for v in copies if v > 0.25 * copy_mib * 1024][:5]
         lvl = [float(r["Counter_Value"]) * 1024 for r in cc if "level_kernel" in r["Kernel_Name"]]
         rec[tag + "_kib_copy"] = sum(big) / len(big)
         rec[tag + "_bytes_per_launch"] = sum(lvl) / max(len(lvl), 1)
@@ -772,7 +774,8 @@ def main():
     if leg is not None:
         cpu = leg.baseline(rp, col, val, xs[0].cpu().numpy().astype(np.float64), nnz)
 
-    copy_gbs = copy_achievable_gbs(torch)
+    # (not in counter runs: its copies would mix with the calibration's)
+    copy_gbs = None if args.calibrate_copy_mib else copy_achievable_gbs(torch)
     traffic = None  # HBM bytes per level_kernel launch from the committed counter profile, if still current
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -828,7 +831,7 @@ def main():
                      "launches": int(max(nwide, 1)),
                      "launch_avg_us": span_ms * 1e3 / nwide if nwide > 0 else tail_ms * 1e3,
                      "achieved_from_traffic": (traffic / (span_ms * 1e-3 / max(nwide, 1)) / 1e9) if traffic else None,
-                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
+                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None,
                      "bytes_per_launch_avg": float(lb.sum() / nwide if nwide > 0 else lb_all.sum()),
                      "bytes_per_sweep": float(lb_all.sum())},
         "cpu_baseline": cpu,
