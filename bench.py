@@ -400,7 +400,10 @@ def bench_tropical(args, torch, gcs, leg, g, rp, col, spec, src, vis_o, counts_o
     fixpoint, whose distances must be the oracle BFS's levels (both checks
     in the CPU leg; vis_o and counts_o are its BFS, None without it)."""
     nnz = int(rp[-1])
+    t_up = time.perf_counter()
     dev = gcs.upload(g, gcs.MIN_PLUS_F32)
+    torch.cuda.synchronize()
+    t_up = time.perf_counter() - t_up
     d0 = torch.full((spec.n,), float("inf"), dtype=torch.float32, device="cuda")
     d0[torch.from_numpy(src).cuda()] = 0
     y = dev.new_y()
@@ -432,7 +435,7 @@ def bench_tropical(args, torch, gcs, leg, g, rp, col, spec, src, vis_o, counts_o
     if vis_o is not None and not (np.array_equal(np.isfinite(dh), vis_o.astype(bool)) and
                                   np.array_equal(hist[1:], counts_o[:len(hist) - 1])):
         raise SystemExit("Bellman-Ford distances disagree with the oracle BFS levels")
-    out = {"ms_per_pass": ms, "nnz_per_s": nnz / (ms * 1e-3), "bellman_ford_passes": passes,
+    out = {"ms_per_pass": ms, "nnz_per_s": nnz / (ms * 1e-3), "upload_s": t_up, "bellman_ford_passes": passes,
            "bellman_ford_s": bf_s, "max_distance": int(len(hist) - 1)}
     log(f"tropical: {ms:.2f} ms per pass; Bellman-Ford fixpoint in {passes} passes, {bf_s:.2f} s")
     dev.free()
@@ -539,7 +542,11 @@ def bench_graph(args, wl, spec, leg):
     st = g.stats()
     log(f"grammar built in {build_s:.1f}s: {st}")
     src = synth.sources(spec.n, wl["n_sources"], wl["source_seed"])
+    t = time.perf_counter()
     dev = gcs.upload(g, gcs.BOOL_OR)
+    torch.cuda.synchronize()
+    upload_s = time.perf_counter() - t
+    log(f"Boolean upload (host layout of level 0 included) in {upload_s:.1f}s")
     f = torch.zeros(spec.n, dtype=torch.uint8, device="cuda")
     f[torch.from_numpy(src).cuda()] = 1
     y = dev.new_y()
@@ -587,7 +594,8 @@ def bench_graph(args, wl, spec, leg):
         "config": {"workload": args.workload, "n": spec.n, "nnz": nnz, "sources": len(src),
                    "grammar": {k: st[k] for k in ("n_rules", "n_passthrough", "depth", "max_width", "c_len",
                                                   "n_terminals", "n_tiles", "n_emit_groups")},
-                   "build_s": build_s, "bfs_passes": len(counts), "bfs_s": bfs_s, "visited": int(vis.sum().item()),
+                   "build_s": build_s, "upload_s": upload_s, "bfs_passes": len(counts), "bfs_s": bfs_s,
+                   "visited": int(vis.sum().item()),
                    "device_bytes": dev_bytes, "csr_bytes_analytic": csr_bytes,
                    "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes, "tropical": tropical,
                    "csr_rocsparse_fp32": csr},

@@ -329,37 +329,45 @@ size_t window_chunk_bound(int64_t groups, int64_t n_long, int32_t S)
 bool build_window_chunks(const Level0Split& l0, int64_t run_groups, std::vector<int4>& wch,
                          int32_t wsl[kSlices + 1])
 {
-    wch.clear();
     const int32_t S = l0.S;
-    auto push = [&](int64_t g0, int64_t g1, bool alone) {
-        int64_t tmin = INT64_MAX, tmax = -1;
-        for (int64_t e = l0.off[g0]; e < l0.off[g1]; ++e) {
-            tmin = std::min<int64_t>(tmin, l0.pos[e]);
-            tmax = std::max<int64_t>(tmax, l0.pos[e]);
-        }
-        const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
-        if (b1 - b0 > kWinBytes) return false;
-        wch.push_back(make_int4((int32_t)g0, alone ? -1 : (int32_t)g1, (int32_t)b0, (int32_t)b1));
-        return true;
-    };
-    for (int x = 0; x < kSlices; ++x) {
-        wsl[x] = (int32_t)wch.size();
-        for (int32_t s = 0; s < S; ++s) {
+    std::array<std::vector<int4>, kSlices> part;
+    std::array<int, kSlices> ok{};
+    per_slice([&](int x) {  // each slice on a thread of its own
+        std::vector<int4>& out = part[x];
+        auto push = [&](int64_t g0, int64_t g1, bool alone) {
+            int64_t tmin = INT64_MAX, tmax = -1;
+            for (int64_t e = l0.off[g0]; e < l0.off[g1]; ++e) {
+                tmin = std::min<int64_t>(tmin, l0.pos[e]);
+                tmax = std::max<int64_t>(tmax, l0.pos[e]);
+            }
+            const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
+            if (b1 - b0 > kWinBytes) return false;
+            out.push_back(make_int4((int32_t)g0, alone ? -1 : (int32_t)g1, (int32_t)b0, (int32_t)b1));
+            return true;
+        };
+        ok[x] = 1;
+        for (int32_t s = 0; s < S && ok[x]; ++s) {
             const int64_t ge = l0.sgs[(size_t)x * S + s + 1];
             int64_t run0 = l0.sgs[(size_t)x * S + s];
-            for (int64_t gi = run0; gi <= ge; ++gi) {
+            for (int64_t gi = run0; gi <= ge && ok[x]; ++gi) {
                 const bool end = gi == ge;
                 const bool longg = !end && l0.off[gi + 1] - l0.off[gi] > kWinLong;
                 if (end || longg || gi - run0 == run_groups) {
-                    if (gi > run0 && !push(run0, gi, false)) return false;
+                    if (gi > run0 && !push(run0, gi, false)) ok[x] = 0;
                     run0 = gi;
                 }
-                if (longg) {
-                    if (!push(gi, gi + 1, true)) return false;
+                if (longg && ok[x]) {
+                    if (!push(gi, gi + 1, true)) ok[x] = 0;
                     run0 = gi + 1;
                 }
             }
         }
+    });
+    wch.clear();
+    for (int x = 0; x < kSlices; ++x) {
+        if (!ok[x]) return false;
+        wsl[x] = (int32_t)wch.size();
+        wch.insert(wch.end(), part[x].begin(), part[x].end());
     }
     wsl[kSlices] = (int32_t)wch.size();
     return true;
