@@ -195,6 +195,7 @@ __device__ __forceinline__ void issue_before(const T& v)
 // ---------------------------------------------------------------- kernels
 
 constexpr int kBlock = 256;
+constexpr int kLeafItems = 4;  // terminals (and accumulators) per lane of the leaf launch
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kEmitItems = 2;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
@@ -214,17 +215,42 @@ __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict_
                                                       typename P::A* __restrict__ acc, int32_t n_acc,
                                                       unsigned* __restrict__ barrier)
 {
-    const int32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if constexpr (kBitTerms<P>) {
-        // every lane of the wave takes part in the ballot; lane i of the wave
-        // gives bit i of the word of terminals i0 .. i0 + 63 (i0 = i - lane)
-        const uint64_t w = __ballot(i < alpha && P::leaf(V[tval[i]], x[tcol[i]]));
-        if ((threadIdx.x & 63) == 0 && i < alpha) ((uint64_t*)T)[i >> 6] = w;
-    } else {
-        if (i < alpha) T[i] = P::leaf(V[tval[i]], x[tcol[i]]);
+    // kLeafItems terminals per lane, i = base + u * kBlock + lane, all loads
+    // issued before the first value is formed (indices past alpha are clamped
+    // to alpha - 1 and their values discarded)
+    const int32_t base = blockIdx.x * (kBlock * kLeafItems) + threadIdx.x;
+    if (alpha > 0) {
+        int32_t c[kLeafItems];
+#pragma unroll
+        for (int u = 0; u < kLeafItems; ++u) c[u] = min(base + u * kBlock, alpha - 1);
+        int32_t col[kLeafItems], val[kLeafItems];
+#pragma unroll
+        for (int u = 0; u < kLeafItems; ++u) {
+            col[u] = tcol[c[u]];
+            val[u] = tval[c[u]];
+        }
+        typename P::A t[kLeafItems];
+#pragma unroll
+        for (int u = 0; u < kLeafItems; ++u) t[u] = P::leaf(V[val[u]], x[col[u]]);
+#pragma unroll
+        for (int u = 0; u < kLeafItems; ++u) {
+            const int32_t i = base + u * kBlock;
+            if constexpr (kBitTerms<P>) {
+                // every lane of the wave takes part in the ballot; lane l gives
+                // bit l of the word of terminals i0 .. i0 + 63 (i0 = i - l)
+                const uint64_t w = __ballot(i < alpha && t[u]);
+                if ((threadIdx.x & 63) == 0 && i < alpha) ((uint64_t*)T)[i >> 6] = w;
+            } else {
+                if (i < alpha) T[i] = t[u];
+            }
+        }
     }
-    if (i < n_acc) acc[i] = P::ident();
-    if (i == 0) {  // the tail kernel's grid barrier counts rounds from 0 in every sweep
+#pragma unroll
+    for (int u = 0; u < kLeafItems; ++u) {
+        const int32_t i = base + u * kBlock;
+        if (i < n_acc) acc[i] = P::ident();
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {  // the tail kernel's grid barrier counts rounds from 0 in every sweep
         barrier[0] = 0;
         barrier[kFlagOffset] = 0;
     }
