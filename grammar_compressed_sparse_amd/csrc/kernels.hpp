@@ -195,7 +195,10 @@ __device__ __forceinline__ void issue_before(const T& v)
 // ---------------------------------------------------------------- kernels
 
 constexpr int kBlock = 256;
-constexpr int kLeafItems = 4;  // terminals (and accumulators) per lane of the leaf launch
+// terminals (and accumulators) per lane of a large leaf launch; a small one
+// keeps one per lane so that its grid still covers the device
+constexpr int kLeafItems = 4;
+constexpr int64_t kLeafMultiMin = (int64_t)kLeafItems * kBlock * 2048;
 constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kEmitItems = 2;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
@@ -206,7 +209,7 @@ constexpr int kFlagOffset = 32;  // tail barrier: release flag, in 4-byte words 
 constexpr int kStreamItems = 4;  // roots per lane and round of a stream emission block
 constexpr int kStreamCap = kBlock * kStreamItems;  // roots per round, and the most groups of a stream chunk
 
-template <class P>
+template <class P, int kLeafItems>
 __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict__ tcol,
                                                       const int32_t* __restrict__ tval,
                                                       const typename P::W* __restrict__ V,

@@ -877,9 +877,15 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
     const int32_t n_acc = kDirectEmit<P> ? (accumulate ? 0 : (int32_t)d->n_rows) : (int32_t)(kSlices * d->n_rows);
     if (has_leaf(d)) {
         mark();
-        leaf_kernel<P><<<std::max(1, ceil_div(std::max<int64_t>(d->alpha, n_acc), kBlock * kLeafItems)), kBlock, 0, s>>>(
-            d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha, acc,
-            n_acc, d->barrier);
+        const int64_t items = std::max<int64_t>(d->alpha, n_acc);
+        if (items >= kLeafMultiMin)
+            leaf_kernel<P, kLeafItems><<<ceil_div(items, kBlock * kLeafItems), kBlock, 0, s>>>(
+                d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha,
+                acc, n_acc, d->barrier);
+        else
+            leaf_kernel<P, 1><<<std::max(1, ceil_div(items, kBlock)), kBlock, 0, s>>>(
+                d->tcol, d->tval, (const typename P::W*)d->V, (const typename P::X*)xv, arena, (int32_t)d->alpha,
+                acc, n_acc, d->barrier);
         mark();
     }
     if (ev && span) (void)hipEventRecord(ev[0], s);
