@@ -286,6 +286,28 @@ def test_loaded_grammar_sweeps_identically(env, synth_mod, c1, tmp_path):
     db.check()
 
 
+def test_loaded_graph_grammar_direct_policies(env, oracle_mod, synth_mod, graph300k, tmp_path, monkeypatch):
+    """A graph grammar saved and loaded back sweeps like the original under
+    the uploads that rebuild level 0's emission (Boolean LDS windows,
+    tropical sub-slice cut, forced so that this small graph takes them) and
+    equals the oracle."""
+    torch, gcs = env
+    spec, g = graph300k
+    rp, col = synth_mod.copy_graph(spec)
+    g.save(tmp_path / "graph.gcs")
+    h = gcs.load_grammar(tmp_path / "graph.gcs")
+    rng = np.random.default_rng(505)
+    xb = (rng.random(spec.n) < 0.05).astype(np.uint8)
+    xt = (rng.random(spec.n) * 9).astype(np.float32)
+    xt[rng.random(spec.n) < 0.7] = np.inf
+    monkeypatch.setenv("GCS_LEVEL0_SPLIT", "4")
+    for policy, x, ref in ((gcs.BOOL_OR, xb, oracle_mod.spmv_bool(rp, col, xb)),
+                           (gcs.MIN_PLUS_F32, xt, oracle_mod.spmv_min_plus(rp, col, None, xt, np.float32))):
+        ya, _ = _sweep(env, g, policy, x)
+        yb, _ = _sweep(env, h, policy, x)
+        assert np.array_equal(ya, yb) and np.array_equal(yb, ref)
+
+
 def test_handles_with_different_lds_images_interleave(env, oracle_mod, synth_mod, c1, monkeypatch):
     """Uploads whose narrow-level LDS images differ in size sweep in any
     interleaving (the kernel's dynamic-LDS limit is shared by all handles)."""
