@@ -137,7 +137,7 @@ inline int64_t level_roots(const Grammar& g, int64_t k)
 // in an atomic, and more sub-slices mean more groups); a 3 MB window is the
 // compromise.
 constexpr double kLevel0Window = 3.0 * 1024 * 1024;
-constexpr double kWinTarget = 40.0 * 1024;  // Boolean LDS window target (window_emit_kernel)
+constexpr double kWinTarget = 26.0 * 1024;  // Boolean LDS window target (window_emit_kernel)
 constexpr int32_t kLevel0MaxSplit = 64;
 
 // first terminal of each column slice (terminals are sorted by column)
@@ -189,7 +189,8 @@ Level0Plan level0_plan(const Grammar& g, gcs_policy p)
     } else if (pl.window) {
         // the widest slice's terminals in windows of about kWinTarget bytes
         // (at most kWinBytes with alignment; smaller windows measured faster:
-        // the copy graph's level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB)
+        // the copy graph's level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB,
+        // 2.02 ms at 26 KB; sixteen groups per lane instead of eight: 2.77 ms)
         pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kWinTarget)));
         pl.cut = true;
     } else {
