@@ -771,6 +771,112 @@ extern "C" gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, con
     }
 }
 
+extern "C" gcs_status gcs_merge_grammars(const gcs_grammar* const* parts, int32_t n_parts, int32_t n_threads,
+                                         gcs_grammar** out)
+{
+    if (!out || n_parts < 1 || !parts) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    *out = nullptr;
+    for (int32_t p = 0; p < n_parts; ++p)
+        if (!parts[p]) {
+            gcs::set_error("null grammar among the parts");
+            return GCS_EINVAL;
+        }
+    const Grammar& g0 = parts[0]->g;
+    int64_t alpha = 0, R = 0, C = 0;
+    int32_t last_col = -1;
+    for (int32_t p = 0; p < n_parts; ++p) {
+        const Grammar& gp = parts[p]->g;
+        if (gp.n_rows != g0.n_rows || gp.n_cols != g0.n_cols) {
+            gcs::set_error("parts differ in shape");
+            return GCS_EINVAL;
+        }
+        if (!gp.tcol.empty()) {
+            if (gp.tcol.front() <= last_col) {
+                gcs::set_error("parts must cover disjoint, increasing column ranges");
+                return GCS_EINVAL;
+            }
+            last_col = gp.tcol.back();
+        }
+        alpha += gp.alpha();
+        R += gp.nrules();
+        C += (int64_t)gp.c_sym.size();
+    }
+    if (alpha + R >= (int64_t)INT32_MAX) {
+        gcs::set_error("merged grammar exceeds the 32-bit symbol space");
+        return GCS_ERANGE;
+    }
+    try {
+        auto* h = new gcs_grammar();
+        Grammar& g = h->g;
+        g.n_rows = g0.n_rows;
+        g.n_cols = g0.n_cols;
+        g.n_tiles = 0;
+        // values: the sorted union of the parts' values
+        for (int32_t p = 0; p < n_parts; ++p) g.V.insert(g.V.end(), parts[p]->g.V.begin(), parts[p]->g.V.end());
+        std::sort(g.V.begin(), g.V.end());
+        g.V.erase(std::unique(g.V.begin(), g.V.end()), g.V.end());
+        g.tcol.reserve((size_t)alpha);
+        g.tval.reserve((size_t)alpha);
+        g.ra.reserve((size_t)R);
+        g.rb.reserve((size_t)R);
+        // symbol s of part p: terminal s < alpha_p -> t_off + s; rule s - alpha_p -> alpha + r_off + (s - alpha_p)
+        std::vector<int64_t> t_off(n_parts), r_off(n_parts);
+        int64_t to = 0, ro = 0;
+        for (int32_t p = 0; p < n_parts; ++p) {
+            const Grammar& gp = parts[p]->g;
+            t_off[p] = to;
+            r_off[p] = ro;
+            to += gp.alpha();
+            ro += gp.nrules();
+            g.nnz += gp.nnz;
+            g.n_tiles += gp.n_tiles;
+            g.t_csrv += gp.t_csrv;
+            g.t_repair += gp.t_repair;
+        }
+        auto sym = [&](int32_t p, int32_t s) -> int32_t {
+            const int64_t ap = parts[p]->g.alpha();
+            return (int32_t)(s < ap ? t_off[p] + s : alpha + r_off[p] + (s - ap));
+        };
+        for (int32_t p = 0; p < n_parts; ++p) {
+            const Grammar& gp = parts[p]->g;
+            for (int64_t t = 0; t < gp.alpha(); ++t) {
+                g.tcol.push_back(gp.tcol[t]);
+                const double v = gp.V[gp.tval[t]];
+                g.tval.push_back((int32_t)(std::lower_bound(g.V.begin(), g.V.end(), v) - g.V.begin()));
+            }
+            for (int64_t i = 0; i < gp.nrules(); ++i) {
+                g.ra.push_back(sym(p, gp.ra[i]));
+                g.rb.push_back(sym(p, gp.rb[i]));
+            }
+        }
+        // C: each row's sequences of the parts, in part (column) order
+        g.c_off.assign((size_t)g.n_rows + 1, 0);
+        g.c_sym.resize((size_t)C);
+        int64_t o = 0;
+        for (int64_t r = 0; r < g.n_rows; ++r) {
+            g.c_off[r] = o;
+            for (int32_t p = 0; p < n_parts; ++p) {
+                const Grammar& gp = parts[p]->g;
+                for (int64_t e = gp.c_off[r]; e < gp.c_off[r + 1]; ++e) g.c_sym[o++] = sym(p, gp.c_sym[e]);
+            }
+        }
+        g.c_off[g.n_rows] = o;
+        gcs_status st = gcs::finish_layout(g, gcs::resolve_threads(n_threads));
+        if (st != GCS_OK) {
+            delete h;
+            return st;
+        }
+        *out = h;
+        return GCS_OK;
+    } catch (const std::bad_alloc&) {
+        gcs::set_error("out of host memory");
+        return GCS_ENOMEM;
+    }
+}
+
 extern "C" gcs_status gcs_grammar_stats(const gcs_grammar* h, gcs_stats* out)
 {
     if (!h || !out) {

@@ -65,6 +65,8 @@ _lib.gcs_last_error.restype = ctypes.c_char_p
 _lib.gcs_build_grammar.argtypes = [ctypes.POINTER(CsrView), ctypes.POINTER(BuildOpts), ctypes.POINTER(_P)]
 _lib.gcs_grammar_from_rules.argtypes = [_I64, _I64, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P, ctypes.POINTER(_P)]
 _lib.gcs_grammar_stats.argtypes = [_P, ctypes.POINTER(Stats)]
+_lib.gcs_merge_grammars.argtypes = [ctypes.POINTER(_P), ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P)]
+_lib.gcs_merge_grammars.restype = _st
 _lib.gcs_level_widths.argtypes = [_P, _P, _I64]
 _lib.gcs_export_grammar.argtypes = [_P] + [_P] * 9
 _lib.gcs_layout_counts.argtypes = [_P, _P]
@@ -228,6 +230,15 @@ def grammar_from_rules(n_rows, n_cols, values, term_col, term_val, rule_a, rule_
     h = _P()
     _check(_lib.gcs_grammar_from_rules(n_rows, n_cols, _ptr(v), v.size, _ptr(tc), _ptr(tv), tc.size, _ptr(a),
                                        _ptr(b), a.size, _ptr(co), _ptr(cs), ctypes.byref(h)))
+    return Grammar(h)
+
+
+def merge_grammars(parts, n_threads=0) -> Grammar:
+    """gcs_merge_grammars: one grammar from grammars of disjoint, increasing
+    column groups of the same matrix (the parts stay valid)."""
+    hs = (_P * len(parts))(*[p._h for p in parts])
+    h = _P()
+    _check(_lib.gcs_merge_grammars(hs, len(parts), n_threads, ctypes.byref(h)))
     return Grammar(h)
 
 

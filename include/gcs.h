@@ -151,6 +151,22 @@ gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, const double* 
                                   const int32_t* rule_a, const int32_t* rule_b, int64_t n_rules,
                                   const int64_t* c_off, const int32_t* c_sym, gcs_grammar** out);
 
+/* One grammar from grammars of disjoint column groups of the same matrix
+ * (section 4.4 builds one grammar per column chunk; a matrix too large to
+ * build whole is built chunk by chunk and merged).  parts[0..n_parts) must
+ * have equal n_rows and n_cols and cover increasing, disjoint column ranges
+ * (part p's terminal columns all below part p+1's).  The merged grammar has
+ * the union of the values, the parts' terminals and rules in part order
+ * (symbols renumbered), each row's sequence the concatenation of the parts'
+ * sequences of that row, and is levelled, completed and laid out afresh
+ * with n_threads host threads (0: as gcs_build_grammar).  Its products
+ * equal the sum (or OR, or min) of the parts' products.  The parts are not
+ * modified; the caller frees them and *out (gcs_free_grammar).
+ * GCS_EINVAL on a shape mismatch or overlapping/unordered columns,
+ * GCS_ERANGE beyond the 32-bit symbol space, GCS_ENOMEM. */
+gcs_status gcs_merge_grammars(const gcs_grammar* const* parts, int32_t n_parts, int32_t n_threads,
+                              gcs_grammar** out);
+
 gcs_status gcs_grammar_stats(const gcs_grammar* g, gcs_stats* out);
 
 /* Completed widths w_k, k = 0..L (w_0 = alpha, the terminal array).  Writes

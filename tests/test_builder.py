@@ -274,3 +274,42 @@ def test_similar_row_tiles_copy_graph(gcs, oracle_mod, synth_mod):
     nat = gcs.build_grammar(rp, col, None, n_cols=spec.n, row_chunk=3000)
     # grouping similar rows keeps more of the sharing than consecutive blocks
     assert g.stats()["c_len"] < nat.stats()["c_len"]
+
+
+def test_merge_column_groups(gcs, oracle_mod, synth_mod):
+    """Grammars of three column groups of one genotype matrix, built apart and
+    merged (gcs_merge_grammars): lossless against the whole matrix, levels
+    and completion as for any grammar, the product equal to the oracle's
+    (host emulation of the merged layout), and the parts' counts adding up."""
+    spec = synth_mod.GenotypeSpec(400, 6000, 8, 100.0, 0.005, seed=21)
+    rp, col, val = synth_mod.genotype(spec)
+    cuts = [(0, 2000), (2000, 1500), (3500, 2500)]
+    parts = []
+    for c0, nc in cuts:
+        prp, pcol, pval = synth_mod.genotype(spec, col0=c0, ncols=nc)
+        parts.append(gcs.build_grammar(prp, pcol, pval, n_cols=spec.n_cols))
+    g = gcs.merge_grammars(parts)
+    ex = _check_grammar(g, rp, col, val, single_tile=False)
+    st, sts = g.stats(), [p.stats() for p in parts]
+    assert st["nnz"] == int(rp[-1]) == sum(s["nnz"] for s in sts)
+    for k in ("n_terminals", "n_rules", "c_len"):
+        assert st[k] == sum(s[k] for s in sts)
+    x = synth_mod.normal(spec.n_cols, 77)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
+    y = H.emulate_layout(g.layout(), ex, x)
+    assert np.all(np.abs(y - yo) <= 1e-12 * absum + 1e-300)
+
+
+def test_merge_refuses_bad_parts(gcs, synth_mod):
+    spec = synth_mod.GenotypeSpec(50, 400, 4, 20.0, 0.01, seed=22)
+    a = gcs.build_grammar(*synth_mod.genotype(spec, col0=0, ncols=200), n_cols=spec.n_cols)
+    b = gcs.build_grammar(*synth_mod.genotype(spec, col0=200, ncols=200), n_cols=spec.n_cols)
+    c = gcs.build_grammar(*synth_mod.genotype(spec, col0=100, ncols=200), n_cols=spec.n_cols)
+    other = gcs.build_grammar(*synth_mod.genotype(synth_mod.GenotypeSpec(51, 400, 4, 20.0, 0.01, seed=22)),
+                              n_cols=400)
+    for bad in ([b, a], [a, c], [a, other]):  # unordered, overlapping, shape mismatch
+        with pytest.raises(gcs.GcsError, match="EINVAL"):
+            gcs.merge_grammars(bad)
+    with pytest.raises(gcs.GcsError):
+        gcs.merge_grammars([])
+    assert gcs.merge_grammars([a]).stats()["nnz"] == a.stats()["nnz"]
