@@ -416,3 +416,28 @@ def test_level0_subslice_cut_identical(env, oracle_mod, synth_mod, graph300k, mo
         assert np.array_equal(y.cpu().numpy(), ref)
         assert np.array_equal(Y[:, 0].cpu().numpy(), ref)
         dev.free()
+
+
+def test_merged_column_groups(env, oracle_mod, synth_mod):
+    """Three column groups of the 2000 x 12000 genotype built apart and merged
+    (gcs_merge_grammars) sweep like the whole matrix: fp32 and fp64 within
+    tolerance of the oracle, Boolean and tropical exactly."""
+    torch, gcs = env
+    spec = synth_mod.GenotypeSpec(2000, 12_000, 32, 300.0, 0.002, seed=12)
+    rp, col, val = synth_mod.genotype(spec)
+    parts = [gcs.build_grammar(*synth_mod.genotype(spec, col0=c0, ncols=nc), n_cols=spec.n_cols, col_chunk=2000)
+             for c0, nc in ((0, 5000), (5000, 1), (5001, 6999))]
+    g = gcs.merge_grammars(parts)
+    assert g.stats()["nnz"] == int(rp[-1])
+    x32 = synth_mod.normal(spec.n_cols, 8).astype(np.float32)
+    yo, absum = oracle_mod.spmv_f64(rp, col, val, x32.astype(np.float64))
+    y, _ = _sweep(env, g, gcs.PLUS_F32, x32)
+    _rel_ok(y, yo, absum, 1e-5)
+    y, _ = _sweep(env, g, gcs.PLUS_F64, x32.astype(np.float64))
+    _rel_ok(y, yo, absum, 1e-12)
+    xb = (x32 > 1.0).astype(np.uint8)
+    y, _ = _sweep(env, g, gcs.BOOL_OR, xb)
+    assert np.array_equal(y, oracle_mod.spmv_bool(rp, col, xb))
+    xt = np.abs(x32)
+    y, _ = _sweep(env, g, gcs.MIN_PLUS_F32, xt)
+    assert np.array_equal(y, oracle_mod.spmv_min_plus(rp, col, val, xt, np.float32))
