@@ -37,7 +37,7 @@ def test_biobank_two_column_groups(synth_mod, oracle_mod):
     y64 = torch.empty(spec.n_rows, dtype=torch.float64, device="cuda")
     yo = np.zeros(rows.size)
     absum = np.zeros(rows.size)
-    devs = []
+    devs, grams = [], []
     for gi, (c0, nc) in enumerate(groups):
         t = time.time()
         rp, col, val = synth_mod.genotype(spec, col0=c0, ncols=nc)
@@ -59,7 +59,8 @@ def test_biobank_two_column_groups(synth_mod, oracle_mod):
         a, b = oracle_mod.spmv_f64_rows(rows, rp, col, val, x32.astype(np.float64))
         yo += a
         absum += b
-        del rp, col, val, g
+        grams.append(g)
+        del rp, col, val
     for d in devs:
         d.check()
     e32 = np.abs(y32.cpu().numpy()[rows].astype(np.float64) - yo)
@@ -67,3 +68,15 @@ def test_biobank_two_column_groups(synth_mod, oracle_mod):
     _say(f"max rel err fp32 {np.max(e32 / absum):.2e}, fp32 -> fp64 {np.max(e64 / absum):.2e}")
     assert np.all(e32 <= 1e-5 * absum)
     assert np.all(e64 <= 1e-12 * absum)
+    # the two groups merged into one grammar (gcs_merge_grammars), one sweep
+    del devs
+    t = time.time()
+    gm = gcs.merge_grammars(grams)
+    _say(f"merged in {time.time() - t:.0f}s: {gm.stats()['nnz']} nonzeros, L={gm.stats()['depth']}")
+    del grams
+    dm = gcs.upload(gm, gcs.PLUS_F32)
+    ym = dm.sweep_right(xd)
+    dm.check()
+    em = np.abs(ym.cpu().numpy()[rows].astype(np.float64) - yo)
+    _say(f"merged: max rel err fp32 {np.max(em / absum):.2e}")
+    assert np.all(em <= 1e-5 * absum)
