@@ -487,34 +487,94 @@ __device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int3
 }
 
 // Level-0 emission of the Boolean policy from LDS.  Level 0's roots are bare
-// terminals, one bit each in T; with level 0's groups cut by column
-// sub-slice, a run of consecutive groups of one sub-slice reads its roots
-// from a window of at most kWinBytes of T.  A workgroup of kWinBlock lanes
-// copies its chunk's window into LDS once (16-byte loads), then:
-//  - a run of short groups (at most kWinLong roots each): lane j takes
-//    groups j, j + kWinBlock, ..., kWinQ of them at a time with all their
-//    index loads issued together, ORs each group's bits from LDS (its first
-//    root first, the rest only while the OR is 0) and stores 1 into its row;
-//  - a long group (one per chunk): the lanes stride over its roots and the
-//    workgroup ORs their bits.
-// A root then costs its 4-byte index in a streamed list instead of an L2
-// request of its own.  Workgroup b takes chunk b: a chunk touches HBM only
-// to stream its lists and load its window once, so it gains nothing from
-// its slice's XCD, and the slices' level-0 work differs.
+// terminals, one bit each in T, and a Boolean emission is an idempotent
+// store (y[row] = 1 when a root's bit is set), so level 0 needs no groups:
+// the upload lists its (row, terminal) pairs per column sub-slice in row
+// order, cut into chunks whose terminals lie in a window of at most
+// kWinBytes of T, and packs every pair into one 32-bit word:
+//   bits [0, 19): the terminal's bit offset from the window's first byte
+//                 (kWordSkip: no terminal, the word only advances the row);
+//   bits [19, 32): the row's increase over the previous word's row (the
+//                 chunk's first row for its first word), at most
+//                 kWordMaxDelta; a longer gap is bridged by skip words.
+// A chunk's words start at a multiple of kWinWords and are padded to one
+// with zero-increase skip words.  A workgroup of kWinBlock lanes copies its
+// chunk's window into LDS once (16-byte loads), then takes kWinWords
+// consecutive words per lane per round: a prefix sum of the increases
+// (in the lane, then over the workgroup) gives each word's row, and the bit
+// comes from LDS.  A root then costs 4 streamed bytes and no L2 request of
+// its own.  Workgroup b takes chunk b: a chunk touches HBM only to stream
+// its words and load its window once, so it gains nothing from its slice's
+// XCD, and the slices' level-0 work differs.
 constexpr int kWinBlock = 1024;
-constexpr int kWinQ = 8;                  // groups per lane in flight
-constexpr int kWinLong = 64;              // longer groups get a chunk (and the whole workgroup) of their own
+constexpr int kWinWords = 8;              // words per lane and round (two 16-byte loads)
 constexpr int32_t kWinBytes = 60 * 1024;  // LDS window: bytes of packed terminals, a multiple of 16
+constexpr int kWordPosBits = 19;
+constexpr uint32_t kWordSkip = (1u << kWordPosBits) - 1;
+constexpr int32_t kWordMaxDelta = (1 << (32 - kWordPosBits)) - 1;
+static_assert((uint32_t)kWinBytes * 8 <= kWordSkip, "every bit of a window has an offset below kWordSkip");
 
 struct WinArgs {
-    // per chunk: first group, end group (-1: one long group), window [b0, b1)
-    // in bytes of T (multiples of 16)
+    // per chunk two int4: {first word, end word, window [b0, b1) in bytes of
+    // T (multiples of 16)} and {row of the first word, 0, 0, 0}
     const int4* chunk;
-    const int32_t* erow;  // level 0's (cut) groups
-    const int32_t* eoff;
-    const int32_t* epos;
+    const uint32_t* word;
     int32_t n_chunks;
 };
+
+// Exclusive prefix sum over the workgroup's lanes (v >= 0); *total gets the
+// sum of all.  Every lane calls it; wsum holds one slot per wave.
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_sum(int32_t v, int32_t* wsum, int32_t* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int32_t t = wsum[w];
+        before += w < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // wsum is rewritten by the next call
+    *total = all;
+    return before + inc - v;
+}
+
+// One round of a chunk: this lane's kWinWords words from word i0 (skip words
+// past e1) and each word's row; *row_base advances past the round.  Called
+// by every lane of the workgroup.
+__device__ __forceinline__ void window_round(const uint32_t* __restrict__ words, int32_t i0, int32_t e1,
+                                             int32_t* row_base, int32_t* wsum, uint32_t (&wd)[kWinWords],
+                                             int32_t (&row)[kWinWords])
+{
+    if (i0 < e1) {
+        const uint4 u0 = ((const uint4*)(words + i0))[0], u1 = ((const uint4*)(words + i0))[1];
+        wd[0] = u0.x, wd[1] = u0.y, wd[2] = u0.z, wd[3] = u0.w;
+        wd[4] = u1.x, wd[5] = u1.y, wd[6] = u1.z, wd[7] = u1.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWinWords; ++i) wd[i] = kWordSkip;
+    }
+    int32_t inc = 0;
+#pragma unroll
+    for (int i = 0; i < kWinWords; ++i) {
+        inc += (int32_t)(wd[i] >> kWordPosBits);
+        row[i] = inc;
+    }
+    int32_t total;
+    const int32_t before = block_exclusive_sum<kWinBlock>(inc, wsum, &total) + *row_base;
+#pragma unroll
+    for (int i = 0; i < kWinWords; ++i) row[i] += before;
+    *row_base += total;
+}
 
 template <class P>
 __global__ __launch_bounds__(kWinBlock) void window_emit_kernel(WinArgs w, const typename P::A* __restrict__ T,
@@ -522,37 +582,21 @@ __global__ __launch_bounds__(kWinBlock) void window_emit_kernel(WinArgs w, const
 {
     static_assert(kBitTerms<P> && kDirectEmit<P>, "window emission reads terminal bits and stores into y");
     extern __shared__ __align__(16) unsigned char win[];
-    const int4 ch = w.chunk[blockIdx.x];
-    const int4* src = (const int4*)(T + ch.z);
+    __shared__ int32_t wsum[kWinBlock / 64];
+    const int4 c0 = w.chunk[2 * blockIdx.x], c1 = w.chunk[2 * blockIdx.x + 1];
+    const int4* src = (const int4*)((const unsigned char*)T + c0.z);
     int4* dst = (int4*)win;
-    for (int32_t i = threadIdx.x; i < (ch.w - ch.z) / 16; i += kWinBlock) dst[i] = src[i];
+    for (int32_t i = threadIdx.x; i < (c0.w - c0.z) / 16; i += kWinBlock) dst[i] = src[i];
     __syncthreads();
-    auto bit = [&](int32_t t) -> uint32_t { return (win[(t >> 3) - ch.z] >> (t & 7)) & 1u; };
-    if (ch.y < 0) {  // one long group
-        const int32_t e0 = w.eoff[ch.x], e1 = w.eoff[ch.x + 1];
-        uint32_t v = 0;
-        for (int32_t e = e0 + threadIdx.x; e < e1; e += kWinBlock) v |= bit(w.epos[e]);
-        if (__syncthreads_or((int)v) && threadIdx.x == 0) y[w.erow[ch.x]] = 1;
-        return;
-    }
-    for (int32_t base = ch.x; base < ch.y; base += kWinQ * kWinBlock) {
-        int32_t e0[kWinQ], e1[kWinQ], row[kWinQ];
+    int32_t row_base = c1.x;
+    for (int32_t base = c0.x; base < c0.y; base += kWinBlock * kWinWords) {
+        uint32_t wd[kWinWords];
+        int32_t row[kWinWords];
+        window_round(w.word, base + (int32_t)threadIdx.x * kWinWords, c0.y, &row_base, wsum, wd, row);
 #pragma unroll
-        for (int q = 0; q < kWinQ; ++q) {
-            const int32_t gi = min(base + threadIdx.x + q * kWinBlock, ch.y - 1);
-            e0[q] = w.eoff[gi];
-            e1[q] = w.eoff[gi + 1];
-            row[q] = w.erow[gi];
-        }
-        int32_t t[kWinQ];
-#pragma unroll
-        for (int q = 0; q < kWinQ; ++q) t[q] = w.epos[e0[q]];  // every group has a root
-#pragma unroll
-        for (int q = 0; q < kWinQ; ++q) {
-            if (base + threadIdx.x + q * kWinBlock >= ch.y) continue;
-            uint32_t v = bit(t[q]);
-            for (int32_t e = e0[q] + 1; e < e1[q] && !v; ++e) v = bit(w.epos[e]);
-            if (v) y[row[q]] = 1;
+        for (int i = 0; i < kWinWords; ++i) {
+            const uint32_t t = wd[i] & kWordSkip;
+            if (t != kWordSkip && ((win[t >> 3] >> (t & 7)) & 1u)) y[row[i]] = 1;
         }
     }
 }
@@ -997,6 +1041,56 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     } else {
         issue_before_row(old);
         if (valid && live) *r = comb_row<P, VW>(old, s);
+    }
+}
+
+// Level-0 emission of the batched Boolean sweep from the same chunks and
+// words as window_emit_kernel: every round's (row, terminal) pairs are
+// staged in LDS, then teams of the least power of two >= B lanes take one
+// pair at a time, lane b reading vector b of the terminal's row of T (or
+// computing it, with the leaves in the sweep) and storing 1 into Y's row
+// where it is set.  (One vector per lane: the level launches' lanes may take
+// several, ba.vb_log2 counts those.)
+template <class P, bool LEAVES>
+__global__ __launch_bounds__(kWinBlock) void window_batch_kernel(WinArgs w, BatchArgs ba,
+                                                                 const typename P::A* __restrict__ T,
+                                                                 typename P::A* __restrict__ Y)
+{
+    static_assert(kDirectEmit<P>, "window emission stores into Y");
+    __shared__ int32_t wsum[kWinBlock / 64];
+    __shared__ int2 pair[kWinBlock * kWinWords / 2];
+    const int4 c0 = w.chunk[2 * blockIdx.x], c1 = w.chunk[2 * blockIdx.x + 1];
+    const int32_t B = ba.B;
+    int32_t lg = 0;
+    while ((1 << lg) < B) ++lg;
+    const int32_t per = kWinBlock >> lg, team = threadIdx.x >> lg, b = threadIdx.x & ((1 << lg) - 1);
+    const int64_t tb = (int64_t)c0.z * 8;  // terminal at the window's first bit
+    int32_t row_base = c1.x;
+    for (int32_t base = c0.x; base < c0.y; base += kWinBlock * kWinWords) {
+        uint32_t wd[kWinWords];
+        int32_t row[kWinWords];
+        window_round(w.word, base + (int32_t)threadIdx.x * kWinWords, c0.y, &row_base, wsum, wd, row);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // the round's pairs in two halves of LDS
+#pragma unroll
+            for (int i = 0; i < kWinWords / 2; ++i) {
+                const uint32_t t = wd[h * (kWinWords / 2) + i] & kWordSkip;
+                pair[threadIdx.x * (kWinWords / 2) + i] =
+                    make_int2(t == kWordSkip ? -1 : row[h * (kWinWords / 2) + i], (int32_t)(tb + t));
+            }
+            __syncthreads();
+            if (b < B)
+                for (int32_t j = team; j < kWinBlock * kWinWords / 2; j += per) {
+                    const int2 q = pair[j];
+                    if (q.x < 0) continue;
+                    const typename P::A v =
+                        LEAVES ? P::leaf(((const typename P::W*)ba.V)[ba.tval[q.y]],
+                                         ((const typename P::X*)ba.X)[(int64_t)ba.tcol[q.y] * B + b])
+                               : T[(int64_t)q.y * B + b];
+                    direct(&Y[(int64_t)q.x * B + b], v);
+                }
+            __syncthreads();
+        }
     }
 }
 

@@ -47,7 +47,8 @@ struct gcs_device {
     bool l0_on = false;                 // level 0's emission groups cut by sub-slice
     int64_t grp_skip = 0;               // groups not uploaded at the start of erow / eoff (level 0's when cut)
     int32_t l0_sub = 1;                 // into this many sub-slices per slice
-    bool win_on = false;                // Boolean level-0 emission by window_emit_kernel
+    bool win_on = false;                // Boolean level-0 emission by window_emit_kernel (words, no groups)
+    int64_t win_words = 0;
     gcs::WinArgs win{};
     int32_t win_grid = 0;
     size_t win_lds = 0;
@@ -108,7 +109,7 @@ size_t v_bytes(gcs_policy p) { return elem_bytes(p); }
 inline size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Image {
-    size_t child, ptsrc, erow, eoff, epos, chunk, l0row, l0off, wchunk, tcol, tval, V, table, flat, total;
+    size_t child, ptsrc, erow, eoff, epos, chunk, l0row, l0off, wchunk, wword, tcol, tval, V, table, flat, total;
 };
 
 // roots emitted at level k (the same whether or not level 0's groups are cut)
@@ -188,16 +189,19 @@ Level0Plan level0_plan(const Grammar& g, gcs_policy p)
         pl.S = std::max(1, pl.S);
     } else if (pl.window) {
         // the widest slice's terminals in windows of about kWinTarget bytes
-        // (at most kWinBytes with alignment; smaller windows measured faster:
-        // the copy graph's level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB,
-        // 2.02 ms at 26 KB; sixteen groups per lane instead of eight: 2.77 ms)
+        // (at most kWinBytes with alignment; smaller windows measured faster
+        // with the earlier, group-based window kernel on the copy graph: its
+        // level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB, 2.02 ms at 26 KB)
         pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kWinTarget)));
         pl.cut = true;
     } else {
         pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
         pl.cut = pl.S > 1;
     }
-    pl.window = pl.window && pl.cut;
+    // a window holds a chunk's terminals, which lie in one sub-slice of at
+    // most ceil(widest / S) terminals; with the 16-byte alignment of both
+    // ends that is at most ceil(widest / S) / 8 + 32 bytes
+    pl.window = pl.window && pl.cut && ((widest + pl.S - 1) / pl.S + 7) / 8 + 32 <= kWinBytes;
     return pl;
 }
 
@@ -211,38 +215,26 @@ void per_slice(Fn fn)
 }
 
 // Level-0 groups after the cut (one per run of equal sub-slice inside a
-// group), and (*n_long) how many of them have more than kWinLong roots.
-int64_t level0_split_groups(const Grammar& g, int32_t S, int64_t* n_long = nullptr)
+// group).
+int64_t level0_split_groups(const Grammar& g, int32_t S)
 {
     const Level& l = g.lv[0];
     const auto t0 = slice_terms(g);
-    std::array<int64_t, kSlices> n{}, nl{};
+    std::array<int64_t, kSlices> n{};
     per_slice([&](int x) {
-        int64_t c = 0, cl = 0;
+        int64_t c = 0;
         for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
             int32_t prev = -1;
-            int64_t run = 0;
             for (int64_t e = g.eoff[l.grp_off + gi]; e < g.eoff[l.grp_off + gi + 1]; ++e) {
                 const int32_t s = sub_of(g.epos[e], x, t0, S);
-                if (s != prev) {
-                    cl += run > kWinLong;
-                    run = 0;
-                    ++c;
-                }
-                ++run;
+                c += s != prev;
                 prev = s;
             }
-            cl += run > kWinLong;
         }
         n[x] = c;
-        nl[x] = cl;
     });
-    int64_t total = 0, tl = 0;
-    for (int x = 0; x < kSlices; ++x) {
-        total += n[x];
-        tl += nl[x];
-    }
-    if (n_long) *n_long = tl;
+    int64_t total = 0;
+    for (int x = 0; x < kSlices; ++x) total += n[x];
     return total;
 }
 
@@ -317,60 +309,106 @@ void level0_split(const Grammar& g, int32_t S, Level0Split& out)
     });
 }
 
-// Window chunks of a Boolean level 0 after its cut, per slice and
-// sub-slice: each group of more than kWinLong roots alone (end -1), the
-// groups between them in runs of at most run_groups; each chunk with the
-// 16-byte aligned range of T bytes its roots' bits lie in.  False if a range
-// exceeds kWinBytes.
-size_t window_chunk_bound(int64_t groups, int64_t n_long, int32_t S)
+// The word stream of a Boolean level 0 after its cut (see
+// window_emit_kernel): per slice and sub-slice, the roots in the cut's
+// (row) order, in chunks of at most window_chunk_entries roots, each chunk
+// with the 16-byte aligned range of T bytes its roots' bits lie in and the
+// row of its first root.  About an 8192th of the roots per chunk: many
+// chunks per workgroup slot of the device (balance), each still loading its
+// window once.  Two int4 per chunk.
+int64_t window_chunk_entries(int64_t roots)
 {
-    return (size_t)(groups / (kWinQ * kWinBlock) + 2 * (n_long + (int64_t)kSlices * S) + 2);
+    const int64_t ce = std::max<int64_t>((int64_t)kWinBlock * kWinWords, roots / 8192);
+    return (ce + kWinWords - 1) / kWinWords * kWinWords;
+}
+size_t window_chunk_bound(int64_t roots, int32_t S)
+{
+    return (size_t)(roots / window_chunk_entries(roots) + (int64_t)kSlices * S + 1);
+}
+// the roots, the skip words (the rows a run's skips bridge add up to fewer
+// than n_rows) and every chunk's padding
+size_t window_word_bound(int64_t roots, int32_t S, int64_t n_rows)
+{
+    return (size_t)(roots + (int64_t)kSlices * S * (n_rows / kWordMaxDelta + 1) +
+                    (int64_t)kWinWords * (int64_t)window_chunk_bound(roots, S));
 }
 
-bool build_window_chunks(const Level0Split& l0, int64_t run_groups, std::vector<int4>& wch,
-                         int32_t wsl[kSlices + 1])
+// False (with the error set) if a window exceeds kWinBytes or rows decrease
+// inside a sub-slice.
+bool build_window_words(const Level0Split& l0, int64_t n_rows, std::vector<uint32_t>& words, std::vector<int4>& wch)
 {
     const int32_t S = l0.S;
-    std::array<std::vector<int4>, kSlices> part;
+    const int64_t ce = window_chunk_entries((int64_t)l0.pos.size());
+    std::array<std::vector<uint32_t>, kSlices> pw;
+    std::array<std::vector<int4>, kSlices> pc;
     std::array<int, kSlices> ok{};
     per_slice([&](int x) {  // each slice on a thread of its own
-        std::vector<int4>& out = part[x];
-        auto push = [&](int64_t g0, int64_t g1, bool alone) {
-            int64_t tmin = INT64_MAX, tmax = -1;
-            for (int64_t e = l0.off[g0]; e < l0.off[g1]; ++e) {
-                tmin = std::min<int64_t>(tmin, l0.pos[e]);
-                tmax = std::max<int64_t>(tmax, l0.pos[e]);
-            }
-            const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
-            if (b1 - b0 > kWinBytes) return false;
-            out.push_back(make_int4((int32_t)g0, alone ? -1 : (int32_t)g1, (int32_t)b0, (int32_t)b1));
-            return true;
-        };
+        std::vector<uint32_t>& W = pw[x];
+        std::vector<int4>& Ch = pc[x];
         ok[x] = 1;
         for (int32_t s = 0; s < S && ok[x]; ++s) {
-            const int64_t ge = l0.sgs[(size_t)x * S + s + 1];
-            int64_t run0 = l0.sgs[(size_t)x * S + s];
-            for (int64_t gi = run0; gi <= ge && ok[x]; ++gi) {
-                const bool end = gi == ge;
-                const bool longg = !end && l0.off[gi + 1] - l0.off[gi] > kWinLong;
-                if (end || longg || gi - run0 == run_groups) {
-                    if (gi > run0 && !push(run0, gi, false)) ok[x] = 0;
-                    run0 = gi;
+            const int64_t g0 = l0.sgs[(size_t)x * S + s], g1 = l0.sgs[(size_t)x * S + s + 1];
+            if (g0 == g1) continue;
+            int64_t gi = g0;
+            const int64_t r_end = l0.off[g1];
+            for (int64_t e = l0.off[g0]; e < r_end && ok[x];) {
+                const int64_t ee = std::min<int64_t>(r_end, e + ce);
+                int64_t tmin = INT64_MAX, tmax = -1;
+                for (int64_t q = e; q < ee; ++q) {
+                    tmin = std::min<int64_t>(tmin, l0.pos[q]);
+                    tmax = std::max<int64_t>(tmax, l0.pos[q]);
                 }
-                if (longg && ok[x]) {
-                    if (!push(gi, gi + 1, true)) ok[x] = 0;
-                    run0 = gi + 1;
+                const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
+                if (b1 - b0 > kWinBytes) {
+                    ok[x] = 0;
+                    break;
                 }
+                while (l0.off[gi + 1] <= e) ++gi;
+                const int32_t row0 = l0.row[gi];
+                const size_t w0 = W.size();
+                int32_t prev = row0;
+                for (int64_t q = e; q < ee; ++q) {
+                    while (l0.off[gi + 1] <= q) ++gi;
+                    const int32_t r = l0.row[gi];
+                    if (r < prev || r >= n_rows) {
+                        ok[x] = -1;
+                        break;
+                    }
+                    int64_t d = r - prev;
+                    for (; d > kWordMaxDelta; d -= kWordMaxDelta)
+                        W.push_back(((uint32_t)kWordMaxDelta << kWordPosBits) | kWordSkip);
+                    W.push_back(((uint32_t)d << kWordPosBits) | (uint32_t)(l0.pos[q] - b0 * 8));
+                    prev = r;
+                }
+                while (W.size() % kWinWords) W.push_back(kWordSkip);
+                Ch.push_back(make_int4((int32_t)w0, (int32_t)W.size(), (int32_t)b0, (int32_t)b1));
+                Ch.push_back(make_int4(row0, 0, 0, 0));
+                e = ee;
             }
         }
     });
+    words.clear();
     wch.clear();
     for (int x = 0; x < kSlices; ++x) {
-        if (!ok[x]) return false;
-        wsl[x] = (int32_t)wch.size();
-        wch.insert(wch.end(), part[x].begin(), part[x].end());
+        if (ok[x] != 1) {
+            set_error(ok[x] == 0 ? "internal error: a level-0 window exceeds the LDS budget"
+                                 : "level-0 emission rows are not in ascending order within a slice");
+            return false;
+        }
+        if (words.size() + pw[x].size() >= (size_t)INT32_MAX) {
+            set_error("level-0 word stream exceeds the 32-bit index space");
+            return false;
+        }
+        const int32_t base = (int32_t)words.size();
+        words.insert(words.end(), pw[x].begin(), pw[x].end());
+        for (size_t i = 0; i < pc[x].size(); i += 2) {
+            int4 c = pc[x][i];
+            c.x += base;
+            c.y += base;
+            wch.push_back(c);
+            wch.push_back(pc[x][i + 1]);
+        }
     }
-    wsl[kSlices] = (int32_t)wch.size();
     return true;
 }
 
@@ -388,8 +426,9 @@ size_t chunk_bound(const Grammar& g, int64_t g0_split)
     return (G + K - 1) / K + 2 * ((C + K - 1) / K) + (size_t)kSlices * (g.L + 1) + 1;
 }
 
-void build_chunks(const Grammar& g, const Level0Split* l0, std::vector<int32_t>& chunk, std::vector<int64_t>& off,
-                  std::vector<std::array<int32_t, kSlices + 1>>& sl)
+// none0: level 0 has no groups on the device (its Boolean words instead)
+void build_chunks(const Grammar& g, const Level0Split* l0, bool none0, std::vector<int32_t>& chunk,
+                  std::vector<int64_t>& off, std::vector<std::array<int32_t, kSlices + 1>>& sl)
 {
     chunk.clear();
     off.assign((size_t)g.L + 1, 0);
@@ -401,6 +440,7 @@ void build_chunks(const Grammar& g, const Level0Split* l0, std::vector<int32_t>&
         const int32_t* eo = cut ? l0->off.data() : g.eoff.data() + l.grp_off;
         const int64_t* gsl = cut ? l0->gsl : l.gsl;
         off[k] = (int64_t)chunk.size();
+        if (k == 0 && none0) continue;
         for (int x = 0; x < kSlices; ++x) {
             sl[k][x] = (int32_t)((int64_t)chunk.size() - off[k]);
             int64_t gi = gsl[x];
@@ -438,8 +478,11 @@ size_t flat_section_words(const Grammar& g)
 Image image_layout(const Grammar& g, gcs_policy p)
 {
     const Level0Plan pl = level0_plan(g, p);
-    int64_t n_long = 0;
-    const int64_t g0 = pl.cut ? level0_split_groups(g, pl.S, &n_long) : 0;
+    const int64_t g0 = pl.cut ? level0_split_groups(g, pl.S) : 0;
+    // level 0's roots; with windows the device holds their words instead of
+    // their groups and root positions, and the root list starts at level 1's
+    const int64_t r0 = g.lv.empty() || g.lv[0].ngrp == 0 ? 0 : g.eoff[g.lv[0].grp_off + g.lv[0].ngrp];
+    const size_t rskip = pl.window ? (size_t)r0 : 0;
     Image m{};
     size_t o = 0;
     m.child = o;
@@ -454,15 +497,18 @@ Image image_layout(const Grammar& g, gcs_policy p)
     m.eoff = o;
     o = al256(o + (g.eoff.size() - skip) * 4);
     m.epos = o;
-    o = al256(o + g.epos.size() * 4);
+    o = al256(o + (g.epos.size() - rskip) * 4);
     m.chunk = o;
     o = al256(o + chunk_bound(g, g0) * 4);
+    const bool groups0 = pl.cut && !pl.window;  // level 0's cut groups on the device
     m.l0row = o;
-    o = al256(o + (pl.cut ? (size_t)g0 * 4 : 0));
+    o = al256(o + (groups0 ? (size_t)g0 * 4 : 0));
     m.l0off = o;
-    o = al256(o + (pl.cut ? (size_t)(g0 + 1) * 4 : 0));
+    o = al256(o + (groups0 ? (size_t)(g0 + 1) * 4 : 0));
     m.wchunk = o;
-    o = al256(o + (pl.window ? window_chunk_bound(g0, n_long, pl.S) * sizeof(int4) : 0));
+    o = al256(o + (pl.window ? 2 * window_chunk_bound(r0, pl.S) * sizeof(int4) : 0));
+    m.wword = o;
+    o = al256(o + (pl.window ? window_word_bound(r0, pl.S, g.n_rows) * 4 : 0));
     m.tcol = o;
     o = al256(o + g.tcol.size() * 4);
     m.tval = o;
@@ -806,6 +852,9 @@ LevelArgs make_args(const gcs_device* d, int64_t k)
     if (k == 1 && d->l0_on) {  // level 0's groups cut by sub-slice
         a.erow = d->l0row;
         a.eoff = d->l0off;
+    } else if (k == 1 && d->win_on) {  // no level-0 groups on the device (never read)
+        a.erow = d->erow;
+        a.eoff = d->eoff;
     } else {  // the uploaded sections begin at group grp_skip
         a.erow = d->erow + (e.grp_off - d->grp_skip);
         a.eoff = d->eoff + (e.grp_off - d->grp_skip);
@@ -899,7 +948,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             mark();
         }
         if constexpr (kBitTerms<P>) {
-            if (k == 1 && d->win_on) {  // level 0's emission from LDS windows of T
+            if (k == 1 && d->win_on) {  // level 0's emission: words, bits from LDS windows of T
                 mark();
                 window_emit_kernel<P><<<d->win_grid, kWinBlock, d->win_lds, s>>>(d->win, arena, y);
                 mark();
@@ -997,9 +1046,16 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
         ba.pb_pt = ceil_div(mp, per * kBinItems);
         ba.pb_emit = ceil_div(mg, per);
         const int64_t grid = (int64_t)kSlices * (ba.pb_bin + ba.pb_pt + ba.pb_emit);
-        if (grid <= 0) continue;
-        if (leaves) launch_level_batch<P, true>(VW, grid, ba, arena, acc, s);
-        else launch_level_batch<P, false>(VW, grid, ba, arena, acc, s);
+        if (grid > 0) {
+            if (leaves) launch_level_batch<P, true>(VW, grid, ba, arena, acc, s);
+            else launch_level_batch<P, false>(VW, grid, ba, arena, acc, s);
+        }
+        if constexpr (kBitTerms<P>) {
+            if (k == 1 && d->win_on) {  // level 0's emission from its words, vector by vector
+                if (leaves) window_batch_kernel<P, true><<<d->win_grid, kWinBlock, 0, s>>>(d->win, ba, arena, acc);
+                else window_batch_kernel<P, false><<<d->win_grid, kWinBlock, 0, s>>>(d->win, ba, arena, acc);
+            }
+        }
     }
     const int64_t n = d->n_rows * B;
     if (n > 0 && !kDirectEmit<P>) {
@@ -1095,28 +1151,35 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     const gcs::Level0Plan l0_plan = gcs::level0_plan(g, p);
     if (l0_plan.cut) gcs::level0_split(g, l0_plan.S, l0);
     const int64_t r0 = g.lv[0].ngrp > 0 ? g.eoff[g.lv[0].grp_off + g.lv[0].ngrp] : 0;  // level 0's roots: [0, r0)
+    const bool win_on = l0_plan.window;  // Boolean level 0 as words (window_emit_kernel)
     if (l0.on && ((int64_t)l0.pos.size() != r0 || g.lv[0].grp_off != 0 ||
-                  im.l0off - im.l0row < l0.row.size() * 4)) {
+                  (!win_on && im.l0off - im.l0row < l0.row.size() * 4))) {
         gcs::set_error("internal error: level-0 sub-slice cut does not match the image");
         return GCS_ESTATE;
     }
+    std::vector<uint32_t> words;
     std::vector<int4> wch;
-    int32_t wsl[gcs::kSlices + 1] = {};
-    // runs of about an 8192th of the groups: many chunks per workgroup slot
-    // of the device (balance), each still loading its window once
-    const int64_t run_groups = std::max<int64_t>(gcs::kWinQ * gcs::kWinBlock, (int64_t)l0.row.size() / 8192);
-    bool win_on = l0_plan.window && gcs::build_window_chunks(l0, run_groups, wch, wsl) && !wch.empty();
-    int64_t n_long = 0;
-    for (size_t gi = 0; win_on && gi + 1 < l0.off.size(); ++gi) n_long += l0.off[gi + 1] - l0.off[gi] > gcs::kWinLong;
-    if (win_on && wch.size() > gcs::window_chunk_bound((int64_t)l0.row.size(), n_long, l0.S)) {
-        gcs::set_error("internal error: more window chunks than the image holds");
-        return GCS_ESTATE;
+    if (win_on) {
+        if (!gcs::build_window_words(l0, g.n_rows, words, wch)) return GCS_ESTATE;
+        if (wch.size() > 2 * gcs::window_chunk_bound(r0, l0.S) ||
+            words.size() > gcs::window_word_bound(r0, l0.S, g.n_rows)) {
+            gcs::set_error("internal error: more window chunks or words than the image holds");
+            return GCS_ESTATE;
+        }
     }
     const size_t skip0 = l0.on ? (size_t)g.lv[0].ngrp : 0;  // the grammar's level-0 groups, not uploaded when cut
+    // with windows the root list on the device starts at level 1's roots:
+    // the uploaded group offsets are rebased by level 0's root count
+    const size_t rskip = win_on ? (size_t)r0 : 0;
+    std::vector<int32_t> eoff_rebased;
+    if (win_on) {
+        eoff_rebased.assign(g.eoff.begin() + (ptrdiff_t)skip0, g.eoff.end());
+        for (int32_t& v : eoff_rebased) v -= (int32_t)r0;
+    }
     std::vector<int32_t> chunk;
     std::vector<int64_t> chunk_off;
     std::vector<std::array<int32_t, gcs::kSlices + 1>> chunk_sl;
-    gcs::build_chunks(g, &l0, chunk, chunk_off, chunk_sl);
+    gcs::build_chunks(g, &l0, win_on, chunk, chunk_off, chunk_sl);
     if (chunk.size() > gcs::chunk_bound(g, l0.on ? (int64_t)l0.row.size() : 0)) {
         gcs::set_error("internal error: more emission chunks than the image holds");
         return GCS_ESTATE;
@@ -1129,13 +1192,16 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     } secs[] = {
         {im.child, g.child.data(), g.child.size() * 4}, {im.ptsrc, g.ptsrc.data(), g.ptsrc.size() * 4},
         {im.erow, g.erow.data() + skip0, (g.erow.size() - skip0) * 4},
-        {im.eoff, g.eoff.data() + skip0, (g.eoff.size() - skip0) * 4},
-        // the root list, level 0's part in the sub-slice order when cut
-        {im.epos, l0.on ? l0.pos.data() : g.epos.data(), (size_t)r0 * 4},
-        {im.epos + (size_t)r0 * 4, g.epos.data() + r0, (g.epos.size() - (size_t)r0) * 4},
+        {im.eoff, win_on ? eoff_rebased.data() : g.eoff.data() + skip0, (g.eoff.size() - skip0) * 4},
+        // the root list, level 0's part in the sub-slice order when cut (and
+        // left out with windows)
+        {im.epos, l0.on ? l0.pos.data() : g.epos.data(), (size_t)(r0 - (int64_t)rskip) * 4},
+        {im.epos + (size_t)(r0 - (int64_t)rskip) * 4, g.epos.data() + r0, (g.epos.size() - (size_t)r0) * 4},
         {im.chunk, chunk.data(), chunk.size() * 4},
-        {im.l0row, l0.row.data(), l0.row.size() * 4},   {im.l0off, l0.off.data(), l0.off.size() * 4},
-        {im.wchunk, wch.data(), win_on ? wch.size() * sizeof(int4) : 0},
+        {im.l0row, l0.row.data(), win_on ? 0 : l0.row.size() * 4},
+        {im.l0off, l0.off.data(), win_on ? 0 : l0.off.size() * 4},
+        {im.wchunk, wch.data(), wch.size() * sizeof(int4)},
+        {im.wword, words.data(), words.size() * 4},
         {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
     };
@@ -1156,24 +1222,25 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->L = g.L;
     d->arena_len = g.arena;
     d->lv = g.lv;
-    if (l0.on) {  // the device's view of level 0: the cut groups
-        d->lv[0].ngrp = (int64_t)l0.row.size();
-        for (int x = 0; x <= gcs::kSlices; ++x) d->lv[0].gsl[x] = l0.gsl[x];
-        d->l0_on = true;
+    if (l0.on) {  // the device's view of level 0: the cut groups, or none with windows
+        d->lv[0].ngrp = win_on ? 0 : (int64_t)l0.row.size();
+        for (int x = 0; x <= gcs::kSlices; ++x) d->lv[0].gsl[x] = win_on ? 0 : l0.gsl[x];
         d->l0_sub = l0.S;
-        d->l0row = (const int32_t*)(base + im.l0row);
-        d->l0off = (const int32_t*)(base + im.l0off);
+        if (!win_on) {
+            d->l0_on = true;
+            d->l0row = (const int32_t*)(base + im.l0row);
+            d->l0off = (const int32_t*)(base + im.l0off);
+        }
     }
     if (win_on) {
         d->win_on = true;
         d->win.chunk = (const int4*)(base + im.wchunk);
-        d->win.erow = d->l0row;
-        d->win.eoff = d->l0off;
-        d->win.epos = (const int32_t*)(base + im.epos);
-        d->win.n_chunks = (int32_t)wch.size();
-        d->win_grid = (int32_t)wch.size();
+        d->win.word = (const uint32_t*)(base + im.wword);
+        d->win.n_chunks = (int32_t)(wch.size() / 2);
+        d->win_grid = d->win.n_chunks;
+        d->win_words = (int64_t)words.size();
         int32_t mb = 0;
-        for (const int4& c : wch) mb = std::max(mb, c.w - c.z);
+        for (size_t i = 0; i < wch.size(); i += 2) mb = std::max(mb, wch[i].w - wch[i].z);
         d->win_lds = (size_t)std::max(mb, 16);
     }
     // emission team per level: about GCS_EMIT_PER_LANE (default 4) roots per
@@ -1243,7 +1310,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     while (d->tail_k0 > 1 && gcs::vblocks(d->largs[d->tail_k0 - 2]) <= tail_vb * quarters * d->tail_wgs) --d->tail_k0;
     // level 0's cut groups are emitted by a wide launch only (the narrow
     // levels' LDS image is built from the grammar's own groups)
-    if (d->l0_on) d->tail_k0 = std::max<int64_t>(d->tail_k0, 2);
+    if (d->l0_on || d->win_on) d->tail_k0 = std::max<int64_t>(d->tail_k0, 2);
     d->tail_nent = g.L + 2 - d->tail_k0;
     // emission mode of each wide launch: chunks where the groups are short
     // and uneven, teams elsewhere (GCS_EMIT_STREAM = 0 keeps teams, 1 takes
@@ -1270,9 +1337,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
                          (long long)d->tail_k0 - 1);
             std::fprintf(stderr,
                          "[gcs upload] level-0 emission in %d sub-slices per slice (%lld groups, %lld before); "
-                         "LDS windows %d (%d chunks, %zu bytes)\n",
-                         d->l0_on ? d->l0_sub : 0, (long long)d->lv[0].ngrp, (long long)g.lv[0].ngrp, (int)d->win_on,
-                         d->win_on ? d->win.n_chunks : 0, d->win_lds);
+                         "LDS windows %d (%d chunks, %lld words, %zu bytes)\n",
+                         d->l0_on || d->win_on ? d->l0_sub : 0, (long long)d->lv[0].ngrp, (long long)g.lv[0].ngrp,
+                         (int)d->win_on, d->win_on ? d->win.n_chunks : 0, (long long)d->win_words, d->win_lds);
         }
     }
     // the narrowest entries at the end run on workgroup 0 alone, in LDS: as

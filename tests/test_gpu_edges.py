@@ -169,8 +169,8 @@ def _window_matrix():
 def test_boolean_window_emission(env, oracle_mod, monkeypatch, capfd, split):
     """Boolean level-0 emission from LDS windows of the bit-packed terminals
     (default, and with 1 and 5 sub-slices) equals the level-kernel emission
-    without a cut and the oracle, overwrite and accumulate, including a group
-    longer than one window chunk."""
+    without a cut and the oracle, overwrite and accumulate, including a row
+    with more bare terminals than one window chunk holds."""
     torch, gcs = env
     n, m, rp, col = _window_matrix()
     g = gcs.build_grammar(rp, col, None, n_cols=m)
@@ -200,3 +200,67 @@ def test_boolean_window_emission(env, oracle_mod, monkeypatch, capfd, split):
         dev.free()
     assert np.array_equal(ys["window"][0], ref) and np.array_equal(ys["plain"][0], ref)
     assert np.array_equal(ys["window"][1], y0 | ref) and np.array_equal(ys["plain"][1], y0 | ref)
+
+
+def _far_rows_matrix():
+    """300,000 rows of which about one in 9,000 holds 1-40 random columns
+    (row gaps above the 8,191 a word's increase holds, bridged by skip
+    words), a run of 50 adjacent rows sharing 30 columns (rules) plus one
+    column each, and the last row."""
+    rng = np.random.default_rng(77)
+    n, m = 300_000, 120_000
+    rows = {}
+    far = np.arange(0, n, 9_000) + rng.integers(0, 400, size=(n + 8_999) // 9_000)
+    for r in far[far < n]:
+        rows[int(r)] = rng.choice(m, int(rng.integers(1, 41)), replace=False)
+    shared = rng.choice(m, 30, replace=False)
+    for r in range(150_000, 150_050):
+        rows[r] = np.unique(np.concatenate([shared, rng.choice(m, 1)]))
+    rows[n - 1] = rng.choice(m, 7, replace=False)
+    lens = np.zeros(n, np.int64)
+    for r, c in rows.items():
+        lens[r] = len(np.unique(c))
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    col = np.concatenate([np.unique(rows[r]) for r in sorted(rows)])
+    return n, m, rp, col.astype(np.int32)
+
+
+@pytest.mark.parametrize("split", [None, "3"])
+def test_boolean_window_far_rows(env, oracle_mod, monkeypatch, capfd, split):
+    """Boolean level-0 words across row gaps longer than one word's increase
+    (skip words): single vector overwrite and accumulate, and batched (B = 3,
+    with and without the leaves in the sweep), equal the oracle, with and
+    without windows."""
+    torch, gcs = env
+    n, m, rp, col = _far_rows_matrix()
+    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    rng = np.random.default_rng(8)
+    X = np.ascontiguousarray((rng.random((m, 3)) < np.array([0.3, 0.02, 1.0])).astype(np.uint8))
+    refs = [oracle_mod.spmv_bool(rp, col, X[:, b].copy()) for b in range(3)]
+    y0 = (rng.random(n) < 0.3).astype(np.uint8)
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    if split is None:
+        monkeypatch.delenv("GCS_LEVEL0_SPLIT", raising=False)
+    else:
+        monkeypatch.setenv("GCS_LEVEL0_SPLIT", split)
+    for window in ("1", "0"):
+        monkeypatch.setenv("GCS_LEVEL0_WINDOW", window)
+        capfd.readouterr()
+        dev = gcs.upload(g, gcs.BOOL_OR)
+        err = capfd.readouterr().err
+        line = [l for l in err.splitlines() if "LDS windows" in l]
+        assert len(line) == 1 and line[0].split("LDS windows ")[1].startswith(window), err
+        Xd = torch.from_numpy(X).cuda()
+        for b in range(3):
+            xb = torch.from_numpy(X[:, b].copy()).cuda()
+            assert np.array_equal(dev.sweep_right(xb).cpu().numpy(), refs[b]), (window, b)
+            ya = torch.from_numpy(y0.copy()).cuda()
+            dev.sweep_right_acc(xb, ya)
+            assert np.array_equal(ya.cpu().numpy(), y0 | refs[b]), (window, b)
+        for leaves in (False, True):
+            Y = dev.sweep_right_batch(Xd, leaves_in_sweep=leaves).cpu().numpy()
+            for b in range(3):
+                assert np.array_equal(Y[:, b], refs[b]), (window, leaves, b)
+        dev.check()
+        dev.free()

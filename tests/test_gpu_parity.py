@@ -385,9 +385,10 @@ def test_stream_emission_bit_identical(env, graph300k, monkeypatch, capfd, pol):
 
 @pytest.mark.parametrize("pol", ["bool", "min_plus_f32", "min_plus_f64"])
 def test_level0_subslice_cut_identical(env, oracle_mod, synth_mod, graph300k, monkeypatch, capfd, pol):
-    """Level-0 emission groups cut by column sub-slice (direct policies)
-    give the same y as the grammar's own groups and as the oracle, single
-    and batched, for several cut counts."""
+    """Level-0 emission groups cut by column sub-slice (direct policies;
+    Boolean: the word stream of LDS windows) give the same y as the grammar's
+    own groups and as the oracle, single and batched (both columns, with and
+    without the leaves in the sweep), for several cut counts."""
     torch, gcs = env
     spec, g = graph300k
     rp, col = synth_mod.copy_graph(spec)
@@ -395,11 +396,13 @@ def test_level0_subslice_cut_identical(env, oracle_mod, synth_mod, graph300k, mo
     if pol == "bool":
         x = (rng.random(spec.n) < 0.1).astype(np.uint8)
         ref = oracle_mod.spmv_bool(rp, col, x)
+        ref2 = oracle_mod.spmv_bool(rp, col, x[::-1].copy())
     else:
         dt = np.float32 if pol == "min_plus_f32" else np.float64
         x = (rng.random(spec.n) * 20).astype(dt)
         x[rng.random(spec.n) < 0.5] = np.inf
         ref = oracle_mod.spmv_min_plus(rp, col, None, x, dt)
+        ref2 = oracle_mod.spmv_min_plus(rp, col, None, x[::-1].copy(), dt)
     X = np.ascontiguousarray(np.stack([x, x[::-1].copy()], axis=1))
     monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
     for cut in ("1", "3", "16"):
@@ -411,10 +414,13 @@ def test_level0_subslice_cut_identical(env, oracle_mod, synth_mod, graph300k, mo
         assert sub == [int(cut)], err
         y = dev.sweep_right(torch.from_numpy(x).cuda())
         Y = dev.sweep_right_batch(torch.from_numpy(X).cuda())
+        YL = dev.sweep_right_batch(torch.from_numpy(X).cuda(), leaves_in_sweep=True)
         dev.check()
         _say(f"{pol} cut {cut}: {err.strip().splitlines()[-1]}")
         assert np.array_equal(y.cpu().numpy(), ref)
-        assert np.array_equal(Y[:, 0].cpu().numpy(), ref)
+        for Yv in (Y, YL):
+            assert np.array_equal(Yv[:, 0].cpu().numpy(), ref)
+            assert np.array_equal(Yv[:, 1].cpu().numpy(), ref2)
         dev.free()
 
 
