@@ -486,13 +486,14 @@ __device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int3
     }
 }
 
-// Level-0 emission of the Boolean policy from LDS.  Level 0's roots are bare
-// terminals, one bit each in T, and a Boolean emission is an idempotent
-// store (y[row] = 1 when a root's bit is set), so level 0 needs no groups:
-// the upload lists its (row, terminal) pairs per column sub-slice in row
-// order, cut into chunks whose terminals lie in a window of at most
-// kWinBytes of T, and packs every pair into one 32-bit word:
-//   bits [0, 19): the terminal's bit offset from the window's first byte
+// Level-0 emission of the direct policies (Boolean, tropical) from LDS.
+// Level 0's roots are bare terminals, and a direct emission updates y[row]
+// in place (a store of 1 where a bit is set; an atomic min), so level 0
+// needs no groups: the upload lists its (row, terminal) pairs per column
+// sub-slice in row order, cut into chunks whose terminals lie in a window of
+// at most kWinBytes of T, and packs every pair into one 32-bit word:
+//   bits [0, 19): the terminal's offset from the window's first terminal
+//                 (Boolean terminals are bits, the others values)
 //                 (kWordSkip: no terminal, the word only advances the row);
 //   bits [19, 32): the row's increase over the previous word's row (the
 //                 chunk's first row for its first word), at most
@@ -502,7 +503,8 @@ __device__ __forceinline__ void stream_block(const LevelArgs& a, int32_t b, int3
 // chunk's window into LDS once (16-byte loads), then takes kWinWords
 // consecutive words per lane per round: a prefix sum of the increases
 // (in the lane, then over the workgroup) gives each word's row, and the bit
-// comes from LDS.  A root then costs 4 streamed bytes and no L2 request of
+// comes from LDS; a lane combines its consecutive words of one row before
+// it updates y.  A root then costs 4 streamed bytes and no L2 request of
 // its own.  Workgroup b takes chunk b: a chunk touches HBM only to stream
 // its words and load its window once, so it gains nothing from its slice's
 // XCD, and the slices' level-0 work differs.
@@ -516,7 +518,8 @@ static_assert((uint32_t)kWinBytes * 8 <= kWordSkip, "every bit of a window has a
 
 struct WinArgs {
     // per chunk two int4: {first word, end word, window [b0, b1) in bytes of
-    // T (multiples of 16)} and {row of the first word, 0, 0, 0}
+    // T (multiples of 16)} and {row of the first word, the window's first
+    // terminal, 0, 0}
     const int4* chunk;
     const uint32_t* word;
     int32_t n_chunks;
@@ -580,7 +583,8 @@ template <class P>
 __global__ __launch_bounds__(kWinBlock) void window_emit_kernel(WinArgs w, const typename P::A* __restrict__ T,
                                                                 typename P::Y* __restrict__ y)
 {
-    static_assert(kBitTerms<P> && kDirectEmit<P>, "window emission reads terminal bits and stores into y");
+    static_assert(kDirectEmit<P>, "window emission updates y in place");
+    using A = typename P::A;
     extern __shared__ __align__(16) unsigned char win[];
     __shared__ int32_t wsum[kWinBlock / 64];
     const int4 c0 = w.chunk[2 * blockIdx.x], c1 = w.chunk[2 * blockIdx.x + 1];
@@ -593,11 +597,27 @@ __global__ __launch_bounds__(kWinBlock) void window_emit_kernel(WinArgs w, const
         uint32_t wd[kWinWords];
         int32_t row[kWinWords];
         window_round(w.word, base + (int32_t)threadIdx.x * kWinWords, c0.y, &row_base, wsum, wd, row);
+        A v[kWinWords];
 #pragma unroll
         for (int i = 0; i < kWinWords; ++i) {
             const uint32_t t = wd[i] & kWordSkip;
-            if (t != kWordSkip && ((win[t >> 3] >> (t & 7)) & 1u)) y[row[i]] = 1;
+            if (t == kWordSkip) v[i] = P::ident();
+            else if constexpr (kBitTerms<P>) v[i] = (win[t >> 3] >> (t & 7)) & 1u;
+            else v[i] = ((const A*)win)[t];
         }
+        // runs of one row (rows never decrease inside a chunk): one update
+        // each; an identity update touches nothing (skip words' rows)
+        A s = v[0];
+#pragma unroll
+        for (int i = 1; i < kWinWords; ++i) {
+            if (row[i] != row[i - 1]) {
+                direct(&y[row[i - 1]], s);
+                s = v[i];
+            } else {
+                s = P::comb(s, v[i]);
+            }
+        }
+        direct(&y[row[kWinWords - 1]], s);
     }
 }
 
@@ -1044,19 +1064,19 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     }
 }
 
-// Level-0 emission of the batched Boolean sweep from the same chunks and
-// words as window_emit_kernel: every round's (row, terminal) pairs are
-// staged in LDS, then teams of the least power of two >= B lanes take one
-// pair at a time, lane b reading vector b of the terminal's row of T (or
-// computing it, with the leaves in the sweep) and storing 1 into Y's row
-// where it is set.  (One vector per lane: the level launches' lanes may take
+// Level-0 emission of the batched sweep of a direct policy from the same
+// chunks and words as window_emit_kernel: every round's (row, terminal)
+// pairs are staged in LDS, then teams of the least power of two >= B lanes
+// take one pair at a time, lane b reading vector b of the terminal's row of
+// T (or computing it, with the leaves in the sweep) and updating Y's row in
+// place.  (One vector per lane: the level launches' lanes may take
 // several, ba.vb_log2 counts those.)
 template <class P, bool LEAVES>
 __global__ __launch_bounds__(kWinBlock) void window_batch_kernel(WinArgs w, BatchArgs ba,
                                                                  const typename P::A* __restrict__ T,
                                                                  typename P::A* __restrict__ Y)
 {
-    static_assert(kDirectEmit<P>, "window emission stores into Y");
+    static_assert(kDirectEmit<P>, "window emission updates Y in place");
     __shared__ int32_t wsum[kWinBlock / 64];
     __shared__ int2 pair[kWinBlock * kWinWords / 2];
     const int4 c0 = w.chunk[2 * blockIdx.x], c1 = w.chunk[2 * blockIdx.x + 1];
@@ -1064,7 +1084,7 @@ __global__ __launch_bounds__(kWinBlock) void window_batch_kernel(WinArgs w, Batc
     int32_t lg = 0;
     while ((1 << lg) < B) ++lg;
     const int32_t per = kWinBlock >> lg, team = threadIdx.x >> lg, b = threadIdx.x & ((1 << lg) - 1);
-    const int64_t tb = (int64_t)c0.z * 8;  // terminal at the window's first bit
+    const int64_t tb = c1.y;  // the window's first terminal
     int32_t row_base = c1.x;
     for (int32_t base = c0.x; base < c0.y; base += kWinBlock * kWinWords) {
         uint32_t wd[kWinWords];

@@ -158,50 +158,64 @@ inline int32_t sub_of(int64_t t, int x, const std::array<int64_t, kSlices + 1>& 
     return (int32_t)std::max<int64_t>(0, std::min<int64_t>(S - 1, sub));
 }
 
-// How level 0's emission is organized on upload.  Tropical policies: cut
-// into S sub-slices per slice when a slice's share of T exceeds
-// kLevel0Window.  Boolean: cut so that every sub-slice's bits fit one LDS
-// window, emitted by window_emit_kernel (its terminals are bits, so S is
-// small: 13 for 5e7 terminals).  GCS_LEVEL0_SPLIT=S forces a count (0: no
-// cut); GCS_LEVEL0_WINDOW=0 keeps the Boolean emission in the level kernel.
+// How level 0's emission is organized on upload (direct policies only).
+// By default as a word stream (window_emit_kernel): cut into S sub-slices
+// per slice so that every sub-slice's terminals fit one LDS window of
+// kWinBytes (Boolean terminals are bits, so S is small: 47 for 5e7
+// terminals; fp32 values need about 480).  Where no S up to
+// kLevel0MaxWindowSplit fits, or with GCS_LEVEL0_WINDOW=0, the level kernel
+// emits level 0's groups, cut into S sub-slices when a slice's share of T
+// exceeds kLevel0Window.  GCS_LEVEL0_SPLIT=S forces a count (0: no cut).
 struct Level0Plan {
     bool cut = false;     // level 0's groups are cut by sub-slice
     int32_t S = 1;        // sub-slices per slice
-    bool window = false;  // Boolean level-0 emission from LDS windows
+    bool window = false;  // level-0 emission as words from LDS windows
 };
+
+constexpr int32_t kLevel0MaxWindowSplit = 4096;
 
 Level0Plan level0_plan(const Grammar& g, gcs_policy p)
 {
     Level0Plan pl;
     if (!direct_emit(p) || g.lv.empty() || g.lv[0].ngrp == 0) return pl;
     const char* ew = std::getenv("GCS_LEVEL0_WINDOW");
-    pl.window = p == GCS_BOOL_OR && !(ew && std::atoi(ew) == 0);
+    const bool allow = !(ew && std::atoi(ew) == 0);
     // the largest slice's share of T (slices are weighted quantiles of the
     // first column, so their terminal counts differ)
-    const double term_bytes = p == GCS_BOOL_OR ? 0.125 : (double)elem_bytes(p);
+    const bool bits = p == GCS_BOOL_OR;
+    const int64_t eb = (int64_t)elem_bytes(p);
     const auto t0 = slice_terms(g);
     int64_t widest = 0;
     for (int x = 0; x < kSlices; ++x) widest = std::max(widest, t0[x + 1] - t0[x]);
-    const double per_slice = (double)widest * term_bytes;
+    const double per_slice = (double)widest * (bits ? 0.125 : (double)eb);
+    // a window holds a chunk's terminals, which lie in one sub-slice of at
+    // most ceil(widest / S) terminals, plus the 16-byte alignment of both ends
+    auto fits = [&](int64_t S) {
+        const int64_t span = (widest + S - 1) / S;
+        return (bits ? (span + 7) / 8 : span * eb) + 32 <= kWinBytes;
+    };
     if (const char* e = std::getenv("GCS_LEVEL0_SPLIT")) {
         pl.S = std::max(0, std::min(kLevel0MaxSplit, std::atoi(e)));
         pl.cut = pl.S >= 1;
         pl.S = std::max(1, pl.S);
-    } else if (pl.window) {
-        // the widest slice's terminals in windows of about kWinTarget bytes
-        // (at most kWinBytes with alignment; smaller windows measured faster
-        // with the earlier, group-based window kernel on the copy graph: its
-        // level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB, 2.02 ms at 26 KB)
-        pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kWinTarget)));
-        pl.cut = true;
-    } else {
-        pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
-        pl.cut = pl.S > 1;
+        pl.window = allow && pl.cut && fits(pl.S);
+        return pl;
     }
-    // a window holds a chunk's terminals, which lie in one sub-slice of at
-    // most ceil(widest / S) terminals; with the 16-byte alignment of both
-    // ends that is at most ceil(widest / S) / 8 + 32 bytes
-    pl.window = pl.window && pl.cut && ((widest + pl.S - 1) / pl.S + 7) / 8 + 32 <= kWinBytes;
+    if (allow) {
+        // Boolean: windows of about kWinTarget bytes (smaller windows
+        // measured faster with the earlier, group-based window kernel on the
+        // copy graph: its level 0 in 2.24 ms at 59 KB, 2.10 ms at 39 KB,
+        // 2.02 ms at 26 KB); values: the fewest sub-slices that fit
+        const double target = bits ? kWinTarget : (double)(kWinBytes - 64);
+        const int64_t S = std::max<int64_t>(1, (int64_t)std::ceil(per_slice / target));
+        if (S <= kLevel0MaxWindowSplit && fits(S)) {
+            pl.S = (int32_t)S;
+            pl.cut = pl.window = true;
+            return pl;
+        }
+    }
+    pl.S = (int32_t)std::max(1.0, std::min((double)kLevel0MaxSplit, std::ceil(per_slice / kLevel0Window)));
+    pl.cut = pl.S > 1;
     return pl;
 }
 
@@ -215,27 +229,43 @@ void per_slice(Fn fn)
 }
 
 // Level-0 groups after the cut (one per run of equal sub-slice inside a
-// group).
-int64_t level0_split_groups(const Grammar& g, int32_t S)
+// group), and how many skip words the word stream would need without chunk
+// boundaries (an upper bound: a chunk restarts its rows): a gap of d rows
+// between consecutive roots of one sub-slice takes (d - 1) / kWordMaxDelta.
+struct Level0Counts {
+    int64_t groups = 0, skips = 0;
+};
+
+Level0Counts level0_counts(const Grammar& g, int32_t S)
 {
     const Level& l = g.lv[0];
     const auto t0 = slice_terms(g);
-    std::array<int64_t, kSlices> n{};
+    std::array<int64_t, kSlices> n{}, sk{};
     per_slice([&](int x) {
-        int64_t c = 0;
+        int64_t c = 0, k = 0;
+        std::vector<int32_t> last((size_t)S, -1);
         for (int64_t gi = l.gsl[x]; gi < l.gsl[x + 1]; ++gi) {
+            const int32_t r = g.erow[l.grp_off + gi];
             int32_t prev = -1;
             for (int64_t e = g.eoff[l.grp_off + gi]; e < g.eoff[l.grp_off + gi + 1]; ++e) {
                 const int32_t s = sub_of(g.epos[e], x, t0, S);
-                c += s != prev;
+                if (s != prev) {
+                    ++c;
+                    if (last[s] >= 0 && r > last[s]) k += (r - last[s] - 1) / kWordMaxDelta;
+                    last[s] = r;
+                }
                 prev = s;
             }
         }
         n[x] = c;
+        sk[x] = k;
     });
-    int64_t total = 0;
-    for (int x = 0; x < kSlices; ++x) total += n[x];
-    return total;
+    Level0Counts out;
+    for (int x = 0; x < kSlices; ++x) {
+        out.groups += n[x];
+        out.skips += sk[x];
+    }
+    return out;
 }
 
 struct Level0Split {
@@ -325,17 +355,17 @@ size_t window_chunk_bound(int64_t roots, int32_t S)
 {
     return (size_t)(roots / window_chunk_entries(roots) + (int64_t)kSlices * S + 1);
 }
-// the roots, the skip words (the rows a run's skips bridge add up to fewer
-// than n_rows) and every chunk's padding
-size_t window_word_bound(int64_t roots, int32_t S, int64_t n_rows)
+// the roots, the skip words (bounded by level0_counts) and every chunk's
+// padding
+size_t window_word_bound(int64_t roots, int32_t S, int64_t skips)
 {
-    return (size_t)(roots + (int64_t)kSlices * S * (n_rows / kWordMaxDelta + 1) +
-                    (int64_t)kWinWords * (int64_t)window_chunk_bound(roots, S));
+    return (size_t)(roots + skips + (int64_t)kWinWords * (int64_t)window_chunk_bound(roots, S));
 }
 
-// False (with the error set) if a window exceeds kWinBytes or rows decrease
-// inside a sub-slice.
-bool build_window_words(const Level0Split& l0, int64_t n_rows, std::vector<uint32_t>& words, std::vector<int4>& wch)
+// eb: bytes per terminal value, 0 for bits.  False (with the error set) if
+// a window exceeds kWinBytes or rows decrease inside a sub-slice.
+bool build_window_words(const Level0Split& l0, int64_t n_rows, int64_t eb, std::vector<uint32_t>& words,
+                        std::vector<int4>& wch)
 {
     const int32_t S = l0.S;
     const int64_t ce = window_chunk_entries((int64_t)l0.pos.size());
@@ -358,8 +388,10 @@ bool build_window_words(const Level0Split& l0, int64_t n_rows, std::vector<uint3
                     tmin = std::min<int64_t>(tmin, l0.pos[q]);
                     tmax = std::max<int64_t>(tmax, l0.pos[q]);
                 }
-                const int64_t b0 = (tmin >> 3) & ~int64_t(15), b1 = ((tmax >> 3) + 16) & ~int64_t(15);
-                if (b1 - b0 > kWinBytes) {
+                const int64_t b0 = eb ? (tmin * eb) & ~int64_t(15) : (tmin >> 3) & ~int64_t(15);
+                const int64_t b1 = eb ? ((tmax + 1) * eb + 15) & ~int64_t(15) : ((tmax >> 3) + 16) & ~int64_t(15);
+                const int64_t term0 = eb ? b0 / eb : b0 * 8;  // the window's first terminal
+                if (b1 - b0 > kWinBytes || term0 > INT32_MAX) {
                     ok[x] = 0;
                     break;
                 }
@@ -377,12 +409,12 @@ bool build_window_words(const Level0Split& l0, int64_t n_rows, std::vector<uint3
                     int64_t d = r - prev;
                     for (; d > kWordMaxDelta; d -= kWordMaxDelta)
                         W.push_back(((uint32_t)kWordMaxDelta << kWordPosBits) | kWordSkip);
-                    W.push_back(((uint32_t)d << kWordPosBits) | (uint32_t)(l0.pos[q] - b0 * 8));
+                    W.push_back(((uint32_t)d << kWordPosBits) | (uint32_t)(l0.pos[q] - term0));
                     prev = r;
                 }
                 while (W.size() % kWinWords) W.push_back(kWordSkip);
                 Ch.push_back(make_int4((int32_t)w0, (int32_t)W.size(), (int32_t)b0, (int32_t)b1));
-                Ch.push_back(make_int4(row0, 0, 0, 0));
+                Ch.push_back(make_int4(row0, (int32_t)term0, 0, 0));
                 e = ee;
             }
         }
@@ -478,7 +510,8 @@ size_t flat_section_words(const Grammar& g)
 Image image_layout(const Grammar& g, gcs_policy p)
 {
     const Level0Plan pl = level0_plan(g, p);
-    const int64_t g0 = pl.cut ? level0_split_groups(g, pl.S) : 0;
+    const Level0Counts lc = pl.cut ? level0_counts(g, pl.S) : Level0Counts{};
+    const int64_t g0 = lc.groups;
     // level 0's roots; with windows the device holds their words instead of
     // their groups and root positions, and the root list starts at level 1's
     const int64_t r0 = g.lv.empty() || g.lv[0].ngrp == 0 ? 0 : g.eoff[g.lv[0].grp_off + g.lv[0].ngrp];
@@ -508,7 +541,7 @@ Image image_layout(const Grammar& g, gcs_policy p)
     m.wchunk = o;
     o = al256(o + (pl.window ? 2 * window_chunk_bound(r0, pl.S) * sizeof(int4) : 0));
     m.wword = o;
-    o = al256(o + (pl.window ? window_word_bound(r0, pl.S, g.n_rows) * 4 : 0));
+    o = al256(o + (pl.window ? window_word_bound(r0, pl.S, lc.skips) * 4 : 0));
     m.tcol = o;
     o = al256(o + g.tcol.size() * 4);
     m.tval = o;
@@ -947,8 +980,8 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             level_kernel<P><<<(int32_t)grid, kBlock, 0, s>>>(a, arena, acc);
             mark();
         }
-        if constexpr (kBitTerms<P>) {
-            if (k == 1 && d->win_on) {  // level 0's emission: words, bits from LDS windows of T
+        if constexpr (kDirectEmit<P>) {
+            if (k == 1 && d->win_on) {  // level 0's emission: words, terminals from LDS windows of T
                 mark();
                 window_emit_kernel<P><<<d->win_grid, kWinBlock, d->win_lds, s>>>(d->win, arena, y);
                 mark();
@@ -1050,7 +1083,7 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
             if (leaves) launch_level_batch<P, true>(VW, grid, ba, arena, acc, s);
             else launch_level_batch<P, false>(VW, grid, ba, arena, acc, s);
         }
-        if constexpr (kBitTerms<P>) {
+        if constexpr (kDirectEmit<P>) {
             if (k == 1 && d->win_on) {  // level 0's emission from its words, vector by vector
                 if (leaves) window_batch_kernel<P, true><<<d->win_grid, kWinBlock, 0, s>>>(d->win, ba, arena, acc);
                 else window_batch_kernel<P, false><<<d->win_grid, kWinBlock, 0, s>>>(d->win, ba, arena, acc);
@@ -1160,9 +1193,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     std::vector<uint32_t> words;
     std::vector<int4> wch;
     if (win_on) {
-        if (!gcs::build_window_words(l0, g.n_rows, words, wch)) return GCS_ESTATE;
-        if (wch.size() > 2 * gcs::window_chunk_bound(r0, l0.S) ||
-            words.size() > gcs::window_word_bound(r0, l0.S, g.n_rows)) {
+        if (!gcs::build_window_words(l0, g.n_rows, p == GCS_BOOL_OR ? 0 : (int64_t)gcs::elem_bytes(p), words, wch))
+            return GCS_ESTATE;
+        if (wch.size() * sizeof(int4) > im.wword - im.wchunk || words.size() * 4 > im.tcol - im.wword) {
             gcs::set_error("internal error: more window chunks or words than the image holds");
             return GCS_ESTATE;
         }
