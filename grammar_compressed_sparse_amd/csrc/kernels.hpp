@@ -134,16 +134,20 @@ __device__ __forceinline__ void direct(uint8_t* p, uint8_t v)
 }
 // IEEE order of non-negative floats is the order of their bits as signed
 // integers, and of negative floats the reverse order of their bits as
-// unsigned integers, so min is an integer min or an unsigned max
+// unsigned integers, so min is an integer min or an unsigned max.  A value
+// no smaller than what y holds changes nothing and skips the atomic (y only
+// decreases, so a stale read can only let an atomic through).
 __device__ __forceinline__ void direct(float* p, float v)
 {
     if (!(v < __builtin_huge_valf())) return;
+    if (!(v < __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) return;
     if (v >= 0.0f) atomicMin((int*)p, __float_as_int(v));
     else atomicMax((unsigned int*)p, __float_as_uint(v));
 }
 __device__ __forceinline__ void direct(double* p, double v)
 {
     if (!(v < __builtin_huge_val())) return;
+    if (!(v < __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) return;
     if (v >= 0.0) atomicMin((long long*)p, __double_as_longlong(v));
     else atomicMax((unsigned long long*)p, (unsigned long long)__double_as_longlong(v));
 }
