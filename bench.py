@@ -537,13 +537,42 @@ def bench_biobank(args, wl, spec, leg):
               "merge_s": merge_s, "device_bytes": dm.device_bytes, "launches_per_sweep": dm.sweep_launches(),
               "depth": st_m["depth"], "max_width": st_m["max_width"], "max_rel_err_sampled": err_m}
     log(f"merged: {merged}")
+    m_dev_bytes = dm.device_bytes
+    dm.free()
+    del dm, ym
+    torch.cuda.empty_cache()
+    # the fp64-accumulate option on the same merged grammar: fp32 x, fp64
+    # terminals, level values and y (PLUS_F32_ACC_F64), checked at 1e-12
+    d64 = gcs.upload(gm, gcs.PLUS_F32_ACC_F64)
+    y64 = d64.new_y()
+    d64.sweep_right(xd, y64)
+    d64.check()
+    err_64 = None
+    if leg is not None:
+        err_64 = float(np.max(np.abs(y64.cpu().numpy()[rows] - yo) / np.maximum(absum, 1e-300)))
+        if err_64 > 1e-12:
+            raise SystemExit(f"merged biobank groups (fp64 accumulate) disagree with the oracle: {err_64:.2e}")
+    for _ in range(args.warmup):
+        d64.sweep_right(xd, y64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        d64.sweep_right(xd, y64)
+    torch.cuda.synchronize()
+    elapsed_64 = time.perf_counter() - t0
+    d64.check()
+    merged["acc_f64"] = {"ms_per_sweep": elapsed_64 * 1e3 / args.steps, "nnz_per_s": nnz * args.steps / elapsed_64,
+                         "device_bytes": d64.device_bytes, "max_rel_err_sampled": err_64}
+    log(f"merged, fp64 accumulate: {merged['acc_f64']}")
+    d64.free()
+    del d64, y64
     dev_bytes = sum(per_group_bytes) + 4 * spec.n_cols + 4 * spec.n_rows
     csr_bytes += 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
     scale = ngroups_full / args.groups
     # the step: the merged grammar's sweep (the groups as separate uploads
     # are context); the full matrix would be a few merged grammars, since one
     # grammar indexes its roots with 32 bits (|C| < 2^31)
-    m_bytes = dm.device_bytes + 4 * spec.n_cols + 4 * spec.n_rows
+    m_bytes = m_dev_bytes + 4 * spec.n_cols + 4 * spec.n_rows
     out = {
         "metric": "nnz/s for y=Mx sweep; achieved HBM GB/s (% peak); device bytes vs CSR",
         "value": nnz * args.steps / elapsed_m, "unit": "nnz/s", "n_gpus": 1, "steps": args.steps,
