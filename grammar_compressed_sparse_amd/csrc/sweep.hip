@@ -1105,6 +1105,46 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
 
 using gcs::Grammar;
 
+extern "C" gcs_status gcs_level0_words(const gcs_grammar* h, gcs_policy p, uint32_t* words, int64_t words_cap,
+                                      int32_t* chunks, int64_t chunks_cap, int64_t* n_words, int64_t* n_chunks,
+                                      int32_t* n_sub)
+{
+    if (!h || !n_words || !n_chunks || !gcs::valid_policy(p) || words_cap < 0 || chunks_cap < 0) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    gcs_status st = gcs::check_values(g, p);
+    if (st != GCS_OK) return st;
+    *n_words = *n_chunks = 0;
+    const gcs::Level0Plan pl = gcs::level0_plan(g, p);
+    if (n_sub) *n_sub = pl.window ? pl.S : 0;
+    if (!pl.window) return GCS_OK;
+    gcs::Level0Split l0;
+    gcs::level0_split(g, pl.S, l0);
+    std::vector<uint32_t> w;
+    std::vector<int4> c;
+    if (!gcs::build_window_words(l0, g.n_rows, p == GCS_BOOL_OR ? 0 : (int64_t)gcs::elem_bytes(p), w, c))
+        return GCS_ESTATE;
+    *n_words = (int64_t)w.size();
+    *n_chunks = (int64_t)(c.size() / 2);
+    if (words) {
+        if (words_cap < *n_words) {
+            gcs::set_error("words capacity too small");
+            return GCS_ERANGE;
+        }
+        std::memcpy(words, w.data(), w.size() * 4);
+    }
+    if (chunks) {
+        if (chunks_cap < 8 * *n_chunks) {
+            gcs::set_error("chunks capacity too small");
+            return GCS_ERANGE;
+        }
+        std::memcpy(chunks, c.data(), c.size() * sizeof(int4));
+    }
+    return GCS_OK;
+}
+
 extern "C" gcs_status gcs_device_layout(const gcs_grammar* h, gcs_policy p, gcs_dev_sizes* out)
 {
     if (!h || !out || !gcs::valid_policy(p)) {

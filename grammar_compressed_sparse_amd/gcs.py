@@ -73,6 +73,9 @@ _lib.gcs_layout_counts.argtypes = [_P, _P]
 _lib.gcs_export_layout.argtypes = [_P] + [_P] * 6
 _lib.gcs_export_slices.argtypes = [_P, _P, _P]
 _lib.gcs_export_slices.restype = _st
+_lib.gcs_level0_words.argtypes = [_P, ctypes.c_int, _P, _I64, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                                  ctypes.POINTER(ctypes.c_int32)]
+_lib.gcs_level0_words.restype = _st
 _lib.gcs_save_grammar.argtypes = [_P, ctypes.c_char_p]
 _lib.gcs_save_grammar.restype = _st
 _lib.gcs_load_grammar.argtypes = [ctypes.c_char_p, ctypes.POINTER(_P)]
@@ -168,6 +171,18 @@ class Grammar:
         out["col_cut"] = np.zeros(9, np.int32)
         _check(_lib.gcs_export_slices(self._h, _ptr(out["slices"]), _ptr(out["col_cut"])))
         return out
+
+    def level0_words(self, policy: int) -> dict:
+        """gcs_level0_words: level 0's word stream and chunk table as the
+        upload for `policy` lays them out (empty arrays when it has none)."""
+        nw, nc, ns = _I64(0), _I64(0), ctypes.c_int32(0)
+        _check(_lib.gcs_level0_words(self._h, policy, None, 0, None, 0, ctypes.byref(nw), ctypes.byref(nc),
+                                     ctypes.byref(ns)))
+        words = np.zeros(nw.value, np.uint32)
+        chunks = np.zeros((nc.value, 8), np.int32)
+        _check(_lib.gcs_level0_words(self._h, policy, _ptr(words), words.size, _ptr(chunks), chunks.size,
+                                     ctypes.byref(nw), ctypes.byref(nc), ctypes.byref(ns)))
+        return {"words": words, "chunks": chunks, "n_sub": ns.value}
 
     def device_layout(self, policy: int) -> dict:
         d = DevSizes()

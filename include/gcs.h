@@ -204,6 +204,27 @@ gcs_status gcs_export_layout(const gcs_grammar* g, int64_t* level_meta, int32_t*
  * to the level's first group).  Either pointer may be NULL. */
 gcs_status gcs_export_slices(const gcs_grammar* g, int64_t* out, int32_t* col_cut);
 
+/* Level 0's word stream as gcs_upload lays it out for a direct policy
+ * (Boolean, tropical), computed on the host with no device call (for
+ * host-side checks).  Level 0's roots are the bare terminals of C (section
+ * 2, 'Grammar'); Listing 1 (section 4.3) loops over levels 1..L, and this
+ * library emits level 0 right after the leaf kernel.  The upload lists
+ * them per column slice and column sub-slice in row order, one 32-bit word
+ * each: bits [0, 19) the terminal's offset from the chunk's first terminal
+ * (0x7FFFF: no terminal, the word only advances the row), bits [19, 32) the
+ * row's increase over the previous word's row (the chunk's first row for
+ * its first word).  chunks[8*i .. 8*i+8) = {first word, end word, first
+ * byte and end byte of the chunk's window in the device terminal array
+ * (Boolean terminals are bits, bit c % 8 of byte c / 8), first row, first
+ * terminal of the window, 0, 0}.  Either array may be NULL (then only the
+ * counts are returned); *n_sub gets the sub-slices per slice (may be NULL).
+ * All counts are 0 when the policy's upload emits level 0 otherwise: a
+ * non-direct policy, GCS_LEVEL0_WINDOW=0, or a slice too wide for an LDS
+ * window.  GCS_ERANGE if words_cap < *n_words or chunks_cap < 8 * *n_chunks;
+ * GCS_ESTATE if the grammar's level-0 rows are out of order. */
+gcs_status gcs_level0_words(const gcs_grammar* g, gcs_policy p, uint32_t* words, int64_t words_cap, int32_t* chunks,
+                            int64_t chunks_cap, int64_t* n_words, int64_t* n_chunks, int32_t* n_sub);
+
 void gcs_free_grammar(gcs_grammar* g);
 
 /* ---- device ----------------------------------------------------------- */
