@@ -264,3 +264,43 @@ def test_boolean_window_far_rows(env, oracle_mod, monkeypatch, capfd, split):
                 assert np.array_equal(Y[:, b], refs[b]), (window, leaves, b)
         dev.check()
         dev.free()
+
+
+@pytest.mark.parametrize("pol,dt", [("min_plus_f32", np.float32), ("min_plus_f64", np.float64)])
+def test_tropical_window_far_rows(env, oracle_mod, monkeypatch, capfd, pol, dt):
+    """Tropical level-0 words (value windows in LDS, skip words across far
+    rows, a lane's same-row words combined): single vector overwrite and
+    accumulate, and batched (B = 3, with and without the leaves in the sweep)
+    equal the oracle exactly, with and without windows."""
+    torch, gcs = env
+    n, m, rp, col = _far_rows_matrix()
+    rng = np.random.default_rng(9)
+    val = rng.integers(1, 5, size=col.size).astype(np.float64)
+    g = gcs.build_grammar(rp, col, val, n_cols=m)
+    X = (rng.random((m, 3)) * 10).astype(dt)
+    X[rng.random((m, 3)) < np.array([0.5, 0.97, 0.0])] = np.inf
+    X = np.ascontiguousarray(X)
+    refs = [oracle_mod.spmv_min_plus(rp, col, val, X[:, b].copy(), dt) for b in range(3)]
+    y0 = (rng.random(n) * 12).astype(dt)
+    y0[rng.random(n) < 0.5] = np.inf
+    monkeypatch.setenv("GCS_UPLOAD_TRACE", "1")
+    monkeypatch.delenv("GCS_LEVEL0_SPLIT", raising=False)
+    for window in ("1", "0"):
+        monkeypatch.setenv("GCS_LEVEL0_WINDOW", window)
+        capfd.readouterr()
+        dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+        err = capfd.readouterr().err
+        line = [l for l in err.splitlines() if "LDS windows" in l]
+        assert len(line) == 1 and line[0].split("LDS windows ")[1].startswith(window), err
+        for b in range(3):
+            xb = torch.from_numpy(X[:, b].copy()).cuda()
+            assert np.array_equal(dev.sweep_right(xb).cpu().numpy(), refs[b]), (window, b)
+            ya = torch.from_numpy(y0.copy()).cuda()
+            dev.sweep_right_acc(xb, ya)
+            assert np.array_equal(ya.cpu().numpy(), np.minimum(y0, refs[b])), (window, b)
+        for leaves in (False, True):
+            Y = dev.sweep_right_batch(torch.from_numpy(X).cuda(), leaves_in_sweep=leaves).cpu().numpy()
+            for b in range(3):
+                assert np.array_equal(Y[:, b], refs[b]), (window, leaves, b)
+        dev.check()
+        dev.free()
