@@ -163,3 +163,28 @@ def test_words_absent(synth_mod, monkeypatch):
     _check_stream(g, gcs.MIN_PLUS_F64, 8)
     monkeypatch.setenv("GCS_LEVEL0_WINDOW", "0")
     assert g.level0_words(gcs.MIN_PLUS_F64)["words"].size == 0
+
+
+def test_words_errors(graph_grammar, monkeypatch):
+    """Capacities below the counts give GCS_ERANGE and an invalid policy or a
+    missing count pointer GCS_EINVAL, nothing written past the capacity."""
+    import ctypes
+    from grammar_compressed_sparse_amd import gcs
+    monkeypatch.delenv("GCS_LEVEL0_SPLIT", raising=False)
+    monkeypatch.delenv("GCS_LEVEL0_WINDOW", raising=False)
+    d = graph_grammar.level0_words(gcs.BOOL_OR)
+    nw, nc = d["words"].size, d["chunks"].shape[0]
+    assert nw > 8 and nc > 0
+    lib, h = gcs._lib, graph_grammar._h
+    cw, cc, cs = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    words = np.full(nw, 0xDEADBEEF, np.uint32)
+    chunks = np.zeros((nc, 8), np.int32)
+    st = lib.gcs_level0_words(h, gcs.BOOL_OR, words.ctypes.data, nw - 1, None, 0, ctypes.byref(cw), ctypes.byref(cc),
+                              ctypes.byref(cs))
+    assert st == -4 and cw.value == nw and np.all(words == 0xDEADBEEF)  # GCS_ERANGE, nothing copied
+    st = lib.gcs_level0_words(h, gcs.BOOL_OR, None, 0, chunks.ctypes.data, 8 * nc - 1, ctypes.byref(cw),
+                              ctypes.byref(cc), None)
+    assert st == -4 and cc.value == nc
+    assert lib.gcs_level0_words(h, 99, None, 0, None, 0, ctypes.byref(cw), ctypes.byref(cc), None) == -1
+    assert lib.gcs_level0_words(h, gcs.BOOL_OR, None, 0, None, 0, None, ctypes.byref(cc), None) == -1
+    assert lib.gcs_level0_words(None, gcs.BOOL_OR, None, 0, None, 0, ctypes.byref(cw), ctypes.byref(cc), None) == -1
