@@ -639,6 +639,7 @@ def bench_graph(args, wl, spec, leg):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dev.check()
+    roofline = graph_window_roofline(args, gcs, g, dev, f, y)
     t = time.perf_counter()
     vis, counts = dev.bfs(src)
     torch.cuda.synchronize()
@@ -676,10 +677,40 @@ def bench_graph(args, wl, spec, leg):
                    "device_bytes": dev_bytes, "csr_bytes_analytic": csr_bytes,
                    "footprint_ratio_csr_over_engine": csr_bytes / dev_bytes, "tropical": tropical,
                    "csr_rocsparse_fp32": csr},
-        "roofline": None,
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def graph_window_roofline(args, gcs, g, dev, f, y):
+    """The largest single kernel of a Boolean pass: level 0's word-stream
+    emission (window_emit_kernel), launched right after the terminal array
+    and level 1's launch.  Algorithmic bytes per launch: 4 per word plus
+    each chunk's window of terminal bits, loaded once (the words and chunk
+    table as the upload lays them out, from gcs_level0_words on the host);
+    duration: HIP events around every launch of args.steps passes (after
+    the timed region)."""
+    lw = g.level0_words(gcs.BOOL_OR)
+    if lw["words"].size == 0:
+        return None
+    ch = lw["chunks"].astype(np.int64)
+    alg = 4 * int(lw["words"].size) + int((ch[:, 3] - ch[:, 2]).sum())
+    idx = 2 if int(g.level_widths()[1]) > 0 else 1  # leaf, level 1 (if any), then the words
+    dev.profile_begin(args.steps, gcs.PROFILE_LAUNCHES)
+    for _ in range(args.steps):
+        dev.sweep_right_profiled(f, y)
+    launch_ms = dev.profile_end()
+    dev.check()
+    us = float(launch_ms[:, idx].mean() * 1e3)
+    achieved = alg / (us * 1e-6) / 1e9
+    log(f"window_emit_kernel: {alg / 1e9:.2f} GB algorithmic per launch in {us:.0f} us: {achieved:.0f} GB/s")
+    return {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s", "frac": achieved / 8000.0,
+            "traffic": None,
+            "kernel": "window_emit_kernel (level 0's 32-bit words and each chunk's LDS window of terminal bits; "
+                      "HIP events around each launch)",
+            "launch_avg_us": us, "bytes_per_launch": alg, "words": int(lw["words"].size),
+            "chunks": int(ch.shape[0])}
 
 
 def main():
