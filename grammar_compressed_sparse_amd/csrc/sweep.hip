@@ -161,8 +161,8 @@ inline int32_t sub_of(int64_t t, int x, const std::array<int64_t, kSlices + 1>& 
 // How level 0's emission is organized on upload (direct policies only).
 // By default as a word stream (window_emit_kernel): cut into S sub-slices
 // per slice so that every sub-slice's terminals fit one LDS window of
-// kWinBytes (Boolean terminals are bits, so S is small: 47 for 5e7
-// terminals; fp32 values need about 480).  Where no S up to
+// kWinBytes (Boolean terminals are bits, so S is small: 47 for the 5e7
+// terminals of the copy graph, whose fp32 values take 646).  Where no S up to
 // kLevel0MaxWindowSplit fits, or with GCS_LEVEL0_WINDOW=0, the level kernel
 // emits level 0's groups, cut into S sub-slices when a slice's share of T
 // exceeds kLevel0Window.  GCS_LEVEL0_SPLIT=S forces a count (0: no cut).
