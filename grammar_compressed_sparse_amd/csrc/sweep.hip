@@ -1007,9 +1007,26 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         int32_t n_grid = d->tail_wgs;
         void* args[] = {&table, &n_multi, &n_grid, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
         const unsigned wgs = (unsigned)d->tail_wgs + (flat.n_ent > 0 ? 1u : 0u);
-        hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(wgs),
-                                                  dim3(kTailBlock), args, d->flat_lds, s);
-        if (e != hipSuccess) return hip_fail(e, "tail launch (cooperative)");
+        // an ordinary launch by default: the grid (at most one workgroup per
+        // CU) has the device to itself behind the sweep's earlier launches,
+        // and the barrier's bounded wait flags the sweep if it ever is not
+        // all resident; a cooperative launch (GCS_TAIL_COOP=1) has the
+        // runtime certify residency, for devices shared with long-running
+        // kernels, and costs ~11 us more launch latency per sweep on MI355X
+        static const bool plain = [] {
+            const char* v = std::getenv("GCS_TAIL_COOP");
+            return !(v && std::atoi(v) != 0);
+        }();
+        hipError_t e;
+        if (plain) {
+            tail_kernel<P><<<dim3(wgs), dim3(kTailBlock), d->flat_lds, s>>>(table, n_multi, n_grid, flat, arena, acc, y,
+                                                                           n_rows, accumulate, bar, errp);
+            e = hipGetLastError();
+        } else {
+            e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(wgs), dim3(kTailBlock),
+                                           args, d->flat_lds, s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "tail launch");
         mark();
     }
     hipError_t err = hipGetLastError();
