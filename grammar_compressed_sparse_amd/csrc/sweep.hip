@@ -1382,12 +1382,14 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         const char* v = std::getenv(name);
         return v ? std::atoi(v) : dflt;
     };
-    // 16 workgroups (2 per XCD), one virtual block per 256-lane quarter and
-    // level: measured best on MI355X for the tail (fewer arrivals per barrier
-    // round; the wider levels this leaves out run faster as launches)
+    // 8 workgroups (one per XCD), one virtual block per 256-lane quarter and
+    // level: measured best on MI355X with the ordinary tail launch (fewest
+    // arrivals per barrier round; the wider levels this leaves out run as
+    // launches): 0.0645 ms per sweep on the 512 x 4096 genotype against 0.071 /
+    // 0.075 / 0.081 ms with 16 / 32 / 64, the bench matrix 0.450 ms either way
     // (at most one fewer than the compute units: the narrow levels' workgroup
-    // joins the cooperative grid, and each of these workgroups needs a CU)
-    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 16), std::max(dev_cu - 1, gcs::kSlices)) /
+    // joins the grid, and each of these workgroups needs a CU)
+    d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 8), std::max(dev_cu - 1, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
     // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
