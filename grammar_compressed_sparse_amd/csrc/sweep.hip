@@ -58,6 +58,7 @@ struct gcs_device {
     int64_t tail_k0 = 1, tail_nent = 0;  // levels tail_k0..L and the last emission run in the tail kernel
     int64_t tail_multi = 0;              // of which the first tail_multi run on the whole tail grid
     int32_t tail_wgs = 0;
+    bool tail_coop = false;              // the tail as a cooperative launch (GCS_TAIL_COOP=1 at upload)
     int64_t grid_max = 0;  // cap on workgroups of a wide level launch (multiple of kSlices)
     const gcs::LevelArgs* tail_table = nullptr;
     gcs::FlatArgs flat{};      // the narrowest tail launches, run in LDS by one workgroup
@@ -1010,15 +1011,11 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         // an ordinary launch by default: the grid (at most one workgroup per
         // CU) has the device to itself behind the sweep's earlier launches,
         // and the barrier's bounded wait flags the sweep if it ever is not
-        // all resident; a cooperative launch (GCS_TAIL_COOP=1) has the
-        // runtime certify residency, for devices shared with long-running
-        // kernels, and costs ~11 us more launch latency per sweep on MI355X
-        static const bool plain = [] {
-            const char* v = std::getenv("GCS_TAIL_COOP");
-            return !(v && std::atoi(v) != 0);
-        }();
+        // all resident; a cooperative launch (tail_coop) has the runtime
+        // certify residency, for devices shared with long-running kernels,
+        // and costs ~11 us more launch latency per sweep on MI355X
         hipError_t e;
-        if (plain) {
+        if (!d->tail_coop) {
             tail_kernel<P><<<dim3(wgs), dim3(kTailBlock), d->flat_lds, s>>>(table, n_multi, n_grid, flat, arena, acc, y,
                                                                            n_rows, accumulate, bar, errp);
             e = hipGetLastError();
@@ -1392,6 +1389,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 8), std::max(dev_cu - 1, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
+    d->tail_coop = env_int("GCS_TAIL_COOP", 0) != 0;
     // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
     // the grid (then workgroups stride over the blocks)
     d->grid_max = std::max(gcs::kSlices, env_int("GCS_GRID_MAX", INT32_MAX) / gcs::kSlices * gcs::kSlices);

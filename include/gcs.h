@@ -359,7 +359,7 @@ gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t
  * failed on the device: the persistent kernel that evaluates the narrow top
  * levels (at most one workgroup per compute unit, launched as an ordinary
  * kernel behind the sweep's earlier launches; GCS_TAIL_COOP=1 in the
- * environment makes it a cooperative launch, for devices shared with
+ * environment at gcs_upload makes it a cooperative launch, for devices shared with
  * long-running kernels) waits at a grid-wide barrier with a bounded wait
  * (about a second), and flags the sweep instead of hanging if its
  * workgroups were not all resident.  GCS_ESTATE (and the flag cleared) if

@@ -447,3 +447,26 @@ def test_merged_column_groups(env, oracle_mod, synth_mod):
     xt = np.abs(x32)
     y, _ = _sweep(env, g, gcs.MIN_PLUS_F32, xt)
     assert np.array_equal(y, oracle_mod.spmv_min_plus(rp, col, val, xt, np.float32))
+
+
+@pytest.mark.parametrize("pol", ["f64", "f32", "i64"])
+def test_tail_launch_kinds_identical(env, synth_mod, c1, monkeypatch, pol):
+    """The tail kernel as an ordinary launch (default) and as a cooperative
+    launch (GCS_TAIL_COOP=1 at upload) runs the same schedule: bit-identical
+    y over several sweeps, and no sweep flagged."""
+    torch, gcs = env
+    spec, rp, col, val, g = c1
+    x = synth_mod.normal(spec.n_cols, 77)
+    dt = {"f64": np.float64, "f32": np.float32, "i64": np.int64}[pol]
+    xs = (np.round(x * 8) if pol == "i64" else x).astype(dt)
+    ys = {}
+    for coop in ("0", "1"):
+        monkeypatch.setenv("GCS_TAIL_COOP", coop)
+        dev = gcs.upload(g, gcs.POLICY_NAMES[pol])
+        xd = torch.from_numpy(xs).cuda()
+        runs = [dev.sweep_right(xd).cpu().numpy() for _ in range(3)]
+        dev.check()
+        ys[coop] = runs
+        dev.free()
+    for r in ys["0"] + ys["1"][1:]:
+        assert np.array_equal(r, ys["1"][0])
