@@ -1368,17 +1368,19 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     // needs more than tail_vb virtual blocks per tail workgroup
     int dev_cu = 0;
     (void)hipDeviceGetAttribute(&dev_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    int coop = 0;
-    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (!coop) {
-        delete d;
-        gcs::set_error("the device does not support cooperative launches");
-        return GCS_EHIP;
-    }
     auto env_int = [](const char* name, int dflt) {
         const char* v = std::getenv(name);
         return v ? std::atoi(v) : dflt;
     };
+    // the tail kernel as a cooperative launch only on request
+    d->tail_coop = env_int("GCS_TAIL_COOP", 0) != 0;
+    int coop = 0;
+    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (d->tail_coop && !coop) {
+        delete d;
+        gcs::set_error("GCS_TAIL_COOP=1: the device does not support cooperative launches");
+        return GCS_EHIP;
+    }
     // 8 workgroups (one per XCD), one virtual block per 256-lane quarter and
     // level: measured best on MI355X with the ordinary tail launch (fewest
     // arrivals per barrier round; the wider levels this leaves out run as
@@ -1389,7 +1391,6 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tail_wgs = std::max(gcs::kSlices, (std::min(env_int("GCS_TAIL_WGS", 8), std::max(dev_cu - 1, gcs::kSlices)) /
                                           gcs::kSlices) * gcs::kSlices);
     const int64_t tail_vb = std::max(1, env_int("GCS_TAIL_VB", 1));
-    d->tail_coop = env_int("GCS_TAIL_COOP", 0) != 0;
     // wide launches: one virtual block per workgroup unless GCS_GRID_MAX caps
     // the grid (then workgroups stride over the blocks)
     d->grid_max = std::max(gcs::kSlices, env_int("GCS_GRID_MAX", INT32_MAX) / gcs::kSlices * gcs::kSlices);
