@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libgcs.so")
 OBJ = os.path.join(PKG, "_build")
 
-HOST_SOURCES = ["builder.cpp", "repair.cpp", "serialize.cpp"]
-DEVICE_SOURCES = ["sweep.hip"]
+HOST_SOURCES = ["builder.cpp", "repair.cpp", "repair_rounds.cpp", "serialize.cpp"]
+DEVICE_SOURCES = ["sweep.hip", "build_gpu.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 instructions are disabled for all device code

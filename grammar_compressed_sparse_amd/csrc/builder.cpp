@@ -372,9 +372,28 @@ gcs_status finish_layout(Grammar& g, int threads)
 // CSRV + RePair
 // ---------------------------------------------------------------------------
 
-static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* opts, Grammar& g)
+int32_t Csrv::vindex(int64_t k) const
 {
-    auto t0 = std::chrono::steady_clock::now();
+    if (kind == GCS_VAL_ONES) return 0;
+    if (kind == GCS_VAL_I8) return i8_index[(int)((const int8_t*)m->val)[k] + 128];
+    const double x = ((const double*)m->val)[k];
+    if (x == 0.0) return -1;
+    return (int32_t)(std::lower_bound(V->begin(), V->end(), x) - V->begin());
+}
+
+int32_t Csrv::term_id(int64_t k) const
+{
+    const int32_t vi = vindex(k);
+    if (vi < 0) return -1;
+    const int32_t j = m->col[k];
+    if (small_v) return (int32_t)(cbase[j] + __builtin_popcountll(cmask[j] & ((1ULL << vi) - 1)));
+    return (int32_t)(std::lower_bound(tkeys.begin(), tkeys.end(), (int64_t)j * nV + vi) - tkeys.begin());
+}
+
+// Input checks, V and the terminal alphabet (CSRV, section 2, Eq. 2.2): the
+// distinct <l, j> in use, compacted and ordered by (column, value index).
+gcs_status csrv_encode(const gcs_csr_view* m, int threads, Grammar& g, Csrv& enc)
+{
     if (!m || m->n_rows < 0 || m->n_cols < 0 || (m->n_rows > 0 && !m->row_ptr)) {
         set_error("invalid matrix view");
         return GCS_EINVAL;
@@ -398,9 +417,11 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
         set_error("missing column array");
         return GCS_EINVAL;
     }
-    const int threads = resolve_threads(opts ? opts->n_threads : 0);
     g.n_rows = n;
     g.n_cols = mc;
+    enc.m = m;
+    enc.kind = m->val_kind;
+    enc.V = &g.V;
 
     // validate rows in parallel
     std::atomic<int> bad{0};
@@ -433,44 +454,45 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
 
     // V: distinct nonzero values, ascending (CSRV, section 2)
     const int kind = m->val_kind;
-    std::vector<int32_t> i8_index(256, -1);
+    for (int c = 0; c < 256; ++c) enc.i8_index[c] = -1;
+    const int64_t nblk_v = std::max<int64_t>(1, std::min<int64_t>(threads, nnz_stored / 65536));
     if (kind == GCS_VAL_ONES) {
         if (nnz_stored > 0) g.V = {1.0};
     } else if (kind == GCS_VAL_I8) {
-        std::vector<char> seen(256, 0);
+        std::vector<std::vector<char>> seen((size_t)nblk_v, std::vector<char>(256, 0));
         const int8_t* v = (const int8_t*)m->val;
-        for (int64_t k = 0; k < nnz_stored; ++k) seen[(int)v[k] + 128] = 1;
-        for (int c = 0; c < 256; ++c)
-            if (seen[c] && c != 128) {
-                i8_index[c] = (int32_t)g.V.size();
+        parallel_for(nblk_v, threads, [&](int64_t b) {
+            for (int64_t k = nnz_stored * b / nblk_v; k < nnz_stored * (b + 1) / nblk_v; ++k) seen[b][(int)v[k] + 128] = 1;
+        });
+        for (int c = 0; c < 256; ++c) {
+            bool any = false;
+            for (auto& sb : seen) any = any || sb[c];
+            if (any && c != 128) {
+                enc.i8_index[c] = (int32_t)g.V.size();
                 g.V.push_back((double)(c - 128));
             }
+        }
+        if (seen.size() && std::any_of(seen.begin(), seen.end(), [](const std::vector<char>& sb) { return sb[128] != 0; }))
+            enc.has_zeros = true;
     } else {
         const double* v = (const double*)m->val;
         std::vector<double> vals;
         vals.reserve((size_t)nnz_stored);
-        for (int64_t k = 0; k < nnz_stored; ++k)
+        for (int64_t k = 0; k < nnz_stored; ++k) {
             if (v[k] != 0.0) vals.push_back(v[k]);
+            else enc.has_zeros = true;
+        }
         std::sort(vals.begin(), vals.end());
         vals.erase(std::unique(vals.begin(), vals.end()), vals.end());
         g.V = vals;
     }
     const int64_t nV = (int64_t)g.V.size();
-    auto vindex = [&](int64_t k) -> int32_t {  // -1 = stored zero (dropped)
-        if (kind == GCS_VAL_ONES) return 0;
-        if (kind == GCS_VAL_I8) return i8_index[(int)((const int8_t*)m->val)[k] + 128];
-        double x = ((const double*)m->val)[k];
-        if (x == 0.0) return -1;
-        return (int32_t)(std::lower_bound(g.V.begin(), g.V.end(), x) - g.V.begin());
-    };
+    enc.nV = nV;
 
     // terminal compaction: distinct <l, j> in use, sorted by (j, l)
-    std::vector<int64_t> cbase;      // per column: first terminal id
-    std::vector<uint64_t> cmask;     // per column: value indices present (|V| <= 64)
-    std::vector<int64_t> tkeys;      // general path: sorted keys j*|V|+l
-    const bool small_v = nV <= 64;
-    if (small_v) {
-        cmask.assign((size_t)mc, 0);
+    enc.small_v = nV <= 64;
+    if (enc.small_v) {
+        enc.cmask.assign((size_t)mc, 0);
         const int64_t nblk = std::min<int64_t>(threads, std::max<int64_t>(1, n / 1024));
         std::vector<std::vector<uint64_t>> part((size_t)nblk);
         parallel_for(nblk, threads, [&](int64_t b) {
@@ -478,53 +500,67 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
             pm.assign((size_t)mc, 0);
             int64_t r0 = n * b / nblk, r1 = n * (b + 1) / nblk;
             for (int64_t k = (n ? m->row_ptr[r0] : 0); k < (n ? m->row_ptr[r1] : 0); ++k) {
-                int32_t vi = vindex(k);
+                int32_t vi = enc.vindex(k);
                 if (vi >= 0) pm[m->col[k]] |= 1ULL << vi;
             }
         });
         for (auto& pm : part)
-            for (int64_t j = 0; j < mc; ++j) cmask[j] |= pm[j];
-        cbase.assign((size_t)mc + 1, 0);
-        for (int64_t j = 0; j < mc; ++j) cbase[j + 1] = cbase[j] + __builtin_popcountll(cmask[j]);
-        const int64_t alpha = cbase[mc];
+            for (int64_t j = 0; j < mc; ++j) enc.cmask[j] |= pm[j];
+        enc.cbase.assign((size_t)mc + 1, 0);
+        for (int64_t j = 0; j < mc; ++j) enc.cbase[j + 1] = enc.cbase[j] + __builtin_popcountll(enc.cmask[j]);
+        const int64_t alpha = enc.cbase[mc];
+        if (alpha >= (int64_t)INT32_MAX) {
+            set_error("too many distinct terminals");
+            return GCS_ERANGE;
+        }
         g.tcol.resize((size_t)alpha);
         g.tval.resize((size_t)alpha);
         for (int64_t j = 0; j < mc; ++j) {
-            int64_t t = cbase[j];
-            for (uint64_t mk = cmask[j]; mk; mk &= mk - 1) {
+            int64_t t = enc.cbase[j];
+            for (uint64_t mk = enc.cmask[j]; mk; mk &= mk - 1) {
                 g.tcol[t] = (int32_t)j;
                 g.tval[t] = __builtin_ctzll(mk);
                 ++t;
             }
         }
     } else {
-        tkeys.reserve((size_t)nnz_stored);
+        enc.tkeys.reserve((size_t)nnz_stored);
         for (int64_t r = 0; r < n; ++r)
             for (int64_t k = m->row_ptr[r]; k < m->row_ptr[r + 1]; ++k) {
-                int32_t vi = vindex(k);
-                if (vi >= 0) tkeys.push_back((int64_t)m->col[k] * nV + vi);
+                int32_t vi = enc.vindex(k);
+                if (vi >= 0) enc.tkeys.push_back((int64_t)m->col[k] * nV + vi);
             }
-        std::sort(tkeys.begin(), tkeys.end());
-        tkeys.erase(std::unique(tkeys.begin(), tkeys.end()), tkeys.end());
-        g.tcol.resize(tkeys.size());
-        g.tval.resize(tkeys.size());
-        for (size_t t = 0; t < tkeys.size(); ++t) {
-            g.tcol[t] = (int32_t)(tkeys[t] / nV);
-            g.tval[t] = (int32_t)(tkeys[t] % nV);
+        std::sort(enc.tkeys.begin(), enc.tkeys.end());
+        enc.tkeys.erase(std::unique(enc.tkeys.begin(), enc.tkeys.end()), enc.tkeys.end());
+        g.tcol.resize(enc.tkeys.size());
+        g.tval.resize(enc.tkeys.size());
+        for (size_t t = 0; t < enc.tkeys.size(); ++t) {
+            g.tcol[t] = (int32_t)(enc.tkeys[t] / nV);
+            g.tval[t] = (int32_t)(enc.tkeys[t] % nV);
         }
     }
-    const int64_t alpha = g.alpha();
-    if (alpha >= (int64_t)INT32_MAX) {
+    if (g.alpha() >= (int64_t)INT32_MAX) {
         set_error("too many distinct terminals");
         return GCS_ERANGE;
     }
-    auto term_id = [&](int64_t k) -> int32_t {
-        int32_t vi = vindex(k);
-        if (vi < 0) return -1;
-        int32_t j = m->col[k];
-        if (small_v) return (int32_t)(cbase[j] + __builtin_popcountll(cmask[j] & ((1ULL << vi) - 1)));
-        return (int32_t)(std::lower_bound(tkeys.begin(), tkeys.end(), (int64_t)j * nV + vi) - tkeys.begin());
-    };
+    return GCS_OK;
+}
+
+static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* opts, Grammar& g)
+{
+    auto t0 = std::chrono::steady_clock::now();
+    const int threads = resolve_threads(opts ? opts->n_threads : 0);
+    if (opts && (opts->repair < GCS_REPAIR_EXACT || opts->repair > GCS_REPAIR_ROUNDS || opts->reserved != 0)) {
+        set_error("unknown RePair mode or nonzero reserved option");
+        return GCS_EINVAL;
+    }
+    const bool rounds_mode = opts && opts->repair == GCS_REPAIR_ROUNDS;
+    Csrv enc;
+    if (gcs_status st = csrv_encode(m, threads, g, enc)) return st;
+    const int64_t n = m->n_rows, mc = m->n_cols;
+    const int64_t alpha = g.alpha();
+    const int64_t vblk = 4096;
+    auto term_id = [&](int64_t k) -> int32_t { return enc.term_id(k); };
     g.t_csrv = ms_since(t0);
 
     // tiles
@@ -600,7 +636,9 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
             return;
         }
         nnz_total += (int64_t)seq.size();
-        if (!repair_tile(seq, off, (int32_t)alpha, res[t])) fail = 1;
+        const bool ok = rounds_mode ? repair_rounds_tile(seq, off, (int32_t)alpha, res[t])
+                                    : repair_tile(seq, off, (int32_t)alpha, res[t]);
+        if (!ok) fail = 1;
     });
     if (fail) {
         set_error(fail == 2 ? "a RePair tile exceeds 2^31-1 symbols (use col_chunk/row_chunk)"

@@ -25,6 +25,10 @@ struct RePairResult {
 };
 bool repair_tile(const std::vector<int32_t>& seq_in, const std::vector<int64_t>& row_off, int32_t nt_base,
                  RePairResult& out);
+// The same contract, round-based (rounds.hpp): many non-overlapping pairs per
+// pass; the host form of the device builder.
+bool repair_rounds_tile(const std::vector<int32_t>& seq_in, const std::vector<int64_t>& row_off, int32_t nt_base,
+                        RePairResult& out);
 
 // Column slices: every level is cut into kSlices contiguous pieces by global
 // first-column thresholds, one piece per XCD of the device.
@@ -69,6 +73,25 @@ struct Grammar {
 
 // Levels, pass-through completion and layout from (tcol/tval, ra/rb, C).
 gcs_status finish_layout(Grammar& g, int threads);
+
+// CSRV encoding of a CSR input (section 2, 'CSRV'): the checks, V and the
+// compacted terminal alphabet; term_id(k) is the terminal of nonzero k (-1 for
+// a stored zero, which is dropped).
+struct Csrv {
+    const gcs_csr_view* m = nullptr;
+    int kind = 0;
+    int32_t i8_index[256];             // int8 value + 128 -> index into V (-1: zero)
+    bool small_v = true;               // |V| <= 64: per-column bit masks
+    bool has_zeros = false;            // some stored entry is zero
+    std::vector<int64_t> cbase;        // small_v: first terminal of each column (n_cols + 1)
+    std::vector<uint64_t> cmask;       // small_v: value indices present in each column
+    std::vector<int64_t> tkeys;        // otherwise: sorted keys col * |V| + value index
+    const std::vector<double>* V = nullptr;
+    int64_t nV = 0;
+    int32_t vindex(int64_t k) const;
+    int32_t term_id(int64_t k) const;
+};
+gcs_status csrv_encode(const gcs_csr_view* m, int threads, Grammar& g, Csrv& enc);
 
 }  // namespace gcs
 

@@ -43,7 +43,7 @@ class CsrView(ctypes.Structure):
 
 class BuildOpts(ctypes.Structure):
     _fields_ = [("n_threads", ctypes.c_int32), ("col_chunk", ctypes.c_int32), ("row_chunk", ctypes.c_int32),
-                ("row_order", ctypes.c_int32)]
+                ("row_order", ctypes.c_int32), ("repair", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -80,6 +80,11 @@ _lib.gcs_save_grammar.argtypes = [_P, ctypes.c_char_p]
 _lib.gcs_save_grammar.restype = _st
 _lib.gcs_load_grammar.argtypes = [ctypes.c_char_p, ctypes.POINTER(_P)]
 _lib.gcs_load_grammar.restype = _st
+_lib.gcs_build_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]
+_lib.gcs_build_workspace_bytes.restype = _st
+_lib.gcs_build_grammar_gpu.argtypes = [ctypes.POINTER(CsrView), ctypes.POINTER(BuildOpts), _I64, _P, ctypes.c_size_t,
+                                       _P, ctypes.POINTER(_P)]
+_lib.gcs_build_grammar_gpu.restype = _st
 _lib.gcs_free_grammar.argtypes = [_P]
 _lib.gcs_free_grammar.restype = None
 _lib.gcs_device_layout.argtypes = [_P, ctypes.c_int, ctypes.POINTER(DevSizes)]
@@ -202,6 +207,7 @@ class Grammar:
 
 
 ROWS_NATURAL, ROWS_SIMILAR = 0, 1
+REPAIR_EXACT, REPAIR_ROUNDS = 0, 1  # gcs_repair_mode
 
 
 def load_grammar(path) -> Grammar:
@@ -211,9 +217,7 @@ def load_grammar(path) -> Grammar:
     return Grammar(h)
 
 
-def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0,
-                  row_order=ROWS_NATURAL) -> Grammar:
-    """gcs_build_grammar on a host CSR matrix (val: None = all ones, int8, or fp64)."""
+def _csr_view(row_ptr, col, val, n_cols):
     rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
     cl = np.ascontiguousarray(col, dtype=np.int32)
     n = rp.shape[0] - 1
@@ -227,9 +231,45 @@ def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0,
         kind, vv = VAL_F64, np.ascontiguousarray(val, dtype=np.float64)
     view = CsrView(n, n_cols, rp.ctypes.data, cl.ctypes.data if cl.size else None, kind, 0,
                    vv.ctypes.data if vv is not None and vv.size else None)
-    opts = BuildOpts(n_threads, col_chunk, row_chunk, row_order)
+    return view, (rp, cl, vv)  # the arrays must outlive the call
+
+
+def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0, row_chunk=0,
+                  row_order=ROWS_NATURAL, repair=REPAIR_EXACT) -> Grammar:
+    """gcs_build_grammar on a host CSR matrix (val: None = all ones, int8, or fp64)."""
+    view, keep = _csr_view(row_ptr, col, val, n_cols)
+    opts = BuildOpts(n_threads, col_chunk, row_chunk, row_order, repair, 0)
     h = _P()
     _check(_lib.gcs_build_grammar(ctypes.byref(view), ctypes.byref(opts), ctypes.byref(h)))
+    return Grammar(h)
+
+
+def build_workspace_bytes(n_rows, n_cols, nnz, table_entries=0) -> int:
+    """gcs_build_workspace_bytes: device bytes gcs_build_grammar_gpu needs."""
+    b = ctypes.c_size_t(0)
+    _check(_lib.gcs_build_workspace_bytes(n_rows, n_cols, nnz, table_entries, ctypes.byref(b)))
+    return int(b.value)
+
+
+def build_grammar_gpu(row_ptr, col, val=None, n_cols=None, n_threads=0, table_entries=0, workspace=None,
+                      device="cuda", stream=None) -> Grammar:
+    """gcs_build_grammar_gpu: CSRV and round-based RePair on the device, layout
+    on the host.  The workspace is a caller-owned uint8 torch tensor (made
+    here unless given, and only needed during the call)."""
+    torch = _torch()
+    view, keep = _csr_view(row_ptr, col, val, n_cols)
+    nnz = int(keep[0][-1]) if keep[0].size else 0
+    need = build_workspace_bytes(view.n_rows, view.n_cols, nnz, table_entries)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need or not workspace.is_cuda:
+        raise GcsError(-1, f"workspace must be a uint8 device tensor of at least {need} bytes")
+    opts = BuildOpts(n_threads, 0, 0, ROWS_NATURAL, REPAIR_ROUNDS, 0)
+    h = _P()
+    with torch.cuda.device(workspace.device):
+        _check(_lib.gcs_build_grammar_gpu(ctypes.byref(view), ctypes.byref(opts), table_entries,
+                                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                          _stream_ptr(stream), ctypes.byref(h)))
     return Grammar(h)
 
 

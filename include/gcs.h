@@ -100,11 +100,28 @@ typedef enum {
  * chunks lose the sharing between rows of different tiles; the pages' prior
  * work partitions by row blocks (section 1).  y is always in the input's row
  * order. */
+/* RePair variant.  Both replace frequent pairs of adjacent symbols of one row
+ * by new nonterminals until no pair occurs twice (section 2 'Grammar',
+ * section 4.1); several grammars are correct, and the sweep accepts any.
+ *   GCS_REPAIR_EXACT   one most frequent pair at a time (Larsson and Moffat's
+ *                      linked-list form; ties: the most recently queued pair)
+ *   GCS_REPAIR_ROUNDS  round-based: each pass over the sequence replaces every
+ *                      non-overlapping occurrence of the pairs whose count is
+ *                      at least a tenth of the largest (the more frequent pair
+ *                      keeps a contested symbol), and makes a rule of each
+ *                      pair replaced at least twice.  Shallower grammars with
+ *                      far fewer pass-through nodes; the form the device
+ *                      builder (gcs_build_grammar_gpu) runs, with identical
+ *                      output. */
+typedef enum { GCS_REPAIR_EXACT = 0, GCS_REPAIR_ROUNDS = 1 } gcs_repair_mode;
+
 typedef struct {
     int32_t n_threads; /* 0 = OMP_NUM_THREADS if set, else the CPUs of the affinity mask */
     int32_t col_chunk; /* columns per tile; 0 = all columns                               */
     int32_t row_chunk; /* rows per tile; 0 = all rows                                     */
     int32_t row_order; /* gcs_row_order: which rows share a row tile                      */
+    int32_t repair;    /* gcs_repair_mode                                                 */
+    int32_t reserved;  /* must be 0                                                       */
 } gcs_build_opts;
 
 /* Structural figures of a built grammar (section 4.4, Table 4.1 columns). */
@@ -226,6 +243,35 @@ gcs_status gcs_level0_words(const gcs_grammar* g, gcs_policy p, uint32_t* words,
                             int64_t chunks_cap, int64_t* n_words, int64_t* n_chunks, int32_t* n_sub);
 
 void gcs_free_grammar(gcs_grammar* g);
+
+/* ---- device builder ---------------------------------------------------- */
+
+/* Bytes of the device workspace gcs_build_grammar_gpu needs for a CSR of
+ * n_rows x n_cols with nnz stored entries and a pair table of table_entries
+ * slots (0: the smallest power of two >= 2 nnz, always enough; a power of two
+ * in [2^10, 2^32] otherwise).  About 22 bytes per nonzero plus 24 per table
+ * slot.  GCS_EINVAL for negative sizes or a bad table size. */
+gcs_status gcs_build_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t nnz, int64_t table_entries,
+                                     size_t* bytes);
+
+/* gcs_build_grammar with the CSRV string and RePair computed on the device
+ * (section 2 'CSRV' and 'Grammar', section 4.1), in the round-based form
+ * (GCS_REPAIR_ROUNDS; the result is bit for bit the grammar gcs_build_grammar
+ * makes with opts.repair = GCS_REPAIR_ROUNDS and one tile); levels,
+ * completion and layout run on the host as there.  m is host memory; opts may
+ * be NULL, otherwise it must ask for one tile (col_chunk = row_chunk = 0,
+ * natural row order) and GCS_REPAIR_ROUNDS; n_threads sets the host threads.
+ * At most 64 distinct values and fewer than 2^31 - 1 nonzeros (larger
+ * matrices: one call per column group).  workspace_dev: caller-owned device
+ * memory of gcs_build_workspace_bytes(n_rows, n_cols, nnz, table_entries)
+ * bytes, 256-byte aligned, free again when the call returns; the call runs on
+ * `stream` and synchronises it several times (twice per RePair round).
+ * *out receives a new host grammar on GCS_OK.  GCS_EINVAL (bad input or
+ * options, small or misaligned workspace), GCS_ERANGE (beyond the 31-bit
+ * symbol space), GCS_ENOMEM (host memory, or the pair table is too small
+ * for the input: pass a larger table_entries), GCS_EHIP. */
+gcs_status gcs_build_grammar_gpu(const gcs_csr_view* m, const gcs_build_opts* opts, int64_t table_entries,
+                                 void* workspace_dev, size_t workspace_bytes, void* stream, gcs_grammar** out);
 
 /* ---- device ----------------------------------------------------------- */
 

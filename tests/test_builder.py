@@ -143,12 +143,13 @@ def _random_csr(rng, n, m, density, nvals):
     return rp, col, val
 
 
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
 @pytest.mark.parametrize("seed,n,m,density,nvals", [(1, 30, 40, 0.5, 2), (2, 200, 60, 0.3, 1), (3, 5, 300, 0.9, 3),
                                                     (4, 100, 100, 0.05, 70), (5, 64, 8, 1.0, 2)])
-def test_random_invariants_and_emulation(gcs, oracle_mod, seed, n, m, density, nvals):
+def test_random_invariants_and_emulation(gcs, oracle_mod, seed, n, m, density, nvals, repair):
     rng = random.Random(seed)
     rp, col, val = _random_csr(rng, n, m, density, nvals)
-    g = gcs.build_grammar(rp, col, val, n_cols=m)
+    g = gcs.build_grammar(rp, col, val, n_cols=m, repair=repair)
     ex = _check_grammar(g, rp, col, val)
     x = np.array([rng.uniform(-1, 1) for _ in range(m)])
     yo, absum = oracle_mod.spmv_f64(rp, col, val, x)
@@ -156,12 +157,13 @@ def test_random_invariants_and_emulation(gcs, oracle_mod, seed, n, m, density, n
     assert np.all(np.abs(y - yo) <= 1e-12 * absum + 1e-300)
 
 
-def test_genotype_tiles_invariants(gcs, oracle_mod, synth_mod):
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
+def test_genotype_tiles_invariants(gcs, oracle_mod, synth_mod, repair):
     spec = synth_mod.GenotypeSpec(300, 3000, 8, 100.0, 0.005, seed=3)
     rp, col, val = synth_mod.genotype(spec)
-    whole = gcs.build_grammar(rp, col, val, n_cols=3000, n_threads=1)
+    whole = gcs.build_grammar(rp, col, val, n_cols=3000, n_threads=1, repair=repair)
     _check_grammar(whole, rp, col, val)
-    tiled = gcs.build_grammar(rp, col, val, n_cols=3000, n_threads=4, col_chunk=700, row_chunk=128)
+    tiled = gcs.build_grammar(rp, col, val, n_cols=3000, n_threads=4, col_chunk=700, row_chunk=128, repair=repair)
     ex = _check_grammar(tiled, rp, col, val, single_tile=False)
     assert tiled.stats()["n_tiles"] == 5 * 3
     x = synth_mod.normal(3000, 77)
@@ -196,32 +198,40 @@ def test_identity_matrix(gcs):
     assert np.array_equal(y, np.arange(n, dtype=np.float64))
 
 
-def test_identical_rows_spine(gcs):
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
+def test_identical_rows_spine(gcs, repair):
     n, k = 6, 33
     rp = np.arange(n + 1, dtype=np.int64) * k
     col = np.tile(np.arange(k, dtype=np.int32), n)
-    g = gcs.build_grammar(rp, col, None, n_cols=k)
+    g = gcs.build_grammar(rp, col, None, n_cols=k, repair=repair)
     st = g.stats()
     assert st["n_rules"] == k - 1 and st["c_len"] == n
+    if repair == 1:
+        # every pair has count n, so a round replaces the local maxima of the
+        # pair hash along the row (about a third of the positions): the rows
+        # become trees of logarithmic depth, not the exact form's spine
+        assert st["depth"] <= 10
     _check_grammar(g, rp, col, None)
     y = H.emulate_layout(g.layout(), g.export(), np.ones(k))
     assert np.array_equal(y, np.full(n, float(k)))
 
 
-def test_single_dense_row(gcs):
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
+def test_single_dense_row(gcs, repair):
     m = 1000
     rp = np.array([0, m], np.int64)
     col = np.arange(m, dtype=np.int32)
-    g = gcs.build_grammar(rp, col, None, n_cols=m)
+    g = gcs.build_grammar(rp, col, None, n_cols=m, repair=repair)
     assert g.stats()["n_rules"] == 0  # no pair occurs twice
     y = H.emulate_layout(g.layout(), g.export(), np.arange(m, dtype=np.float64))
     assert y[0] == m * (m - 1) / 2
 
 
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
 @pytest.mark.parametrize("n,m", [(0, 0), (0, 5), (7, 0), (7, 9)])
-def test_empty(gcs, n, m):
+def test_empty(gcs, n, m, repair):
     rp = np.zeros(n + 1, np.int64)
-    g = gcs.build_grammar(rp, np.zeros(0, np.int32), None, n_cols=m)
+    g = gcs.build_grammar(rp, np.zeros(0, np.int32), None, n_cols=m, repair=repair)
     st = g.stats()
     assert st["nnz"] == 0 and st["n_rules"] == 0 and st["c_len"] == 0
     assert g.device_layout(gcs.PLUS_F32)["grammar_bytes"] > 0
@@ -313,3 +323,20 @@ def test_merge_refuses_bad_parts(gcs, synth_mod):
     with pytest.raises(gcs.GcsError):
         gcs.merge_grammars([])
     assert gcs.merge_grammars([a]).stats()["nnz"] == a.stats()["nnz"]
+
+
+def test_rounds_mode_shallower_copy_graph_and_options(gcs, synth_mod):
+    """Round-based RePair against the one-pair-at-a-time form on a copy-model
+    graph: lossless and complete (checked above for both), a grammar within a
+    few per cent of the exact form's size, and never deeper; unknown modes are
+    refused."""
+    spec = synth_mod.GraphSpec(3_000, seed=9)
+    rp, col = synth_mod.copy_graph(spec)
+    ex_g = gcs.build_grammar(rp, col, None, n_cols=spec.n, repair=gcs.REPAIR_EXACT)
+    ro_g = gcs.build_grammar(rp, col, None, n_cols=spec.n, repair=gcs.REPAIR_ROUNDS)
+    _check_grammar(ro_g, rp, col, None)
+    a, b = ex_g.stats(), ro_g.stats()
+    assert b["n_rules"] + b["c_len"] <= 1.1 * (a["n_rules"] + a["c_len"])
+    assert b["depth"] <= a["depth"]
+    with pytest.raises(gcs.GcsError, match="EINVAL"):
+        gcs.build_grammar(rp, col, None, n_cols=spec.n, repair=7)
