@@ -105,73 +105,170 @@ gcs_status finish_layout(Grammar& g, int threads)
     g.lvl.assign((size_t)R, 0);
     g.plast.assign((size_t)R, 0);
     std::vector<int32_t> fc((size_t)R, 0);  // first column of the expansion
-    int32_t L = 0;
-    for (int64_t i = 0; i < R; ++i) {
-        int32_t a = g.ra[i], b = g.rb[i];
-        int32_t la = a < alpha ? 0 : g.lvl[a - alpha], lb = b < alpha ? 0 : g.lvl[b - alpha];
-        int32_t l = 1 + std::max(la, lb);
-        g.lvl[i] = l;
-        fc[i] = a < alpha ? g.tcol[a] : fc[a - alpha];
-        L = std::max(L, l);
-        if (a >= alpha) g.plast[a - alpha] = std::max(g.plast[a - alpha], l);
-        if (b >= alpha) g.plast[b - alpha] = std::max(g.plast[b - alpha], l);
+    // Eq. 3.1 in blocks of consecutive rules none of which references a rule
+    // of its own block (the rules of one RePair round form such a block), so
+    // a block's rules are independent
+    {
+        std::vector<int64_t> bstart{0};
+        for (int64_t i = 0, s = 0; i < R; ++i) {
+            const int64_t hi = std::max<int64_t>(g.ra[i], g.rb[i]) - alpha;  // < 0: two terminals
+            if (hi >= s) bstart.push_back(s = i);
+        }
+        bstart.push_back(R);
+        auto one = [&](int64_t i) {
+            const int32_t a = g.ra[i], b = g.rb[i];
+            const int32_t la = a < alpha ? 0 : g.lvl[a - alpha], lb = b < alpha ? 0 : g.lvl[b - alpha];
+            g.lvl[i] = 1 + std::max(la, lb);
+            fc[i] = a < alpha ? g.tcol[a] : fc[a - alpha];
+        };
+        for (size_t x = 0; x + 1 < bstart.size(); ++x) {
+            const int64_t b0 = bstart[x], b1 = bstart[x + 1];
+            if (b1 - b0 < 65536) {
+                for (int64_t i = b0; i < b1; ++i) one(i);
+            } else {
+                const int64_t nch = (b1 - b0 + 16383) / 16384;
+                parallel_for(nch, threads, [&](int64_t c) {
+                    for (int64_t i = b0 + c * 16384; i < std::min(b1, b0 + (c + 1) * 16384); ++i) one(i);
+                });
+            }
+        }
     }
+    // P(v): highest level of a rule parent
+    const int64_t nch_r = std::max<int64_t>(1, (R + 65535) / 65536);
+    std::vector<int32_t> lmax_ch((size_t)nch_r, 0);
+    parallel_for(nch_r, threads, [&](int64_t c) {
+        auto amax = [](int32_t* p, int32_t v) {
+            int32_t cur = __atomic_load_n(p, __ATOMIC_RELAXED);
+            while (cur < v && !__atomic_compare_exchange_n(p, &cur, v, true, __ATOMIC_RELAXED, __ATOMIC_RELAXED)) {
+            }
+        };
+        int32_t m = 0;
+        for (int64_t i = c * 65536; i < std::min(R, (c + 1) * 65536); ++i) {
+            const int32_t l = g.lvl[i];
+            m = std::max(m, l);
+            if (g.ra[i] >= alpha) amax(&g.plast[g.ra[i] - alpha], l);
+            if (g.rb[i] >= alpha) amax(&g.plast[g.rb[i] - alpha], l);
+        }
+        lmax_ch[c] = m;
+    });
+    int32_t L = 0;
+    for (int32_t m : lmax_ch) L = std::max(L, m);
     g.L = L;
     tr.mark("levels (Eq. 3.1)");
 
-    // rules of each level, ordered by (first column, id)
+    // rules ordered by (first column, id), then by (level, first column, id):
+    // stable parallel counting sorts (16-bit digits of the column, then the level)
+    const int T = std::max(1, threads);
+    auto stable_sort_by = [&](const std::vector<int32_t>& in, std::vector<int32_t>& out, int64_t nbuckets,
+                              auto&& key) {
+        const int64_t nt = std::min<int64_t>(T, std::max<int64_t>(1, (int64_t)in.size() / 65536));
+        std::vector<int64_t> off((size_t)(nt * nbuckets), 0);
+        const int64_t n = (int64_t)in.size();
+        parallel_for(nt, threads, [&](int64_t t) {
+            int64_t* h = &off[(size_t)(t * nbuckets)];
+            for (int64_t p = n * t / nt; p < n * (t + 1) / nt; ++p) h[key(in[p])]++;
+        });
+        int64_t run = 0;
+        for (int64_t d = 0; d < nbuckets; ++d)
+            for (int64_t t = 0; t < nt; ++t) {
+                const int64_t c = off[(size_t)(t * nbuckets + d)];
+                off[(size_t)(t * nbuckets + d)] = run;
+                run += c;
+            }
+        out.resize(in.size());
+        parallel_for(nt, threads, [&](int64_t t) {
+            int64_t* h = &off[(size_t)(t * nbuckets)];
+            for (int64_t p = n * t / nt; p < n * (t + 1) / nt; ++p) out[h[key(in[p])]++] = in[p];
+        });
+    };
+    std::vector<int32_t> byfc((size_t)R), tmp;
+    std::iota(byfc.begin(), byfc.end(), 0);
+    int32_t fcmax = 0;
+    for (int64_t i = 0; i < R; ++i) fcmax = std::max(fcmax, fc[i]);
+    stable_sort_by(byfc, tmp, 65536, [&](int32_t v) { return fc[v] & 0xFFFF; });
+    if (fcmax >= 65536) {
+        stable_sort_by(tmp, byfc, 65536, [&](int32_t v) { return (uint32_t)fc[v] >> 16; });
+    } else {
+        byfc.swap(tmp);
+    }
+    std::vector<int32_t> order;
+    stable_sort_by(byfc, order, (int64_t)L + 1, [&](int32_t v) { return g.lvl[v]; });
     std::vector<int64_t> cnt_lvl((size_t)L + 2, 0);
     for (int64_t i = 0; i < R; ++i) cnt_lvl[g.lvl[i]]++;
     std::vector<int64_t> lvl_start((size_t)L + 2, 0);
     for (int k = 1; k <= L + 1; ++k) lvl_start[k] = lvl_start[k - 1] + cnt_lvl[k - 1];
-    std::vector<int32_t> order((size_t)R);
-    {
-        std::vector<int64_t> fill(lvl_start.begin(), lvl_start.end());
-        for (int64_t i = 0; i < R; ++i) order[fill[g.lvl[i]]++] = (int32_t)i;
-    }
-    auto by_fc = [&](int32_t u, int32_t v) { return fc[u] != fc[v] ? fc[u] < fc[v] : u < v; };
     std::vector<int32_t> pos((size_t)R, 0);  // position within own level
-    parallel_for(L, threads, [&](int64_t km1) {
-        const int k = (int)km1 + 1;
-        auto b = order.begin() + lvl_start[k], e = order.begin() + lvl_start[k + 1];
-        std::sort(b, e, by_fc);  // ids are unique: the order is total
-        int32_t p = 0;
-        for (auto it = b; it != e; ++it) pos[*it] = p++;
+    parallel_for(nch_r, threads, [&](int64_t c) {
+        for (int64_t p = c * 65536; p < std::min(R, (c + 1) * 65536); ++p)
+            pos[order[p]] = (int32_t)(p - lvl_start[g.lvl[order[p]]]);
     });
-
     tr.mark("order levels by column");
+
+    // pass-through lists: v is carried at levels lvl(v)+1 .. P(v)-1
+    // (section 4.2), each level's list ordered by (first column, id); ptpos
+    // holds v's position in the list of each level it is carried at
     g.lv.assign((size_t)L + 1, Level{});
-    g.lv[0] = Level{};
-    g.wmax = 0;
-    g.pt_total = 0;
-    // pass-through lists, level by level: pt(k) = {v : lvl v < k <= P(v) - 1}
-    std::vector<int32_t> pt_prev, pt_cur;        // rule ids, sorted by (fc, id)
-    std::vector<int32_t> ptpos_a((size_t)R, -1), ptpos_b((size_t)R, -1);
-    std::vector<int32_t>* ptpos_prev = &ptpos_a;  // position in level k-1's pt segment
-    std::vector<int32_t>* ptpos_cur = &ptpos_b;
-    std::vector<int64_t> nb_of((size_t)L + 1, 0), npt_of((size_t)L + 1, 0);
-    std::vector<std::vector<int32_t>> pt_lists((size_t)L + 1);
-    for (int k = 1; k <= L; ++k) {
-        // carried binaries of level k-1 (P >= k+1) and continuing pass-throughs (P >= k+1)
-        pt_cur.clear();
-        if (k >= 2) {
-            auto b = order.begin() + lvl_start[k - 1], e = order.begin() + lvl_start[k];
-            std::vector<int32_t> carried;
-            for (auto it = b; it != e; ++it)
-                if (g.plast[*it] >= k + 1) carried.push_back(*it);
-            std::vector<int32_t> cont;
-            for (int32_t v : pt_prev)
-                if (g.plast[v] >= k + 1) cont.push_back(v);
-            pt_cur.resize(carried.size() + cont.size());
-            std::merge(carried.begin(), carried.end(), cont.begin(), cont.end(), pt_cur.begin(), by_fc);
-        }
-        pt_lists[k] = pt_cur;
-        nb_of[k] = cnt_lvl[k];
-        npt_of[k] = (int64_t)pt_cur.size();
-        g.pt_total += npt_of[k];
-        g.wmax = std::max<int64_t>(g.wmax, nb_of[k] + npt_of[k]);
-        pt_prev.swap(pt_cur);
+    std::vector<int64_t> ptidx((size_t)R + 1, 0);  // first entry of v in ptpos
+    {
+        std::vector<int64_t> part((size_t)nch_r + 1, 0);
+        parallel_for(nch_r, threads, [&](int64_t c) {
+            int64_t s = 0;
+            for (int64_t v = c * 65536; v < std::min(R, (c + 1) * 65536); ++v)
+                s += std::max(0, g.plast[v] - g.lvl[v] - 1);
+            part[c + 1] = s;
+        });
+        for (int64_t c = 0; c < nch_r; ++c) part[c + 1] += part[c];
+        parallel_for(nch_r, threads, [&](int64_t c) {
+            int64_t s = part[c];
+            for (int64_t v = c * 65536; v < std::min(R, (c + 1) * 65536); ++v) {
+                ptidx[v] = s;
+                s += std::max(0, g.plast[v] - g.lvl[v] - 1);
+            }
+        });
+        ptidx[R] = part[nch_r];
     }
+    g.pt_total = ptidx[R];
+    std::vector<int32_t> ptflat((size_t)g.pt_total), ptpos((size_t)g.pt_total);
+    std::vector<int64_t> pt_off((size_t)L + 2, 0);
+    {
+        const int64_t nt = std::min<int64_t>(T, std::max<int64_t>(1, R / 65536));
+        const int64_t nl = (int64_t)L + 1;
+        std::vector<int64_t> cnt((size_t)(nt * nl), 0);
+        parallel_for(nt, threads, [&](int64_t t) {
+            int64_t* h = &cnt[(size_t)(t * nl)];
+            for (int64_t p = R * t / nt; p < R * (t + 1) / nt; ++p) {
+                const int32_t v = byfc[p];
+                for (int k = g.lvl[v] + 1; k < g.plast[v]; ++k) h[k]++;
+            }
+        });
+        std::vector<int64_t> npt((size_t)nl, 0);
+        for (int64_t k = 0; k < nl; ++k)
+            for (int64_t t = 0; t < nt; ++t) npt[k] += cnt[(size_t)(t * nl + k)];
+        for (int64_t k = 0; k < nl; ++k) pt_off[k + 1] = pt_off[k] + npt[k];
+        for (int64_t k = 0; k < nl; ++k) {
+            int64_t run = pt_off[k];
+            for (int64_t t = 0; t < nt; ++t) {
+                const int64_t c = cnt[(size_t)(t * nl + k)];
+                cnt[(size_t)(t * nl + k)] = run;
+                run += c;
+            }
+        }
+        parallel_for(nt, threads, [&](int64_t t) {
+            int64_t* h = &cnt[(size_t)(t * nl)];
+            for (int64_t p = R * t / nt; p < R * (t + 1) / nt; ++p) {
+                const int32_t v = byfc[p];
+                for (int k = g.lvl[v] + 1; k < g.plast[v]; ++k) {
+                    const int64_t e = h[k]++;
+                    ptflat[e] = v;
+                    ptpos[ptidx[v] + (k - g.lvl[v] - 1)] = (int32_t)(e - pt_off[k]);
+                }
+            }
+        });
+    }
+    g.wmax = 0;
+    for (int k = 1; k <= L; ++k) g.wmax = std::max<int64_t>(g.wmax, cnt_lvl[k] + (pt_off[k + 1] - pt_off[k]));
+    std::vector<int32_t>().swap(byfc);
+    std::vector<int32_t>().swap(tmp);
     tr.mark("pass-through lists");
     auto align64 = [](int64_t v) { return (v + 63) & ~int64_t(63); };
     g.buf_a = align64(alpha);
@@ -181,10 +278,14 @@ gcs_status finish_layout(Grammar& g, int threads)
         set_error("value arena exceeds 2^31-1 elements");
         return GCS_ERANGE;
     }
+    int64_t co = 0;
     for (int k = 1; k <= L; ++k) {
-        g.lv[k].nb = nb_of[k];
-        g.lv[k].npt = npt_of[k];
+        g.lv[k].nb = cnt_lvl[k];
+        g.lv[k].npt = pt_off[k + 1] - pt_off[k];
         g.lv[k].base = (k & 1) ? g.buf_a : g.buf_b;
+        g.lv[k].child_off = co;
+        g.lv[k].pt_off = pt_off[k];
+        co += cnt_lvl[k];
     }
 
     // column slices: weighted quantiles of the first column, every rule
@@ -218,13 +319,12 @@ gcs_status finish_layout(Grammar& g, int threads)
     for (int k = 1; k <= L; ++k) {
         Level& l = g.lv[k];
         auto b = order.begin() + lvl_start[k];
+        auto pb = ptflat.begin() + pt_off[k];
         for (int x = 0; x <= kSlices; ++x) {
             const int32_t cut = g.col_cut[x];
             l.bsl[x] = x == kSlices ? l.nb : std::partition_point(b, b + l.nb, [&](int32_t v) { return fc[v] < cut; }) - b;
-            const auto& pl = pt_lists[k];
             l.psl[x] = x == kSlices ? l.npt
-                                    : std::partition_point(pl.begin(), pl.end(), [&](int32_t v) { return fc[v] < cut; }) -
-                                          pl.begin();
+                                    : std::partition_point(pb, pb + l.npt, [&](int32_t v) { return fc[v] < cut; }) - pb;
         }
     }
     for (int x = 0; x <= kSlices; ++x) {
@@ -232,35 +332,33 @@ gcs_status finish_layout(Grammar& g, int threads)
     }
 
     tr.mark("column slices");
-    // children and pass-through sources
+    // children and pass-through sources: the arena offset of nonterminal w as
+    // read from level j (w alive at level j: its own level or a carried copy)
+    auto slot = [&](int32_t w, int j) -> int32_t {
+        const Level& P = g.lv[j];
+        if (g.lvl[w] == j) return (int32_t)(P.base + pos[w]);
+        return (int32_t)(P.base + P.nb + ptpos[ptidx[w] + (j - g.lvl[w] - 1)]);
+    };
     g.child.resize((size_t)2 * R);
     g.ptsrc.resize((size_t)g.pt_total);
-    int64_t co = 0, po = 0;
-    for (int k = 1; k <= L; ++k) {
-        const Level& P = g.lv[k - 1];
-        // arena offset of nonterminal v as read at level k (v alive at level k-1)
-        auto read_off = [&](int32_t v) -> int32_t {
-            if (g.lvl[v] == k - 1) return (int32_t)(P.base + pos[v]);
-            return (int32_t)(P.base + P.nb + (*ptpos_prev)[v]);
-        };
-        g.lv[k].child_off = co;
-        for (int64_t t = lvl_start[k]; t < lvl_start[k + 1]; ++t) {
-            int32_t v = order[t];
-            int32_t a = g.ra[v], b = g.rb[v];
-            g.child[2 * (co + pos[v])] = a < alpha ? a : read_off(a - (int32_t)alpha);
-            g.child[2 * (co + pos[v]) + 1] = b < alpha ? b : read_off(b - (int32_t)alpha);
+    parallel_for(nch_r, threads, [&](int64_t c) {
+        for (int64_t v = c * 65536; v < std::min(R, (c + 1) * 65536); ++v) {
+            const int k = g.lvl[v];
+            const int32_t a = g.ra[v], b = g.rb[v];
+            const int64_t at = 2 * (g.lv[k].child_off + pos[v]);
+            g.child[at] = a < alpha ? a : slot(a - (int32_t)alpha, k - 1);
+            g.child[at + 1] = b < alpha ? b : slot(b - (int32_t)alpha, k - 1);
         }
-        co += nb_of[k];
-        g.lv[k].pt_off = po;
-        const auto& pl = pt_lists[k];
-        for (size_t i = 0; i < pl.size(); ++i) {
-            g.ptsrc[po + i] = read_off(pl[i]);
-            (*ptpos_cur)[pl[i]] = (int32_t)i;
+    });
+    const int64_t nch_p = std::max<int64_t>(1, (g.pt_total + 65535) / 65536);
+    parallel_for(nch_p, threads, [&](int64_t c) {
+        const int64_t e0 = c * 65536, e1 = std::min(g.pt_total, (c + 1) * 65536);
+        int k = (int)(std::upper_bound(pt_off.begin(), pt_off.end(), e0) - pt_off.begin()) - 1;
+        for (int64_t e = e0; e < e1; ++e) {
+            while (e >= pt_off[k + 1]) ++k;
+            g.ptsrc[e] = slot(ptflat[e], k - 1);
         }
-        po += (int64_t)pl.size();
-        std::swap(ptpos_prev, ptpos_cur);
-        std::vector<int32_t>().swap(pt_lists[k]);
-    }
+    });
 
     // emission groups: C-occurrences at their symbol's level (section 4.3: a
     // root is emitted the moment its level is computed), grouped by (level,
