@@ -7,6 +7,11 @@ separately as on the pages' Table B.1).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
+The default workload is the largest configuration, the 200,000 x 2,000,000
+genotype (about 1.2e11 nonzeros), built as 100 column groups on the device
+(about five minutes) and swept whole; genotype_20000x100000_f32 and the other
+WORKLOADS names in grammar_compressed_sparse_amd/synth select the others.
+
 Prints one JSON line (metric, value = nnz/s, roofline of the level kernel,
 CPU baseline = the oracle on the host cores, footprint vs CSR).
 """
@@ -448,157 +453,140 @@ def bench_tropical(args, torch, gcs, leg, g, rp, col, spec, src, vis_o, counts_o
 
 
 def bench_biobank(args, wl, spec, leg):
-    """The 200,000 x 2,000,000 genotype (about 1.2e11 nonzeros, 982 GB as fp32
-    CSR) as independent 10,000-column groups: the first args.groups groups are
-    built at the full row count, all kept resident, and one step sweeps every
-    resident group (gcs_sweep_right for the first, gcs_sweep_right_acc for the
-    rest) into one y.  Sampled rows are checked against the oracle summed over
-    the same groups (CPU leg); the full matrix (200 groups) is extrapolated."""
-    import torch
-    from grammar_compressed_sparse_amd import gcs, synth
+    """The 200,000 x 2,000,000 genotype (about 1.2e11 nonzeros; fp32 CSR about
+    982 GB, beyond one GPU's 288 GB) as independent column groups of
+    args.group_cols columns, each built by the device builder and all kept
+    resident (grammar_compressed_sparse_amd.groups); one step sweeps every
+    group into one y.  The CPU leg checks 4,098 seeded rows against the oracle
+    (on each group's CSR as it is generated) and times the oracle on one group."""
+    import threading
 
-    width, ngroups_full = 10_000, spec.n_cols // 10_000
+    import torch
+    from grammar_compressed_sparse_amd import gcs, groups, synth
+
+    acc64 = args.policy == "f32_acc_f64"
+    policy = gcs.PLUS_F32_ACC_F64 if acc64 else gcs.PLUS_F32
+    tol = 1e-12 if acc64 else 1e-5
+    yelem = 8 if acc64 else 4
     x64 = synth.normal(spec.n_cols, wl["x_seeds"][0])
     x32 = x64.astype(np.float32)
+    xo = x32.astype(np.float64)  # the values the device sees
     xd = torch.from_numpy(x32).cuda()
-    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(spec.n_rows, 256, replace=False),
+    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(spec.n_rows, 4096, replace=False),
                                      [0, spec.n_rows - 1]]))
     yo, absum = np.zeros(rows.size), np.zeros(rows.size)
-    devs, grams, nnz, build_s, csr_bytes = [], [], 0, 0.0, 0
-    for gi in range(args.groups):
-        t = time.perf_counter()
-        rp, col, val = synth.genotype(spec, col0=gi * width, ncols=width)
-        t_gen = time.perf_counter() - t
-        t = time.perf_counter()
-        g = gcs.build_grammar(rp, col, val, n_cols=spec.n_cols, col_chunk=2000)
-        build_s += time.perf_counter() - t
-        devs.append(gcs.upload(g, gcs.PLUS_F32))
+    lock = threading.Lock()
+    nnz_of, lbytes = {}, {}
+
+    def on_group(i, c0, nc, rp, col, val):
         if leg is not None:
-            a, b = leg.rows_f64(rows, rp, col, val, x32.astype(np.float64))
-            yo += a
-            absum += b
-        nnz += int(rp[-1])
-        csr_bytes += 8 * int(rp[-1])
-        log(f"group {gi}: {int(rp[-1])} nonzeros, generated in {t_gen:.0f} s, built in "
-            f"{time.perf_counter() - t:.0f} s, {devs[-1].device_bytes / 1e6:.0f} MB on the device")
-        grams.append(g)  # kept for the merged grammar below
-        del rp, col, val
-    y = devs[0].new_y()
+            a, b = leg.rows_f64(rows, rp, col, val, xo)
+            with lock:
+                yo[:] += a
+                absum[:] += b
 
-    def step():
-        devs[0].sweep_right(xd, y)
-        for d in devs[1:]:
-            d.sweep_right_acc(xd, y)
+    def on_built(i, g, dev):
+        st = g.stats()
+        lay = g.layout_meta()
+        lay["alpha"] = st["n_terminals"]
+        nwide = dev.sweep_launches() - 2
+        lb = level_bytes(lay, yelem, yelem)
+        with lock:
+            nnz_of[i] = st["nnz"]
+            lbytes[i] = (float(lb[:max(nwide, 0)].sum()), float(lb.sum()), nwide)
 
-    step()
-    for d in devs:
-        d.check()
-    per_group_bytes = [d.device_bytes for d in devs]
+    log(f"building {spec.n_rows}x{spec.n_cols} as groups of {args.group_cols} columns "
+        f"({args.build_workers} build workers)")
+    cg = groups.build_column_groups(lambda c0, nc: synth.genotype(spec, col0=c0, ncols=nc), spec.n_rows,
+                                    spec.n_cols, args.group_cols, policy, workers=args.build_workers,
+                                    table_entries=1 << 28, on_group=on_group, on_built=on_built, log=log)
+    nnz = sum(nnz_of.values())
+    log(f"built {len(cg.devices)} groups in {cg.build_s:.0f}s: nnz={nnz}, device {cg.device_bytes / 1e9:.1f} GB")
+    y = cg.sweep_right(xd)
+    cg.check()
     err = None
     if leg is not None:
         err = float(np.max(np.abs(y.cpu().numpy()[rows].astype(np.float64) - yo) / np.maximum(absum, 1e-300)))
-        if err > 1e-5:
-            raise SystemExit(f"biobank groups disagree with the oracle: {err:.2e}")
+        log(f"sampled-row check: {rows.size} rows, max rel err {err:.2e} (tol {tol})")
+        if err > tol:
+            raise SystemExit(f"biobank sweep disagrees with the oracle: {err:.2e}")
     for _ in range(args.warmup):
-        step()
+        cg.sweep_right(xd, y)
+    torch.cuda.synchronize()
+    # timed region: K full sweeps; each group's sweep records one pair of HIP
+    # events (its stream) around its wide level launches, the dominant kernel
+    cg.profile_begin(args.steps, gcs.PROFILE_LEVEL_SPAN)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        cg.sweep_right_profiled(xd, y)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    for d in devs:
-        d.check()
-    # the same groups merged into one grammar (gcs_merge_grammars): one
-    # upload, one sweep per step
-    t = time.perf_counter()
-    gm = gcs.merge_grammars(grams)
-    merge_s = time.perf_counter() - t
-    del grams
-    for d in devs:
-        d.free()
-    devs = []
-    torch.cuda.empty_cache()
-    dm = gcs.upload(gm, gcs.PLUS_F32)
-    ym = dm.new_y()
-    dm.sweep_right(xd, ym)
-    dm.check()
-    err_m = None
+    spans = cg.profile_end()
+    cg.check()
+    ms_per_step = elapsed * 1e3 / args.steps
+    span_ms = float(sum(float(sp[:, 0].mean()) for sp in spans))  # per full sweep
+    wide_bytes = sum(v[0] for v in lbytes.values())
+    all_bytes = sum(v[1] for v in lbytes.values())
+    nwide = sum(v[2] for v in lbytes.values())
+    achieved = wide_bytes / (span_ms * 1e-3) / 1e9
+    log(f"{ms_per_step:.2f} ms per sweep ({nnz / (ms_per_step * 1e-3):.3e} nnz/s); wide levels {nwide} launches in "
+        f"{span_ms:.2f} ms, {wide_bytes / 1e9:.1f} GB -> {achieved:.0f} GB/s")
+    cpu = None
     if leg is not None:
-        err_m = float(np.max(np.abs(ym.cpu().numpy()[rows].astype(np.float64) - yo) / np.maximum(absum, 1e-300)))
-        if err_m > 1e-5:
-            raise SystemExit(f"merged biobank groups disagree with the oracle: {err_m:.2e}")
-    for _ in range(args.warmup):
-        dm.sweep_right(xd, ym)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dm.sweep_right(xd, ym)
-    torch.cuda.synchronize()
-    elapsed_m = time.perf_counter() - t0
-    dm.check()
-    st_m = gm.stats()
-    merged = {"ms_per_sweep": elapsed_m * 1e3 / args.steps, "nnz_per_s": nnz * args.steps / elapsed_m,
-              "merge_s": merge_s, "device_bytes": dm.device_bytes, "launches_per_sweep": dm.sweep_launches(),
-              "depth": st_m["depth"], "max_width": st_m["max_width"], "max_rel_err_sampled": err_m}
-    log(f"merged: {merged}")
-    m_dev_bytes = dm.device_bytes
-    dm.free()
-    del dm, ym
-    torch.cuda.empty_cache()
-    # the fp64-accumulate option on the same merged grammar: fp32 x, fp64
-    # terminals, level values and y (PLUS_F32_ACC_F64), checked at 1e-12
-    d64 = gcs.upload(gm, gcs.PLUS_F32_ACC_F64)
-    y64 = d64.new_y()
-    d64.sweep_right(xd, y64)
-    d64.check()
-    err_64 = None
-    if leg is not None:
-        err_64 = float(np.max(np.abs(y64.cpu().numpy()[rows] - yo) / np.maximum(absum, 1e-300)))
-        if err_64 > 1e-12:
-            raise SystemExit(f"merged biobank groups (fp64 accumulate) disagree with the oracle: {err_64:.2e}")
-    for _ in range(args.warmup):
-        d64.sweep_right(xd, y64)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        d64.sweep_right(xd, y64)
-    torch.cuda.synchronize()
-    elapsed_64 = time.perf_counter() - t0
-    d64.check()
-    merged["acc_f64"] = {"ms_per_sweep": elapsed_64 * 1e3 / args.steps, "nnz_per_s": nnz * args.steps / elapsed_64,
-                         "device_bytes": d64.device_bytes, "max_rel_err_sampled": err_64}
-    log(f"merged, fp64 accumulate: {merged['acc_f64']}")
-    d64.free()
-    del d64, y64
-    dev_bytes = sum(per_group_bytes) + 4 * spec.n_cols + 4 * spec.n_rows
-    csr_bytes += 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
-    scale = ngroups_full / args.groups
-    # the step: the merged grammar's sweep (the groups as separate uploads
-    # are context); the full matrix would be a few merged grammars, since one
-    # grammar indexes its roots with 32 bits (|C| < 2^31)
-    m_bytes = m_dev_bytes + 4 * spec.n_cols + 4 * spec.n_rows
+        # the oracle on the host cores over group 0 (regenerated), about 10 s
+        rp, col, val = synth.genotype(spec, col0=0, ncols=args.group_cols)
+        g_nnz = int(rp[-1])
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            leg.o.spmv_f64(rp, col, val, xo)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or passes >= 50:
+                break
+        cpu = {"value": g_nnz * passes / el, "unit": "nnz/s", "cores": leg.threads(), "kind": "oracle",
+               "sample": f"column group 0 (columns [0, {args.group_cols}), all {spec.n_rows} rows, {g_nnz} "
+                         f"nonzeros), {passes} fp64 compensated CSR passes ({el:.1f} s)"}
+        del rp, col, val
+    copy_gbs = copy_achievable_gbs(torch)
+    csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
+    eng_bytes = cg.device_bytes + 4 * spec.n_cols + yelem * spec.n_rows
+    sts = cg.stats
     out = {
         "metric": "nnz/s for y=Mx sweep; achieved HBM GB/s (% peak); device bytes vs CSR",
-        "value": nnz * args.steps / elapsed_m, "unit": "nnz/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": elapsed_m * 1e3 / args.steps, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded genotype mosaic)",
-        "config": {"workload": args.workload, "n_rows": spec.n_rows, "n_cols": spec.n_cols,
-                   "groups_swept": args.groups, "group_cols": width, "nnz_swept": nnz, "build_s": build_s,
-                   "merge_s": merge_s, "max_rel_err_sampled": err_m, "sampled_rows": int(rows.size),
-                   "device_bytes": m_bytes, "csr_bytes_analytic": csr_bytes,
-                   "footprint_ratio_csr_over_engine": csr_bytes / m_bytes,
-                   "merged_one_grammar": merged,
-                   "per_group_uploads": {"ms_per_sweep": elapsed * 1e3 / args.steps,
-                                         "nnz_per_s": nnz * args.steps / elapsed, "device_bytes": dev_bytes,
-                                         "max_rel_err_sampled": err},
-                   "extrapolated_full": {"groups": ngroups_full, "nnz": nnz * scale,
-                                         "device_bytes": m_bytes * scale,
-                                         "ms_per_sweep": elapsed_m * 1e3 / args.steps * scale,
-                                         "host_build_s": (build_s + merge_s) * scale}},
-        "roofline": None, "cpu_baseline": None,
+        "value": nnz * args.steps / elapsed, "unit": "nnz/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32->f64" if acc64 else "f32",
+        "data": "synthetic (seeded genotype mosaic)",
+        "config": {"workload": args.workload, "n_rows": spec.n_rows, "n_cols": spec.n_cols, "nnz": nnz,
+                   "founders": spec.founders, "seg_mean": spec.seg_mean, "mu": spec.mu, "seed": spec.seed,
+                   "policy": args.policy, "groups": len(cg.devices), "group_cols": args.group_cols,
+                   "builder": "device (round-based RePair on the GPU; levels and layout on the host)",
+                   "build_s": cg.build_s,
+                   "grammar": {"n_rules": sum(s["n_rules"] for s in sts),
+                               "n_passthrough": sum(s["n_passthrough"] for s in sts),
+                               "c_len": sum(s["c_len"] for s in sts),
+                               "n_terminals": sum(s["n_terminals"] for s in sts),
+                               "depth_max": max(s["depth"] for s in sts),
+                               "max_width_max": max(s["max_width"] for s in sts)},
+                   "launches_per_sweep": cg.launches_per_sweep(),
+                   "max_rel_err_sampled": err, "sampled_rows": int(rows.size),
+                   "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
+                   "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
+                   "hbm_bytes_total": int(torch.cuda.get_device_properties(0).total_memory),
+                   "wide_levels": nwide, "level_span_ms": span_ms,
+                   "bytes_per_sweep": all_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "level_kernel (the wide levels of every group's sweep, one launch each; each group "
+                               "timed from before its first to after its last wide launch)",
+                     "launches": nwide, "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
+                     "bytes_per_launch_avg": wide_bytes / max(nwide, 1),
+                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    cg.free()
 
 
 def bench_graph(args, wl, spec, leg):
@@ -726,13 +714,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="genotype_20000x100000_f32")
+    ap.add_argument("--workload", default="genotype_200000x2000000_f32")
     ap.add_argument("--col-chunk", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg: the oracle's timing and the sampled checks against it")
     ap.add_argument("--no-csr", action="store_true")
-    ap.add_argument("--groups", type=int, default=6,
-                    help="column groups of 10,000 columns built and swept for the 200,000 x 2,000,000 workload")
+    ap.add_argument("--group-cols", type=int, default=20_000,
+                    help="columns per group of the 200,000 x 2,000,000 workload (each group one device build)")
+    ap.add_argument("--build-workers", type=int, default=3,
+                    help="groups of the 200,000 x 2,000,000 workload built concurrently")
+    ap.add_argument("--policy", default="f32", choices=["f32", "f32_acc_f64"],
+                    help="200,000 x 2,000,000 workload: fp32, or fp32 x with fp64 accumulation")
     ap.add_argument("--batches", default="32,64",
                     help="batched sweeps (Y = M X) to time after the headline, comma-separated B; empty: none")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,

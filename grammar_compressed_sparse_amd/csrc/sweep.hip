@@ -7,8 +7,8 @@
 //   grammar image  child pairs | pass-through sources | emission groups
 //                  (erow, eoff, epos) | emission chunks | terminal
 //                  descriptors | V | launch table | narrow levels' LDS image
-//   workspace      value arena [T (alpha) | buffer A | buffer B] | slice
-//                  accumulators | counters
+//   workspace      counters (256 B) | value arena [T (alpha) | buffer A |
+//                  buffer B] | slice accumulators
 //   batch workspace (batched sweeps only, per call)
 #include <hip/hip_runtime.h>
 
@@ -1358,9 +1358,11 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     d->tcol = (const int32_t*)(base + im.tcol);
     d->tval = (const int32_t*)(base + im.tval);
     d->V = base + im.V;
-    d->arena = workspace_dev;
-    d->acc = (unsigned char*)workspace_dev + gcs::arena_bytes(g, p);
-    d->counters = (unsigned long long*)((unsigned char*)workspace_dev + gcs::arena_bytes(g, p) + gcs::acc_bytes(g, p));
+    // [counters (256 B) | arena | accumulators]: the counters come first so
+    // that uploads sharing one workspace share them at the same address
+    d->counters = (unsigned long long*)workspace_dev;
+    d->arena = (unsigned char*)workspace_dev + 256;
+    d->acc = (unsigned char*)workspace_dev + 256 + gcs::arena_bytes(g, p);
     d->barrier = (unsigned*)(d->counters + 2);
     d->err = (int*)(d->counters + 3);
     // launch arguments of every level; the narrow levels at the top go to the
@@ -1634,6 +1636,23 @@ extern "C" gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev,
     }
     const int64_t per = 2 * prof_pairs(d);
     gcs_status st = sweep_dispatch(d, x_dev, y_dev, stream, d->events.data() + per * d->prof_used, 0,
+                                   d->prof_mode == GCS_PROFILE_LEVEL_SPAN);
+    if (st == GCS_OK) d->prof_used++;
+    return st;
+}
+
+extern "C" gcs_status gcs_sweep_right_acc_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream)
+{
+    if (!d || !d->profiling) {
+        gcs::set_error("gcs_profile_begin was not called");
+        return GCS_ESTATE;
+    }
+    if (d->prof_used == d->prof_max) {
+        gcs::set_error("more sweeps than gcs_profile_begin reserved");
+        return GCS_ERANGE;
+    }
+    const int64_t per = 2 * prof_pairs(d);
+    gcs_status st = sweep_dispatch(d, x_dev, y_dev, stream, d->events.data() + per * d->prof_used, 1,
                                    d->prof_mode == GCS_PROFILE_LEVEL_SPAN);
     if (st == GCS_OK) d->prof_used++;
     return st;

@@ -98,6 +98,8 @@ _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
 _lib.gcs_profile_begin.argtypes = [_P, _I64, ctypes.c_int32]
 _lib.gcs_sweep_right_profiled.argtypes = [_P, _P, _P, _P]
+_lib.gcs_sweep_right_acc_profiled.argtypes = [_P, _P, _P, _P]
+_lib.gcs_sweep_right_acc_profiled.restype = _st
 _lib.gcs_profile_end.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
 _lib.gcs_device_check.argtypes = [_P, _P]
 _lib.gcs_device_check.restype = _st
@@ -175,6 +177,16 @@ class Grammar:
         out["slices"] = np.zeros((nl, 3, 9), np.int64)
         out["col_cut"] = np.zeros(9, np.int32)
         _check(_lib.gcs_export_slices(self._h, _ptr(out["slices"]), _ptr(out["col_cut"])))
+        return out
+
+    def layout_meta(self) -> dict:
+        """level_meta and eoff of the layout only (gcs_export_layout with the
+        other arrays skipped): enough to count each level's nodes and roots."""
+        c = np.zeros(8, np.int64)
+        _check(_lib.gcs_layout_counts(self._h, _ptr(c)))
+        nl, ng = int(c[0]), int(c[3])
+        out = dict(level_meta=np.zeros((nl, 8), np.int64), eoff=np.zeros(ng + 1, np.int32))
+        _check(_lib.gcs_export_layout(self._h, _ptr(out["level_meta"]), None, None, None, _ptr(out["eoff"]), None))
         return out
 
     def level0_words(self, policy: int) -> dict:
@@ -374,10 +386,10 @@ class Device:
         one pair around the wide level launches of each sweep."""
         _check(_lib.gcs_profile_begin(self._h, max_sweeps, mode))
 
-    def sweep_right_profiled(self, x, y, stream=None):
+    def sweep_right_profiled(self, x, y, stream=None, accumulate=False):
         _check_xy(self, x, y)
-        _check(_lib.gcs_sweep_right_profiled(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                                             _stream_ptr(stream)))
+        fn = _lib.gcs_sweep_right_acc_profiled if accumulate else _lib.gcs_sweep_right_profiled
+        _check(fn(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), _stream_ptr(stream)))
         return y
 
     def profile_end(self) -> np.ndarray:
@@ -400,8 +412,10 @@ class Device:
             pass
 
 
-def upload(grammar: Grammar, policy, device="cuda", stream=None) -> Device:
-    """gcs_device_layout + caller-owned torch allocations + gcs_upload."""
+def upload(grammar: Grammar, policy, device="cuda", stream=None, workspace=None) -> Device:
+    """gcs_device_layout + caller-owned torch allocations + gcs_upload.
+    ``workspace``: a uint8 device tensor to use (and share with other
+    uploads whose sweeps are all ordered on one stream) instead of a new one."""
     torch = _torch()
     policy = POLICY_NAMES.get(policy, policy)
     sz = grammar.device_layout(policy)
@@ -412,7 +426,14 @@ def upload(grammar: Grammar, policy, device="cuda", stream=None) -> Device:
         dev = torch.device("cuda", torch.cuda.current_device())
     with torch.cuda.device(dev):
         gbuf = torch.empty(max(sz["grammar_bytes"], 256), dtype=torch.uint8, device=dev)
-        wbuf = torch.empty(max(sz["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            if workspace.dtype != torch.uint8 or workspace.numel() < sz["workspace_bytes"] or \
+                    workspace.device != dev:
+                raise GcsError(-1, f"workspace must be a uint8 tensor of at least {sz['workspace_bytes']} bytes "
+                                   f"on {dev}")
+            wbuf = workspace
+        else:
+            wbuf = torch.empty(max(sz["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
         h = _P()
         _check(_lib.gcs_upload(grammar.handle, policy, ctypes.c_void_p(gbuf.data_ptr()), gbuf.numel(),
                                ctypes.c_void_p(wbuf.data_ptr()), wbuf.numel(), _stream_ptr(stream),

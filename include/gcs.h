@@ -303,8 +303,13 @@ gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* 
 
 /* One-time host-to-device copy (the host/device boundary) of the grammar
  * image into grammar_dev (>= grammar_bytes, 256-byte aligned) on `stream`;
- * workspace_dev (>= workspace_bytes, 256-byte aligned) is the value arena.
- * Both stay owned by the caller.  The grammar object may be freed after this
+ * workspace_dev (>= workspace_bytes, 256-byte aligned) holds 256 bytes of
+ * counters, the value arena and the row accumulators.  Both stay owned by the
+ * caller.  Several uploads may share one workspace (at least the largest of
+ * their sizes) when every sweep on any of them is ordered after the others
+ * (one stream): a sweep writes every arena value before reading it, and the
+ * uploads then share the counters, the failure flag of gcs_device_check
+ * included.  The grammar object may be freed after this
  * call returns.  The call synchronises `stream`: the copy is complete when it
  * returns. */
 gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
@@ -399,6 +404,8 @@ typedef enum {
  * were profiled or cap is too small; GCS_ESTATE without gcs_profile_begin. */
 gcs_status gcs_profile_begin(gcs_device* d, int64_t max_sweeps, int32_t mode);
 gcs_status gcs_sweep_right_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
+/* gcs_sweep_right_acc with the same events (a matrix swept as column groups). */
+gcs_status gcs_sweep_right_acc_profiled(gcs_device* d, const void* x_dev, void* y_dev, void* stream);
 gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t* sweeps, int64_t* launches);
 
 /* Synchronises `stream` and reports whether any sweep since the last check
