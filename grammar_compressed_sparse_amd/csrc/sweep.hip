@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <thread>
 #include <utility>
 #include <vector>
@@ -1177,6 +1178,35 @@ extern "C" gcs_status gcs_device_layout(const gcs_grammar* h, gcs_policy p, gcs_
     return GCS_OK;
 }
 
+// ------------------------------------------------------------ fixed scratch
+// The batch workspace of gcs_sweep_right_batch_scratch: one array per GPU in
+// the library's device code, for callers that cannot allocate.  Host code
+// never passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+hipError_t g_scratch_err[kScratchDevices] = {};
+bool g_scratch_done[kScratchDevices] = {};
+
+// resolves the scratch address of device `dev`, which must be current
+void scratch_setup(int dev)
+{
+    if (dev < 0 || dev >= kScratchDevices) return;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_done[dev]) return;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+    g_scratch_err[dev] = e;
+    g_scratch_done[dev] = true;
+}
+}  // namespace
+
 extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
                                  void* workspace_dev, size_t workspace_bytes, void* stream, gcs_device** out)
 {
@@ -1205,6 +1235,7 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return gcs::hip_fail(e, "hipGetDevice");
+    scratch_setup(dev);  // device set-up: the fixed scratch of this GPU
 
     // policy-typed V
     std::vector<unsigned char> vbuf(g.V.size() * gcs::v_bytes(p));
@@ -1543,6 +1574,9 @@ extern "C" gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nve
     return GCS_OK;
 }
 
+static gcs_status batch_dispatch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, void* workspace_dev,
+                                 int32_t flags, hipStream_t s);
+
 extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec,
                                             void* workspace_dev, size_t workspace_bytes, int32_t flags,
                                             void* stream)
@@ -1565,7 +1599,12 @@ extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, vo
         gcs::set_error("cannot select the upload's device");
         return GCS_EHIP;
     }
-    hipStream_t s = (hipStream_t)stream;
+    return batch_dispatch(d, x_dev, y_dev, nvec, workspace_dev, flags, (hipStream_t)stream);
+}
+
+static gcs_status batch_dispatch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, void* workspace_dev,
+                                 int32_t flags, hipStream_t s)
+{
     switch (d->policy) {
     case GCS_PLUS_F64: return gcs::run_sweep_batch<gcs::PolPlusF64>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
     case GCS_PLUS_F32: return gcs::run_sweep_batch<gcs::PolPlusF32>(d, x_dev, y_dev, nvec, workspace_dev, flags, s);
@@ -1580,6 +1619,42 @@ extern "C" gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, vo
     }
     gcs::set_error("invalid policy");
     return GCS_EINVAL;
+}
+
+extern "C" gcs_status gcs_sweep_right_batch_scratch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec,
+                                                    int32_t flags, void* stream)
+{
+    if (!d || nvec < 1 || nvec > gcs::kMaxBatch || !batch_flags_ok(flags) || (d->n_cols > 0 && !x_dev) ||
+        (d->n_rows > 0 && !y_dev)) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    const size_t need = gcs::batch_workspace_bytes(gcs::batch_arena_rows(d, flags), d->n_rows, d->policy, nvec);
+    if (need > kScratchBytes) {
+        gcs::set_error("this batched sweep needs " + std::to_string(need) + " bytes of workspace; the fixed scratch "
+                       "array holds " + std::to_string(kScratchBytes) + " (use gcs_sweep_right_batch with a "
+                       "caller-provided workspace, or fewer vectors)");
+        return GCS_ERANGE;
+    }
+    gcs::DeviceGuard guard(d->device);
+    if (!guard.ok) {
+        gcs::set_error("cannot select the upload's device");
+        return GCS_EHIP;
+    }
+    scratch_setup(d->device);  // done at upload already; no-op then
+    void* ws = nullptr;
+    hipError_t se = hipSuccess;
+    if (d->device >= 0 && d->device < kScratchDevices) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        ws = g_scratch_ptr[d->device];
+        se = g_scratch_err[d->device];
+    }
+    if (!ws) {
+        gcs::set_error(std::string("no scratch address for this device: ") +
+                       (se != hipSuccess ? hipGetErrorString(se) : "device index out of range"));
+        return GCS_EHIP;
+    }
+    return batch_dispatch(d, x_dev, y_dev, nvec, ws, flags, (hipStream_t)stream);
 }
 
 extern "C" int64_t gcs_sweep_launches(const gcs_device* d) { return d ? gcs::count_launches(d) : 0; }

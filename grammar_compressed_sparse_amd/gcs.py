@@ -94,6 +94,8 @@ _lib.gcs_sweep_right_acc.argtypes = [_P, _P, _P, _P]
 _lib.gcs_bfs.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64), _P]
 _lib.gcs_batch_workspace_bytes.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.gcs_sweep_right_batch.argtypes = [_P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, ctypes.c_int32, _P]
+_lib.gcs_sweep_right_batch_scratch.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P]
+_lib.gcs_sweep_right_batch_scratch.restype = _st
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
 _lib.gcs_profile_begin.argtypes = [_P, _I64, ctypes.c_int32]
@@ -501,6 +503,30 @@ def sweep_right_batch(dev: Device, X, Y=None, accumulate=False, leaves_in_sweep=
     with torch.cuda.device(dev.device):
         _check(_lib.gcs_sweep_right_batch(dev.handle, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
                                           B, ctypes.c_void_p(w.data_ptr()), w.numel(), flags, _stream_ptr(stream)))
+    return Y
+
+
+def sweep_right_batch_scratch(dev: Device, X, Y=None, accumulate=False, leaves_in_sweep=False, stream=None):
+    """gcs_sweep_right_batch_scratch: Y = M X with the library's fixed 64 MiB
+    scratch as the batch workspace (no allocation in the library; Y is made
+    here only when not given)."""
+    torch = _torch()
+    if not dev.handle:
+        raise GcsError(-5, "device handle already freed")
+    if X.dim() != 2 or X.shape[0] != dev.sizes["x_len"] or X.dtype != dev.x_dtype or not X.is_contiguous() \
+            or X.device != dev.device:
+        raise GcsError(-1, f"X must be a contiguous {dev.x_dtype} tensor of shape ({dev.sizes['x_len']}, B) on "
+                           f"{dev.device}")
+    B = int(X.shape[1])
+    if Y is None:
+        Y = torch.empty((dev.sizes["y_len"], B), dtype=dev.y_dtype, device=dev.device)
+    if tuple(Y.shape) != (dev.sizes["y_len"], B) or Y.dtype != dev.y_dtype or not Y.is_contiguous() \
+            or Y.device != dev.device:
+        raise GcsError(-1, f"Y must be a contiguous {dev.y_dtype} tensor of shape ({dev.sizes['y_len']}, {B})")
+    flags = (BATCH_ACCUMULATE if accumulate else 0) | (BATCH_LEAVES_IN_SWEEP if leaves_in_sweep else 0)
+    with torch.cuda.device(dev.device):
+        _check(_lib.gcs_sweep_right_batch_scratch(dev.handle, ctypes.c_void_p(X.data_ptr()),
+                                                  ctypes.c_void_p(Y.data_ptr()), B, flags, _stream_ptr(stream)))
     return Y
 
 

@@ -363,6 +363,23 @@ gcs_status gcs_batch_workspace_bytes(const gcs_device* d, int32_t nvec, int32_t 
 gcs_status gcs_sweep_right_batch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, void* workspace_dev,
                                  size_t workspace_bytes, int32_t flags, void* stream);
 
+/* gcs_sweep_right_batch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, bit for bit, with the batch
+ * workspace taken from a fixed array of 64 MiB (67,108,864 bytes) in the
+ * library's device code instead of a workspace argument.  Each GPU holds its
+ * own copy of the array from the first gcs_upload on it until the process
+ * ends.  Allocates nothing (no hipMalloc, hipFree or allocating routine).
+ * GCS_ERANGE, with the size in the message, when gcs_batch_workspace_bytes(d,
+ * nvec, flags) exceeds 64 MiB; other errors as gcs_sweep_right_batch.
+ * Every call on a GPU shares that GPU's array and keeps the previous call's
+ * contents there; a call writes every part it reads (terminal rows, level
+ * buffers, accumulators cleared by its first launch) before reading it.
+ * Calls that overlap on one GPU (concurrent streams or threads, any handle)
+ * race on the array: order them. */
+gcs_status gcs_sweep_right_batch_scratch(gcs_device* d, const void* x_dev, void* y_dev, int32_t nvec, int32_t flags,
+                                         void* stream);
+
 /* BFS fixpoint with the Boolean policy on a square matrix (section 5: one
  * Boolean pass is one frontier expansion; the fixpoint repeats it):
  *   f = visited = sources; repeat { y = M f; f = y AND NOT visited;
