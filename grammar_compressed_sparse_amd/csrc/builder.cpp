@@ -644,6 +644,67 @@ gcs_status csrv_encode(const gcs_csr_view* m, int threads, Grammar& g, Csrv& enc
     return GCS_OK;
 }
 
+// Tiles of a (row chunk x column chunk) partition, RePaired apart, as one
+// grammar: rule ids = tile rule base + local index; row r of C = its tiles'
+// sequences in column-chunk order.  where[r] = position of row r in the
+// tiles' row order.
+static gcs_status merge_tiles(Grammar& g, std::vector<RePairResult>& res, int64_t ncc, int64_t rc,
+                              const std::vector<int32_t>& where, int threads)
+{
+    const int64_t ntiles = (int64_t)res.size(), n = g.n_rows, alpha = g.alpha();
+    const int64_t vblk = 4096;
+    std::vector<int64_t> rbase((size_t)ntiles + 1, 0);
+    for (int64_t t = 0; t < ntiles; ++t) rbase[t + 1] = rbase[t] + (int64_t)res[t].rule_a.size();
+    const int64_t R = rbase[ntiles];
+    if (alpha + R >= (int64_t)INT32_MAX) {
+        set_error("grammar exceeds the 32-bit symbol space");
+        return GCS_ERANGE;
+    }
+    try {
+        g.ra.resize((size_t)R);
+        g.rb.resize((size_t)R);
+        parallel_for(ntiles, threads, [&](int64_t t) {
+            const int32_t shift = (int32_t)rbase[t];
+            auto remap = [&](int32_t s) { return s < alpha ? s : s + shift; };
+            for (size_t i = 0; i < res[t].rule_a.size(); ++i) {
+                g.ra[rbase[t] + i] = remap(res[t].rule_a[i]);
+                g.rb[rbase[t] + i] = remap(res[t].rule_b[i]);
+            }
+        });
+        // C: row r = concatenation over column chunks of its tile sequences
+        g.c_off.assign((size_t)n + 1, 0);
+        std::vector<std::vector<int64_t>> tile_row_start((size_t)ntiles);
+        for (int64_t t = 0; t < ntiles; ++t) {
+            auto& s = tile_row_start[t];
+            s.resize(res[t].row_len.size() + 1, 0);
+            for (size_t i = 0; i < res[t].row_len.size(); ++i) s[i + 1] = s[i] + res[t].row_len[i];
+        }
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t rb = where[r] / rc, ri = where[r] - rb * rc, len = 0;
+            for (int64_t cb = 0; cb < ncc; ++cb) len += res[rb * ncc + cb].row_len[ri];
+            g.c_off[r + 1] = g.c_off[r] + len;
+        }
+        g.c_sym.resize((size_t)g.c_off[n]);
+        parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
+            for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
+                int64_t rb = where[r] / rc, ri = where[r] - rb * rc, o = g.c_off[r];
+                for (int64_t cb = 0; cb < ncc; ++cb) {
+                    const int64_t t = rb * ncc + cb;
+                    const int32_t shift = (int32_t)rbase[t];
+                    for (int64_t e = tile_row_start[t][ri]; e < tile_row_start[t][ri + 1]; ++e) {
+                        int32_t s = res[t].seq[e];
+                        g.c_sym[o++] = s < alpha ? s : s + shift;
+                    }
+                }
+            }
+        });
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory merging tiles");
+        return GCS_ENOMEM;
+    }
+    return GCS_OK;
+}
+
 static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* opts, Grammar& g)
 {
     auto t0 = std::chrono::steady_clock::now();
@@ -745,56 +806,227 @@ static gcs_status build_from_csr(const gcs_csr_view* m, const gcs_build_opts* op
     }
     g.nnz = nnz_total;
 
-    // merge: global rule ids = tile rule base + local index
-    std::vector<int64_t> rbase((size_t)ntiles + 1, 0);
-    for (int64_t t = 0; t < ntiles; ++t) rbase[t + 1] = rbase[t] + (int64_t)res[t].rule_a.size();
-    const int64_t R = rbase[ntiles];
-    if (alpha + R >= (int64_t)INT32_MAX) {
-        set_error("grammar exceeds the 32-bit symbol space");
+    if (gcs_status st = merge_tiles(g, res, ncc, rc, where, threads)) return st;
+    g.t_repair = ms_since(t1);
+    return finish_layout(g, threads);
+}
+
+// The host builder fed by a row source, tile by tile (the CSR of a whole
+// matrix never exists in this process).  Pass 1 fetches every tile once for
+// V and the terminal alphabet (per-column masks of value indices: first-seen
+// ids, renumbered once V is sorted); pass 2 fetches the tiles again in waves
+// of `threads`, encodes them and runs RePair on the wave in parallel.  The
+// result equals build_from_csr on the assembled matrix with the same options.
+static gcs_status build_from_source(gcs_row_source src, void* ctx, int64_t n, int64_t mc, int32_t val_kind,
+                                    const gcs_build_opts* opts, Grammar& g)
+{
+    auto t0 = std::chrono::steady_clock::now();
+    if (!src || n < 0 || mc < 0 || (val_kind != GCS_VAL_ONES && val_kind != GCS_VAL_F64)) {
+        set_error("invalid row source, shape or value kind (GCS_VAL_ONES or GCS_VAL_F64)");
+        return GCS_EINVAL;
+    }
+    if (n >= (int64_t)INT32_MAX || mc >= (int64_t)INT32_MAX) {
+        set_error("matrix dimensions exceed 2^31-1");
         return GCS_ERANGE;
     }
-    try {
-        g.ra.resize((size_t)R);
-        g.rb.resize((size_t)R);
-        parallel_for(ntiles, threads, [&](int64_t t) {
-            const int32_t shift = (int32_t)rbase[t];
-            auto remap = [&](int32_t s) { return s < alpha ? s : s + shift; };
-            for (size_t i = 0; i < res[t].rule_a.size(); ++i) {
-                g.ra[rbase[t] + i] = remap(res[t].rule_a[i]);
-                g.rb[rbase[t] + i] = remap(res[t].rule_b[i]);
+    if (opts && (opts->repair < GCS_REPAIR_EXACT || opts->repair > GCS_REPAIR_ROUNDS || opts->reserved != 0 ||
+                 opts->row_order != GCS_ROWS_NATURAL)) {
+        set_error("unknown RePair mode, nonzero reserved option, or a row order other than natural");
+        return GCS_EINVAL;
+    }
+    const int threads = resolve_threads(opts ? opts->n_threads : 0);
+    const bool rounds_mode = opts && opts->repair == GCS_REPAIR_ROUNDS;
+    const bool ones = val_kind == GCS_VAL_ONES;
+    g.n_rows = n;
+    g.n_cols = mc;
+    const int64_t cc = (opts && opts->col_chunk > 0) ? opts->col_chunk : std::max<int64_t>(mc, 1);
+    const int64_t rc = (opts && opts->row_chunk > 0) ? opts->row_chunk : std::max<int64_t>(n, 1);
+    const int64_t ncc = std::max<int64_t>(1, (mc + cc - 1) / cc), nrc = std::max<int64_t>(1, (n + rc - 1) / rc);
+    const int64_t ntiles = ncc * nrc;
+    g.n_tiles = ntiles;
+    struct Tile {
+        std::vector<int64_t> rp;
+        std::vector<int32_t> col;
+        std::vector<double> val;
+    };
+    // one tile from the source, checked like a CSR input
+    auto fetch = [&](int64_t t, Tile& T) -> gcs_status {
+        const int64_t r0 = (t / ncc) * rc, nr = std::min(n, r0 + rc) - r0;
+        const int64_t c0 = (t % ncc) * cc, nc = std::min(mc, c0 + cc) - c0;
+        const int64_t cnt = src(ctx, r0, nr, c0, nc, nullptr, nullptr, nullptr, 0);
+        if (cnt < 0) {
+            set_error("the row source reported a failure");
+            return GCS_EINVAL;
+        }
+        if (cnt >= (int64_t)INT32_MAX) {
+            set_error("a tile exceeds 2^31-1 nonzeros (use col_chunk/row_chunk)");
+            return GCS_ERANGE;
+        }
+        T.rp.assign((size_t)nr + 1, 0);
+        T.col.resize((size_t)cnt);
+        T.val.resize(ones ? 0 : (size_t)cnt);
+        const int64_t got = src(ctx, r0, nr, c0, nc, T.rp.data(), cnt ? T.col.data() : nullptr,
+                                ones || !cnt ? nullptr : T.val.data(), cnt);
+        if (got != cnt || T.rp[0] != 0 || T.rp[nr] != cnt) {
+            set_error("the row source returned a different count than it reported, or row_ptr[0] != 0");
+            return GCS_EINVAL;
+        }
+        for (int64_t r = 0; r < nr; ++r) {
+            if (T.rp[r + 1] < T.rp[r]) {
+                set_error("row_ptr not monotone in a tile from the row source");
+                return GCS_EINVAL;
             }
-        });
-        // C: row r = concatenation over column chunks of its tile sequences
-        g.c_off.assign((size_t)n + 1, 0);
-        std::vector<std::vector<int64_t>> tile_row_start((size_t)ntiles);
-        for (int64_t t = 0; t < ntiles; ++t) {
-            auto& s = tile_row_start[t];
-            s.resize(res[t].row_len.size() + 1, 0);
-            for (size_t i = 0; i < res[t].row_len.size(); ++i) s[i + 1] = s[i] + res[t].row_len[i];
-        }
-        for (int64_t r = 0; r < n; ++r) {
-            int64_t rb = where[r] / rc, ri = where[r] - rb * rc, len = 0;
-            for (int64_t cb = 0; cb < ncc; ++cb) len += res[rb * ncc + cb].row_len[ri];
-            g.c_off[r + 1] = g.c_off[r] + len;
-        }
-        g.c_sym.resize((size_t)g.c_off[n]);
-        parallel_for((n + vblk - 1) / vblk, threads, [&](int64_t b) {
-            for (int64_t r = b * vblk; r < std::min(n, (b + 1) * vblk); ++r) {
-                int64_t rb = where[r] / rc, ri = where[r] - rb * rc, o = g.c_off[r];
-                for (int64_t cb = 0; cb < ncc; ++cb) {
-                    const int64_t t = rb * ncc + cb;
-                    const int32_t shift = (int32_t)rbase[t];
-                    for (int64_t e = tile_row_start[t][ri]; e < tile_row_start[t][ri + 1]; ++e) {
-                        int32_t s = res[t].seq[e];
-                        g.c_sym[o++] = s < alpha ? s : s + shift;
-                    }
+            for (int64_t k = T.rp[r]; k < T.rp[r + 1]; ++k) {
+                const int32_t c = T.col[k];
+                if (c < c0 || c >= c0 + nc || (k > T.rp[r] && c <= T.col[k - 1])) {
+                    set_error("columns of a source tile must be strictly increasing and inside the tile");
+                    return GCS_EINVAL;
+                }
+                if (!ones && !std::isfinite(T.val[k])) {
+                    set_error("non-finite matrix value");
+                    return GCS_EINVAL;
                 }
             }
-        });
-    } catch (const std::bad_alloc&) {
-        set_error("out of host memory merging tiles");
-        return GCS_ENOMEM;
+        }
+        return GCS_OK;
+    };
+    // pass 1: V (distinct nonzero values) and, while |V| <= 64, per-column
+    // masks of first-seen value ids; otherwise the distinct (column, value)
+    std::vector<double> seen;         // first-seen order
+    std::vector<uint64_t> cm((size_t)mc, 0);
+    std::vector<std::pair<int32_t, double>> keys;  // general case
+    bool small = true;
+    int64_t nnz = 0;
+    for (int64_t t = 0; t < ntiles; ++t) {
+        Tile T;
+        if (gcs_status st = fetch(t, T)) return st;
+        for (size_t k = 0; k < T.col.size(); ++k) {
+            const double v = ones ? 1.0 : T.val[k];
+            if (v == 0.0) continue;
+            ++nnz;
+            if (small) {
+                size_t id = std::find(seen.begin(), seen.end(), v) - seen.begin();
+                if (id == seen.size()) {
+                    if (seen.size() == 64) {
+                        // more than 64 values: keep (column, value) keys instead
+                        small = false;
+                        for (int64_t j = 0; j < mc; ++j)
+                            for (uint64_t mk = cm[j]; mk; mk &= mk - 1) keys.push_back({(int32_t)j, seen[__builtin_ctzll(mk)]});
+                        std::vector<uint64_t>().swap(cm);
+                    } else {
+                        seen.push_back(v);
+                    }
+                }
+                if (small) {
+                    cm[T.col[k]] |= 1ULL << id;
+                    continue;
+                }
+            }
+            keys.push_back({T.col[k], v});
+        }
+        if (!small && keys.size() > 1u << 24) {  // keep the key list compact
+            std::sort(keys.begin(), keys.end());
+            keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+        }
     }
+    if (small) {
+        g.V = seen;
+    } else {
+        std::sort(keys.begin(), keys.end());
+        keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+        for (const auto& kv : keys) g.V.push_back(kv.second);
+    }
+    std::sort(g.V.begin(), g.V.end());
+    g.V.erase(std::unique(g.V.begin(), g.V.end()), g.V.end());
+    auto vidx = [&](double v) { return (int32_t)(std::lower_bound(g.V.begin(), g.V.end(), v) - g.V.begin()); };
+    std::vector<int64_t> cbase;
+    if (small) {
+        int32_t perm[64];
+        for (size_t i = 0; i < seen.size(); ++i) perm[i] = vidx(seen[i]);
+        cbase.assign((size_t)mc + 1, 0);
+        for (int64_t j = 0; j < mc; ++j) {
+            uint64_t m2 = 0;
+            for (uint64_t mk = cm[j]; mk; mk &= mk - 1) m2 |= 1ULL << perm[__builtin_ctzll(mk)];
+            cm[j] = m2;
+            cbase[j + 1] = cbase[j] + __builtin_popcountll(m2);
+        }
+        if (cbase[mc] >= (int64_t)INT32_MAX) {
+            set_error("too many distinct terminals");
+            return GCS_ERANGE;
+        }
+        g.tcol.resize((size_t)cbase[mc]);
+        g.tval.resize((size_t)cbase[mc]);
+        for (int64_t j = 0; j < mc; ++j) {
+            int64_t t = cbase[j];
+            for (uint64_t mk = cm[j]; mk; mk &= mk - 1, ++t) {
+                g.tcol[t] = (int32_t)j;
+                g.tval[t] = __builtin_ctzll(mk);
+            }
+        }
+    } else {
+        std::sort(keys.begin(), keys.end());
+        keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+        if ((int64_t)keys.size() >= (int64_t)INT32_MAX) {
+            set_error("too many distinct terminals");
+            return GCS_ERANGE;
+        }
+        g.tcol.resize(keys.size());
+        g.tval.resize(keys.size());
+        for (size_t t = 0; t < keys.size(); ++t) {
+            g.tcol[t] = keys[t].first;
+            g.tval[t] = vidx(keys[t].second);
+        }
+    }
+    const int64_t alpha = g.alpha();
+    auto term_id = [&](int32_t j, double v) -> int32_t {
+        const int32_t vi = vidx(v);
+        if (small) return (int32_t)(cbase[j] + __builtin_popcountll(cm[j] & ((1ULL << vi) - 1)));
+        return (int32_t)(std::lower_bound(keys.begin(), keys.end(), std::make_pair(j, v)) - keys.begin());
+    };
+    g.t_csrv = ms_since(t0);
+    // pass 2: waves of tiles, RePair in parallel
+    auto t1 = std::chrono::steady_clock::now();
+    std::vector<RePairResult> res((size_t)ntiles);
+    const int64_t wave = std::max(1, threads);
+    std::atomic<int> fail{0};
+    for (int64_t w0 = 0; w0 < ntiles; w0 += wave) {
+        const int64_t w1 = std::min(ntiles, w0 + wave);
+        std::vector<Tile> tiles((size_t)(w1 - w0));
+        for (int64_t t = w0; t < w1; ++t)
+            if (gcs_status st = fetch(t, tiles[t - w0])) return st;
+        parallel_for(w1 - w0, threads, [&](int64_t i) {
+            Tile& T = tiles[i];
+            std::vector<int32_t> seq;
+            std::vector<int64_t> off;
+            try {
+                seq.reserve(T.col.size());
+                off.reserve(T.rp.size());
+                off.push_back(0);
+                for (size_t r = 0; r + 1 < T.rp.size(); ++r) {
+                    for (int64_t k = T.rp[r]; k < T.rp[r + 1]; ++k) {
+                        const double v = ones ? 1.0 : T.val[k];
+                        if (v != 0.0) seq.push_back(term_id(T.col[k], v));
+                    }
+                    off.push_back((int64_t)seq.size());
+                }
+                std::vector<int32_t>().swap(T.col);
+                std::vector<double>().swap(T.val);
+                const bool ok = rounds_mode ? repair_rounds_tile(seq, off, (int32_t)alpha, res[w0 + i])
+                                            : repair_tile(seq, off, (int32_t)alpha, res[w0 + i]);
+                if (!ok) fail = 1;
+            } catch (const std::bad_alloc&) {
+                fail = 1;
+            }
+        });
+        if (fail) {
+            set_error("out of host memory in RePair");
+            return GCS_ENOMEM;
+        }
+    }
+    g.nnz = nnz;
+    std::vector<int32_t> where((size_t)n);
+    for (int64_t r = 0; r < n; ++r) where[r] = (int32_t)r;
+    if (gcs_status st = merge_tiles(g, res, ncc, rc, where, threads)) return st;
     g.t_repair = ms_since(t1);
     return finish_layout(g, threads);
 }
@@ -829,6 +1061,63 @@ extern "C" gcs_status gcs_build_grammar(const gcs_csr_view* m, const gcs_build_o
         gcs::set_error("out of host memory");
         return GCS_ENOMEM;
     }
+}
+
+extern "C" gcs_status gcs_build_grammar_rows(gcs_row_source src, void* ctx, int64_t n_rows, int64_t n_cols,
+                                             int32_t val_kind, const gcs_build_opts* opts, gcs_grammar** out)
+{
+    if (!out) {
+        gcs::set_error("null output pointer");
+        return GCS_EINVAL;
+    }
+    *out = nullptr;
+    try {
+        auto* h = new gcs_grammar();
+        gcs_status st = gcs::build_from_source(src, ctx, n_rows, n_cols, val_kind, opts, h->g);
+        if (st != GCS_OK) {
+            delete h;
+            return st;
+        }
+        *out = h;
+        return GCS_OK;
+    } catch (const std::bad_alloc&) {
+        gcs::set_error("out of host memory");
+        return GCS_ENOMEM;
+    }
+}
+
+extern "C" gcs_status gcs_expand_row(const gcs_grammar* h, int64_t r, int32_t* sym, int64_t cap, int64_t* len)
+{
+    if (!h || !len || cap < 0 || (cap > 0 && !sym)) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    if (r < 0 || r >= g.n_rows) {
+        gcs::set_error("row out of range");
+        return GCS_EINVAL;
+    }
+    const int64_t alpha = g.alpha();
+    int64_t n = 0;
+    std::vector<int32_t> stack;
+    for (int64_t e = g.c_off[r + 1] - 1; e >= g.c_off[r]; --e) stack.push_back(g.c_sym[e]);
+    while (!stack.empty()) {  // leftmost symbol on top
+        const int32_t s = stack.back();
+        stack.pop_back();
+        if (s < alpha) {
+            if (n < cap) sym[n] = s;
+            ++n;
+        } else {
+            stack.push_back(g.rb[s - alpha]);
+            stack.push_back(g.ra[s - alpha]);
+        }
+    }
+    *len = n;
+    if (n > cap) {
+        gcs::set_error("the expanded row is longer than cap");
+        return GCS_ERANGE;
+    }
+    return GCS_OK;
 }
 
 extern "C" gcs_status gcs_grammar_from_rules(int64_t n_rows, int64_t n_cols, const double* values, int64_t n_values,

@@ -80,6 +80,13 @@ _lib.gcs_save_grammar.argtypes = [_P, ctypes.c_char_p]
 _lib.gcs_save_grammar.restype = _st
 _lib.gcs_load_grammar.argtypes = [ctypes.c_char_p, ctypes.POINTER(_P)]
 _lib.gcs_load_grammar.restype = _st
+ROW_SOURCE = ctypes.CFUNCTYPE(ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64)
+_lib.gcs_build_grammar_rows.argtypes = [ROW_SOURCE, _P, _I64, _I64, ctypes.c_int32, ctypes.POINTER(BuildOpts),
+                                        ctypes.POINTER(_P)]
+_lib.gcs_build_grammar_rows.restype = _st
+_lib.gcs_expand_row.argtypes = [_P, _I64, _P, _I64, ctypes.POINTER(_I64)]
+_lib.gcs_expand_row.restype = _st
 _lib.gcs_build_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]
 _lib.gcs_build_workspace_bytes.restype = _st
 _lib.gcs_build_grammar_gpu.argtypes = [ctypes.POINTER(CsrView), ctypes.POINTER(BuildOpts), _I64, _P, ctypes.c_size_t,
@@ -181,6 +188,16 @@ class Grammar:
         _check(_lib.gcs_export_slices(self._h, _ptr(out["slices"]), _ptr(out["col_cut"])))
         return out
 
+    def expand_row(self, r: int) -> np.ndarray:
+        """gcs_expand_row: row r's C sequence expanded through R (terminal ids)."""
+        n = _I64(0)
+        st = _lib.gcs_expand_row(self._h, r, None, 0, ctypes.byref(n))
+        if st not in (0, -4):
+            _check(st)
+        out = np.zeros(n.value, np.int32)
+        _check(_lib.gcs_expand_row(self._h, r, _ptr(out), out.size, ctypes.byref(n)))
+        return out
+
     def layout_meta(self) -> dict:
         """level_meta and eoff of the layout only (gcs_export_layout with the
         other arrays skipped): enough to count each level's nodes and roots."""
@@ -255,6 +272,52 @@ def build_grammar(row_ptr, col, val=None, n_cols=None, n_threads=0, col_chunk=0,
     opts = BuildOpts(n_threads, col_chunk, row_chunk, row_order, repair, 0)
     h = _P()
     _check(_lib.gcs_build_grammar(ctypes.byref(view), ctypes.byref(opts), ctypes.byref(h)))
+    return Grammar(h)
+
+
+def build_grammar_rows(source, n_rows, n_cols, ones=False, n_threads=0, col_chunk=0, row_chunk=0,
+                       repair=REPAIR_EXACT) -> Grammar:
+    """gcs_build_grammar_rows: the host builder pulling tiles from
+    source(row0, nrows, col0, ncols) -> (row_ptr, col, val), a block's CSR
+    (row_ptr relative to the block, absolute columns; val ignored when
+    ones).  The callback marshals the block into the library's buffers."""
+    cache = {}
+    err = []
+
+    def cb(ctx, row0, nrows, col0, ncols, rp_p, col_p, val_p, cap):
+        try:
+            key = (row0, nrows, col0, ncols)
+            if key not in cache:
+                cache.clear()
+                rp, col, val = source(row0, nrows, col0, ncols)
+                rp = np.ascontiguousarray(rp, np.int64)
+                col = np.ascontiguousarray(col, np.int32)
+                val = None if ones or val is None else np.ascontiguousarray(val, np.float64)
+                cache[key] = (rp, col, val)
+            rp, col, val = cache[key]
+            nnz = int(rp[-1]) if rp.size else 0
+            if rp_p:
+                if cap < nnz:
+                    return -1
+                ctypes.memmove(rp_p, rp.ctypes.data, rp.nbytes)
+                if nnz:
+                    ctypes.memmove(col_p, col.ctypes.data, 4 * nnz)
+                    if val_p and val is not None:
+                        ctypes.memmove(val_p, val.ctypes.data, 8 * nnz)
+                cache.clear()
+            return nnz
+        except Exception as e:  # reported after the call
+            err.append(e)
+            return -1
+
+    fn = ROW_SOURCE(cb)
+    opts = BuildOpts(n_threads, col_chunk, row_chunk, ROWS_NATURAL, repair, 0)
+    h = _P()
+    st = _lib.gcs_build_grammar_rows(fn, None, n_rows, n_cols, VAL_ONES if ones else VAL_F64, ctypes.byref(opts),
+                                     ctypes.byref(h))
+    if err:
+        raise err[0]
+    _check(st)
     return Grammar(h)
 
 

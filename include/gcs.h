@@ -152,6 +152,39 @@ typedef struct gcs_device gcs_device;
  * opts may be NULL (defaults).  *out receives a new grammar on GCS_OK. */
 gcs_status gcs_build_grammar(const gcs_csr_view* m, const gcs_build_opts* opts, gcs_grammar** out);
 
+/* A row source: the matrix handed over block by block, so that a matrix too
+ * large for host memory never has to exist whole (section 2, 'CSRV': S is
+ * built row by row).  Called with row_ptr == NULL it returns the number of
+ * stored entries of rows [row0, row0 + nrows) in columns [col0, col0 + ncols);
+ * called with arrays (row_ptr: nrows + 1 entries, col and val: cap entries;
+ * val is NULL for GCS_VAL_ONES) it fills that block as CSR -- row_ptr
+ * relative to the block (row_ptr[0] = 0), absolute column indices, strictly
+ * increasing per row -- and returns the count again.  A negative return
+ * aborts the build (GCS_EINVAL).  Called from the building thread only. */
+typedef int64_t (*gcs_row_source)(void* ctx, int64_t row0, int64_t nrows, int64_t col0, int64_t ncols,
+                                  int64_t* row_ptr, int32_t* col, double* val, int64_t cap);
+
+/* gcs_build_grammar on a matrix pulled from a row source, one tile (row
+ * chunk x column chunk of opts; whole matrix by default) at a time: one
+ * pass over the tiles for V and the terminal alphabet, a second that
+ * encodes and runs RePair on n_threads tiles at a time, so host memory holds
+ * about n_threads tiles plus the grammar.  val_kind: GCS_VAL_ONES or
+ * GCS_VAL_F64 (int8 values are handed over as doubles).  The grammar equals
+ * gcs_build_grammar's on the assembled CSR with the same options; the row
+ * order must be GCS_ROWS_NATURAL.  Errors as gcs_build_grammar, plus
+ * GCS_EINVAL for a source that fails, changes its count between the two
+ * calls, or returns columns outside the requested block. */
+gcs_status gcs_build_grammar_rows(gcs_row_source src, void* ctx, int64_t n_rows, int64_t n_cols, int32_t val_kind,
+                                  const gcs_build_opts* opts, gcs_grammar** out);
+
+/* Row r as the grammar encodes it: C[r] expanded through R (Lemma 2.2: the
+ * roots of row r expand to its CSRV row), i.e. the terminals of row r's
+ * nonzeros in column order (term_col / term_val of gcs_export_grammar give
+ * their column and value index).  Writes min(cap, *len) terminal ids to sym
+ * and the full length to *len.  GCS_ERANGE if cap < *len, GCS_EINVAL for r
+ * outside [0, n_rows).  A test and inspection hook. */
+gcs_status gcs_expand_row(const gcs_grammar* g, int64_t r, int32_t* sym, int64_t cap, int64_t* len);
+
 /* A grammar given explicitly (e.g. Eq. 2.3-2.4 of the pages' worked
  * example), then levelled, completed and laid out as above.
  *   values[n_values]        V, distinct nonzero values

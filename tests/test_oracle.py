@@ -178,28 +178,58 @@ def test_min_plus_brute_force(oracle_mod, seed):
         assert y32[r] == best32 and y32.dtype == np.float32
 
 
-def test_min_plus_path_distances(oracle_mod):
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_min_plus_path_distances(oracle_mod, dtype):
     """Relaxing to the fixpoint on a path (out-list of i is {i+1}, unit
     weights) from node n-1 gives the closed-form distance n-1-i."""
     n = 30
     rp = np.arange(n + 1, dtype=np.int64).clip(max=n - 1)
     col = np.arange(1, n, dtype=np.int32)
-    d = np.full(n, np.inf)
+    d = np.full(n, np.inf, dtype)
     d[n - 1] = 0.0
     for _ in range(n):
-        d = np.minimum(d, oracle_mod.spmv_min_plus(rp, col, None, d, np.float64))
-    assert np.array_equal(d, np.arange(n - 1, -1, -1, dtype=np.float64))
+        d = np.minimum(d, oracle_mod.spmv_min_plus(rp, col, None, d, dtype))
+    assert d.dtype == dtype
+    assert np.array_equal(d, np.arange(n - 1, -1, -1, dtype=dtype))
 
 
-def test_min_plus_reduces_to_boolean(oracle_mod):
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_min_plus_reduces_to_boolean(oracle_mod, dtype):
     """With zero weights and x in {0, +inf}, y[r] = 0 exactly where the
     Boolean pass of (x == 0) is 1, +inf elsewhere (empty rows included)."""
     rng = random.Random(9)
     n, m = 60, 40
     rows, rp, col = _random_csr(rng, n, m)
     xb = np.array([rng.random() < 0.3 for _ in range(m)], np.uint8)
-    x = np.where(xb == 1, 0.0, np.inf)
-    y = oracle_mod.spmv_min_plus(rp, col, np.zeros(col.size), x, np.float64)
+    x = np.where(xb == 1, 0.0, np.inf).astype(dtype)
+    y = oracle_mod.spmv_min_plus(rp, col, np.zeros(col.size), x, dtype)
     yb = oracle_mod.spmv_bool(rp, col, xb)
     assert np.array_equal(y == 0.0, yb == 1)
     assert np.all(np.isinf(y[yb == 0]))
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_min_plus_fixpoint_is_shortest_paths(oracle_mod, dtype):
+    """Bellman-Ford from the tropical pass (d <- min(d, M d), section 5) on a
+    random digraph with integer weights 1..9 equals scipy's Dijkstra
+    distances to the source set (the row of i lists its out-edges, so d[i]
+    is the distance from i to a source); integer sums below 2^24 are exact
+    in fp32 too."""
+    from scipy.sparse import csr_matrix
+    from scipy.sparse.csgraph import shortest_path
+    rng = random.Random(21)
+    n = 120
+    rows, rp, col = _random_csr(rng, n, n)
+    w = np.array([rng.randint(1, 9) for _ in range(col.size)], np.float64)
+    srcs = [3, 50, 97]
+    d = np.full(n, np.inf, dtype)
+    d[srcs] = 0
+    for _ in range(n):
+        nd = np.minimum(d, oracle_mod.spmv_min_plus(rp, col, w, d, dtype))
+        if np.array_equal(nd, d):
+            break
+        d = nd
+    A = csr_matrix((w, col, rp), shape=(n, n))
+    ref = shortest_path(A.T.tocsr(), method="D", directed=True, indices=srcs).min(axis=0)
+    assert np.array_equal(d.astype(np.float64), ref)
+    assert np.isfinite(ref).sum() > n // 2  # the pin covers most nodes
