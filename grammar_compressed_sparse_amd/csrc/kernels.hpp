@@ -30,6 +30,8 @@
 namespace gcs {
 
 // ---------------------------------------------------------------- policies
+// poison(): what y holds after a sweep whose tail grid barrier timed out (a
+// value no correct sweep produces: NaN, 0xFF for a Boolean, INT64_MIN)
 
 struct PolPlusF64 {
     using X = double;  // x element
@@ -41,6 +43,7 @@ struct PolPlusF64 {
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0; }
     __device__ static A ident() { return 0.0; }
+    __device__ static Y poison() { return __builtin_nan(""); }
 };
 struct PolPlusF32 {
     using X = float;
@@ -52,6 +55,7 @@ struct PolPlusF32 {
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0f; }
     __device__ static A ident() { return 0.0f; }
+    __device__ static Y poison() { return __builtin_nanf(""); }
 };
 struct PolPlusF32AccF64 {
     using X = float;
@@ -63,6 +67,7 @@ struct PolPlusF32AccF64 {
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0.0; }
     __device__ static A ident() { return 0.0; }
+    __device__ static Y poison() { return __builtin_nan(""); }
 };
 struct PolBoolOr {
     using X = uint8_t;
@@ -74,6 +79,7 @@ struct PolBoolOr {
     __device__ static Y emit(Y y, A s) { return y | s; }
     __device__ static Y yzero() { return 0; }
     __device__ static A ident() { return 0; }
+    __device__ static Y poison() { return 0xFF; }
 };
 struct PolPlusI64 {
     using X = int64_t;
@@ -85,6 +91,7 @@ struct PolPlusI64 {
     __device__ static Y emit(Y y, A s) { return y + s; }
     __device__ static Y yzero() { return 0; }
     __device__ static A ident() { return 0; }
+    __device__ static Y poison() { return INT64_MIN; }
 };
 
 // tropical (min, +): leaf = matrix value + x[j], combine = min, identity
@@ -100,6 +107,7 @@ struct PolMinPlusF32 {
     __device__ static Y emit(Y y, A s) { return s < y ? s : y; }
     __device__ static Y yzero() { return __builtin_huge_valf(); }
     __device__ static A ident() { return __builtin_huge_valf(); }
+    __device__ static Y poison() { return __builtin_nanf(""); }
 };
 struct PolMinPlusF64 {
     using X = double;
@@ -111,6 +119,7 @@ struct PolMinPlusF64 {
     __device__ static Y emit(Y y, A s) { return s < y ? s : y; }
     __device__ static Y yzero() { return __builtin_huge_val(); }
     __device__ static A ident() { return __builtin_huge_val(); }
+    __device__ static Y poison() { return __builtin_nan(""); }
 };
 
 // Policies whose emission goes straight into y because the combination is
@@ -260,6 +269,7 @@ __global__ __launch_bounds__(kBlock) void leaf_kernel(const int32_t* __restrict_
     if (blockIdx.x == 0 && threadIdx.x == 0) {  // the tail kernel's grid barrier counts rounds from 0 in every sweep
         barrier[0] = 0;
         barrier[kFlagOffset] = 0;
+        barrier[kFlagOffset + 1] = 0;  // and this sweep has not failed yet
     }
 }
 
@@ -646,15 +656,19 @@ __global__ __launch_bounds__(kBlock) void level_kernel(LevelArgs a, typename P::
 
 // Grid-wide barrier for the co-resident tail grid.  bar[0] counts arrivals
 // in this sweep; bar[kFlagOffset] (another cache line) holds the last round
-// released.  Every wave first waits for its own stores to complete; one lane
-// per workgroup then arrives with a device-scope release increment, the last
-// arriver of the round publishes the round number with a release store, and
-// the others poll that flag with relaxed device-scope loads (pollers never
-// touch the line the arrivals update) and acquire once it is released.  The
-// wait is bounded: after about a second of polling the workgroup gives up and
-// returns false (the caller flags the sweep as failed), so the grid always
-// drains.
-__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, const int* err)
+// released and bar[kFlagOffset + 1] whether this sweep has failed (both
+// cleared by the sweep's leaf launch).  Every wave first waits for its own
+// stores to complete; one lane per workgroup then arrives with a
+// device-scope release increment, the last arriver of the round publishes
+// the round number with a release store, and the others poll that flag with
+// relaxed device-scope loads (pollers never touch the line the arrivals
+// update) and acquire once it is released.  The wait is bounded: after
+// spin_limit polls (about a second by default; 0 = never wait, which fails
+// every workgroup but the last arriver, for tests) the workgroup gives up
+// and returns false, and the caller marks the sweep failed; a sweep already
+// marked failed waits no more, so the grid always drains, and the next
+// sweep starts with a clean mark.
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, unsigned spin_limit)
 {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
     __syncthreads();
@@ -665,14 +679,16 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned round, cons
         const unsigned prev = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         if (prev + 1 == round * gridDim.x) {
             __hip_atomic_store(flag, round, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        } else if (spin_limit == 0) {
+            ok = 0;  // never wait: the failure path on purpose (tests)
+        } else if (__hip_atomic_load(flag + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
             unsigned spins = 0;
             while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < round) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins == (1u << 25)) {
+                if (++spins == spin_limit) {
                     ok = 0;
                     break;
                 }
+                __builtin_amdgcn_s_sleep(2);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -851,8 +867,14 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
                                                           typename P::A* __restrict__ acc,
                                                           typename P::Y* __restrict__ y, int32_t n_rows,
                                                           int32_t accumulate, unsigned* __restrict__ bar,
-                                                          int* __restrict__ err)
+                                                          int* __restrict__ err, unsigned spin_limit)
 {
+    // a timed-out barrier marks this sweep failed (bar[kFlagOffset + 1]) and
+    // raises the sticky flag gcs_device_check reports
+    auto fail = [&]() {
+        __hip_atomic_store(bar + kFlagOffset + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     constexpr int Q = kTailBlock / kBlock;
     const int32_t q = threadIdx.x / kBlock, ltid = threadIdx.x % kBlock;
     const bool flat_wg = f.n_ent > 0 && (int32_t)blockIdx.x == n_grid;
@@ -865,13 +887,11 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
             for (int32_t vb = blockIdx.x + q * n_grid; vb < nvb; vb += Q * n_grid)
                 level_block<P>(a, vb, ltid, arena, acc);
         }
-        if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
-            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!grid_barrier(bar, ++round, spin_limit) && threadIdx.x == 0) fail();
     }
     if (f.n_ent > 0) {
         if (flat_wg) flat_phase<P>(f, arena, acc);
-        if (!grid_barrier(bar, ++round, err) && threadIdx.x == 0)
-            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!grid_barrier(bar, ++round, spin_limit) && threadIdx.x == 0) fail();
     }
     if constexpr (!kDirectEmit<P>) {
         for (int32_t r = blockIdx.x * kTailBlock + threadIdx.x; r < n_rows; r += gridDim.x * kTailBlock) {
@@ -880,6 +900,12 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
             for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
             y[r] = P::emit(accumulate ? y[r] : P::yzero(), s);
         }
+    }
+    // a failed sweep leaves no plausible y: every workgroup that sees the
+    // mark overwrites all of y after its own writes
+    if (__hip_atomic_load(bar + kFlagOffset + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        __syncthreads();
+        for (int32_t r = threadIdx.x; r < n_rows; r += kTailBlock) y[r] = P::poison();
     }
 }
 

@@ -60,6 +60,7 @@ struct gcs_device {
     int64_t tail_multi = 0;              // of which the first tail_multi run on the whole tail grid
     int32_t tail_wgs = 0;
     bool tail_coop = false;              // the tail as a cooperative launch (GCS_TAIL_COOP=1 at upload)
+    unsigned spin_limit = 1u << 25;      // polls before a tail barrier gives up (GCS_TAIL_SPIN_LIMIT at upload)
     int64_t grid_max = 0;  // cap on workgroups of a wide level launch (multiple of kSlices)
     const gcs::LevelArgs* tail_table = nullptr;
     gcs::FlatArgs flat{};      // the narrowest tail launches, run in LDS by one workgroup
@@ -1007,7 +1008,8 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
             d->flat_attr = true;
         }
         int32_t n_grid = d->tail_wgs;
-        void* args[] = {&table, &n_multi, &n_grid, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp};
+        unsigned spin = d->spin_limit;
+        void* args[] = {&table, &n_multi, &n_grid, &flat, &arena, &acc, &y, &n_rows, &accumulate, &bar, &errp, &spin};
         const unsigned wgs = (unsigned)d->tail_wgs + (flat.n_ent > 0 ? 1u : 0u);
         // an ordinary launch by default: the grid (at most one workgroup per
         // CU) has the device to itself behind the sweep's earlier launches,
@@ -1018,7 +1020,7 @@ gcs_status run_sweep(gcs_device* d, const void* xv, void* yv, hipStream_t s, hip
         hipError_t e;
         if (!d->tail_coop) {
             tail_kernel<P><<<dim3(wgs), dim3(kTailBlock), d->flat_lds, s>>>(table, n_multi, n_grid, flat, arena, acc, y,
-                                                                           n_rows, accumulate, bar, errp);
+                                                                           n_rows, accumulate, bar, errp, spin);
             e = hipGetLastError();
         } else {
             e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tail_kernel<P>), dim3(wgs), dim3(kTailBlock),
@@ -1407,6 +1409,9 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
     };
     // the tail kernel as a cooperative launch only on request
     d->tail_coop = env_int("GCS_TAIL_COOP", 0) != 0;
+    // polls before a tail barrier gives up and marks the sweep failed: about
+    // a second by default; a small value forces the failure path (tests)
+    d->spin_limit = (unsigned)std::max(0, env_int("GCS_TAIL_SPIN_LIMIT", 1 << 25));
     int coop = 0;
     (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
     if (d->tail_coop && !coop) {
@@ -1812,11 +1817,22 @@ extern "C" gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t
         gcs::bfs_update_kernel<<<grid, gcs::kBlock, 0, s>>>(y_dev, frontier_dev, visited_dev, n, d->counters, slot);
         e = hipGetLastError();
         if (e != hipSuccess) return gcs::hip_fail(e, "bfs update launch");
-        e = hipMemcpyAsync(d->pinned, d->counters + slot, 8, hipMemcpyDeviceToHost, s);
+        // the pass's count and the failure flag (counters[3]) in one read
+        e = hipMemcpyAsync(d->pinned, d->counters, 32, hipMemcpyDeviceToHost, s);
         if (e != hipSuccess) return gcs::hip_fail(e, "hipMemcpyAsync (bfs count)");
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return gcs::hip_fail(e, "hipStreamSynchronize (bfs)");
-        const int64_t c = d->pinned[0];
+        int failed = 0;
+        std::memcpy(&failed, d->pinned + 3, sizeof(int));
+        if (failed) {
+            (void)hipMemsetAsync(d->err, 0, sizeof(int), s);  // reported here, not again by gcs_device_check
+            (void)hipStreamSynchronize(s);
+            gcs::set_error("BFS pass " + std::to_string(t + 1) + ": its tail kernel timed out at a grid barrier; "
+                           "the visited set is invalid");
+            *passes = t;
+            return GCS_ESTATE;
+        }
+        const int64_t c = d->pinned[slot];
         new_counts[t++] = c;
         if (c == 0) break;
     }

@@ -7,8 +7,10 @@ There is no fallback: if the library is missing, importing this module fails.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 
 import numpy as np
 
@@ -395,10 +397,30 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Device handles still alive when the interpreter exits are freed by an
+# atexit hook, registered at the first upload (after torch is imported, so it
+# runs before torch's own exit handlers): no HIP call is left for object
+# finalization, when the runtime may already be tearing down.
+_LIVE = weakref.WeakSet()
+_EXIT_HOOK = []
+
+
+def _release_all():
+    for d in list(_LIVE):
+        try:
+            d.free()
+        except Exception:
+            pass
+
+
 class Device:
     """An uploaded grammar (``gcs_device``) plus the torch buffers it lives in."""
 
     def __init__(self, handle, policy, grammar_buf, workspace, sizes, device):
+        if not _EXIT_HOOK:
+            atexit.register(_release_all)
+            _EXIT_HOOK.append(True)
+        _LIVE.add(self)
         self._h = handle
         self.policy = policy
         self.grammar_buf = grammar_buf
@@ -469,6 +491,7 @@ class Device:
         if self._h:
             _lib.gcs_free_device(self._h)
             self._h = None
+        _LIVE.discard(self)
 
     def __del__(self):
         try:
