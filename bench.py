@@ -476,7 +476,7 @@ def bench_biobank(args, wl, spec, leg):
                                      [0, spec.n_rows - 1]]))
     yo, absum = np.zeros(rows.size), np.zeros(rows.size)
     lock = threading.Lock()
-    nnz_of, lbytes = {}, {}
+    nnz_of, lbytes, spans = {}, {}, {}
 
     def on_group(i, c0, nc, rp, col, val):
         if leg is not None:
@@ -491,9 +491,13 @@ def bench_biobank(args, wl, spec, leg):
         lay["alpha"] = st["n_terminals"]
         nwide = dev.sweep_launches() - 2
         lb = level_bytes(lay, yelem, yelem)
+        sp = g.edge_spans()
         with lock:
             nnz_of[i] = st["nnz"]
             lbytes[i] = (float(lb[:max(nwide, 0)].sum()), float(lb.sum()), nwide)
+            for d, c in enumerate(sp.tolist()):
+                if c:
+                    spans[d] = spans.get(d, 0) + c
 
     log(f"building {spec.n_rows}x{spec.n_cols} as groups of {args.group_cols} columns "
         f"({args.build_workers} build workers)")
@@ -568,7 +572,8 @@ def bench_biobank(args, wl, spec, leg):
                                "c_len": sum(s["c_len"] for s in sts),
                                "n_terminals": sum(s["n_terminals"] for s in sts),
                                "depth_max": max(s["depth"] for s in sts),
-                               "max_width_max": max(s["max_width"] for s in sts)},
+                               "max_width_max": max(s["max_width"] for s in sts),
+                               "edge_spans": {str(d): spans[d] for d in sorted(spans)}},
                    "launches_per_sweep": cg.launches_per_sweep(),
                    "max_rel_err_sampled": err, "sampled_rows": int(rows.size),
                    "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
@@ -911,8 +916,9 @@ def main():
             "founders": spec.founders, "seg_mean": spec.seg_mean, "mu": spec.mu, "seed": spec.seed,
             "vectors": len(xs),
             "multiply_many": per_vector,
-            "grammar": {k: st[k] for k in ("n_rules", "n_passthrough", "depth", "max_width", "c_len",
-                                           "n_terminals", "n_tiles", "n_emit_groups")},
+            "grammar": dict({k: st[k] for k in ("n_rules", "n_passthrough", "depth", "max_width", "c_len",
+                                                "n_terminals", "n_tiles", "n_emit_groups")},
+                            edge_spans={str(d): int(c) for d, c in enumerate(g.edge_spans().tolist()) if c}),
             "build_s": build_s, "upload_s": upload_s,
             "launches_per_sweep": int(launch_ms.shape[1]),
             "grammar_bytes_per_s": (8 * st["n_rules"] + 8 * st["n_emit_groups"] + 4 * st["c_len"] +

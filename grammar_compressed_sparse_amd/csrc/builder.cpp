@@ -1086,6 +1086,25 @@ extern "C" gcs_status gcs_build_grammar_rows(gcs_row_source src, void* ctx, int6
     }
 }
 
+extern "C" gcs_status gcs_edge_spans(const gcs_grammar* h, int64_t* hist, int64_t cap, int64_t* max_span)
+{
+    if (!h || cap < 0 || (cap > 0 && !hist)) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    const Grammar& g = h->g;
+    const int64_t alpha = g.alpha(), R = g.nrules();
+    std::vector<int64_t> cnt((size_t)g.L + 1, 0);
+    for (int64_t i = 0; i < R; ++i)
+        for (int32_t c : {g.ra[i], g.rb[i]}) cnt[g.lvl[i] - (c < alpha ? 0 : g.lvl[c - alpha])]++;
+    int64_t mx = 0;
+    for (int64_t d = 0; d <= g.L; ++d)
+        if (cnt[d]) mx = d;
+    for (int64_t d = 0; d < cap; ++d) hist[d] = d <= g.L ? cnt[d] : 0;
+    if (max_span) *max_span = mx;
+    return GCS_OK;
+}
+
 extern "C" gcs_status gcs_expand_row(const gcs_grammar* h, int64_t r, int32_t* sym, int64_t cap, int64_t* len)
 {
     if (!h || !len || cap < 0 || (cap > 0 && !sym)) {

@@ -40,6 +40,7 @@ struct Rec {
 
 inline uint64_t pair_key(int32_t a, int32_t b) { return ((uint64_t)(uint32_t)a << 32) | (uint32_t)b; }
 
+// 64-bit finalizer of MurmurHash3 (fmix64, public domain)
 inline uint64_t hmix(uint64_t k)
 {
     k ^= k >> 33;

@@ -70,6 +70,8 @@ _lib.gcs_grammar_stats.argtypes = [_P, ctypes.POINTER(Stats)]
 _lib.gcs_merge_grammars.argtypes = [ctypes.POINTER(_P), ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P)]
 _lib.gcs_merge_grammars.restype = _st
 _lib.gcs_level_widths.argtypes = [_P, _P, _I64]
+_lib.gcs_edge_spans.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64)]
+_lib.gcs_edge_spans.restype = _st
 _lib.gcs_export_grammar.argtypes = [_P] + [_P] * 9
 _lib.gcs_layout_counts.argtypes = [_P, _P]
 _lib.gcs_export_layout.argtypes = [_P] + [_P] * 6
@@ -164,6 +166,14 @@ class Grammar:
         w = np.zeros(L + 1, np.int64)
         _check(_lib.gcs_level_widths(self._h, _ptr(w), L + 1))
         return w
+
+    def edge_spans(self) -> np.ndarray:
+        """gcs_edge_spans: hist[d] = edges rule -> child spanning d levels."""
+        L = self.stats()["depth"]
+        h = np.zeros(L + 1, np.int64)
+        mx = _I64(0)
+        _check(_lib.gcs_edge_spans(self._h, _ptr(h), L + 1, ctypes.byref(mx)))
+        return h
 
     def export(self) -> dict:
         s = self.stats()

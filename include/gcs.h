@@ -223,6 +223,14 @@ gcs_status gcs_grammar_stats(const gcs_grammar* g, gcs_stats* out);
  * min(cap, L+1) entries. */
 gcs_status gcs_level_widths(const gcs_grammar* g, int64_t* w, int64_t cap);
 
+/* Distribution of edge spans (section 4.1: RePair's level-skipping edges,
+ * reported beside the depth L; section 4.2: completion's cost follows it):
+ * hist[d] = number of edges rule -> child with lvl(rule) - lvl(child) = d,
+ * both children of every rule, a terminal child at level 0; d = 1..L
+ * (hist[0] = 0).  Writes cap entries (zeros past L); *max_span (may be
+ * NULL) gets the largest span present. */
+gcs_status gcs_edge_spans(const gcs_grammar* g, int64_t* hist, int64_t cap, int64_t* max_span);
+
 /* Copies of the grammar (test and inspection hooks).  Each pointer may be
  * NULL to skip that array; sizes follow gcs_grammar_stats.
  *   values[|V|]; term_col/term_val[alpha]; rule_a/rule_b/rule_level/

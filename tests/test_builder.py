@@ -340,3 +340,37 @@ def test_rounds_mode_shallower_copy_graph_and_options(gcs, synth_mod):
     assert b["depth"] <= a["depth"]
     with pytest.raises(gcs.GcsError, match="EINVAL"):
         gcs.build_grammar(rp, col, None, n_cols=spec.n, repair=7)
+
+
+@pytest.mark.parametrize("repair", [0, 1], ids=["exact", "rounds"])
+def test_edge_spans(gcs, synth_mod, worked_example, repair):
+    """gcs_edge_spans against the definition (section 4.1): the span of an
+    edge is the level of the rule minus the level of its child (0 for a
+    terminal); completion (section 4.2) carries a child for its longest
+    nonterminal edge minus one level."""
+    spec = synth_mod.GenotypeSpec(300, 3000, 8, 100.0, 0.005, seed=3)
+    rp, col, val = synth_mod.genotype(spec)
+    g = gcs.build_grammar(rp, col, val, n_cols=3000, repair=repair)
+    ex, st = g.export(), g.stats()
+    a = st["n_terminals"]
+    lv = ex["rule_level"]
+    spans = []
+    longest = np.zeros(st["n_rules"], np.int64)
+    for i in range(st["n_rules"]):
+        for c in (ex["rule_a"][i], ex["rule_b"][i]):
+            d = int(lv[i] - (0 if c < a else lv[c - a]))
+            spans.append(d)
+            if c >= a:
+                longest[c - a] = max(longest[c - a], d)
+    h = g.edge_spans()
+    assert h[0] == 0 and h.sum() == 2 * st["n_rules"]
+    assert np.array_equal(h, np.bincount(spans, minlength=st["depth"] + 1))
+    assert st["n_passthrough"] == int(np.maximum(longest - 1, 0).sum())
+    # the pages' grammar (Eq. 2.3): one level-skipping nonterminal edge, N8 -> N4
+    gw = gcs.grammar_from_rules(**H.we_grammar_arrays(worked_example))
+    exw = gw.export()
+    aw = len(exw["term_col"])
+    skip = [(i + 1, int(c) - aw + 1) for i in range(len(exw["rule_a"])) for c in (exw["rule_a"][i], exw["rule_b"][i])
+            if c >= aw and exw["rule_level"][i] - exw["rule_level"][c - aw] > 1]
+    assert skip == [(8, 4)]
+    assert gw.edge_spans().sum() == 2 * len(exw["rule_a"])
