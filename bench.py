@@ -476,7 +476,7 @@ def bench_biobank(args, wl, spec, leg):
                                      [0, spec.n_rows - 1]]))
     yo, absum = np.zeros(rows.size), np.zeros(rows.size)
     lock = threading.Lock()
-    nnz_of, lbytes, spans = {}, {}, {}
+    nnz_of, lbytes, espan = {}, {}, {}
 
     def on_group(i, c0, nc, rp, col, val):
         if leg is not None:
@@ -491,19 +491,26 @@ def bench_biobank(args, wl, spec, leg):
         lay["alpha"] = st["n_terminals"]
         nwide = dev.sweep_launches() - 2
         lb = level_bytes(lay, yelem, yelem)
+        # the emission of the last level (its own launch in a fused sweep)
+        meta, eoff = lay["level_meta"], lay["eoff"]
+        L = meta.shape[0] - 1
+        g0, ng = int(meta[L][6]), int(meta[L][7])
+        last = 8 * ng + 4 * int(eoff[g0 + ng] - eoff[g0]) + 2 * yelem * ng if ng else 0
         sp = g.edge_spans()
         with lock:
             nnz_of[i] = st["nnz"]
-            lbytes[i] = (float(lb[:max(nwide, 0)].sum()), float(lb.sum()), nwide)
+            lbytes[i] = (float(lb[:max(nwide, 0)].sum()), float(lb.sum() + last), nwide, L + 1)
             for d, c in enumerate(sp.tolist()):
                 if c:
-                    spans[d] = spans.get(d, 0) + c
+                    espan[d] = espan.get(d, 0) + c
 
     log(f"building {spec.n_rows}x{spec.n_cols} as groups of {args.group_cols} columns "
         f"({args.build_workers} build workers)")
     cg = groups.build_column_groups(lambda c0, nc: synth.genotype(spec, col0=c0, ncols=nc), spec.n_rows,
                                     spec.n_cols, args.group_cols, policy, workers=args.build_workers,
-                                    table_entries=1 << 28, on_group=on_group, on_built=on_built, log=log)
+                                    table_entries=1 << 28, on_group=on_group, on_built=on_built, log=log,
+                                    fuse=not args.no_fuse, fuse_batch=args.fuse_batch)
+    fused = cg.fused is not None
     nnz = sum(nnz_of.values())
     log(f"built {len(cg.devices)} groups in {cg.build_s:.0f}s: nnz={nnz}, device {cg.device_bytes / 1e9:.1f} GB")
     y = cg.sweep_right(xd)
@@ -517,8 +524,10 @@ def bench_biobank(args, wl, spec, leg):
     for _ in range(args.warmup):
         cg.sweep_right(xd, y)
     torch.cuda.synchronize()
-    # timed region: K full sweeps; each group's sweep records one pair of HIP
-    # events (its stream) around its wide level launches, the dominant kernel
+    # timed region: K full sweeps with HIP events (on the sweep's stream)
+    # around the level launches, the dominant kernel: fused, one pair around
+    # all level launches of a sweep (level_group_kernel); otherwise one pair
+    # per group around its wide level launches (level_kernel)
     cg.profile_begin(args.steps, gcs.PROFILE_LEVEL_SPAN)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -529,10 +538,20 @@ def bench_biobank(args, wl, spec, leg):
     spans = cg.profile_end()
     cg.check()
     ms_per_step = elapsed * 1e3 / args.steps
-    span_ms = float(sum(float(sp[:, 0].mean()) for sp in spans))  # per full sweep
-    wide_bytes = sum(v[0] for v in lbytes.values())
     all_bytes = sum(v[1] for v in lbytes.values())
-    nwide = sum(v[2] for v in lbytes.values())
+    if fused:
+        span_ms = float(sum(float(sp.mean()) for sp in spans))  # per full sweep, over the batches
+        wide_bytes = all_bytes
+        nwide = cg.launches_per_sweep() - 2 * len(cg.fused)  # every level launch (leaves and reductions aside)
+        kernel = (f"level_group_kernel (one launch per level, each covering that level of a batch of "
+                  f"{args.fuse_batch} column groups; per batch timed from before its first to after its last "
+                  f"level launch, gaps included)")
+    else:
+        span_ms = float(sum(float(sp[:, 0].mean()) for sp in spans))  # per full sweep
+        wide_bytes = sum(v[0] for v in lbytes.values())
+        nwide = sum(v[2] for v in lbytes.values())
+        kernel = ("level_kernel (the wide levels of every group's sweep, one launch each; each group timed "
+                  "from before its first to after its last wide launch)")
     achieved = wide_bytes / (span_ms * 1e-3) / 1e9
     log(f"{ms_per_step:.2f} ms per sweep ({nnz / (ms_per_step * 1e-3):.3e} nnz/s); wide levels {nwide} launches in "
         f"{span_ms:.2f} ms, {wide_bytes / 1e9:.1f} GB -> {achieved:.0f} GB/s")
@@ -565,6 +584,7 @@ def bench_biobank(args, wl, spec, leg):
         "config": {"workload": args.workload, "n_rows": spec.n_rows, "n_cols": spec.n_cols, "nnz": nnz,
                    "founders": spec.founders, "seg_mean": spec.seg_mean, "mu": spec.mu, "seed": spec.seed,
                    "policy": args.policy, "groups": len(cg.devices), "group_cols": args.group_cols,
+                   "fused_group_sweep": fused, "fuse_batch": args.fuse_batch if fused else None,
                    "builder": "device (round-based RePair on the GPU; levels and layout on the host)",
                    "build_s": cg.build_s,
                    "grammar": {"n_rules": sum(s["n_rules"] for s in sts),
@@ -573,7 +593,7 @@ def bench_biobank(args, wl, spec, leg):
                                "n_terminals": sum(s["n_terminals"] for s in sts),
                                "depth_max": max(s["depth"] for s in sts),
                                "max_width_max": max(s["max_width"] for s in sts),
-                               "edge_spans": {str(d): spans[d] for d in sorted(spans)}},
+                               "edge_spans": {str(d): espan[d] for d in sorted(espan)}},
                    "launches_per_sweep": cg.launches_per_sweep(),
                    "max_rel_err_sampled": err, "sampled_rows": int(rows.size),
                    "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
@@ -583,8 +603,7 @@ def bench_biobank(args, wl, spec, leg):
                    "bytes_per_sweep": all_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "level_kernel (the wide levels of every group's sweep, one launch each; each group "
-                               "timed from before its first to after its last wide launch)",
+                     "kernel": kernel,
                      "launches": nwide, "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
                      "bytes_per_launch_avg": wide_bytes / max(nwide, 1),
                      "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
@@ -728,6 +747,12 @@ def main():
                     help="columns per group of the 200,000 x 2,000,000 workload (each group one device build)")
     ap.add_argument("--build-workers", type=int, default=3,
                     help="groups of the 200,000 x 2,000,000 workload built concurrently")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="200,000 x 2,000,000 workload: sweep the column groups one after the other (shared "
+                         "workspace) instead of one launch per level for all groups")
+    ap.add_argument("--fuse-batch", type=int, default=25,
+                    help="200,000 x 2,000,000 workload: column groups per fused sweep (each needs its own "
+                         "workspace; batches share them)")
     ap.add_argument("--policy", default="f32", choices=["f32", "f32_acc_f64"],
                     help="200,000 x 2,000,000 workload: fp32, or fp32 x with fp64 accumulation")
     ap.add_argument("--batches", default="32,64",

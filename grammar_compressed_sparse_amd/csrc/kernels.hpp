@@ -909,6 +909,91 @@ __global__ __launch_bounds__(kTailBlock) void tail_kernel(const LevelArgs* __res
     }
 }
 
+// ---------------------------------------------------------------- column groups swept together
+
+// Several uploaded grammars of one matrix (disjoint column groups, section
+// 4.4) swept as one: launch k runs level k (with the emission of level k-1)
+// of every group that has it.  A group's entry holds its launch arguments,
+// its own arena and accumulators, and the first virtual block of its share of
+// the launch; shares are multiples of kSlices, so a virtual block keeps its
+// slice's XCD.  Narrow levels of many groups together fill the chip, so no
+// persistent tail is needed.
+struct GroupEntry {
+    LevelArgs a;
+    void* arena;
+    void* acc;
+    int32_t block0, pad;
+};
+struct LeafEntry {
+    const int32_t *tcol, *tval;
+    const void* V;
+    void *T, *acc;
+    int32_t alpha, n_acc, block0, pad;
+};
+constexpr int kGroupLeafItems = 4;
+
+template <class E>
+__device__ __forceinline__ int32_t find_entry(const E* __restrict__ ents, int32_t n, int32_t vb)
+{
+    int32_t lo = 0, hi = n - 1;  // the last entry with block0 <= vb
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (ents[mid].block0 <= vb) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void leaf_group_kernel(const LeafEntry* __restrict__ ents, int32_t n_ent,
+                                                            const typename P::X* __restrict__ x)
+{
+    const LeafEntry& e = ents[find_entry(ents, n_ent, (int32_t)blockIdx.x)];
+    auto* T = (typename P::A*)e.T;
+    auto* acc = (typename P::A*)e.acc;
+    const auto* V = (const typename P::W*)e.V;
+    const int32_t base = ((int32_t)blockIdx.x - e.block0) * (kBlock * kGroupLeafItems) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kGroupLeafItems; ++u) {
+        const int32_t i = base + u * kBlock;
+        if (i < e.alpha) T[i] = P::leaf(V[e.tval[i]], x[e.tcol[i]]);
+        if (i < e.n_acc) acc[i] = P::ident();
+    }
+}
+
+template <class P>
+__global__ __launch_bounds__(kBlock) void level_group_kernel(const GroupEntry* __restrict__ ents, int32_t n_ent)
+{
+    const GroupEntry& e = ents[find_entry(ents, n_ent, (int32_t)blockIdx.x)];
+    const LevelArgs& a = e.a;
+    const int32_t b = (int32_t)blockIdx.x - e.block0, nodes = kSlices * (a.pb_bin + a.pb_pt);
+    auto* arena = (typename P::A*)e.arena;
+    auto* acc = (typename P::A*)e.acc;
+    if (a.stream && b >= nodes) stream_block<P>(a, b - nodes, threadIdx.x, arena, acc);
+    else level_block<P>(a, b, threadIdx.x, arena, acc);
+}
+
+// y[r] = y0 (+) s_0 (+) s_1 ... with s_g the combination of group g's eight
+// slice accumulators of row r in slice order: the additions, in the same
+// order, of a sweep of group 0 followed by accumulating sweeps of the others
+template <class P>
+__global__ __launch_bounds__(kBlock) void reduce_group_kernel(void* const* __restrict__ accs, int32_t n_grp,
+                                                              typename P::Y* __restrict__ y, int32_t n_rows,
+                                                              int32_t accumulate)
+{
+    for (int32_t r = blockIdx.x * kBlock + threadIdx.x; r < n_rows; r += gridDim.x * kBlock) {
+        typename P::Y v = accumulate ? y[r] : P::yzero();
+        for (int32_t gi = 0; gi < n_grp; ++gi) {
+            const auto* acc = (const typename P::A*)accs[gi];
+            typename P::A s = acc[r];
+#pragma unroll
+            for (int x = 1; x < kSlices; ++x) s = P::comb(s, acc[(int64_t)x * n_rows + r]);
+            v = P::emit(v, s);
+        }
+        y[r] = v;
+    }
+}
+
 // ---------------------------------------------------------------- batched right product
 
 // Y = M X for B vectors at once (X: m x B and Y: n x B, row-major).  Every

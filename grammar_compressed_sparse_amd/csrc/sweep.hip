@@ -1869,3 +1869,335 @@ extern "C" void gcs_free_device(gcs_device* d)
     if (d->pinned) (void)hipHostFree(d->pinned);
     delete d;
 }
+
+// ------------------------------------------------------------ column groups swept together
+
+struct gcs_group {
+    gcs_policy policy;
+    int device;
+    int64_t n_rows, n_cols;
+    std::vector<gcs_device*> devs;
+    int64_t n_launch = 0;                 // level launches: the largest L + 1 of the groups
+    std::vector<int64_t> ent_off;         // launch k (1-based) uses entries [ent_off[k-1], ent_off[k])
+    std::vector<int64_t> vblocks;         // virtual blocks of launch k at index k-1
+    int64_t leaf_blocks = 0, n_leaf = 0;  // leaf table: n_leaf entries (groups with terminals or rows)
+    const gcs::GroupEntry* ents = nullptr;
+    const gcs::LeafEntry* leaf = nullptr;
+    void* const* accs = nullptr;
+    // profiling: one pair of events around the level launches of each sweep
+    std::vector<hipEvent_t> events;
+    int64_t prof_max = 0, prof_used = 0;
+    bool profiling = false;
+};
+
+namespace {
+
+bool group_policy_ok(gcs_policy p)
+{
+    return p == GCS_PLUS_F64 || p == GCS_PLUS_F32 || p == GCS_PLUS_F32_ACC_F64 || p == GCS_PLUS_I64;
+}
+
+// entries of every launch, the leaf table and the accumulator pointers
+struct GroupPlan {
+    std::vector<gcs::GroupEntry> ents;
+    std::vector<int64_t> ent_off, vblocks;
+    std::vector<gcs::LeafEntry> leaf;
+    std::vector<void*> accs;
+    int64_t n_launch = 0, leaf_blocks = 0;
+    size_t off_leaf = 0, off_accs = 0, total = 0;
+};
+
+gcs_status group_plan(gcs_device* const* devs, int32_t n, GroupPlan& pl)
+{
+    if (!devs || n < 1) {
+        gcs::set_error("invalid argument: no device handles");
+        return GCS_EINVAL;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const gcs_device* d = devs[i];
+        if (!d) {
+            gcs::set_error("invalid argument: null device handle");
+            return GCS_EINVAL;
+        }
+        if (!group_policy_ok(d->policy) || d->policy != devs[0]->policy || d->n_rows != devs[0]->n_rows ||
+            d->n_cols != devs[0]->n_cols || d->device != devs[0]->device) {
+            gcs::set_error("group sweeps take uploads of one matrix shape, one device and one plus-times policy "
+                           "(fp64, fp32, fp32->fp64, int64)");
+            return GCS_EINVAL;
+        }
+    }
+    // each group needs its own arena and accumulators: workspaces must not overlap
+    const size_t eb = gcs::elem_bytes(devs[0]->policy);
+    std::vector<std::pair<uintptr_t, uintptr_t>> ws;
+    for (int32_t i = 0; i < n; ++i) {
+        const gcs_device* d = devs[i];
+        const uintptr_t b = (uintptr_t)d->counters;
+        const uintptr_t e = (uintptr_t)d->acc + (size_t)gcs::kSlices * d->n_rows * eb;
+        ws.push_back({b, e});
+    }
+    std::sort(ws.begin(), ws.end());
+    for (size_t i = 1; i < ws.size(); ++i)
+        if (ws[i].first < ws[i - 1].second) {
+            gcs::set_error("group sweeps need a separate workspace per upload (these overlap)");
+            return GCS_EINVAL;
+        }
+    for (int32_t i = 0; i < n; ++i) pl.n_launch = std::max<int64_t>(pl.n_launch, devs[i]->L + 1);
+    pl.ent_off.assign((size_t)pl.n_launch + 1, 0);
+    pl.vblocks.assign((size_t)pl.n_launch, 0);
+    for (int64_t k = 1; k <= pl.n_launch; ++k) {
+        int64_t vb = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            gcs_device* d = devs[i];
+            if (k > d->L + 1) continue;
+            const gcs::LevelArgs& a = d->largs[k - 1];
+            const int64_t nb = gcs::vblocks(a);
+            if (nb == 0) continue;
+            gcs::GroupEntry e{};
+            e.a = a;
+            e.arena = d->arena;
+            e.acc = d->acc;
+            e.block0 = (int32_t)vb;
+            pl.ents.push_back(e);
+            vb += nb;
+        }
+        if (vb >= (int64_t)INT32_MAX) {
+            gcs::set_error("a group launch exceeds 2^31 workgroups");
+            return GCS_ERANGE;
+        }
+        pl.vblocks[k - 1] = vb;
+        pl.ent_off[k] = (int64_t)pl.ents.size();
+    }
+    const int64_t per = (int64_t)gcs::kBlock * gcs::kGroupLeafItems;
+    for (int32_t i = 0; i < n; ++i) {
+        gcs_device* d = devs[i];
+        const int64_t n_acc = (int64_t)gcs::kSlices * d->n_rows;
+        const int64_t items = std::max<int64_t>(d->alpha, n_acc);
+        gcs::LeafEntry e{};
+        e.tcol = d->tcol;
+        e.tval = d->tval;
+        e.V = d->V;
+        e.T = d->arena;
+        e.acc = d->acc;
+        e.alpha = (int32_t)d->alpha;
+        e.n_acc = (int32_t)n_acc;
+        e.block0 = (int32_t)pl.leaf_blocks;
+        if (items == 0) continue;
+        pl.leaf.push_back(e);
+        pl.leaf_blocks += (items + per - 1) / per;
+    }
+    for (int32_t i = 0; i < n; ++i) pl.accs.push_back(devs[i]->acc);
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    pl.off_leaf = al(pl.ents.size() * sizeof(gcs::GroupEntry));
+    pl.off_accs = pl.off_leaf + al(pl.leaf.size() * sizeof(gcs::LeafEntry));
+    pl.total = pl.off_accs + al(pl.accs.size() * sizeof(void*));
+    return GCS_OK;
+}
+
+void release_group_events(gcs_group* g)
+{
+    for (hipEvent_t e : g->events) (void)hipEventDestroy(e);
+    g->events.clear();
+    g->profiling = false;
+    g->prof_max = g->prof_used = 0;
+}
+
+template <class P>
+gcs_status run_group(gcs_group* g, const void* xv, void* yv, int32_t accumulate, hipStream_t s, hipEvent_t* ev)
+{
+    using namespace gcs;
+    const int32_t n_leaf = (int32_t)g->n_leaf;
+    if (g->leaf_blocks > 0)
+        leaf_group_kernel<P><<<(unsigned)g->leaf_blocks, kBlock, 0, s>>>(g->leaf, n_leaf,
+                                                                         (const typename P::X*)xv);
+    if (ev) (void)hipEventRecord(ev[0], s);
+    for (int64_t k = 1; k <= g->n_launch; ++k) {
+        const int64_t e0 = g->ent_off[k - 1], e1 = g->ent_off[k];
+        if (e1 == e0) continue;
+        level_group_kernel<P><<<(unsigned)g->vblocks[k - 1], kBlock, 0, s>>>(g->ents + e0, (int32_t)(e1 - e0));
+    }
+    if (ev) (void)hipEventRecord(ev[1], s);
+    if (g->n_rows > 0) {
+        const int64_t grid = std::min<int64_t>((g->n_rows + kBlock - 1) / kBlock, 1 << 16);
+        reduce_group_kernel<P><<<(unsigned)grid, kBlock, 0, s>>>(g->accs, (int32_t)g->devs.size(),
+                                                                 (typename P::Y*)yv, (int32_t)g->n_rows, accumulate);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "group sweep launch");
+    return GCS_OK;
+}
+
+}  // namespace
+
+extern "C" gcs_status gcs_group_layout(gcs_device* const* devs, int32_t n, size_t* table_bytes)
+{
+    if (!table_bytes) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    GroupPlan pl;
+    if (gcs_status st = group_plan(devs, n, pl)) return st;
+    *table_bytes = pl.total;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_group_create(gcs_device* const* devs, int32_t n, void* table_dev, size_t table_bytes,
+                                       void* stream, gcs_group** out)
+{
+    if (!out || !table_dev) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    *out = nullptr;
+    try {
+        GroupPlan pl;
+        if (gcs_status st = group_plan(devs, n, pl)) return st;
+        if (table_bytes < pl.total || ((uintptr_t)table_dev & 255)) {
+            gcs::set_error("group table smaller than gcs_group_layout reports, or not 256-byte aligned");
+            return GCS_EINVAL;
+        }
+        gcs::DeviceGuard guard(devs[0]->device);
+        if (!guard.ok) {
+            gcs::set_error("cannot select the uploads' device");
+            return GCS_EHIP;
+        }
+        hipStream_t s = (hipStream_t)stream;
+        std::vector<unsigned char> img(pl.total, 0);
+        if (!pl.ents.empty()) std::memcpy(img.data(), pl.ents.data(), pl.ents.size() * sizeof(gcs::GroupEntry));
+        if (!pl.leaf.empty())
+            std::memcpy(img.data() + pl.off_leaf, pl.leaf.data(), pl.leaf.size() * sizeof(gcs::LeafEntry));
+        std::memcpy(img.data() + pl.off_accs, pl.accs.data(), pl.accs.size() * sizeof(void*));
+        hipError_t e = hipMemcpyAsync(table_dev, img.data(), pl.total, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return gcs::hip_fail(e, "hipMemcpyAsync (group table)");
+        auto* g = new gcs_group();
+        g->policy = devs[0]->policy;
+        g->device = devs[0]->device;
+        g->n_rows = devs[0]->n_rows;
+        g->n_cols = devs[0]->n_cols;
+        g->devs.assign(devs, devs + n);
+        g->n_launch = pl.n_launch;
+        g->ent_off = pl.ent_off;
+        g->vblocks = pl.vblocks;
+        g->leaf_blocks = pl.leaf_blocks;
+        g->n_leaf = (int64_t)pl.leaf.size();
+        auto* base = (unsigned char*)table_dev;
+        g->ents = (const gcs::GroupEntry*)base;
+        g->leaf = (const gcs::LeafEntry*)(base + pl.off_leaf);
+        g->accs = (void* const*)(base + pl.off_accs);
+        *out = g;
+        return GCS_OK;
+    } catch (const std::bad_alloc&) {
+        gcs::set_error("out of host memory");
+        return GCS_ENOMEM;
+    }
+}
+
+static gcs_status group_dispatch(gcs_group* g, const void* x_dev, void* y_dev, int32_t accumulate, void* stream,
+                                 hipEvent_t* ev)
+{
+    if (!g || (g->n_cols > 0 && !x_dev) || (g->n_rows > 0 && !y_dev) || (accumulate & ~1)) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    gcs::DeviceGuard guard(g->device);
+    if (!guard.ok) {
+        gcs::set_error("cannot select the uploads' device");
+        return GCS_EHIP;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    switch (g->policy) {
+    case GCS_PLUS_F64: return run_group<gcs::PolPlusF64>(g, x_dev, y_dev, accumulate, s, ev);
+    case GCS_PLUS_F32: return run_group<gcs::PolPlusF32>(g, x_dev, y_dev, accumulate, s, ev);
+    case GCS_PLUS_F32_ACC_F64: return run_group<gcs::PolPlusF32AccF64>(g, x_dev, y_dev, accumulate, s, ev);
+    case GCS_PLUS_I64: return run_group<gcs::PolPlusI64>(g, x_dev, y_dev, accumulate, s, ev);
+    default: break;
+    }
+    gcs::set_error("corrupt group handle");
+    return GCS_ESTATE;
+}
+
+extern "C" gcs_status gcs_group_sweep_right(gcs_group* g, const void* x_dev, void* y_dev, int32_t accumulate,
+                                            void* stream)
+{
+    return group_dispatch(g, x_dev, y_dev, accumulate, stream, nullptr);
+}
+
+extern "C" int64_t gcs_group_launches(const gcs_group* g)
+{
+    if (!g) return 0;
+    int64_t n = (g->leaf_blocks > 0 ? 1 : 0) + (g->n_rows > 0 ? 1 : 0);
+    for (int64_t k = 1; k <= g->n_launch; ++k) n += g->ent_off[k] > g->ent_off[k - 1] ? 1 : 0;
+    return n;
+}
+
+extern "C" gcs_status gcs_group_profile_begin(gcs_group* g, int64_t max_sweeps)
+{
+    if (!g || max_sweeps < 1) {
+        gcs::set_error("invalid argument");
+        return GCS_EINVAL;
+    }
+    gcs::DeviceGuard guard(g->device);
+    release_group_events(g);
+    g->events.resize((size_t)(2 * max_sweeps));
+    for (auto& e : g->events) {
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) {
+            g->events.clear();
+            return gcs::hip_fail(err, "hipEventCreate");
+        }
+    }
+    g->prof_max = max_sweeps;
+    g->prof_used = 0;
+    g->profiling = true;
+    return GCS_OK;
+}
+
+extern "C" gcs_status gcs_group_sweep_right_profiled(gcs_group* g, const void* x_dev, void* y_dev,
+                                                     int32_t accumulate, void* stream)
+{
+    if (!g || !g->profiling) {
+        gcs::set_error("gcs_group_profile_begin was not called");
+        return GCS_ESTATE;
+    }
+    if (g->prof_used == g->prof_max) {
+        gcs::set_error("more sweeps than gcs_group_profile_begin reserved");
+        return GCS_ERANGE;
+    }
+    gcs_status st = group_dispatch(g, x_dev, y_dev, accumulate, stream, g->events.data() + 2 * g->prof_used);
+    if (st == GCS_OK) g->prof_used++;
+    return st;
+}
+
+extern "C" gcs_status gcs_group_profile_end(gcs_group* g, float* level_ms, int64_t cap, int64_t* sweeps)
+{
+    if (!g || !g->profiling || !sweeps) {
+        gcs::set_error("gcs_group_profile_begin was not called");
+        return GCS_ESTATE;
+    }
+    gcs::DeviceGuard guard(g->device);
+    if (cap < g->prof_used || (g->prof_used > 0 && !level_ms)) {
+        gcs::set_error("level_ms holds fewer entries than profiled sweeps");
+        return GCS_ERANGE;
+    }
+    for (int64_t i = 0; i < g->prof_used; ++i) {
+        hipError_t e = hipEventSynchronize(g->events[2 * i + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&level_ms[i], g->events[2 * i], g->events[2 * i + 1]);
+        if (e != hipSuccess) {
+            release_group_events(g);
+            return gcs::hip_fail(e, "group profile events");
+        }
+    }
+    *sweeps = g->prof_used;
+    release_group_events(g);
+    return GCS_OK;
+}
+
+extern "C" void gcs_group_free(gcs_group* g)
+{
+    if (!g) return;
+    {
+        gcs::DeviceGuard guard(g->device);
+        release_group_events(g);
+    }
+    delete g;
+}

@@ -19,6 +19,12 @@ _SO = os.path.join(_PKG, "libgcs.so")
 
 if not os.path.exists(_SO):
     raise ImportError(f"{_SO} is not built; run __graft_entry__.build() (hipcc for gfx950)")
+# torch first: it loads the HIP and HSA runtimes it was built with, and
+# libgcs.so (which asks for the same sonames) then binds to those.  Loaded
+# the other way round, the process would hold two HIP runtimes, and device
+# memory of one is not usable from the other.
+import torch as _torch_mod  # noqa: E402,F401
+
 _lib = ctypes.CDLL(_SO)
 
 # policies (gcs_policy)
@@ -107,6 +113,22 @@ _lib.gcs_batch_workspace_bytes.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, c
 _lib.gcs_sweep_right_batch.argtypes = [_P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 _lib.gcs_sweep_right_batch_scratch.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P]
 _lib.gcs_sweep_right_batch_scratch.restype = _st
+_lib.gcs_group_layout.argtypes = [ctypes.POINTER(_P), ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+_lib.gcs_group_layout.restype = _st
+_lib.gcs_group_create.argtypes = [ctypes.POINTER(_P), ctypes.c_int32, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]
+_lib.gcs_group_create.restype = _st
+_lib.gcs_group_sweep_right.argtypes = [_P, _P, _P, ctypes.c_int32, _P]
+_lib.gcs_group_sweep_right.restype = _st
+_lib.gcs_group_profile_begin.argtypes = [_P, _I64]
+_lib.gcs_group_profile_begin.restype = _st
+_lib.gcs_group_sweep_right_profiled.argtypes = [_P, _P, _P, ctypes.c_int32, _P]
+_lib.gcs_group_sweep_right_profiled.restype = _st
+_lib.gcs_group_profile_end.argtypes = [_P, _P, _I64, ctypes.POINTER(_I64)]
+_lib.gcs_group_profile_end.restype = _st
+_lib.gcs_group_launches.argtypes = [_P]
+_lib.gcs_group_launches.restype = _I64
+_lib.gcs_group_free.argtypes = [_P]
+_lib.gcs_group_free.restype = None
 _lib.gcs_sweep_launches.argtypes = [_P]
 _lib.gcs_sweep_launches.restype = _I64
 _lib.gcs_profile_begin.argtypes = [_P, _I64, ctypes.c_int32]
@@ -500,6 +522,66 @@ class Device:
     def free(self):
         if self._h:
             _lib.gcs_free_device(self._h)
+            self._h = None
+        _LIVE.discard(self)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+class Group:
+    """Uploads of a matrix's column groups swept as one (``gcs_group``)."""
+
+    def __init__(self, devices, stream=None):
+        torch = _torch()
+        self.devices = list(devices)  # kept alive while the group lives
+        hs = (_P * len(self.devices))(*[d.handle for d in self.devices])
+        n = ctypes.c_size_t(0)
+        _check(_lib.gcs_group_layout(hs, len(self.devices), ctypes.byref(n)))
+        dev = self.devices[0].device
+        self.table = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+        h = _P()
+        with torch.cuda.device(dev):
+            _check(_lib.gcs_group_create(hs, len(self.devices), ctypes.c_void_p(self.table.data_ptr()),
+                                         self.table.numel(), _stream_ptr(stream), ctypes.byref(h)))
+        self._h = h
+        if not _EXIT_HOOK:
+            atexit.register(_release_all)
+            _EXIT_HOOK.append(True)
+        _LIVE.add(self)
+
+    def sweep_right(self, x, y=None, accumulate=False, stream=None, profiled=False):
+        """gcs_group_sweep_right: y = M x (or y += M x) over every group."""
+        d0 = self.devices[0]
+        if y is None:
+            y = d0.new_y()
+        _check_xy(d0, x, y)
+        torch = _torch()
+        fn = _lib.gcs_group_sweep_right_profiled if profiled else _lib.gcs_group_sweep_right
+        with torch.cuda.device(d0.device):
+            _check(fn(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), int(accumulate),
+                      _stream_ptr(stream)))
+        return y
+
+    def profile_begin(self, max_sweeps: int):
+        _check(_lib.gcs_group_profile_begin(self._h, max_sweeps))
+
+    def profile_end(self) -> np.ndarray:
+        """Span (ms) of the level launches of each profiled sweep."""
+        buf = np.zeros(1 << 16, np.float32)
+        n = _I64(0)
+        _check(_lib.gcs_group_profile_end(self._h, _ptr(buf), buf.size, ctypes.byref(n)))
+        return buf[:n.value].copy()
+
+    def launches(self) -> int:
+        return int(_lib.gcs_group_launches(self._h))
+
+    def free(self):
+        if getattr(self, "_h", None):
+            _lib.gcs_group_free(self._h)
             self._h = None
         _LIVE.discard(self)
 

@@ -7,10 +7,13 @@ terminals: each group of consecutive columns is a grammar of its own, and the
 product is the sum (OR, min) of the groups' products.
 
 Each group is built by the device builder (gcs_build_grammar_gpu), uploaded,
-and its host grammar dropped; all groups stay resident.  A sweep runs
-gcs_sweep_right on the first group and gcs_sweep_right_acc on every other one
-into the same y, all on one stream, so the groups share one workspace (value
-arena and counters; see gcs_upload).  Building overlaps across a few worker
+and its host grammar dropped; all groups stay resident.  For the plus-times
+policies the groups are then swept together (gcs_group_*): one launch per
+level covers that level of every group, each group with its own workspace.
+Otherwise a sweep runs gcs_sweep_right on the first group and
+gcs_sweep_right_acc on every other one into the same y, all on one stream,
+so the groups share one workspace (value arena and counters; see
+gcs_upload).  Building overlaps across a few worker
 threads, each with its own build workspace and stream: while one worker's
 group is in the device rounds, others generate their CSR or lay out their
 grammar on the host (the library calls release the GIL).
@@ -30,13 +33,16 @@ from . import gcs
 class ColumnGroups:
     """Resident column groups of one matrix (see build_column_groups)."""
 
-    def __init__(self, devices, bounds, stats, n_rows, n_cols, shared, build_s):
+    def __init__(self, devices, bounds, stats, n_rows, n_cols, shared, build_s, fused=None):
         self.devices = devices
         self.bounds = bounds
         self.stats = stats
         self.n_rows, self.n_cols = n_rows, n_cols
         self.shared = shared
         self.build_s = build_s
+        # gcs.Group per batch of groups: a batch's level k in one launch,
+        # batches one after the other (accumulating into y)
+        self.fused = fused
 
     @property
     def device_bytes(self) -> int:
@@ -56,23 +62,39 @@ class ColumnGroups:
         """y = M x over all groups (asynchronous on the stream)."""
         if y is None:
             y = self.new_y()
+        if self.fused is not None:
+            for b, grp in enumerate(self.fused):
+                grp.sweep_right(x, y, accumulate=b > 0, stream=stream)
+            return y
         self.devices[0].sweep_right(x, y, stream)
         for d in self.devices[1:]:
             d.sweep_right_acc(x, y, stream)
         return y
 
     def profile_begin(self, max_sweeps, mode):
+        if self.fused is not None:
+            for grp in self.fused:
+                grp.profile_begin(max_sweeps)
+            return
         for d in self.devices:
             d.profile_begin(max_sweeps, mode)
 
     def sweep_right_profiled(self, x, y, stream=None):
+        if self.fused is not None:
+            for b, grp in enumerate(self.fused):
+                grp.sweep_right(x, y, accumulate=b > 0, stream=stream, profiled=True)
+            return y
         self.devices[0].sweep_right_profiled(x, y, stream)
         for d in self.devices[1:]:
             d.sweep_right_profiled(x, y, stream, accumulate=True)
         return y
 
     def profile_end(self):
-        """Per group, the profile_end array of its device."""
+        """Level-launch spans (ms) of each profiled sweep: per batch of a
+        fused sweep an array over sweeps; otherwise, per group, its device's
+        profile_end array."""
+        if self.fused is not None:
+            return [grp.profile_end() for grp in self.fused]
         return [d.profile_end() for d in self.devices]
 
     def check(self, stream=None):
@@ -80,16 +102,23 @@ class ColumnGroups:
             d.check(stream)
 
     def launches_per_sweep(self) -> int:
+        if self.fused is not None:
+            return sum(grp.launches() for grp in self.fused)
         return sum(d.sweep_launches() for d in self.devices)
 
     def free(self):
+        if self.fused is not None:
+            for grp in self.fused:
+                grp.free()
+            self.fused = None
         for d in self.devices:
             d.free()
         self.devices = []
 
 
 def build_column_groups(source, n_rows, n_cols, group_cols, policy, workers=3, table_entries=1 << 28,
-                        n_threads=0, on_group=None, on_built=None, log=None, device="cuda") -> ColumnGroups:
+                        n_threads=0, on_group=None, on_built=None, log=None, device="cuda",
+                        fuse=True, fuse_batch=25) -> ColumnGroups:
     """Build, upload and keep resident every group of `group_cols` consecutive
     columns of an n_rows x n_cols matrix.
 
@@ -98,15 +127,21 @@ def build_column_groups(source, n_rows, n_cols, group_cols, policy, workers=3, t
     int8 or float64, at most 64 distinct values).  on_group(i, col0, ncols,
     row_ptr, col, val), if given, sees each group's CSR before it is dropped,
     and on_built(i, grammar, device) each host grammar before it is freed
-    (both called from the worker threads).  Groups are uploaded under `policy`
-    sharing one workspace sized to the largest group (grown once if a later
-    group needs more; the first groups then keep their own)."""
+    (both called from the worker threads).  With fuse (plus-times policies
+    only) the groups are swept in batches of fuse_batch (gcs_group_*: one
+    launch per level for a whole batch); the groups of a batch need their
+    own workspaces, batches run one after the other, so group i shares its
+    workspace with the groups i +- fuse_batch.  Without, all groups share one
+    workspace and are swept one after the other.  A workspace is sized by the
+    first group that uses it (with a margin) and replaced for later groups if
+    one needs more."""
+    fuse = fuse and policy in (gcs.PLUS_F64, gcs.PLUS_F32, gcs.PLUS_F32_ACC_F64, gcs.PLUS_I64)
     torch = gcs._torch()
     policy = gcs.POLICY_NAMES.get(policy, policy)
     bounds = [(c0, min(group_cols, n_cols - c0)) for c0 in range(0, n_cols, group_cols)]
     t_start = time.perf_counter()
     lock = threading.Lock()
-    shared = {"ws": None}
+    shared = {}  # workspace slot -> tensor
     local = threading.local()
     build_ws = {}  # per worker thread: its build workspace (replaced, never accumulated)
 
@@ -136,13 +171,12 @@ def build_column_groups(source, n_rows, n_cols, group_cols, policy, workers=3, t
                                   workspace=local.ws, device=device, stream=local.stream)
         t_build = time.perf_counter() - t1
         del rp, col, val
+        slot = i % max(1, fuse_batch) if fuse else 0
         need_ws = g.device_layout(policy)["workspace_bytes"]
         with lock:
-            if shared["ws"] is None or shared["ws"].numel() < need_ws:
-                # the first group sets the size (with a margin); a later,
-                # larger group replaces it for the groups after it
-                shared["ws"] = torch.empty(max(int(need_ws * 1.25), 256), dtype=torch.uint8, device=device)
-            wsh = shared["ws"]
+            if slot not in shared or shared[slot].numel() < need_ws:
+                shared[slot] = torch.empty(max(int(need_ws * 1.25), 256), dtype=torch.uint8, device=device)
+            wsh = shared[slot]
         dev = gcs.upload(g, policy, device=device, stream=local.stream, workspace=wsh)
         st = g.stats()
         st.update(col0=c0, ncols=nc, t_gen_s=t_gen, t_build_s=t_build)
@@ -162,5 +196,10 @@ def build_column_groups(source, n_rows, n_cols, group_cols, policy, workers=3, t
     build_ws.clear()
     local = None
     torch.cuda.empty_cache()
-    return ColumnGroups([r[0] for r in results], bounds, [r[1] for r in results], n_rows, n_cols, shared["ws"],
-                        time.perf_counter() - t_start)
+    devs = [r[0] for r in results]
+    fused = None
+    if fuse:
+        nb = max(1, fuse_batch)
+        fused = [gcs.Group(devs[b:b + nb]) for b in range(0, len(devs), nb)]
+    return ColumnGroups(devs, bounds, [r[1] for r in results], n_rows, n_cols, shared,
+                        time.perf_counter() - t_start, fused)

@@ -435,6 +435,42 @@ gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t n_sources,
                    uint8_t* visited_dev, uint8_t* y_dev, int64_t* new_counts, int64_t cap, int64_t* passes,
                    void* stream);
 
+/* ---- column groups swept together ---------------------------------------- */
+
+/* Uploads of the column groups of one matrix (section 4.4: built per column
+ * chunk; each group's rules reference only its own terminals, so the product
+ * is the sum of the groups' products) swept as one: launch k evaluates level
+ * k, with the emission of level k-1, of every group that has it, so narrow
+ * levels of many groups fill the device together and need no persistent
+ * tail; a last launch folds every group's slice accumulators into y.
+ * y = y0 + sum_g M_g x with exactly the additions, in the same order, of
+ * gcs_sweep_right on group 0 followed by gcs_sweep_right_acc on the others
+ * (bit for bit).  Plus-times policies only (fp64, fp32, fp32->fp64, int64);
+ * all uploads on one device with one policy and shape, each with its own
+ * workspace (GCS_EINVAL if workspaces overlap).  The handles must outlive
+ * the group.
+ *   gcs_group_layout: bytes of the device launch table (caller-owned memory).
+ *   gcs_group_create: copies the table into table_dev (256-byte aligned,
+ *     synchronises `stream`).
+ *   gcs_group_sweep_right: y = M x (accumulate = 0) or y += M x (1),
+ *     asynchronous on `stream`; sweeps of a group, and of its member
+ *     handles, must be ordered.
+ *   gcs_group_profile_begin / _sweep_right_profiled / _profile_end: events
+ *     right before the first and after the last level launch of each sweep;
+ *     level_ms[s] = that span of sweep s.
+ *   gcs_group_launches: launches per sweep. */
+typedef struct gcs_group gcs_group;
+gcs_status gcs_group_layout(gcs_device* const* devs, int32_t n, size_t* table_bytes);
+gcs_status gcs_group_create(gcs_device* const* devs, int32_t n, void* table_dev, size_t table_bytes, void* stream,
+                            gcs_group** out);
+gcs_status gcs_group_sweep_right(gcs_group* g, const void* x_dev, void* y_dev, int32_t accumulate, void* stream);
+gcs_status gcs_group_profile_begin(gcs_group* g, int64_t max_sweeps);
+gcs_status gcs_group_sweep_right_profiled(gcs_group* g, const void* x_dev, void* y_dev, int32_t accumulate,
+                                          void* stream);
+gcs_status gcs_group_profile_end(gcs_group* g, float* level_ms, int64_t cap, int64_t* sweeps);
+int64_t gcs_group_launches(const gcs_group* g);
+void gcs_group_free(gcs_group* g);
+
 /* ---- profiling --------------------------------------------------------- */
 
 /* Kernel launches of one sweep: 1 (terminal array, clear accumulators), one
