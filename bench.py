@@ -398,6 +398,133 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     print("\n".join(lines))
 
 
+def summarize_group_trace(kt_dir, out_md, title, commands, bench_log=None):
+    """Text summary of a rocprofv3 kernel trace of the column-group bench:
+    the kernel time table, and per product (leaf_group_kernel ... the last
+    reduce_group_kernel of its batches) the level_group_kernel launches'
+    kernel time against the bench's own HIP-event span of the same launches."""
+    import csv
+    import glob
+
+    def rows(pat):
+        fs = glob.glob(os.path.join(kt_dir, "**", pat), recursive=True)
+        return list(csv.DictReader(open(fs[0]))) if fs else []
+
+    stats = rows("*kernel_stats.csv")
+    lines = [f"# rocprofv3 summary: {title}", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "## Kernel time (--kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us | total ms | share |", "|---|---|---|---|---|---|---|"]
+    for r in stats[:16]:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    trace = sorted(rows("*kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    lv = [r for r in trace if "level_group_kernel" in r["Kernel_Name"]]
+    if lv:
+        d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in lv])
+        lines += ["", "## level_group_kernel (the dominant kernel)", "",
+                  f"- {len(lv)} launches, average duration {d.mean():.1f} us (median {np.median(d):.1f} us), "
+                  f"{d.sum() / 1e3:.1f} ms in all"]
+        # batch sweeps: the group launches up to and including a reduce_group_kernel
+        prods, cur = [], []
+        for r in trace:
+            n = r["Kernel_Name"]
+            if "group_kernel" in n:
+                cur.append(r)
+            if "reduce_group_kernel" in n and cur:
+                prods.append(cur)
+                cur = []
+        if prods:
+            lvl_ms = [sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in p
+                          if "level_group_kernel" in r["Kernel_Name"]) / 1e6 for p in prods]
+            span_ms = [(int(p[-1]["End_Timestamp"]) - int(p[0]["Start_Timestamp"])) / 1e6 for p in prods]
+            lines += [f"- per batch sweep (leaf to reduction, {len(prods)} batch sweeps): level kernel time "
+                      f"{np.median(lvl_ms):.2f} ms, first start to last end {np.median(span_ms):.2f} ms (medians)"]
+    if bench_log and os.path.exists(bench_log):
+        with open(bench_log) as f:
+            js = [ln for ln in f if ln.startswith("{")]
+        if js:
+            b = json.loads(js[-1])
+            rf = b["roofline"]
+            lines += ["", "## The same run's bench line", "",
+                      f"- {b['ms_per_step']:.2f} ms per product, value {b['value']:.4g} nnz/s; roofline: "
+                      f"{rf['launches']} level launches per product, span {rf['launch_avg_us']:.1f} us per launch "
+                      f"(gaps included), achieved {rf['achieved']:.0f} GB/s = {rf['frac']:.3f} of peak"]
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_per_level(kt_dir, fetch_dir, write_dir, levels_json, out_md, copy_mib, commands):
+    """Per-level hardware-counter table of one sweep: every level_kernel
+    dispatch of a single-vector sweep is matched to its level k by its order
+    after the sweep's leaf_kernel; FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, scaled by the same counters on a known-size copy) are averaged
+    per level over the run's sweeps, and divided by the mean kernel duration
+    of that level from the kernel trace.  levels_json: the bench's JSON line
+    run with GCS_BENCH_LEVELS=1 (algorithmic bytes per level)."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        fs = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        return list(csv.DictReader(open(fs[0]))) if fs else []
+
+    def per_level(recs, key):
+        """level k -> list of values, from dispatches in dispatch order"""
+        recs = sorted(recs, key=lambda r: int(r["Dispatch_Id"]))
+        out, k = {}, None
+        for r in recs:
+            n = r["Kernel_Name"]
+            if "leaf_kernel" in n and "batch" not in n:
+                k = 0
+            elif "level_kernel" in n and k is not None:
+                k += 1
+                out.setdefault(k, []).append(key(r))
+            elif "tail_kernel" in n:
+                k = None
+        return out
+
+    with open(levels_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    lv = {p["k"]: p for p in json.loads(line)["config"]["per_level"]}
+    copy = copy_mib << 20
+    scales = {}
+    vals = {}
+    for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        cc = [r for r in rows(d, "*counter_collection.csv") if r.get("Counter_Name", tag) == tag]
+        big = [float(r["Counter_Value"]) for r in sorted(cc, key=lambda r: int(r["Dispatch_Id"]))
+               if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer") and float(r["Counter_Value"]) > 0.25 * copy_mib * 1024][:5]
+        scales[tag] = copy / (sum(big) / len(big) * 1024)
+        vals[tag] = per_level(cc, lambda r: float(r["Counter_Value"]) * 1024 * scales[tag])
+    kt = rows(kt_dir, "*kernel_trace.csv")
+    dur = per_level([dict(r, Dispatch_Id=r.get("Dispatch_Id", r.get("Correlation_Id", 0))) for r in kt],
+                    lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Per-level HBM traffic: level_kernel on genotype_20000x100000_f32, one sweep", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the same counters on {copy_mib} MiB "
+                  f"device copies (scale {scales['FETCH_SIZE']:.4f} / {scales['WRITE_SIZE']:.4f}); a level "
+                  "launch k computes level k and emits level k-1. Durations: mean kernel time of that launch in "
+                  "the kernel trace. Algorithmic bytes as in bench.py's level formula.", "",
+              "| k | width | algorithmic MB | FETCH MB | WRITE MB | traffic / algorithmic | us | algorithmic GB/s | "
+              "measured GB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals["FETCH_SIZE"]):
+        if k not in lv or k not in vals["WRITE_SIZE"] or k not in dur:
+            continue
+        f = float(np.mean(vals["FETCH_SIZE"][k]))
+        w = float(np.mean(vals["WRITE_SIZE"][k]))
+        us = float(np.mean(dur[k]))
+        a = float(lv[k]["bytes"])
+        lines.append(f"| {k} | {lv[k]['width']} | {a / 1e6:.1f} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / a:.2f} | "
+                     f"{us:.1f} | {a / (us * 1e-6) / 1e9:.0f} | {(f + w) / (us * 1e-6) / 1e9:.0f} |")
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def bench_tropical(args, torch, gcs, leg, g, rp, col, spec, src, vis_o, counts_o):
     """Tropical (min, +) policy with unit weights on the same graph: K timed
     single passes from d0 (0 at the sources, +inf elsewhere), one checked
@@ -729,6 +856,15 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-kernel-trace":
         # bench.py --summarize-kernel-trace KT_DIR OUT_MD TITLE "command" ...
         summarize_kernel_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-group-trace":
+        # bench.py --summarize-group-trace KT_DIR OUT_MD TITLE BENCH_LOG "command" ...
+        summarize_group_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6:], bench_log=sys.argv[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-per-level":
+        # bench.py --summarize-per-level KT_DIR FETCH_DIR WRITE_DIR LEVELS_JSON OUT_MD COPY_MIB "command" ...
+        summarize_per_level(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], int(sys.argv[7]),
+                            sys.argv[8:])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-rocprof":
         # bench.py --summarize-rocprof KT_DIR FETCH_DIR WRITE_DIR OUT_MD COPY_MIB "command" ...
