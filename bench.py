@@ -228,6 +228,7 @@ def bench_batched(torch, gcs, leg, synth, dev, lay, rp, col, val, spec, elem, xd
 
 KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "kernels.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
+GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_group_kernel_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -452,6 +453,58 @@ def summarize_group_trace(kt_dir, out_md, title, commands, bench_log=None):
                       f"- {b['ms_per_step']:.2f} ms per product, value {b['value']:.4g} nnz/s; roofline: "
                       f"{rf['launches']} level launches per product, span {rf['launch_avg_us']:.1f} us per launch "
                       f"(gaps included), achieved {rf['achieved']:.0f} GB/s = {rf['frac']:.3f} of peak"]
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_group_counters(fetch_dir, write_dir, out_md, copy_mib, commands, bench_logs):
+    """HBM traffic of level_group_kernel from a --pmc FETCH_SIZE run and a
+    --pmc WRITE_SIZE run of the default bench (each calibrated by device
+    copies of a known size issued first): mean scaled bytes per dispatch,
+    written to GROUP_TRAFFIC_FILE with the kernel source's hash (bench.py
+    reports it as roofline.traffic only while that hash still matches) and
+    summarised in out_md."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        fs = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        return list(csv.DictReader(open(fs[0]))) if fs else []
+
+    rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20, "kernel": "level_group_kernel"}
+    for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
+        cc = sorted(rows(d, "*counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in cc if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        big = [v for v in copies if v > 0.25 * copy_mib * 1024][:5]
+        lvl = [float(r["Counter_Value"]) * 1024 for r in cc if "level_group_kernel" in r["Kernel_Name"]]
+        rec[tag + "_kib_copy"] = sum(big) / len(big)
+        rec[tag + "_scale"] = rec["copy_bytes"] / (rec[tag + "_kib_copy"] * 1024)
+        rec[tag + "_bytes_per_launch"] = sum(lvl) / max(len(lvl), 1) * rec[tag + "_scale"]
+        rec[tag + "_launches"] = len(lvl)
+    rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    alg = None
+    for lg in bench_logs:
+        if os.path.exists(lg):
+            js = [ln for ln in open(lg) if ln.startswith("{")]
+            if js:
+                alg = json.loads(js[-1])["roofline"]["bytes_per_launch_avg"]
+    lines = ["# HBM traffic of level_group_kernel on genotype_200000x2000000_f32 (the default bench)", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"- calibration: a device copy of {copy_mib} MiB reads {rec['fetch_kib_copy']:.1f} KiB "
+                  f"(FETCH_SIZE) and writes {rec['write_kib_copy']:.1f} KiB (WRITE_SIZE): scales "
+                  f"{rec['fetch_scale']:.4f} / {rec['write_scale']:.4f}",
+              f"- level_group_kernel, mean over {rec['fetch_launches']} / {rec['write_launches']} dispatches: "
+              f"FETCH {rec['fetch_bytes_per_launch'] / 1e6:.1f} MB, WRITE {rec['write_bytes_per_launch'] / 1e6:.1f} MB, "
+              f"traffic {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB per launch (scaled)"]
+    if alg:
+        rec["algorithmic_bytes_per_launch"] = alg
+        lines.append(f"- algorithmic bytes per launch (the bench's formula): {alg / 1e6:.1f} MB; traffic / "
+                     f"algorithmic = {rec['traffic_bytes_per_launch'] / alg:.2f}")
+    lines.append(f"- kernel source sha256[:16] = {rec['source_sha256']}")
+    with open(GROUP_TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
     with open(out_md, "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -698,7 +751,13 @@ def bench_biobank(args, wl, spec, leg):
                "sample": f"column group 0 (columns [0, {args.group_cols}), all {spec.n_rows} rows, {g_nnz} "
                          f"nonzeros), {passes} fp64 compensated CSR passes ({el:.1f} s)"}
         del rp, col, val
-    copy_gbs = copy_achievable_gbs(torch)
+    copy_gbs = None if args.calibrate_copy_mib else copy_achievable_gbs(torch)
+    traffic = None  # HBM bytes per level_group_kernel launch from the committed counters, if still current
+    if fused and not acc64 and args.fuse_batch == 25 and os.path.exists(GROUP_TRAFFIC_FILE):
+        with open(GROUP_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("source_sha256") == kernel_source_hash():
+            traffic = rec["traffic_bytes_per_launch"]
     csr_bytes = 8 * nnz + 4 * (spec.n_rows + 1) + 4 * spec.n_cols + 4 * spec.n_rows
     eng_bytes = cg.device_bytes + 4 * spec.n_cols + yelem * spec.n_rows
     sts = cg.stats
@@ -729,11 +788,12 @@ def bench_biobank(args, wl, spec, leg):
                    "wide_levels": nwide, "level_span_ms": span_ms,
                    "bytes_per_sweep": all_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "achieved_from_traffic": (traffic / (span_ms * 1e-3 / max(nwide, 1)) / 1e9) if traffic else None,
                      "kernel": kernel,
                      "launches": nwide, "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
                      "bytes_per_launch_avg": wide_bytes / max(nwide, 1),
-                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -856,6 +916,11 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-kernel-trace":
         # bench.py --summarize-kernel-trace KT_DIR OUT_MD TITLE "command" ...
         summarize_kernel_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-group-counters":
+        # bench.py --summarize-group-counters FETCH_DIR WRITE_DIR OUT_MD COPY_MIB BENCH_LOG "command" ...
+        summarize_group_counters(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[7:],
+                                 [sys.argv[6]])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-group-trace":
         # bench.py --summarize-group-trace KT_DIR OUT_MD TITLE BENCH_LOG "command" ...
