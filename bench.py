@@ -229,6 +229,75 @@ def bench_batched(torch, gcs, leg, synth, dev, lay, rp, col, val, spec, elem, xd
 KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "kernels.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
 GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_group_kernel_traffic.json")
+L2_FILE = os.path.join(ROOT, "profiles", "l2_requests.json")
+# L2 request rate of the chip: 8 XCDs x 16 L2 channels, one request per
+# channel per clock at 2.4 GHz (G requests/s).  A 4-byte gather costs a whole
+# request, so a gather-bound kernel meets this bound long before the HBM one.
+L2_REQ_PEAK_G = 8 * 16 * 2.4
+
+
+def grammar_bytes(st) -> int:
+    """Bytes of the grammar a sweep streams: 8 per binary rule (two child
+    references), 4 per pass-through node, 8 per entry of C (reference and
+    row position), 4 per terminal."""
+    return 8 * st["n_rules"] + 4 * st["n_passthrough"] + 8 * st["c_len"] + 4 * st["n_terminals"]
+
+
+def l2_bound(kernel, workload, launch_avg_us):
+    """The second bound of the roofline: L2 requests per launch of `kernel`
+    on `workload` from the committed counter record (while the kernel
+    source's hash still matches), their rate over the bench's own launch
+    time, against L2_REQ_PEAK_G."""
+    if not os.path.exists(L2_FILE):
+        return None
+    with open(L2_FILE) as f:
+        rec = json.load(f).get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    rate = rec["requests_per_launch"] / (launch_avg_us * 1e-6) / 1e9
+    return {"bound": "l2_requests", "requests_per_launch": rec["requests_per_launch"], "achieved": rate,
+            "peak": L2_REQ_PEAK_G, "unit": "G requests/s", "frac": rate / L2_REQ_PEAK_G,
+            "hit_rate": rec["hit_rate"],
+            "peak_basis": "8 XCDs x 16 L2 channels x 2.4 GHz, one request per channel per clock"}
+
+
+def summarize_l2(hit_dir, out_md, kernel, workload, commands):
+    """L2 requests (TCC_HIT_sum + TCC_MISS_sum) per dispatch of gcs::kernel
+    from one --pmc TCC_HIT_sum TCC_MISS_sum run: the mean over the run's
+    dispatches is recorded in L2_FILE under kernel:workload with the kernel
+    source's hash, and summarised in out_md."""
+    import csv
+    import glob
+    fs = glob.glob(os.path.join(hit_dir, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for r in csv.DictReader(open(fs[0])):
+        if f"gcs::{kernel}<" not in r["Kernel_Name"]:
+            continue
+        h = per.setdefault(int(r["Dispatch_Id"]), [0.0, 0.0])
+        h[0 if r["Counter_Name"].startswith("TCC_HIT") else 1] += float(r["Counter_Value"])
+    v = np.array(list(per.values()))
+    req = v.sum(axis=1)
+    rec = {"source_sha256": kernel_source_hash(), "kernel": kernel, "workload": workload,
+           "launches": int(v.shape[0]), "requests_per_launch": float(req.mean()),
+           "hit_rate": float(v[:, 0].sum() / req.sum())}
+    allrec = {}
+    if os.path.exists(L2_FILE):
+        with open(L2_FILE) as f:
+            allrec = json.load(f)
+    allrec[f"{kernel}:{workload}"] = rec
+    with open(L2_FILE, "w") as f:
+        json.dump(allrec, f, indent=1)
+    lines = [f"# L2 requests of {kernel} on {workload}", "",
+             "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"- {rec['launches']} dispatches of gcs::{kernel}; L2 requests (hits + misses, all XCDs) per "
+                  f"dispatch: mean {rec['requests_per_launch'] / 1e6:.2f} M, median {np.median(req) / 1e6:.2f} M, "
+                  f"max {req.max() / 1e6:.2f} M; hit rate {rec['hit_rate']:.3f}",
+              f"- request peak: {L2_REQ_PEAK_G:.1f} G requests/s (8 XCDs x 16 channels x 2.4 GHz)",
+              f"- kernel source sha256[:16] = {rec['source_sha256']}"]
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def kernel_source_hash() -> str:
@@ -686,12 +755,16 @@ def bench_biobank(args, wl, spec, leg):
 
     log(f"building {spec.n_rows}x{spec.n_cols} as groups of {args.group_cols} columns "
         f"({args.build_workers} build workers)")
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
     cg = groups.build_column_groups(lambda c0, nc: synth.genotype(spec, col0=c0, ncols=nc), spec.n_rows,
                                     spec.n_cols, args.group_cols, policy, workers=args.build_workers,
                                     table_entries=1 << 28, on_group=on_group, on_built=on_built, log=log,
                                     fuse=not args.no_fuse, fuse_batch=args.fuse_batch)
     fused = cg.fused is not None
     nnz = sum(nnz_of.values())
+    torch.cuda.synchronize()
+    mem_resident = torch.cuda.memory_allocated() - mem0  # cross-check of the footprint (torch's own count)
     log(f"built {len(cg.devices)} groups in {cg.build_s:.0f}s: nnz={nnz}, device {cg.device_bytes / 1e9:.1f} GB")
     y = cg.sweep_right(xd)
     cg.check()
@@ -719,6 +792,19 @@ def bench_biobank(args, wl, spec, leg):
     cg.check()
     ms_per_step = elapsed * 1e3 / args.steps
     all_bytes = sum(v[1] for v in lbytes.values())
+    # sustained: back-to-back products for at least 1.5 s (after the timed region)
+    torch.cuda.synchronize()
+    t_s, n_s = time.perf_counter(), 0
+    while True:
+        for _ in range(5):
+            cg.sweep_right(xd, y)
+        n_s += 5
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_s >= 1.5:
+            break
+    sustained = {"seconds": time.perf_counter() - t_s, "products": n_s}
+    sustained["nnz_per_s"] = nnz * n_s / sustained["seconds"]
+    cg.check()
     if fused:
         span_ms = float(sum(float(sp.mean()) for sp in spans))  # per full sweep, over the batches
         wide_bytes = all_bytes
@@ -747,9 +833,23 @@ def bench_biobank(args, wl, spec, leg):
             el = time.perf_counter() - t0
             if el >= 10.0 or passes >= 50:
                 break
-        cpu = {"value": g_nnz * passes / el, "unit": "nnz/s", "cores": leg.threads(), "kind": "oracle",
+        cores = leg.threads()
+        cpu = {"value": g_nnz * passes / el, "unit": "nnz/s", "cores": cores, "kind": "oracle",
                "sample": f"column group 0 (columns [0, {args.group_cols}), all {spec.n_rows} rows, {g_nnz} "
                          f"nonzeros), {passes} fp64 compensated CSR passes ({el:.1f} s)"}
+        # one core, over every 64th row of the same group (context: the single-thread rate)
+        rows1 = np.arange(0, spec.n_rows, 64)
+        leg.o.set_threads(1)
+        try:
+            t0 = time.perf_counter()
+            leg.o.spmv_f64_rows(rows1, rp, col, val, xo)
+            el1 = time.perf_counter() - t0
+        finally:
+            leg.o.set_threads(cores)
+        nnz1 = int((rp[rows1 + 1] - rp[rows1]).sum())
+        cpu["one_core"] = {"value": nnz1 / el1, "unit": "nnz/s",
+                           "sample": f"rows 0, 64, 128, ... of column group 0 ({rows1.size} rows, {nnz1} nonzeros, "
+                                     f"{el1:.1f} s)"}
         del rp, col, val
     copy_gbs = None if args.calibrate_copy_mib else copy_achievable_gbs(torch)
     traffic = None  # HBM bytes per level_group_kernel launch from the committed counters, if still current
@@ -784,7 +884,10 @@ def bench_biobank(args, wl, spec, leg):
                    "max_rel_err_sampled": err, "sampled_rows": int(rows.size),
                    "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
                    "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
+                   "device_bytes_torch_allocated": int(mem_resident),
                    "hbm_bytes_total": int(torch.cuda.get_device_properties(0).total_memory),
+                   "grammar_bytes_per_s": sum(grammar_bytes(s) for s in sts) / (ms_per_step * 1e-3),
+                   "sustained": sustained,
                    "wide_levels": nwide, "level_span_ms": span_ms,
                    "bytes_per_sweep": all_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -793,7 +896,9 @@ def bench_biobank(args, wl, spec, leg):
                      "kernel": kernel,
                      "launches": nwide, "launch_avg_us": span_ms * 1e3 / max(nwide, 1),
                      "bytes_per_launch_avg": wide_bytes / max(nwide, 1),
-                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None},
+                     "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None,
+                     "second_bound": l2_bound("level_group_kernel" if fused else "level_kernel", args.workload,
+                                              span_ms * 1e3 / max(nwide, 1))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -925,6 +1030,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-group-trace":
         # bench.py --summarize-group-trace KT_DIR OUT_MD TITLE BENCH_LOG "command" ...
         summarize_group_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6:], bench_log=sys.argv[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-l2":
+        # bench.py --summarize-l2 HIT_DIR OUT_MD KERNEL WORKLOAD "command" ...
+        summarize_l2(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6:])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-per-level":
         # bench.py --summarize-per-level KT_DIR FETCH_DIR WRITE_DIR LEVELS_JSON OUT_MD COPY_MIB "command" ...
@@ -1147,8 +1256,7 @@ def main():
                             edge_spans={str(d): int(c) for d, c in enumerate(g.edge_spans().tolist()) if c}),
             "build_s": build_s, "upload_s": upload_s,
             "launches_per_sweep": int(launch_ms.shape[1]),
-            "grammar_bytes_per_s": (8 * st["n_rules"] + 8 * st["n_emit_groups"] + 4 * st["c_len"] +
-                                    8 * st["n_terminals"]) / (ms_per_step * 1e-3),
+            "grammar_bytes_per_s": grammar_bytes(st) / (ms_per_step * 1e-3),
             "device_bytes": eng_bytes, "csr_bytes_analytic": csr_bytes,
             "upload_bytes_torch_peak": int(upload_peak),
             "footprint_ratio_csr_over_engine": csr_bytes / eng_bytes,
@@ -1173,7 +1281,9 @@ def main():
                      "achieved_from_traffic": (traffic / (span_ms * 1e-3 / max(nwide, 1)) / 1e9) if traffic else None,
                      "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None,
                      "bytes_per_launch_avg": float(lb.sum() / nwide if nwide > 0 else lb_all.sum()),
-                     "bytes_per_sweep": float(lb_all.sum())},
+                     "bytes_per_sweep": float(lb_all.sum()),
+                     "second_bound": l2_bound("level_kernel", args.workload, span_ms * 1e3 / nwide)
+                     if nwide > 0 else None},
         "cpu_baseline": cpu,
     }
     if os.environ.get("GCS_BENCH_LEVELS"):
