@@ -14,6 +14,8 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (run through the HIP library)")
     config.addinivalue_line("markers", "slow: large CPU build; skipped unless selected")
+    import helpers
+    helpers.CAPTURE = config.pluginmanager.getplugin("capturemanager")
 
 
 @pytest.fixture(scope="session")

@@ -7,7 +7,26 @@ parity of products is always judged against ``oracle``.
 """
 from __future__ import annotations
 
+import threading
+
 import numpy as np
+
+# pytest's capture manager, set by conftest at configure time, so that the
+# progress lines of long GPU tests reach the terminal while the test runs
+CAPTURE = None
+_PROGRESS_LOCK = threading.Lock()
+
+
+def progress(msg):
+    """Print a progress line at once, past pytest's output capture: a test
+    that prints nothing for minutes is indistinguishable from a hung one.
+    Worker threads may call it (one at a time: capture is process-wide)."""
+    with _PROGRESS_LOCK:
+        if CAPTURE is not None:
+            with CAPTURE.global_and_fixture_disabled():
+                print(msg, flush=True)
+        else:
+            print(msg, flush=True)
 
 
 def csr_from_dense(M):

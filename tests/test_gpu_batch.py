@@ -5,7 +5,6 @@ Tolerances are those of the single-vector sweep (per row r of column b,
 s_rb = sum_j |M[r][j] X[j][b]|): 1e-12 s_rb for fp64 and fp32->fp64, 1e-5 s_rb
 for fp32; int64, Boolean, X = ones and X = e_j columns bit-exact.
 """
-import sys
 
 import numpy as np
 import pytest
@@ -16,8 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    H.progress(msg)
 
 
 @pytest.fixture(scope="module")

@@ -10,12 +10,13 @@ x = ones for all rows bit for bit (integer row sums below 2^24 are exact in
 fp32 in any order).  The fp32 -> fp64 accumulate policy is checked at 1e-12
 on the first three groups (60,000 columns, all rows).
 """
-import sys
 import threading
 import time
 
 import numpy as np
 import pytest
+
+import helpers
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +24,7 @@ GROUP_COLS = 20_000
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 def test_biobank_full_f32_every_row(oracle_mod, synth_mod):

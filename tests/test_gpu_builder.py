@@ -8,7 +8,6 @@ a round.  The sweep of the device-built grammar is then checked against the
 oracle (fp64, 1e-12 of the row's sum of |terms|).
 """
 import random
-import sys
 import time
 
 import numpy as np
@@ -20,8 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    H.progress(msg)
 
 
 @pytest.fixture(scope="module")

@@ -7,18 +7,18 @@ rows, each of the 32 multiply-many vectors on all rows, and every column of
 the batched B = 32 sweep on all rows; x = ones bit for bit against the
 oracle's exact integer product.
 """
-import sys
 import time
 
 import numpy as np
 import pytest
 
+import helpers
+
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 @pytest.fixture(scope="module")

@@ -7,18 +7,18 @@ many out-neighbours share a tile), RePair running on the tiles in parallel.
 This is the heaviest test (about 1 GB of edges generated sequentially, a
 multi-minute host build); it prints each step.
 """
-import sys
 import time
 
 import numpy as np
 import pytest
 
+import helpers
+
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 def test_copy_graph_50M_bfs(synth_mod, oracle_mod):

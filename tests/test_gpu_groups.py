@@ -3,17 +3,17 @@ launch, then one reduction of every group's slice accumulators.  The result
 must equal, bit for bit, gcs_sweep_right on group 0 followed by
 gcs_sweep_right_acc on the others (the same additions in the same order),
 and the oracle within the policy's tolerance."""
-import sys
 
 import numpy as np
 import pytest
+
+import helpers
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 @pytest.fixture(scope="module")

@@ -11,7 +11,6 @@ depth * 2^-24 * s_r (Higham, Accuracy and Stability of Numerical Algorithms,
 section 4.2); depths here stay below 170.
 """
 import os
-import sys
 
 import numpy as np
 import pytest
@@ -22,8 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    H.progress(msg)
 
 
 @pytest.fixture(scope="module")

@@ -7,17 +7,17 @@ returns GCS_ESTATE at the failing pass, and the mark is per sweep: a handle
 uploaded without the knob, and the failing handle's own flag once checked,
 are unaffected."""
 import os
-import sys
 
 import numpy as np
 import pytest
+
+import helpers
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 def _upload(gcs, g, policy, spin=None):

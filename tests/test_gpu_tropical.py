@@ -1,17 +1,17 @@
 """Tropical (min, +) policy on the GPU (through the C ABI) against the oracle:
 bit-exact, since min never rounds and each sum is formed once, in the leaf
 (section 5: combine = min, leaf = value + x[j], identity +inf)."""
-import sys
 
 import numpy as np
 import pytest
+
+import helpers
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 @pytest.fixture(scope="module")

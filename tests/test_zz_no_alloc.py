@@ -4,17 +4,17 @@ against gcs_sweep_right_batch with a caller-provided workspace: the same
 results bit for bit, and the oracle's within the fp64 tolerance, on two calls
 in a row, the second with a smaller input; a request larger than the array
 is refused before any device work."""
-import sys
 
 import numpy as np
 import pytest
+
+import helpers
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    helpers.progress(msg)
 
 
 def test_scratch_batch_matches_workspace_batch(oracle_mod, synth_mod):
