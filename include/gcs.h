@@ -429,8 +429,11 @@ gcs_status gcs_sweep_right_batch_scratch(gcs_device* d, const void* x_dev, void*
  * visited_dev, y_dev: n-byte device arrays.  new_counts (host, cap entries)
  * receives |f| after each pass (the last pass gives 0); *passes the number
  * of passes.  Synchronises `stream` once per pass to read the count.
- * GCS_ESTATE if not uploaded with GCS_BOOL_OR or not square; GCS_ERANGE if the
- * fixpoint needs more than cap passes. */
+ * GCS_ESTATE if not uploaded with GCS_BOOL_OR or not square, or at the first
+ * pass whose persistent tail kernel gave up at a grid barrier (read with that
+ * pass's count; the device flag is cleared, *passes counts the failed pass,
+ * and frontier and visited are not to be used); GCS_ERANGE if the fixpoint
+ * needs more than cap passes. */
 gcs_status gcs_bfs(gcs_device* d, const int64_t* sources_dev, int64_t n_sources, uint8_t* frontier_dev,
                    uint8_t* visited_dev, uint8_t* y_dev, int64_t* new_counts, int64_t cap, int64_t* passes,
                    void* stream);
@@ -509,8 +512,11 @@ gcs_status gcs_profile_end(gcs_device* d, float* launch_ms, int64_t cap, int64_t
  * environment at gcs_upload makes it a cooperative launch, for devices shared with
  * long-running kernels) waits at a grid-wide barrier with a bounded wait
  * (about a second), and flags the sweep instead of hanging if its
- * workgroups were not all resident.  GCS_ESTATE (and the flag cleared) if
- * so, GCS_OK otherwise. */
+ * workgroups were not all resident.  A flagged sweep leaves y poisoned (NaN
+ * for floating-point policies, 0xFF bytes for Boolean, INT64_MIN for int64),
+ * and the flag marks only that sweep: later sweeps wait at their barriers as
+ * usual.  GCS_ESTATE (and the flag cleared) if a sweep since the last check
+ * was flagged, GCS_OK otherwise. */
 gcs_status gcs_device_check(gcs_device* d, void* stream);
 
 void gcs_free_device(gcs_device* d);
