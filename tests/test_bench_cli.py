@@ -35,3 +35,52 @@ def test_kernel_source_hash(tmp_path, monkeypatch):
         hashes[name] = bench.kernel_source_hash()
     assert hashes["base"] == hashes["comment"] == hashes["spaces"]
     assert hashes["code"] != hashes["base"]
+
+
+def _counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_l2_record_and_bound(tmp_path, monkeypatch):
+    """summarize_l2 averages TCC_HIT_sum + TCC_MISS_sum over the dispatches of
+    the named kernel only (level_kernel is not level_group_kernel or
+    level_batch_kernel), records them under kernel:workload with the source
+    hash, and l2_bound turns them into a rate against the request peak; a
+    changed kernel source voids the record."""
+    sys.path.insert(0, ROOT)
+    import bench
+    d = tmp_path / "pmc"
+    d.mkdir()
+    rows = []
+    for i in range(4):  # level_kernel: 900 + 100 i hits, 100 misses
+        rows += [(i, "void gcs::level_kernel<gcs::PolPlusF32>(gcs::LevelArgs)", "TCC_HIT_sum", 900 + 100 * i),
+                 (i, "void gcs::level_kernel<gcs::PolPlusF32>(gcs::LevelArgs)", "TCC_MISS_sum", 100)]
+    rows += [(10, "void gcs::level_batch_kernel<gcs::PolPlusF32, 4, false>(x)", "TCC_HIT_sum", 1e9),
+             (11, "void gcs::level_group_kernel<gcs::PolPlusF32>(x)", "TCC_MISS_sum", 1e9)]
+    _counter_csv(d / "run_counter_collection.csv", rows)
+    src = tmp_path / "k.hpp"
+    src.write_text("int a;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "L2_FILE", str(tmp_path / "l2.json"))
+    bench.summarize_l2(str(d), str(tmp_path / "out.md"), "level_kernel", "wl", ["cmd"])
+    b = bench.l2_bound("level_kernel", "wl", launch_avg_us=1.0)
+    assert b["requests_per_launch"] == 1150.0  # mean of 1000, 1100, 1200, 1300
+    assert abs(b["hit_rate"] - 4200 / 4600) < 1e-12
+    assert abs(b["achieved"] - 1150.0 / 1e-6 / 1e9) < 1e-9 and b["unit"] == "G requests/s"
+    assert abs(b["frac"] - b["achieved"] / bench.L2_REQ_PEAK_G) < 1e-12
+    assert bench.l2_bound("level_kernel", "other", 1.0) is None
+    src.write_text("int b;\n")
+    assert bench.l2_bound("level_kernel", "wl", 1.0) is None
+
+
+def test_grammar_bytes_formula():
+    """(8 N_bin + 4 N_pt + 8 |C| + 4 alpha): the bytes of the grammar a sweep
+    streams."""
+    sys.path.insert(0, ROOT)
+    import bench
+    st = {"n_rules": 10, "n_passthrough": 3, "c_len": 7, "n_terminals": 5}
+    assert bench.grammar_bytes(st) == 8 * 10 + 4 * 3 + 8 * 7 + 4 * 5
