@@ -227,6 +227,9 @@ def bench_batched(torch, gcs, leg, synth, dev, lay, rp, col, val, spec, elem, xd
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "kernels.hpp")
+# the layout (node order, slices, emission groups) decides the kernels' access
+# pattern as much as their code does
+LAYOUT_SOURCE = os.path.join(ROOT, "grammar_compressed_sparse_amd", "csrc", "builder.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
 GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_group_kernel_traffic.json")
 L2_FILE = os.path.join(ROOT, "profiles", "l2_requests.json")
@@ -301,17 +304,20 @@ def summarize_l2(hit_dir, out_md, kernel, workload, commands):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the device source without its comments and with whitespace
-    runs collapsed: a comment edit keeps the recorded counter profile valid,
-    any change to the code voids it."""
+    """Hash of the device source and of the layout code, without their
+    comments and with whitespace runs collapsed: a comment edit keeps the
+    recorded counter profile valid, any change to the code voids it."""
     import hashlib
     import re
-    with open(KERNEL_SOURCE) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    src = " ".join(src.split())
-    return hashlib.sha256(src.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, LAYOUT_SOURCE):
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def copy_achievable_gbs(torch, mib=2048, reps=10):

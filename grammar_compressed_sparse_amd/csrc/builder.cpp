@@ -287,6 +287,65 @@ gcs_status finish_layout(Grammar& g, int threads)
         g.lv[k].pt_off = pt_off[k];
         co += cnt_lvl[k];
     }
+    // the arena offset of nonterminal w as read from level j (w alive at
+    // level j: its own level or a carried copy)
+    auto slot = [&](int32_t w, int j) -> int32_t {
+        const Level& P = g.lv[j];
+        if (g.lvl[w] == j) return (int32_t)(P.base + pos[w]);
+        return (int32_t)(P.base + P.nb + ptpos[ptidx[w] + (j - g.lvl[w] - 1)]);
+    };
+    // Within a run of equal first column, binary nodes are ordered by the
+    // arena offset of their right child and pass-through nodes by that of
+    // their source, level by level upwards (so the level below is final).
+    // Left children share the parent's first column, so they stay as close
+    // as before; a wavefront's right children, which start where the left
+    // child's expansion ends, come from fewer cache lines.
+    {
+        auto refine = [&](int32_t* list, int64_t n, auto&& key) {
+            const int64_t nch = std::max<int64_t>(1, n / 65536);
+            parallel_for(nch, threads, [&](int64_t c) {
+                // this chunk's runs: those that start inside [n c / nch, n (c+1) / nch)
+                auto run_start = [&](int64_t i) {
+                    while (i < n && i > 0 && fc[list[i - 1]] == fc[list[i]]) ++i;
+                    return i;
+                };
+                const int64_t s = run_start(n * c / nch), e = run_start(n * (c + 1) / nch);
+                std::vector<std::pair<int64_t, int32_t>> buf;
+                for (int64_t i = s; i < e;) {
+                    int64_t j = i + 1;
+                    while (j < e && fc[list[j]] == fc[list[i]]) ++j;
+                    if (j - i > 1) {
+                        buf.clear();
+                        for (int64_t t = i; t < j; ++t) buf.emplace_back(key(list[t]), list[t]);
+                        std::stable_sort(buf.begin(), buf.end(),
+                                         [](const auto& p, const auto& q) { return p.first < q.first; });
+                        for (int64_t t = i; t < j; ++t) list[t] = buf[(size_t)(t - i)].second;
+                    }
+                    i = j;
+                }
+            });
+        };
+        for (int k = 1; k <= L; ++k) {
+            int32_t* b = order.data() + lvl_start[k];
+            refine(b, cnt_lvl[k], [&](int32_t v) -> int64_t {
+                const int32_t r = g.rb[v];
+                return r < alpha ? r : slot(r - (int32_t)alpha, k - 1);
+            });
+            parallel_for(std::max<int64_t>(1, (cnt_lvl[k] + 65535) / 65536), threads, [&](int64_t c) {
+                for (int64_t p = c * 65536; p < std::min(cnt_lvl[k], (c + 1) * 65536); ++p) pos[b[p]] = (int32_t)p;
+            });
+            const int64_t np = pt_off[k + 1] - pt_off[k];
+            int32_t* pl = ptflat.data() + pt_off[k];
+            refine(pl, np, [&](int32_t v) -> int64_t { return slot(v, k - 1); });
+            parallel_for(std::max<int64_t>(1, (np + 65535) / 65536), threads, [&](int64_t c) {
+                for (int64_t p = c * 65536; p < std::min(np, (c + 1) * 65536); ++p) {
+                    const int32_t v = pl[p];
+                    ptpos[ptidx[v] + (k - g.lvl[v] - 1)] = (int32_t)p;
+                }
+            });
+        }
+    }
+    tr.mark("order within first-column runs");
 
     // column slices: weighted quantiles of the first column, every rule
     // weighted by the level slots it occupies (itself plus its chain)
@@ -332,13 +391,7 @@ gcs_status finish_layout(Grammar& g, int threads)
     }
 
     tr.mark("column slices");
-    // children and pass-through sources: the arena offset of nonterminal w as
-    // read from level j (w alive at level j: its own level or a carried copy)
-    auto slot = [&](int32_t w, int j) -> int32_t {
-        const Level& P = g.lv[j];
-        if (g.lvl[w] == j) return (int32_t)(P.base + pos[w]);
-        return (int32_t)(P.base + P.nb + ptpos[ptidx[w] + (j - g.lvl[w] - 1)]);
-    };
+    // children and pass-through sources (slot above)
     g.child.resize((size_t)2 * R);
     g.ptsrc.resize((size_t)g.pt_total);
     parallel_for(nch_r, threads, [&](int64_t c) {

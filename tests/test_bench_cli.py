@@ -1,7 +1,7 @@
 """Host-side checks of bench.py's contract (no device): more than one GPU is
-refused with a message and no result line, and the kernel-source hash that
-decides whether recorded hardware-counter traffic still applies ignores
-comments and whitespace but not code."""
+refused with a message and no result line, and the source hash that decides
+whether recorded hardware-counter figures still apply (kernels and layout)
+ignores comments and whitespace but not code."""
 import os
 import subprocess
 import sys
@@ -33,6 +33,15 @@ def test_kernel_source_hash(tmp_path, monkeypatch):
         f.write_text(text)
         monkeypatch.setattr(bench, "KERNEL_SOURCE", str(f))
         hashes[name] = bench.kernel_source_hash()
+    # the layout source counts as well
+    lay = tmp_path / "layout.cpp"
+    lay.write_text("int order;\n")
+    monkeypatch.setattr(bench, "LAYOUT_SOURCE", str(lay))
+    before = bench.kernel_source_hash()
+    lay.write_text("int order = 1;\n")
+    assert bench.kernel_source_hash() != before
+    lay.write_text("int order;  // comment\n")
+    assert bench.kernel_source_hash() == before
     assert hashes["base"] == hashes["comment"] == hashes["spaces"]
     assert hashes["code"] != hashes["base"]
 
@@ -65,6 +74,7 @@ def test_l2_record_and_bound(tmp_path, monkeypatch):
     src = tmp_path / "k.hpp"
     src.write_text("int a;\n")
     monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "LAYOUT_SOURCE", str(src))
     monkeypatch.setattr(bench, "L2_FILE", str(tmp_path / "l2.json"))
     bench.summarize_l2(str(d), str(tmp_path / "out.md"), "level_kernel", "wl", ["cmd"])
     b = bench.l2_bound("level_kernel", "wl", launch_avg_us=1.0)
