@@ -276,8 +276,11 @@ def summarize_l2(hit_dir, out_md, kernel, workload, commands):
     for r in csv.DictReader(open(fs[0])):
         if f"gcs::{kernel}<" not in r["Kernel_Name"]:
             continue
+        name = r["Counter_Name"]
+        if not name.startswith(("TCC_HIT", "TCC_MISS")):
+            continue  # other counters of the same pass
         h = per.setdefault(int(r["Dispatch_Id"]), [0.0, 0.0])
-        h[0 if r["Counter_Name"].startswith("TCC_HIT") else 1] += float(r["Counter_Value"])
+        h[0 if name.startswith("TCC_HIT") else 1] += float(r["Counter_Value"])
     v = np.array(list(per.values()))
     req = v.sum(axis=1)
     rec = {"source_sha256": kernel_source_hash(), "kernel": kernel, "workload": workload,
@@ -297,7 +300,7 @@ def summarize_l2(hit_dir, out_md, kernel, workload, commands):
                   f"dispatch: mean {rec['requests_per_launch'] / 1e6:.2f} M, median {np.median(req) / 1e6:.2f} M, "
                   f"max {req.max() / 1e6:.2f} M; hit rate {rec['hit_rate']:.3f}",
               f"- request peak: {L2_REQ_PEAK_G:.1f} G requests/s (8 XCDs x 16 channels x 2.4 GHz)",
-              f"- kernel source sha256[:16] = {rec['source_sha256']}"]
+              f"- kernel and layout source sha256[:16] = {rec['source_sha256']}"]
     with open(out_md, "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -425,7 +428,8 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     lines += sweep_breakdown(rows(kt_dir, "*kernel_trace.csv"), "PolPlusF32")
     rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20}
     for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
-        cc = rows(d, "*counter_collection.csv")
+        cname = "FETCH_SIZE" if tag == "fetch" else "WRITE_SIZE"
+        cc = [r for r in rows(d, "*counter_collection.csv") if r.get("Counter_Name", cname) == cname]
         # the calibration copies: the first five large copy dispatches of the
         # run (issued before anything else; later large copies, such as the
         # achievable-bandwidth copy, are not of the calibrated size)
@@ -444,7 +448,8 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
     # and the summed bytes and kernel time over all of its dispatches
     bt = {}
     for tag, d, sc in (("fetch", fetch_dir, scale_f), ("write", write_dir, scale_w)):
-        cc = rows(d, "*counter_collection.csv")
+        cname = "FETCH_SIZE" if tag == "fetch" else "WRITE_SIZE"
+        cc = [r for r in rows(d, "*counter_collection.csv") if r.get("Counter_Name", cname) == cname]
         v = [float(r["Counter_Value"]) * 1024 * sc for r in cc if "level_batch_kernel" in r["Kernel_Name"]]
         bt[tag] = (sum(v), len(v))
     kt_batch = [r for r in stats if "level_batch_kernel" in r["Name"]]
@@ -462,7 +467,7 @@ def summarize_rocprof(kt_dir, fetch_dir, write_dir, out_md, copy_mib, commands):
               f"- level_kernel, mean over {rec['fetch_launches']} dispatches: FETCH "
               f"{rec['fetch_bytes_per_launch'] / 1e6:.2f} MB, WRITE {rec['write_bytes_per_launch'] / 1e6:.2f} MB, "
               f"traffic {rec['traffic_bytes_per_launch'] / 1e6:.2f} MB per launch (scaled)",
-              f"- kernel source sha256[:16] = {rec['source_sha256']}"]
+              f"- kernel and layout source sha256[:16] = {rec['source_sha256']}"]
     if "batch_traffic_GBs" in rec:
         lines += [f"- level_batch_kernel (batched sweeps of the same run): {rec['batch_traffic_bytes_per_dispatch'] / 1e6:.2f} "
                   f"MB of HBM traffic per dispatch on average, {rec['batch_kernel_avg_ns'] / 1e3:.1f} us average "
@@ -549,7 +554,9 @@ def summarize_group_counters(fetch_dir, write_dir, out_md, copy_mib, commands, b
 
     rec = {"source_sha256": kernel_source_hash(), "copy_bytes": copy_mib << 20, "kernel": "level_group_kernel"}
     for tag, d in (("fetch", fetch_dir), ("write", write_dir)):
-        cc = sorted(rows(d, "*counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+        cname = "FETCH_SIZE" if tag == "fetch" else "WRITE_SIZE"
+        cc = sorted((r for r in rows(d, "*counter_collection.csv") if r.get("Counter_Name", cname) == cname),
+                    key=lambda r: int(r["Dispatch_Id"]))
         copies = [float(r["Counter_Value"]) for r in cc if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
         big = [v for v in copies if v > 0.25 * copy_mib * 1024][:5]
         lvl = [float(r["Counter_Value"]) * 1024 for r in cc if "level_group_kernel" in r["Kernel_Name"]]
@@ -577,7 +584,7 @@ def summarize_group_counters(fetch_dir, write_dir, out_md, copy_mib, commands, b
         rec["algorithmic_bytes_per_launch"] = alg
         lines.append(f"- algorithmic bytes per launch (the bench's formula): {alg / 1e6:.1f} MB; traffic / "
                      f"algorithmic = {rec['traffic_bytes_per_launch'] / alg:.2f}")
-    lines.append(f"- kernel source sha256[:16] = {rec['source_sha256']}")
+    lines.append(f"- kernel and layout source sha256[:16] = {rec['source_sha256']}")
     with open(GROUP_TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     with open(out_md, "w") as fo:
