@@ -264,6 +264,30 @@ def l2_bound(kernel, workload, launch_avg_us):
             "peak_basis": "8 XCDs x 16 L2 channels x 2.4 GHz, one request per channel per clock"}
 
 
+def filter_counters(in_dir, out_dir, kernel, n_copies=20):
+    """Reduce a counter run's CSV to what the summaries read: every row of the
+    dispatches of gcs::kernel and of the first n_copies copy dispatches (the
+    calibration copies are issued first).  A run that builds many grammars
+    makes hundreds of thousands of other dispatches, far more than the
+    summaries need."""
+    import csv
+    import glob
+    fs = glob.glob(os.path.join(in_dir, "**", "*counter_collection.csv"), recursive=True)
+    os.makedirs(out_dir, exist_ok=True)
+    with open(fs[0]) as f:
+        rd = csv.DictReader(f)
+        rows = list(rd)
+        fields = rd.fieldnames
+    copies = sorted({int(r["Dispatch_Id"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")})
+    keep_copy = set(copies[:n_copies])
+    out = [r for r in rows if f"gcs::{kernel}<" in r["Kernel_Name"] or int(r["Dispatch_Id"]) in keep_copy]
+    with open(os.path.join(out_dir, "filtered_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(out)
+    print(f"{len(out)} of {len(rows)} rows kept")
+
+
 def summarize_l2(hit_dir, out_md, kernel, workload, commands):
     """L2 requests (TCC_HIT_sum + TCC_MISS_sum) per dispatch of gcs::kernel
     from one --pmc TCC_HIT_sum TCC_MISS_sum run: the mean over the run's
@@ -1044,6 +1068,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-group-trace":
         # bench.py --summarize-group-trace KT_DIR OUT_MD TITLE BENCH_LOG "command" ...
         summarize_group_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[6:], bench_log=sys.argv[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--filter-counters":
+        # bench.py --filter-counters IN_DIR OUT_DIR KERNEL
+        filter_counters(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-l2":
         # bench.py --summarize-l2 HIT_DIR OUT_MD KERNEL WORKLOAD "command" ...
