@@ -212,12 +212,7 @@ constexpr int kBlock = 256;
 // keeps one per lane so that its grid still covers the device
 constexpr int kLeafItems = 4;
 constexpr int64_t kLeafMultiMin = (int64_t)kLeafItems * kBlock * 2048;
-constexpr int kBinItems = 4;  // binary (or pass-through) nodes per lane: independent gathers in flight
-// the same in a launch over many column groups at once (levels that wide
-// gain from more gathers per lane; one grammar's narrow levels lose from
-// fewer workgroups), and per row slot of a batched launch
-constexpr int kGroupBinItems = 8;
-constexpr int kBatchItems = 4;
+constexpr int kBinItems = 4;  // binary nodes per lane (independent gathers in flight)
 constexpr int kEmitItems = 2;  // roots per emission lane loaded before the first combine
 constexpr int kTailBlock = 1024;  // lanes per workgroup of the persistent tail
 constexpr size_t kFlatLdsMax = 160 * 1024;  // LDS cap of the tail's single-workgroup phase
@@ -344,7 +339,7 @@ __device__ __forceinline__ typename P::A team_combine(typename P::A s, int32_t t
 // the part are clamped to its last element, which exists because a block
 // with no element returns first), so a lane keeps all of its independent
 // gathers in flight at once; only the stores and the combines are masked.
-template <class P, int NI = kBinItems>
+template <class P>
 __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32_t tid,
                                             typename P::A* __restrict__ arena, typename P::A* __restrict__ acc)
 {
@@ -352,19 +347,19 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     const int32_t part_bin = a.pb_bin * kSlices, part_pt = a.pb_pt * kSlices;
     if (b < part_bin) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
-        const int32_t first = a.bsl[x] + i * (kBlock * NI);
+        const int32_t first = a.bsl[x] + i * (kBlock * kBinItems);
         if (first >= end) return;
         const int32_t t0 = first + tid;
-        int2 c[NI];
+        int2 c[kBinItems];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) c[u] = a.child[min(t0 + u * kBlock, end - 1)];
-        A v[NI];
+        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * kBlock, end - 1)];
+        A v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) v[u] = P::comb(fetch<P>(arena, c[u].x, a.alpha), fetch<P>(arena, c[u].y, a.alpha));
+        for (int u = 0; u < kBinItems; ++u) v[u] = P::comb(fetch<P>(arena, c[u].x, a.alpha), fetch<P>(arena, c[u].y, a.alpha));
 #pragma unroll
-        for (int u = 0; u < NI; ++u) issue_before(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
-        for (int u = 0; u < NI; ++u) {
+        for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
             if (t < end) arena[a.cur + t] = v[u];
         }
@@ -373,19 +368,19 @@ __device__ __forceinline__ void level_block(const LevelArgs& a, int32_t b, int32
     b -= part_bin;
     if (b < part_pt) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
-        const int32_t first = a.psl[x] + i * (kBlock * NI);
+        const int32_t first = a.psl[x] + i * (kBlock * kBinItems);
         if (first >= end) return;
         const int32_t t0 = first + tid;
-        int32_t src[NI];
+        int32_t src[kBinItems];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) src[u] = a.ptsrc[min(t0 + u * kBlock, end - 1)];
-        A v[NI];
+        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * kBlock, end - 1)];
+        A v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) v[u] = fetch<P>(arena, src[u], a.alpha);
+        for (int u = 0; u < kBinItems; ++u) v[u] = fetch<P>(arena, src[u], a.alpha);
 #pragma unroll
-        for (int u = 0; u < NI; ++u) issue_before(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before(v[u]);
 #pragma unroll
-        for (int u = 0; u < NI; ++u) {
+        for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * kBlock;
             if (t < end) arena[a.cur + a.nb + t] = v[u];
         }
@@ -975,7 +970,7 @@ __global__ __launch_bounds__(kBlock) void level_group_kernel(const GroupEntry* _
     auto* arena = (typename P::A*)e.arena;
     auto* acc = (typename P::A*)e.acc;
     if (a.stream && b >= nodes) stream_block<P>(a, b - nodes, threadIdx.x, arena, acc);
-    else level_block<P, kGroupBinItems>(a, b, threadIdx.x, arena, acc);
+    else level_block<P>(a, b, threadIdx.x, arena, acc);
 }
 
 // y[r] = y0 (+) s_0 (+) s_1 ... with s_g the combination of group g's eight
@@ -1103,19 +1098,19 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     const int32_t part_bin = ba.pb_bin * kSlices, part_pt = ba.pb_pt * kSlices;
     if (b < part_bin) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.bsl[x + 1];
-        const int32_t first = a.bsl[x] + i * (per * kBatchItems);
+        const int32_t first = a.bsl[x] + i * (per * kBinItems);
         if (first >= end) return;
         const int32_t t0 = first + slot;
-        int2 c[kBatchItems];
+        int2 c[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
-        R v[kBatchItems];
+        for (int u = 0; u < kBinItems; ++u) c[u] = a.child[min(t0 + u * per, end - 1)];
+        R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) v[u] = comb_row<P, VW>(row_of(c[u].x), row_of(c[u].y));
+        for (int u = 0; u < kBinItems; ++u) v[u] = comb_row<P, VW>(row_of(c[u].x), row_of(c[u].y));
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) issue_before_row(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) {
+        for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
             if (t < end && live) arena[(int64_t)(a.cur + t - ba.tbase) * W + vw] = v[u];
         }
@@ -1124,19 +1119,19 @@ __global__ __launch_bounds__(kBlock) void level_batch_kernel(BatchArgs ba, typen
     b -= part_bin;
     if (b < part_pt) {
         const int32_t x = b % kSlices, i = b / kSlices, end = a.psl[x + 1];
-        const int32_t first = a.psl[x] + i * (per * kBatchItems);
+        const int32_t first = a.psl[x] + i * (per * kBinItems);
         if (first >= end) return;
         const int32_t t0 = first + slot;
-        int32_t src[kBatchItems];
+        int32_t src[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
-        R v[kBatchItems];
+        for (int u = 0; u < kBinItems; ++u) src[u] = a.ptsrc[min(t0 + u * per, end - 1)];
+        R v[kBinItems];
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) v[u] = row_of(src[u]);
+        for (int u = 0; u < kBinItems; ++u) v[u] = row_of(src[u]);
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) issue_before_row(v[u]);
+        for (int u = 0; u < kBinItems; ++u) issue_before_row(v[u]);
 #pragma unroll
-        for (int u = 0; u < kBatchItems; ++u) {
+        for (int u = 0; u < kBinItems; ++u) {
             const int32_t t = t0 + u * per;
             if (t < end && live) arena[(int64_t)(a.cur + a.nb + t - ba.tbase) * W + vw] = v[u];
         }

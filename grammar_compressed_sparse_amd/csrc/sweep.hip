@@ -1092,8 +1092,8 @@ gcs_status run_sweep_batch(gcs_device* d, const void* xv, void* yv, int32_t B, v
             mp = std::max<int64_t>(mp, ba.a.psl[x + 1] - ba.a.psl[x]);
             mg = std::max<int64_t>(mg, ba.a.gsl[x + 1] - ba.a.gsl[x]);
         }
-        ba.pb_bin = ceil_div(mb, per * kBatchItems);
-        ba.pb_pt = ceil_div(mp, per * kBatchItems);
+        ba.pb_bin = ceil_div(mb, per * kBinItems);
+        ba.pb_pt = ceil_div(mp, per * kBinItems);
         ba.pb_emit = ceil_div(mg, per);
         const int64_t grid = (int64_t)kSlices * (ba.pb_bin + ba.pb_pt + ba.pb_emit);
         if (grid > 0) {
@@ -1954,19 +1954,11 @@ gcs_status group_plan(gcs_device* const* devs, int32_t n, GroupPlan& pl)
             if (nb == 0) continue;
             gcs::GroupEntry e{};
             e.a = a;
-            // the group launch gives each lane kGroupBinItems nodes
-            int64_t mb = 0, mp = 0;
-            for (int x = 0; x < gcs::kSlices; ++x) {
-                mb = std::max<int64_t>(mb, a.bsl[x + 1] - a.bsl[x]);
-                mp = std::max<int64_t>(mp, a.psl[x + 1] - a.psl[x]);
-            }
-            e.a.pb_bin = (int32_t)gcs::ceil_div(mb, gcs::kBlock * gcs::kGroupBinItems);
-            e.a.pb_pt = (int32_t)gcs::ceil_div(mp, gcs::kBlock * gcs::kGroupBinItems);
             e.arena = d->arena;
             e.acc = d->acc;
             e.block0 = (int32_t)vb;
             pl.ents.push_back(e);
-            vb += gcs::vblocks(e.a);
+            vb += nb;
         }
         if (vb >= (int64_t)INT32_MAX) {
             gcs::set_error("a group launch exceeds 2^31 workgroups");
