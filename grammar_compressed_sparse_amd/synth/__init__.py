@@ -61,10 +61,6 @@ def _load():
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         lib.synth_genotype_block.argtypes = [ctypes.POINTER(_Geno), I64, I64, I64, I64, P, P, P, P]
         lib.synth_genotype_block.restype = ctypes.c_int
-        lib.synth_genotype_begin.argtypes = [ctypes.POINTER(_Geno), I64, I64, I64, I64, P]
-        lib.synth_genotype_begin.restype = ctypes.c_void_p
-        lib.synth_genotype_finish.argtypes = [ctypes.c_void_p, P, P, P]
-        lib.synth_genotype_finish.restype = ctypes.c_int
         lib.synth_site_maf.argtypes = [ctypes.POINTER(_Geno), I64]
         lib.synth_site_maf.restype = ctypes.c_double
         lib.synth_graph_degree.argtypes = [ctypes.POINTER(_Graph), I64]
@@ -116,31 +112,6 @@ def genotype(spec: GenotypeSpec, row0: int = 0, nrows: int | None = None, col0: 
              ncols: int | None = None):
     """CSR block of the genotype matrix: rows [row0, row0+nrows), columns
     [col0, col0+ncols) (absolute column indices).  Returns (row_ptr, col, val)."""
-    lib = _load()
-    nrows = spec.n_rows - row0 if nrows is None else nrows
-    ncols = spec.n_cols - col0 if ncols is None else ncols
-    if not (0 <= row0 and row0 + nrows <= spec.n_rows and 0 <= col0 and col0 + ncols <= spec.n_cols):
-        raise ValueError("block outside the matrix")
-    P = spec._c()
-    cnt = np.zeros(max(nrows, 1), np.int64)
-    # one pass over the haplotypes: the library keeps the entries until the
-    # arrays exist (genotype_two_pass gives the same arrays)
-    h = lib.synth_genotype_begin(ctypes.byref(P), row0, nrows, col0, ncols, _p(cnt))
-    if not h:
-        raise MemoryError("genotype generator: allocation failed")
-    row_ptr = np.zeros(nrows + 1, np.int64)
-    np.cumsum(cnt[:nrows], out=row_ptr[1:])
-    nnz = int(row_ptr[-1])
-    col = np.empty(max(nnz, 1), np.int32)
-    val = np.empty(max(nnz, 1), np.int8)
-    lib.synth_genotype_finish(h, _p(row_ptr), _p(col), _p(val))
-    return row_ptr, col[:nnz], val[:nnz]
-
-
-def genotype_two_pass(spec: GenotypeSpec, row0: int = 0, nrows: int | None = None, col0: int = 0,
-                      ncols: int | None = None):
-    """genotype() by two passes (count, then fill), each generating every
-    row's haplotypes; kept to check the one-pass form against."""
     lib = _load()
     nrows = spec.n_rows - row0 if nrows is None else nrows
     ncols = spec.n_cols - col0 if ncols is None else ncols

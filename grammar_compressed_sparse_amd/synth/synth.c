@@ -193,131 +193,6 @@ int synth_genotype_block(const synth_geno_params* P, int64_t row0, int64_t nrows
     return failed ? -1 : 0;
 }
 
-/*
- * One-pass form of the same block: every row's haplotypes are generated once
- * (a haplotype walks its segments from column 0, so far-right blocks cost the
- * walk again in each pass of the two-pass form).  Rows are split into one
- * contiguous range per thread; each range keeps its rows' (column, value)
- * entries in a buffer of its own.
- *   synth_genotype_begin: generates, fills row_nnz[0..nrows), returns a
- *     handle (NULL on allocation failure);
- *   synth_genotype_finish: copies the entries to col/val at row_ptr (row_ptr
- *     relative to this block, as pass 2 above) and frees the handle; returns
- *     0, or -1 if h is NULL.
- * The output is the two-pass form's, entry for entry.
- */
-typedef struct {
-    int64_t r0, r1;     /* rows [r0, r1) of the block */
-    int64_t n, cap;     /* entries held, capacity     */
-    int32_t* col;
-    int8_t* val;
-} geno_range;
-
-typedef struct {
-    int nr;
-    geno_range* r;
-} geno_pending;
-
-void* synth_genotype_begin(const synth_geno_params* P, int64_t row0, int64_t nrows, int64_t col0, int64_t ncols,
-                           int64_t* row_nnz)
-{
-    geno_pending* g = (geno_pending*)calloc(1, sizeof(geno_pending));
-    if (!g) return NULL;
-    int nt = 1;
-#ifdef _OPENMP
-    nt = omp_get_max_threads();
-#endif
-    if (nrows <= 0 || ncols <= 0) {
-        for (int64_t i = 0; i < nrows; ++i) row_nnz[i] = 0;
-        return g;
-    }
-    if (nt > nrows) nt = (int)nrows;
-    g->nr = nt;
-    g->r = (geno_range*)calloc((size_t)nt, sizeof(geno_range));
-    uint8_t* ftab = g->r ? founder_table(P, col0, ncols) : NULL;
-    if (!ftab) {
-        free(g->r);
-        free(g);
-        return NULL;
-    }
-    int failed = 0;
-#pragma omp parallel num_threads(nt)
-    {
-        int t = 0;
-#ifdef _OPENMP
-        t = omp_get_thread_num();
-#endif
-        geno_range* R = &g->r[t];
-        R->r0 = nrows * t / nt;
-        R->r1 = nrows * (t + 1) / nt;
-        uint8_t* h0 = (uint8_t*)malloc((size_t)ncols);
-        uint8_t* h1 = (uint8_t*)malloc((size_t)ncols);
-        int ok = h0 && h1;
-        for (int64_t i = R->r0; ok && i < R->r1; ++i) {
-            int64_t r = row0 + i;
-            haplotype(P, ftab, 2 * r, col0, ncols, h0);
-            haplotype(P, ftab, 2 * r + 1, col0, ncols, h1);
-            if (R->cap - R->n < ncols) {
-                int64_t nc = R->cap ? 2 * R->cap : (R->r1 - R->r0) * ncols / 3 + ncols;
-                if (nc - R->n < ncols) nc = R->n + ncols;
-                int32_t* c2 = (int32_t*)realloc(R->col, (size_t)nc * sizeof(int32_t));
-                if (c2) R->col = c2;
-                int8_t* v2 = c2 ? (int8_t*)realloc(R->val, (size_t)nc) : NULL;
-                if (v2) R->val = v2;
-                if (!c2 || !v2) {
-                    ok = 0;
-                    break;
-                }
-                R->cap = nc;
-            }
-            int64_t o = R->n;
-            for (int64_t j = 0; j < ncols; ++j) {
-                int gv = h0[j] + h1[j];
-                if (gv) { R->col[o] = (int32_t)(col0 + j); R->val[o] = (int8_t)gv; ++o; }
-            }
-            row_nnz[i] = o - R->n;
-            R->n = o;
-        }
-        if (!ok) {
-#pragma omp atomic write
-            failed = 1;
-        }
-        free(h0);
-        free(h1);
-    }
-    free(ftab);
-    if (failed) {
-        for (int t = 0; t < g->nr; ++t) {
-            free(g->r[t].col);
-            free(g->r[t].val);
-        }
-        free(g->r);
-        free(g);
-        return NULL;
-    }
-    return g;
-}
-
-int synth_genotype_finish(void* handle, const int64_t* row_ptr, int32_t* col, int8_t* val)
-{
-    geno_pending* g = (geno_pending*)handle;
-    if (!g) return -1;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int t = 0; t < g->nr; ++t) {
-        geno_range* R = &g->r[t];
-        if (R->n > 0) {
-            const int64_t o = row_ptr[R->r0];
-            memcpy(col + o, R->col, (size_t)R->n * sizeof(int32_t));
-            memcpy(val + o, R->val, (size_t)R->n);
-        }
-        free(R->col);
-        free(R->val);
-    }
-    free(g->r);
-    free(g);
-    return 0;
-}
-
 /* ------------------------------------------------------------------ */
 /* copy-model digraph                                                   */
 /* ------------------------------------------------------------------ */

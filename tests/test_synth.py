@@ -67,21 +67,3 @@ def test_normal_and_sources(synth_mod):
     assert np.array_equal(z[:10], synth_mod.normal(10, 101))
     s = synth_mod.sources(1000, 16, 501)
     assert len(set(s.tolist())) == 16 and s.min() >= 0 and s.max() < 1000
-
-
-def test_genotype_one_pass_equals_two_pass(synth_mod):
-    """The one-pass block generator returns the two-pass generator's arrays,
-    on blocks that start at row or column 0, sit at the far right, hold a
-    single row or column, or are empty."""
-    import numpy as np
-    cases = [(synth_mod.GENOTYPE_512x4096, (0, None, 0, None)),
-             (synth_mod.GENOTYPE_512x4096, (5, 100, 1000, 333)),
-             (synth_mod.GENOTYPE_512x4096, (511, 1, 4095, 1)),
-             (synth_mod.GENOTYPE_512x4096, (0, 0, 0, 10)),
-             (synth_mod.GENOTYPE_512x4096, (0, 10, 0, 0)),
-             (synth_mod.GENOTYPE_200000x2000000, (199_000, 300, 1_990_000, 10_000))]
-    for spec, (r0, nr, c0, nc) in cases:
-        a = synth_mod.genotype(spec, r0, nr, c0, nc)
-        b = synth_mod.genotype_two_pass(spec, r0, nr, c0, nc)
-        for x, y in zip(a, b):
-            assert np.array_equal(x, y), (r0, nr, c0, nc)
