@@ -39,6 +39,7 @@
 
 #include "grammar.hpp"
 #include "rounds.hpp"
+#include "staging.hpp"
 
 namespace gcs {
 namespace gb {
@@ -531,13 +532,13 @@ gcs_status build(const gcs_csr_view* m, const gcs_build_opts* opts, int64_t tabl
     {
         std::vector<int32_t> cb((size_t)std::max<int64_t>(mc, 1), 0);
         for (int64_t j = 0; j < mc; ++j) cb[j] = (int32_t)enc.cbase[j];
-        if (nnz > 0) {
-            e = hipMemcpyAsync(slot, col, 4 * (size_t)nnz, hipMemcpyHostToDevice, st);
-            if (e == hipSuccess && !ones)
-                e = hipMemcpyAsync(flag, val8, (size_t)nnz, hipMemcpyHostToDevice, st);
+        gcs::PinnedStage stage;  // the large host arrays go through pinned buffers
+        e = stage.init();
+        if (e == hipSuccess && nnz > 0) {
+            e = stage.h2d(slot, col, 4 * (size_t)nnz, st);
+            if (e == hipSuccess && !ones) e = stage.h2d(flag, val8, (size_t)nnz, st);
         }
-        if (e == hipSuccess && n > 0)
-            e = hipMemcpyAsync(d_rp, rp, 8 * (size_t)(n + 1), hipMemcpyHostToDevice, st);
+        if (e == hipSuccess && n > 0) e = stage.h2d(d_rp, rp, 8 * (size_t)(n + 1), st);
         if (e == hipSuccess && mc > 0)
             e = hipMemcpyAsync(d_cmask, enc.cmask.data(), 8 * (size_t)mc, hipMemcpyHostToDevice, st);
         if (e == hipSuccess && mc > 0) e = hipMemcpyAsync(d_cbase, cb.data(), 4 * (size_t)mc, hipMemcpyHostToDevice, st);

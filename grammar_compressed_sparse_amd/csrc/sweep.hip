@@ -24,6 +24,7 @@
 
 #include "grammar.hpp"
 #include "kernels.hpp"
+#include "staging.hpp"
 
 // ------------------------------------------------------------ device handle
 
@@ -1325,13 +1326,18 @@ extern "C" gcs_status gcs_upload(const gcs_grammar* h, gcs_policy p, void* gramm
         {im.tcol, g.tcol.data(), g.tcol.size() * 4},
         {im.tval, g.tval.data(), g.tval.size() * 4},    {im.V, vbuf.data(), vbuf.size()},
     };
-    for (const Sec& c : secs) {
-        if (!c.bytes) continue;
-        e = hipMemcpyAsync(base + c.off, c.src, c.bytes, hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return gcs::hip_fail(e, "hipMemcpyAsync (upload)");
+    {
+        gcs::PinnedStage stage;
+        e = stage.init();
+        if (e != hipSuccess) return gcs::hip_fail(e, "hipHostMalloc (upload staging)");
+        for (const Sec& c : secs) {
+            if (!c.bytes) continue;
+            e = stage.h2d(base + c.off, c.src, c.bytes, s);
+            if (e != hipSuccess) return gcs::hip_fail(e, "hipMemcpyAsync (upload)");
+        }
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return gcs::hip_fail(e, "hipStreamSynchronize (upload)");
     }
-    e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return gcs::hip_fail(e, "hipStreamSynchronize (upload)");
 
     auto* d = new gcs_device();
     d->policy = p;
