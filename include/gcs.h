@@ -306,8 +306,9 @@ gcs_status gcs_build_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t nnz
  * matrices: one call per column group).  workspace_dev: caller-owned device
  * memory of gcs_build_workspace_bytes(n_rows, n_cols, nnz, table_entries)
  * bytes, 256-byte aligned, free again when the call returns; the call runs on
- * `stream` and synchronises it several times (twice per RePair round).
- * *out receives a new host grammar on GCS_OK.  GCS_EINVAL (bad input or
+ * `stream` and synchronises it several times (twice per RePair round); the
+ * CSR arrays go through two 16 MiB pinned host buffers that the call
+ * allocates and frees.  *out receives a new host grammar on GCS_OK.  GCS_EINVAL (bad input or
  * options, small or misaligned workspace), GCS_ERANGE (beyond the 31-bit
  * symbol space), GCS_ENOMEM (host memory, or the pair table is too small
  * for the input: pass a larger table_entries), GCS_EHIP. */
@@ -352,7 +353,8 @@ gcs_status gcs_device_layout(const gcs_grammar* g, gcs_policy p, gcs_dev_sizes* 
  * uploads then share the counters, the failure flag of gcs_device_check
  * included.  The grammar object may be freed after this
  * call returns.  The call synchronises `stream`: the copy is complete when it
- * returns. */
+ * returns.  The image goes through two 16 MiB pinned host buffers that the
+ * call allocates and frees (GCS_EHIP if they cannot be had). */
 gcs_status gcs_upload(const gcs_grammar* g, gcs_policy p, void* grammar_dev, size_t grammar_bytes,
                       void* workspace_dev, size_t workspace_bytes, void* stream, gcs_device** out);
 
