@@ -94,3 +94,44 @@ def test_grammar_bytes_formula():
     import bench
     st = {"n_rules": 10, "n_passthrough": 3, "c_len": 7, "n_terminals": 5}
     assert bench.grammar_bytes(st) == 8 * 10 + 4 * 3 + 8 * 7 + 4 * 5
+
+
+def test_group_counters_record_and_filter(tmp_path, monkeypatch):
+    """filter_counters keeps the named kernel's dispatches and the first
+    copies only; summarize_group_counters scales FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) by what the same counter reads for the 1 GiB
+    calibration copies, takes each counter's rows by name (a pass may carry
+    others), and records the mean bytes per launch with the source hash."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "k.hpp"
+    src.write_text("int a;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "LAYOUT_SOURCE", str(src))
+    monkeypatch.setattr(bench, "GROUP_TRAFFIC_FILE", str(tmp_path / "gt.json"))
+    kern = "void gcs::level_group_kernel<gcs::PolPlusF32>(x)"
+    copy = "__amd_rocclr_copyBuffer"
+    # FETCH_SIZE reads half of the copied bytes (scale 2), WRITE_SIZE all of them
+    fetch = [(1, copy, "FETCH_SIZE", 512 * 1024), (2, copy, "FETCH_SIZE", 512 * 1024)]
+    fetch += [(10 + i, kern, "FETCH_SIZE", 1000 + 100 * i) for i in range(3)]
+    fetch += [(100 + i, "void gcs::gb::k_count(x)", "FETCH_SIZE", 9e9) for i in range(50)]
+    write = [(1, copy, "WRITE_SIZE", 1024 * 1024), (1, copy, "TCC_HIT_sum", 5)]
+    write += [(10 + i, kern, "WRITE_SIZE", 400) for i in range(3)]
+    write += [(10 + i, kern, "TCC_MISS_sum", 7e9) for i in range(3)]
+    for name, rows in (("f", fetch), ("w", write)):
+        raw = tmp_path / ("raw_" + name)
+        raw.mkdir()
+        _counter_csv(raw / "x_counter_collection.csv", rows)
+        bench.filter_counters(str(raw), str(tmp_path / name), "level_group_kernel", n_copies=2)
+    import csv
+    kept = list(csv.DictReader(open(tmp_path / "f" / "filtered_counter_collection.csv")))
+    assert {r["Dispatch_Id"] for r in kept} == {"1", "2", "10", "11", "12"}
+    bench.summarize_group_counters(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "out.md"), 1024, ["cmd"],
+                                   [])
+    import json
+    rec = json.load(open(tmp_path / "gt.json"))
+    assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
+    assert abs(rec["fetch_bytes_per_launch"] - 1100 * 1024 * 2.0) < 1e-6
+    assert abs(rec["write_bytes_per_launch"] - 400 * 1024) < 1e-6
+    assert rec["traffic_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["source_sha256"] == bench.kernel_source_hash()
