@@ -368,6 +368,36 @@ def copy_achievable_gbs(torch, mib=2048, reps=10):
     return gbs
 
 
+def random_gather_rates(torch, windows=(1 << 20, 8 << 20, 1 << 30), n=1 << 26, reps=5):
+    """Measured ceiling for gather-bound kernels: 4-byte random gathers per
+    second (torch.take with int64 indices, n per launch) when every run of
+    consecutive outputs reads at random inside one window of `w` bytes of
+    the source, for a few window sizes; HIP events, after one warm-up."""
+    out = {}
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for w in windows:
+        per = w // 4
+        base = (torch.arange(n, device="cuda", dtype=torch.int64) // per) * per % src.numel()
+        idx = base + torch.randint(0, per, (n,), device="cuda", generator=g, dtype=torch.int64)
+        dst = torch.take(src, idx)
+        e0.record()
+        for _ in range(reps):
+            dst = torch.take(src, idx)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[str(w)] = n / (ms * 1e-3) / 1e9
+        del idx, base, dst
+    del src
+    torch.cuda.empty_cache()
+    log("random 4-byte gathers (torch.take): " + ", ".join(f"{int(w) >> 20} MiB windows {r:.0f} G/s"
+                                                         for w, r in out.items()))
+    return out
+
+
 def sweep_breakdown(trace, pol):
     """Lines describing the launches of one sweep of policy `pol` (leaf_kernel
     up to the tail_kernel) in a rocprofv3 kernel trace, averaged over the
@@ -889,6 +919,7 @@ def bench_biobank(args, wl, spec, leg):
                                      f"{el1:.1f} s)"}
         del rp, col, val
     copy_gbs = None if args.calibrate_copy_mib else copy_achievable_gbs(torch)
+    gathers = None if args.calibrate_copy_mib else random_gather_rates(torch)
     traffic = None  # HBM bytes per level_group_kernel launch from the committed counters, if still current
     if fused and not acc64 and args.fuse_batch == 25 and os.path.exists(GROUP_TRAFFIC_FILE):
         with open(GROUP_TRAFFIC_FILE) as f:
@@ -936,7 +967,8 @@ def bench_biobank(args, wl, spec, leg):
                      "copy_achievable_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs if copy_gbs else None,
                      # the L2 record was taken with the default fp32 policy and batch size
                      "second_bound": l2_bound("level_group_kernel", args.workload, span_ms * 1e3 / max(nwide, 1))
-                     if fused and not acc64 and args.fuse_batch == 25 else None},
+                     if fused and not acc64 and args.fuse_batch == 25 else None,
+                     "random_gather_G_per_s_by_window_bytes": gathers},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -1266,6 +1298,7 @@ def main():
 
     # (not in counter runs: its copies would mix with the calibration's)
     copy_gbs = None if args.calibrate_copy_mib else copy_achievable_gbs(torch)
+    gathers = None if args.calibrate_copy_mib else random_gather_rates(torch)
     traffic = None  # HBM bytes per level_kernel launch from the committed counter profile, if still current
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -1325,7 +1358,8 @@ def main():
                      "bytes_per_launch_avg": float(lb.sum() / nwide if nwide > 0 else lb_all.sum()),
                      "bytes_per_sweep": float(lb_all.sum()),
                      "second_bound": l2_bound("level_kernel", args.workload, span_ms * 1e3 / nwide)
-                     if nwide > 0 else None},
+                     if nwide > 0 else None,
+                     "random_gather_G_per_s_by_window_bytes": gathers},
         "cpu_baseline": cpu,
     }
     if os.environ.get("GCS_BENCH_LEVELS"):
